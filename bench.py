@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verifier on one MI355X.
+
+One step = one sd_verify call (row statistics, accept scan, residual/bonus
+sampling, counters) over the ngram workload: B=256 requests, k=4 one-hot
+drafts, V=151936, bf16 target logits resident in HBM.  The metric is verified
+draft positions per second (B*k per call).  Inputs rotate over several
+device copies so that the 256 MB Infinity Cache cannot hold them.
+
+Printed as one JSON line, with
+  roofline      the row-statistics kernel's algorithmic bytes (logits + mask)
+                over its average duration, timed with HIP events recorded
+                around that kernel on the launch stream, against 8 TB/s HBM;
+  cpu_baseline  the CPU oracle timed on the host over the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload ngram]
+  python bench.py --copy-calibration    # plain 1 GiB device copy, for PMC scaling
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec + achieved HBM GB/s (B=256,k=4,V=151936 bf16)"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_ngram_traffic.txt")
+SOURCES = ["rejection_sampling_verification_amd/csrc/sd_verify.hip",
+           "rejection_sampling_verification_amd/csrc/philox.h",
+           "rejection_sampling_verification_amd/csrc/wave.h",
+           "include/sd_verify.h"]
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(digest):
+    """HBM bytes per row-statistics launch from the committed PMC summary,
+    if it was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_digest") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 5}), flush=True)
+
+
+def cpu_baseline(wl, n_requests):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import to_numpy
+    req = list(range(n_requests))
+    host = to_numpy(wl, req)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.sd_verify(host["logits"], host["draft_token_ids"], host["draft_probs"],
+                         host["bitmask"], host["temperature"], seed=wl["seed"],
+                         top_k=host["top_k"], request_ids=req)
+        dt = time.perf_counter() - t0
+    k = host["draft_token_ids"].shape[1]
+    return {"value": n_requests * k / dt, "unit": "verified draft positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_requests} of {wl['logits'].shape[0]} requests of the same workload, "
+                      f"float64 NumPy, one thread, {dt:.2f} s",
+            "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ngram")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--cpu-requests", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this verifier build runs on "
+              "exactly one GPU (requests shard across GPUs with no exchange but a 4-counter sum)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import rejection_sampling_verification_amd as sdv
+    from workloads import algorithmic_bytes, make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    wl = make_workload(args.workload, device=dev)
+    lg = wl["logits"]
+    B, kp1, V = lg.shape
+    k = kp1 - 1
+    copies = [lg] + [lg.clone() for _ in range(max(0, args.copies - 1))]
+    v = sdv.Verifier(B, k, V, lg.dtype, dev)
+    call_args = (wl["draft_token_ids"], wl["draft_probs"], wl["bitmask"], wl["temperature"],
+                 wl["seed"], wl["top_k"])
+
+    for s in range(args.warmup):
+        v(copies[s % len(copies)], *call_args)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # ---- timed region: whole steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(args.steps):
+        v(copies[s % len(copies)], *call_args)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    step_s = max(wall, gpu_ms / 1e3) / args.steps
+    value = B * k / step_s
+    print(f"[bench] timed {args.steps} steps: {step_s * 1e6:.1f} us/step", file=sys.stderr, flush=True)
+
+    # ---- timed region: row-statistics kernel alone, HIP events around it
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in pairs:  # materialise the underlying hipEvents
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for s, (a, b) in enumerate(pairs):
+        v(copies[s % len(copies)], *call_args, row_stats_events=(a.cuda_event, b.cuda_event))
+    torch.cuda.synchronize()
+    k1_ms = sorted(a.elapsed_time(b) for a, b in pairs)
+    k1_avg_s = sum(k1_ms) / len(k1_ms) / 1e3
+    k1_bytes = lg.numel() * lg.element_size() + (
+        wl["bitmask"].numel() * 4 if wl["bitmask"] is not None else 0)
+    achieved = k1_bytes / k1_avg_s / 1e9
+    digest = source_digest()
+    traffic = measured_traffic(digest)
+
+    # ---- one debug call for the flag counts
+    vd = sdv.Verifier(B, k, V, lg.dtype, dev, debug=True)
+    r = vd(lg, *call_args)
+    torch.cuda.synchronize()
+    n_res = int((r.out_num_accepted < k).sum().item()) if wl["draft_probs"] is not None else 0
+    algo = algorithmic_bytes(wl, n_res)
+    flags = [int(f) for f in r.flags.cpu().tolist()]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_requests or B)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={B} k={k} V={V} "
+                               f"{'bf16' if lg.dtype == torch.bfloat16 else 'fp32'} logits, "
+                               f"{'one-hot' if wl['draft_probs'] is None else 'dense'} drafts",
+                   "batch": B, "num_draft": k, "vocab": V, "input_copies": len(copies)},
+        "hbm_gbps_whole_call": algo / step_s / 1e9,
+        "algorithmic_bytes_per_call": algo,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "row_stats", "avg_us": k1_avg_s * 1e6,
+                     "p10_us": k1_ms[len(k1_ms) // 10] * 1e3, "p90_us": k1_ms[(9 * len(k1_ms)) // 10] * 1e3,
+                     "bytes_per_launch": k1_bytes, "source_digest": digest},
+        "cpu_baseline": cpu,
+        "flags": {"accept_boundary": flags[0], "gumbel_near_tie": flags[1]},
+        "gpu_ms_timed_region": gpu_ms,
+        "wall_s_timed_region": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -228,7 +228,7 @@ def _verify_request(l, x, q, allowed, T, top_k, seed, b, block):
 
 
 def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperature=None,
-              seed=0, top_k=None, block=BLOCK, requests=None):
+              seed=0, top_k=None, block=BLOCK, request_ids=None):
     """Verify a batch of drafted requests.
 
     logits:          [B, k+1, V] float (bf16 values given exactly as float32/64)
@@ -238,8 +238,9 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
     temperature:     [B] float; 0 selects the greedy rule
     seed:            64-bit Philox key
     top_k:           [B] integer or None; values <= 0 switch top-k off
-    requests:        optional subset of request indices to evaluate (the rest
-                     keep their fill values and do not enter the counters)
+    request_ids:     optional [B] global request index of each batch entry, used
+                     as b in the Philox counters (for checking a sample of a
+                     larger batch one request at a time); default 0 .. B-1
 
     Returns a dict with out_tokens [B, k+1] (-1 padded), num_accepted [B],
     counters (R, I, D, A), status (OR of request bits), per-request status,
@@ -252,7 +253,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
     T_all = np.asarray(temperature, dtype=np.float64).reshape(B)
     tk_all = np.zeros(B, dtype=np.int64) if top_k is None else \
         np.asarray(top_k, dtype=np.int64).reshape(B)
-    idx = range(B) if requests is None else [int(r) for r in requests]
+    gid = list(range(B)) if request_ids is None else [int(r) for r in request_ids]
 
     out = {
         "out_tokens": np.full((B, k + 1), -1, dtype=np.int64),
@@ -265,7 +266,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
     }
     R = I = A = 0
     status = 0
-    for b in idx:
+    for b in range(B):
         l = logits[b].astype(np.float64)
         if bitmask is None:
             allowed = np.ones((k + 1, V), dtype=bool)
@@ -273,7 +274,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
             allowed = unpack_bitmask(np.asarray(bitmask[b]), V)
         q = None if draft_probs is None else np.asarray(draft_probs[b], dtype=np.float64)
         r = _verify_request(l, x_all[b], q, allowed, float(T_all[b]), int(tk_all[b]),
-                            seed, b, block)
+                            seed, gid[b], block)
         out["out_tokens"][b] = r["tokens"]
         out["num_accepted"][b] = r["num_accepted"]
         out["request_status"][b] = r["status"]

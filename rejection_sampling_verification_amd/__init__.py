@@ -1,0 +1,243 @@
+"""Python binding of the MI355X speculative-decoding verifier (libsdverify.so).
+
+Argument marshalling only: every step of verification runs in the HIP kernels
+behind the C ABI declared in include/sd_verify.h.  PyTorch supplies device
+memory and the current stream.  Importing this package fails loudly when the
+library has not been built (python -m rejection_sampling_verification_amd.build).
+
+Entry points mirror the C ABI names: ``sd_verify``, ``sd_verify_workspace_size``,
+``sd_status_string``, ``sd_rates``; ``Verifier`` keeps the workspace and
+outputs of repeated same-shape calls.
+"""
+import ctypes
+import math
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG_DIR, "libsdverify.so")
+
+SD_OK = 0
+SD_DTYPE_F32 = 0
+SD_DTYPE_BF16 = 1
+SD_MAX_DRAFT = 64
+SD_MAX_VOCAB = 1 << 23
+SD_BLOCK_TOKENS = 2048
+
+SD_STATUS_DRAFT_ID = 1
+SD_STATUS_TEMPERATURE = 2
+SD_STATUS_EMPTY_ROW = 4
+SD_STATUS_BAD_LOGIT = 8
+SD_STATUS_BAD_DRAFT_PROB = 16
+
+# every symbol include/sd_verify.h declares
+EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates")
+
+
+class SdParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_draft", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("logits_dtype", ctypes.c_int),
+        ("top_k", ctypes.c_void_p),
+        ("dbg_row_lse", ctypes.c_void_p),
+        ("dbg_accept_prob", ctypes.c_void_p),
+        ("dbg_request_flags", ctypes.c_void_p),
+        ("dbg_flags", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+        ("row_stats_event_begin", ctypes.c_void_p),
+        ("row_stats_event_end", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(
+            f"{LIBRARY_PATH} is missing: build it with "
+            "`python -m rejection_sampling_verification_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    lib.sd_verify_workspace_size.argtypes = [ctypes.POINTER(SdParams)]
+    lib.sd_verify_workspace_size.restype = ctypes.c_size_t
+    lib.sd_verify.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(SdParams), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    lib.sd_verify.restype = ctypes.c_int
+    lib.sd_status_string.argtypes = [ctypes.c_int]
+    lib.sd_status_string.restype = ctypes.c_char_p
+    lib.sd_rates.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint64,
+                             ctypes.POINTER(ctypes.c_double)]
+    lib.sd_rates.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes handle of libsdverify.so."""
+    return _lib
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return SD_DTYPE_BF16
+    if dt == torch.float32:
+        return SD_DTYPE_F32
+    raise ValueError(f"target_logits must be bfloat16 or float32, got {dt}")
+
+
+def _params(batch, num_draft, vocab, dtype_code):
+    p = SdParams()
+    p.batch, p.num_draft, p.vocab, p.logits_dtype = int(batch), int(num_draft), int(vocab), int(dtype_code)
+    return p
+
+
+def sd_verify_workspace_size(batch, num_draft, vocab, logits_dtype=torch.bfloat16):
+    """Device workspace bytes for these sizes."""
+    return int(_lib.sd_verify_workspace_size(
+        ctypes.byref(_params(batch, num_draft, vocab, _dtype_code(logits_dtype)))))
+
+
+def sd_status_string(code):
+    return _lib.sd_status_string(int(code)).decode()
+
+
+def sd_rates(counters, steps):
+    """(survival D/R, acceptance A/D, yield A/R, mean acceptance length) from
+    R, I, D, A counters; NaN where a denominator is zero."""
+    c = (ctypes.c_uint64 * 4)(*[int(v) for v in counters])
+    out = (ctypes.c_double * 4)()
+    rc = _lib.sd_rates(c, ctypes.c_uint64(int(steps)), out)
+    if rc != SD_OK:
+        raise ValueError(f"sd_rates: {sd_status_string(rc)}")
+    return tuple(out)
+
+
+class VerifyResult(NamedTuple):
+    out_tokens: torch.Tensor          # [B, k+1] int32
+    out_num_accepted: torch.Tensor    # [B] int32
+    out_counters: torch.Tensor        # [4] int64 holding the uint64 R, I, D, A
+    status: torch.Tensor              # [1] int32 holding the uint32 status bits
+    row_lse: Optional[torch.Tensor] = None         # [B, k+1] float64
+    accept_prob: Optional[torch.Tensor] = None     # [B, k] float64
+    request_flags: Optional[torch.Tensor] = None   # [B] int32 (uint32 bits)
+    flags: Optional[torch.Tensor] = None           # [2] int32 (uint32 counts)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Verifier:
+    """Outputs and workspace for repeated calls of one shape.
+
+    Each call overwrites the tensors it returns.
+    """
+
+    def __init__(self, batch, num_draft, vocab, logits_dtype=torch.bfloat16, device=None,
+                 debug=False):
+        dev = torch.device(device) if device is not None else torch.device("cuda")
+        if dev.type != "cuda":
+            raise ValueError("the verifier runs on a HIP device")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.B, self.k, self.V = int(batch), int(num_draft), int(vocab)
+        self.dtype = logits_dtype
+        self.params = _params(self.B, self.k, self.V, _dtype_code(logits_dtype))
+        ws = int(_lib.sd_verify_workspace_size(ctypes.byref(self.params)))
+        dev = self.device
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.workspace_bytes = ws
+        self.out_tokens = torch.empty((self.B, self.k + 1), dtype=torch.int32, device=dev)
+        self.out_num_accepted = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.out_counters = torch.empty(4, dtype=torch.int64, device=dev)
+        self.status = torch.empty(1, dtype=torch.int32, device=dev)
+        self.params.status = self.status.data_ptr()
+        self.debug = debug
+        if debug:
+            self.row_lse = torch.empty((self.B, self.k + 1), dtype=torch.float64, device=dev)
+            self.accept_prob = torch.empty((self.B, self.k), dtype=torch.float64, device=dev)
+            self.request_flags = torch.empty(self.B, dtype=torch.int32, device=dev)
+            self.flags = torch.empty(2, dtype=torch.int32, device=dev)
+            self.params.dbg_row_lse = self.row_lse.data_ptr()
+            self.params.dbg_accept_prob = self.accept_prob.data_ptr()
+            self.params.dbg_request_flags = self.request_flags.data_ptr()
+            self.params.dbg_flags = self.flags.data_ptr()
+
+    def __call__(self, target_logits, draft_token_ids, draft_probs=None, bitmask=None,
+                 temperature=None, seed=0, top_k=None, stream=None, row_stats_events=None):
+        B, k, V, dev = self.B, self.k, self.V, self.device
+        _check(target_logits, "target_logits", self.dtype, (B, k + 1, V), dev)
+        if k > 0 or draft_token_ids is not None:
+            _check(draft_token_ids, "draft_token_ids", torch.int32, (B, k), dev)
+        _check(draft_probs, "draft_probs", torch.float32, (B, k, V), dev)
+        _check(bitmask, "bitmask", torch.int32, (B, k + 1, (V + 31) // 32), dev)
+        if temperature is None:
+            raise ValueError("temperature is required ([B] float32, 0 = greedy)")
+        _check(temperature, "temperature", torch.float32, (B,), dev)
+        _check(top_k, "top_k", torch.int32, (B,), dev)
+        self.params.top_k = None if top_k is None else top_k.data_ptr()
+        if row_stats_events is not None:
+            self.params.row_stats_event_begin, self.params.row_stats_event_end = row_stats_events
+        else:
+            self.params.row_stats_event_begin = self.params.row_stats_event_end = None
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = _lib.sd_verify(
+            _ptr(target_logits), _ptr(draft_token_ids), _ptr(draft_probs), _ptr(bitmask),
+            _ptr(temperature), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+            _ptr(self.out_tokens), _ptr(self.out_num_accepted), _ptr(self.out_counters),
+            ctypes.byref(self.params), ctypes.c_void_p(self.workspace.data_ptr()),
+            ctypes.c_size_t(self.workspace_bytes), ctypes.c_void_p(int(stream)))
+        if rc != SD_OK:
+            raise RuntimeError(f"sd_verify failed: {sd_status_string(rc)} ({rc})")
+        if self.debug:
+            return VerifyResult(self.out_tokens, self.out_num_accepted, self.out_counters,
+                                self.status, self.row_lse, self.accept_prob,
+                                self.request_flags, self.flags)
+        return VerifyResult(self.out_tokens, self.out_num_accepted, self.out_counters, self.status)
+
+
+def sd_verify(target_logits, draft_token_ids, draft_probs=None, bitmask=None, temperature=None,
+              seed=0, top_k=None, debug=False, stream=None):
+    """Verify one batch; returns fresh output tensors (see VerifyResult).
+
+    target_logits [B, k+1, V] bf16/fp32, draft_token_ids [B, k] int32,
+    draft_probs [B, k, V] fp32 or None (one-hot drafts), bitmask
+    [B, k+1, ceil(V/32)] int32 or None, temperature [B] fp32 (0 = greedy),
+    seed (64-bit Philox key), top_k [B] int32 or None.
+    """
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, k+1, V]")
+    B, kp1, V = target_logits.shape
+    v = Verifier(B, kp1 - 1, V, target_logits.dtype, target_logits.device, debug=debug)
+    return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream)
+
+
+def rates_from_counters(counters, steps):
+    """Ratios as a dict (convenience over sd_rates)."""
+    s, a, y, m = sd_rates(counters, steps)
+    nan2none = (lambda v: None if math.isnan(v) else v)
+    return {"survival": nan2none(s), "acceptance": nan2none(a), "yield": nan2none(y),
+            "mean_acceptance_length": nan2none(m)}

@@ -1,0 +1,47 @@
+"""Build the HIP verifier library in-tree for gfx950.
+
+    python -m rejection_sampling_verification_amd.build
+
+compiles csrc/sd_verify.hip into libsdverify.so next to this file.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+SOURCE = os.path.join(PKG_DIR, "csrc", "sd_verify.hip")
+LIBRARY = os.path.join(PKG_DIR, "libsdverify.so")
+ARCH = "gfx950"
+
+
+def hipcc_path():
+    return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def compile_command(output=LIBRARY, extra=()):
+    return [
+        hipcc_path(), "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-shared", "-fPIC",
+        # packed fp32 VALU forms are kept out of every kernel
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        *extra, "-o", output, SOURCE,
+    ]
+
+
+def build_library(verbose=False):
+    tmp = LIBRARY + ".tmp"
+    cmd = compile_command(tmp)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    os.replace(tmp, LIBRARY)
+    if verbose:
+        print("built", LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    build_library(verbose=True)
+    sys.exit(0)

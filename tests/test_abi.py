@@ -1,0 +1,130 @@
+"""The C ABI library loads, exports every symbol include/sd_verify.h declares,
+and its host-only logic behaves (no GPU compute here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(
+        ["sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates"])
+
+
+def test_library_exports_every_declared_symbol():
+    import rejection_sampling_verification_amd as sdv
+    lib = sdv.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(sdv.EXPORTED_SYMBOLS) == _declared_functions()
+
+
+def test_params_struct_layout_matches_header():
+    import rejection_sampling_verification_amd as sdv
+    # 3 x int32 + enum, then 8 pointers
+    assert ctypes.sizeof(sdv.SdParams) == 16 + 8 * 8
+    assert sdv.SdParams.top_k.offset == 16
+
+
+def test_status_strings():
+    import rejection_sampling_verification_amd as sdv
+    assert sdv.sd_status_string(0) == "ok"
+    assert "workspace" in sdv.sd_status_string(-3)
+    assert sdv.sd_status_string(12345) == "unknown status"
+
+
+def test_rates_match_the_pages_example():
+    """fanout, "Work a denominator example" and "Mean acceptance length"."""
+    import rejection_sampling_verification_amd as sdv
+    s, a, y, m = sdv.sd_rates([1000, 200, 800, 600], 100)
+    assert (s, a, y) == pytest.approx((0.8, 0.75, 0.6), abs=1e-15)
+    assert sdv.sd_rates([1000, 0, 1000, 600], 1)[1] == pytest.approx(0.6)
+    assert sdv.sd_rates([1000, 0, 1000, 750], 1)[1] == pytest.approx(0.75)
+    assert sdv.sd_rates([300, 0, 300, 180], 100)[3] == pytest.approx(2.8)
+    r = sdv.sd_rates([0, 0, 0, 0], 0)
+    assert all(math.isnan(v) for v in r)
+    with pytest.raises(ValueError):
+        sdv.sd_rates([10, 2, 9, 1], 1)      # D != R - I
+    with pytest.raises(ValueError):
+        sdv.sd_rates([10, 2, 8, 9], 1)      # A > D
+
+
+def test_rates_agree_with_oracle():
+    import numpy as np
+
+    import oracle
+    import rejection_sampling_verification_amd as sdv
+    rng = np.random.default_rng(0)
+    for _ in range(100):
+        R = int(rng.integers(1, 10**6))
+        I = int(rng.integers(0, R + 1))
+        A = int(rng.integers(0, R - I + 1))
+        steps = int(rng.integers(1, 10**5))
+        o = oracle.sd_rates(R, I, A, steps)
+        g = sdv.sd_rates([R, I, R - I, A], steps)
+        want = [o["survival"], o["acceptance"] if R - I else float("nan"), o["yield"],
+                o["mean_acceptance_length"]]
+        for gv, wv in zip(g, want):
+            assert (math.isnan(gv) and math.isnan(wv)) or gv == pytest.approx(wv, rel=1e-15)
+
+
+def test_workspace_size():
+    import rejection_sampling_verification_amd as sdv
+    assert sdv.sd_verify_workspace_size(0, 4, 100) == 0
+    assert sdv.sd_verify_workspace_size(4, -1, 100) == 0
+    assert sdv.sd_verify_workspace_size(4, 65, 100) == 0
+    assert sdv.sd_verify_workspace_size(4, 4, 0) == 0
+    # rows * blocks * 8 bytes of block statistics, per-request records, a ticket
+    ws = sdv.sd_verify_workspace_size(256, 4, 151936)
+    rows, C = 256 * 5, -(-151936 // 2048)
+    assert ws >= rows * C * 8 + 256 * 32 and ws % 256 == 0
+
+
+def test_host_argument_checks_return_before_any_launch():
+    import rejection_sampling_verification_amd as sdv
+    lib = sdv.library()
+    p = sdv.SdParams()
+    p.batch, p.num_draft, p.vocab, p.logits_dtype = 4, 3, 100, 1
+    nul = ctypes.c_void_p(0)
+    counters = (ctypes.c_uint64 * 4)()
+    # missing params / counters
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, None, nul, 0, nul) == -1
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, nul, ctypes.byref(p), nul, 0, nul) == -1
+    # bad dtype, bad sizes, unsupported sizes
+    p.logits_dtype = 7
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -1
+    p.logits_dtype, p.num_draft = 1, 65
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -2
+    p.num_draft, p.vocab = 3, (1 << 23) + 1
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -2
+    # missing required tensors
+    p.vocab = 100
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -1
+    # workspace too small (all tensors given as fake non-null device addresses)
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.sd_verify(fake, fake, nul, nul, fake, 0, fake, fake, counters, ctypes.byref(p),
+                         fake, 16, nul) == -3
+
+
+def test_package_refuses_to_import_without_the_library(tmp_path, monkeypatch):
+    import importlib.util
+    import shutil
+    pkg_src = os.path.join(ROOT, "rejection_sampling_verification_amd", "__init__.py")
+    dst = tmp_path / "sdv_copy"
+    dst.mkdir()
+    shutil.copy(pkg_src, dst / "__init__.py")
+    spec = importlib.util.spec_from_file_location("sdv_copy", dst / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="missing"):
+        spec.loader.exec_module(mod)

@@ -1,0 +1,254 @@
+"""Parity of the HIP verifier with the oracle on the GPU.
+
+Small and scaled workloads are compared request by request in full; the full
+ngram and structured workloads (the benchmark's shapes and launch
+configuration) are compared on a sample of requests recomputed by the oracle
+one at a time, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity import announce, assert_parity, run_gpu, run_oracle
+from workloads import make_workload, pack_bitmask
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _custom(B, k, V, dtype=torch.bfloat16, dense=True, masked=False, greedy_frac=0.0,
+            std=3.0, density=0.3, seed=0, x_argmax_frac=0.3, integer_logits=False):
+    """Small synthetic case with any shape (inputs only)."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    kp1 = k + 1
+    if integer_logits:
+        lg = torch.randint(-3, 4, (B, kp1, V), generator=g, device=DEV).float()
+    else:
+        lg = torch.randn((B, kp1, V), generator=g, device=DEV) * std
+    lg = lg.to(dtype)
+    allowed = None
+    mask = None
+    if masked:
+        allowed = torch.rand((B, kp1, V), generator=g, device=DEV) < density
+        allowed[..., 0] = True
+        mask = pack_bitmask(allowed)
+    q = None
+    if dense:
+        z = lg[:, :k].float() + torch.randn((B, k, V), generator=g, device=DEV)
+        q = torch.softmax(z, -1).contiguous()
+        x = torch.multinomial(q.reshape(B * k, V), 1, generator=g)[:, 0].reshape(B, k)
+    else:
+        x = torch.randint(0, V, (B, k), generator=g, device=DEV)
+    amax = torch.argmax(lg[:, :k].float(), -1) if k else x
+    pick = torch.rand((B, k), generator=g, device=DEV) < x_argmax_frac
+    x = torch.where(pick, amax, x)
+    T = 0.5 + torch.rand(B, generator=g, device=DEV)
+    T = torch.where(torch.rand(B, generator=g, device=DEV) < greedy_frac, torch.zeros_like(T), T)
+    return {"name": "custom", "logits": lg.contiguous(), "draft_token_ids": x.to(torch.int32).contiguous(),
+            "draft_probs": q, "bitmask": mask, "temperature": T.float().contiguous(), "top_k": None,
+            "seed": 12345 + seed}
+
+
+# ------------------------------------------------------------ whole workloads
+
+def test_tiny_full():
+    announce("tiny full")
+    wl = make_workload("tiny", device=DEV)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_draft_model_full():
+    announce("draft_model full B=64 k=5 V=32000")
+    wl = make_workload("draft_model", device=DEV)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_draft_model_as_one_hot():
+    announce("draft_model drafts without q")
+    wl = make_workload("draft_model", device=DEV, batch=32)
+    wl["draft_probs"] = None
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_ngram_scaled():
+    announce("ngram B=16 k=4 V=151936")
+    wl = make_workload("ngram", device=DEV, batch=16)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_structured_scaled():
+    announce("structured B=12 k=5 V=128256")
+    wl = make_workload("structured", device=DEV, batch=12)
+    gpu, orc = run_gpu(wl), run_oracle(wl)
+    assert_parity(gpu, orc)
+    R, I, D, A = (int(v) for v in gpu["counters"])
+    assert R == 60 and I == 12 and D == 48        # exactly 20% invalid drafts
+
+
+def test_ngram_full_sampled():
+    announce("ngram full B=256 k=4 V=151936, 16 requests rechecked by the oracle")
+    wl = make_workload("ngram", device=DEV)
+    gpu = run_gpu(wl)
+    B, k = 256, 4
+    rng = np.random.default_rng(0)
+    req = sorted(set([0, 1, 127, 255] + list(rng.choice(B, 12, replace=False))))
+    orc = run_oracle(wl, requests=req)
+    assert_parity(gpu, orc, requests=req, max_flagged=1)
+    # properties over the whole batch
+    R, I, D, A = (int(v) for v in gpu["counters"])
+    na = gpu["out_num_accepted"]
+    assert (R, I, D) == (B * k, 0, B * k) and A == int(na.sum())
+    x = wl["draft_token_ids"].cpu().numpy()
+    tok = gpu["out_tokens"]
+    for b in range(B):
+        assert np.array_equal(tok[b, :na[b]], x[b, :na[b]])
+        assert 0 <= tok[b, na[b]] < 151936 and np.all(tok[b, na[b] + 1:] == -1)
+    assert gpu["status"] == 0
+    assert gpu["flags"][0] + gpu["flags"][1] <= 2
+
+
+def test_structured_full_sampled():
+    announce("structured full B=128 k=5 V=128256, 12 requests rechecked by the oracle")
+    wl = make_workload("structured", device=DEV)
+    gpu = run_gpu(wl)
+    req = [0, 5, 17, 33, 64, 65, 90, 100, 111, 120, 126, 127]
+    orc = run_oracle(wl, requests=req)
+    assert_parity(gpu, orc, requests=req, max_flagged=1)
+    R, I, D, A = (int(v) for v in gpu["counters"])
+    assert (R, I, D) == (640, 128, 512)           # survival exactly 80%
+    assert A == int(gpu["out_num_accepted"].sum()) and A <= D
+
+
+# ------------------------------------------------------- shapes and variants
+
+@pytest.mark.parametrize("V", [1, 7, 8, 1001, 2047, 2048, 2049, 6144, 6150])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_vocab_sizes_and_alignment(V, dtype):
+    announce(f"custom V={V} dtype={dtype}")
+    for dense, masked in [(True, False), (False, True)]:
+        wl = _custom(6, 3, V, dtype=dtype, dense=dense, masked=masked, greedy_frac=0.3,
+                     seed=V + (7 if dense else 0))
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_masked_dense_one_hot_and_greedy_mix():
+    announce("custom B=24 k=6 V=40000 masked dense greedy mix")
+    wl = _custom(24, 6, 40000, dense=True, masked=True, greedy_frac=0.4, density=0.1, seed=3)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+    wl["draft_probs"] = None
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_greedy_ties():
+    announce("integer logits, greedy, many ties")
+    wl = _custom(32, 4, 5000, dense=False, greedy_frac=1.0, integer_logits=True, seed=9,
+                 x_argmax_frac=0.8)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_k_zero_bonus_only():
+    announce("k=0")
+    wl = _custom(10, 0, 3000, dense=False, greedy_frac=0.3, seed=4)
+    wl["draft_token_ids"] = torch.zeros((10, 0), dtype=torch.int32, device=DEV)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_empty_batch():
+    announce("B=0")
+    import rejection_sampling_verification_amd as sdv
+    v = sdv.Verifier(0, 3, 100, torch.float32, DEV)
+    r = v(torch.zeros((0, 4, 100), device=DEV), torch.zeros((0, 3), dtype=torch.int32, device=DEV),
+          temperature=torch.zeros(0, device=DEV))
+    torch.cuda.synchronize()
+    assert r.out_counters.cpu().tolist() == [0, 0, 0, 0] and int(r.status.item()) == 0
+
+
+def test_malformed_requests():
+    announce("status bits")
+    wl = _custom(8, 3, 3000, dense=True, masked=True, seed=5)
+    wl["draft_token_ids"][1, 2] = 3000                        # draft id out of range
+    wl["temperature"][2] = -1.0                               # bad temperature
+    wl["logits"][3, 1, 17] = float("nan")                     # NaN at ...
+    wl["bitmask"][3, 1, 0] |= (1 << 17)                       # ... an allowed token
+    wl["bitmask"][4, 2, :] = 0                                # empty row
+    wl["draft_probs"][5, 0, wl["draft_token_ids"][5, 0]] = float("inf")
+    gpu, orc = run_gpu(wl), run_oracle(wl)
+    assert list(orc["request_status"][:6]) == [0, 1, 2, 8, 4, 16]
+    assert_parity(gpu, orc)
+    assert gpu["status"] == 1 | 2 | 4 | 8 | 16
+
+
+def test_determinism_and_seed():
+    announce("determinism")
+    wl = make_workload("draft_model", device=DEV, batch=64)
+    a, b = run_gpu(wl), run_gpu(wl)
+    for key in ("out_tokens", "out_num_accepted", "out_counters", "row_lse", "accept_prob"):
+        assert np.array_equal(a[key], b[key]), key
+    c = run_gpu(wl, seed=wl["seed"] + 1)
+    assert not np.array_equal(a["out_tokens"], c["out_tokens"])
+
+
+def test_counter_example_on_gpu():
+    """fanout, "Work a denominator example": R=1000, I=200, D=800, A=600."""
+    announce("counter example")
+    B, k, V = 200, 5, 64
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    lg = torch.randn((B, k + 1, V), generator=g)
+    gm = torch.randint(0, V, (B, k + 1), generator=g)
+    lg.scatter_(2, gm[..., None], 20.0)
+    x = gm[:, :k].clone()
+    allowed = torch.ones((B, k + 1, V), dtype=torch.bool)
+    for b in range(120, 200):
+        x[b] = (gm[b, :k] + 1) % V
+        if b < 160:
+            allowed[b, torch.arange(k), x[b]] = False
+    wl = {"logits": lg.to(DEV), "draft_token_ids": x.to(torch.int32).to(DEV), "draft_probs": None,
+          "bitmask": pack_bitmask(allowed).to(DEV), "temperature": torch.zeros(B, device=DEV),
+          "top_k": None, "seed": 1}
+    gpu = run_gpu(wl)
+    assert [int(v) for v in gpu["counters"]] == [1000, 200, 800, 600]
+
+
+@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked"])
+def test_chi_square_on_gpu(mode):
+    """Emitted tokens follow the target law (pyshine, "Verification": the output
+    is statistically indistinguishable from undrafted decoding)."""
+    from scipy import stats
+    from oracle import verify as ov
+    announce(f"chi-square {mode}")
+    B, k, V = 200000, 2, 8
+    g = torch.Generator(device="cpu")
+    g.manual_seed(11)
+    l1 = torch.randn((k + 1, V), generator=g)
+    allowed = torch.ones((k + 1, V), dtype=torch.bool)
+    if mode == "masked":
+        allowed = torch.rand((k + 1, V), generator=g) < 0.7
+        allowed[:, :2] = True
+    T = 0.9
+    p = np.array([ov.target_distribution(l1[i].double().numpy(), allowed[i].numpy(), T, 0)[0]
+                  for i in range(k + 1)])
+    q1 = torch.softmax(torch.randn((k, V), generator=g), -1)
+    x = torch.stack([torch.multinomial(q1[i], B, replacement=True, generator=g) for i in range(k)], 1)
+    wl = {"logits": l1.expand(B, k + 1, V).contiguous().to(DEV),
+          "draft_token_ids": x.to(torch.int32).to(DEV),
+          "draft_probs": None if mode == "one_hot" else q1.expand(B, k, V).contiguous().to(DEV),
+          "bitmask": None if mode != "masked" else pack_bitmask(allowed).expand(B, k + 1, 1).contiguous().to(DEV),
+          "temperature": torch.full((B,), T, device=DEV), "top_k": None, "seed": 2024}
+    gpu = run_gpu(wl)
+    tok, na = gpu["out_tokens"], gpu["out_num_accepted"]
+    for i in range(k + 1):
+        sel = na >= i
+        counts = np.bincount(tok[sel, i], minlength=V)
+        assert counts[p[i] == 0].sum() == 0
+        live = p[i] > 0
+        pv = stats.chisquare(counts[live], p[i][live] * counts[live].sum()).pvalue
+        assert pv > 1e-3, (mode, i, pv)
