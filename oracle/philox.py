@@ -16,7 +16,7 @@ Counter layout (word0, word1, word2, word3) of each stream, key = (seed low
 32 bits, seed high 32 bits):
 
 * accept uniform of request b, draft position i:  (0, i, b, 0), output word 0
-* level-1 Gumbel of request b, sampled row a, block c:  (c, a, b, 1), word 0
+* level-1 Gumbel of request b, sampled row a, block c:  (c >> 2, a, b, 1), word c & 3
 * level-2 Gumbel of request b, row a, token j:  (j >> 2, a, b, 2), word j & 3
 
 Uniform maps (both exact in float32 and float64):
@@ -94,11 +94,13 @@ def u_block(seed, b, a, c):
     """Level-1 Gumbel uniforms of request b, sampled row a, blocks c."""
     c = np.atleast_1d(np.asarray(c, dtype=np.uint64))
     ctr = np.zeros(c.shape + (4,), dtype=np.uint64)
-    ctr[..., 0] = c
+    ctr[..., 0] = c >> np.uint64(2)
     ctr[..., 1] = a
     ctr[..., 2] = b
     ctr[..., 3] = 1
-    return uniform_open(philox4x32_10(ctr, key_of_seed(seed))[..., 0])
+    words = philox4x32_10(ctr, key_of_seed(seed))
+    lane = (c & np.uint64(3)).astype(np.int64)
+    return uniform_open(np.take_along_axis(words, lane[..., None], axis=-1)[..., 0])
 
 
 def u_token(seed, b, a, j):

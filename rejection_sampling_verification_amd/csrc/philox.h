@@ -8,7 +8,7 @@
 //
 // Streams (key = seed low word, seed high word):
 //   accept draw of request b, position i  : counter (0, i, b, 0), word 0
-//   level-1 draw of request b, row a, block c : (c, a, b, 1), word 0
+//   level-1 draw of request b, row a, block c : (c >> 2, a, b, 1), word c & 3
 //   level-2 draw of request b, row a, token j : (j >> 2, a, b, 2), word j & 3
 #pragma once
 #include <hip/hip_runtime.h>
@@ -24,10 +24,11 @@ constexpr uint32_t kWeyl1 = 0xBB67AE85u;     // 2^32 * (sqrt(3) - 1)
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t lo0 = kPhiloxM0 * c.x;
-        const uint32_t hi0 = __umulhi(kPhiloxM0, c.x);
-        const uint32_t lo1 = kPhiloxM1 * c.z;
-        const uint32_t hi1 = __umulhi(kPhiloxM1, c.z);
+        // both halves of each 32 x 32 product from one 64-bit multiply
+        const uint64_t p0 = uint64_t(kPhiloxM0) * c.x;
+        const uint64_t p1 = uint64_t(kPhiloxM1) * c.z;
+        const uint32_t lo0 = uint32_t(p0), hi0 = uint32_t(p0 >> 32);
+        const uint32_t lo1 = uint32_t(p1), hi1 = uint32_t(p1 >> 32);
         c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
         k0 += kWeyl0;
         k1 += kWeyl1;
@@ -48,35 +49,37 @@ __device__ __forceinline__ double uniform_accept(uint32_t w) {
     return static_cast<double>(w >> 8) * 0x1p-24;
 }
 
-// (0, 1): odd multiples of 2^-24 from the top 23 bits.
-__device__ __forceinline__ double uniform_open(uint32_t w) {
-    return (static_cast<double>(w >> 9) * 2.0 + 1.0) * 0x1p-24;
+// Standard Gumbel variate -ln(-ln u) in fp32 for u = (2n + 1) 2^-24.  The
+// inner logarithm is log1p(u - 1): u - 1 is exact in fp32 for every such u,
+// so -ln u keeps its relative accuracy near u = 1.  Over all 2^23 possible u
+// the result is within about 6e-7 of the exact value.
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+    const float u = static_cast<float>((w >> 9) * 2u + 1u) * 0x1p-24f;
+    return -logf(-log1pf(u - 1.0f));
 }
-
-__device__ __forceinline__ double gumbel_of(double u) { return -log(-log(u)); }
 
 __device__ __forceinline__ double draw_accept(PhiloxKey key, uint32_t b, uint32_t i) {
     return uniform_accept(philox4x32_10(make_uint4(0u, i, b, 0u), key.k0, key.k1).x);
 }
 
-__device__ __forceinline__ double draw_block_gumbel(PhiloxKey key, uint32_t b, uint32_t a,
-                                                    uint32_t c) {
-    return gumbel_of(uniform_open(philox4x32_10(make_uint4(c, a, b, 1u), key.k0, key.k1).x));
+// Level-1 Gumbel variates of blocks 4 g4 .. 4 g4 + 3 of row a of request b.
+__device__ __forceinline__ void draw_block_gumbels4(PhiloxKey key, uint32_t b, uint32_t a,
+                                                    uint32_t g4, float g[4]) {
+    const uint4 w = philox4x32_10(make_uint4(g4, a, b, 1u), key.k0, key.k1);
+    g[0] = gumbel_of(w.x);
+    g[1] = gumbel_of(w.y);
+    g[2] = gumbel_of(w.z);
+    g[3] = gumbel_of(w.w);
 }
 
-// Gumbel variates of the 8 tokens j0 .. j0+7 (j0 a multiple of 8).
-__device__ __forceinline__ void draw_token_gumbels8(PhiloxKey key, uint32_t b, uint32_t a,
-                                                    uint32_t j0, double g[8]) {
-    const uint4 w0 = philox4x32_10(make_uint4(j0 >> 2, a, b, 2u), key.k0, key.k1);
-    const uint4 w1 = philox4x32_10(make_uint4((j0 >> 2) + 1u, a, b, 2u), key.k0, key.k1);
-    g[0] = gumbel_of(uniform_open(w0.x));
-    g[1] = gumbel_of(uniform_open(w0.y));
-    g[2] = gumbel_of(uniform_open(w0.z));
-    g[3] = gumbel_of(uniform_open(w0.w));
-    g[4] = gumbel_of(uniform_open(w1.x));
-    g[5] = gumbel_of(uniform_open(w1.y));
-    g[6] = gumbel_of(uniform_open(w1.z));
-    g[7] = gumbel_of(uniform_open(w1.w));
+// Level-2 Gumbel variates of tokens j0 .. j0 + 3 (j0 a multiple of 4).
+__device__ __forceinline__ void draw_token_gumbels4(PhiloxKey key, uint32_t b, uint32_t a,
+                                                    uint32_t j0, float g[4]) {
+    const uint4 w = philox4x32_10(make_uint4(j0 >> 2, a, b, 2u), key.k0, key.k1);
+    g[0] = gumbel_of(w.x);
+    g[1] = gumbel_of(w.y);
+    g[2] = gumbel_of(w.z);
+    g[3] = gumbel_of(w.w);
 }
 
 }  // namespace sdv

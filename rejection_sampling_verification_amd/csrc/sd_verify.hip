@@ -30,18 +30,25 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "sd_verify.h"
 #include "philox.h"
 #include "wave.h"
 
 #ifndef SDV_BLOCKS_PER_WAVE
-#define SDV_BLOCKS_PER_WAVE 4
+#define SDV_BLOCKS_PER_WAVE 4   // element kernel: 2048-token blocks per wave task
+#endif
+#ifndef SDV_ROW_STATS_GRID
+#define SDV_ROW_STATS_GRID 2048 // vector kernel: workgroups of the block sweep
 #endif
 
 namespace sdv {
 
 constexpr int kBlock = SD_BLOCK_TOKENS;
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // row statistics: 4 waves per workgroup
+constexpr int kFinalThreads = 512;  // finalize: 8 waves per request
+constexpr int kFinalWaves = kFinalThreads / 64;
 constexpr int kMaxDraft = SD_MAX_DRAFT;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kLn2 = 0.6931471805599453;
@@ -134,21 +141,46 @@ __device__ __forceinline__ float scale_of(float T) {
     return static_cast<float>(kLog2e / static_cast<double>(T));
 }
 
+// A wave-uniform read of memory no kernel of the call writes, through the
+// constant address space so that it becomes a scalar load (its own counter,
+// no wait on outstanding vector loads).
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T *p) {
+    typedef const __attribute__((address_space(4))) T ConstT;
+    return *(ConstT *)(reinterpret_cast<uintptr_t>(p));
+}
+
+// Raw buffer resource over `bytes` bytes at p (GFX9 word 3: raw 32-bit
+// format).  Loads at offsets >= bytes return zero instead of faulting.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
+                                             kBufferWord3);
+}
+
 // ------------------------------------------------------------ row statistics
 
 struct RowStatsArgs {
     const void *logits;
-    const uint32_t *mask;  // nullptr = no bitmask
+    const uint32_t *mask;     // nullptr = no bitmask
     const float *temperature;
-    float2 *bstats;        // [rows, C]
-    uint32_t *ticket;
-    int64_t ntasks;        // rows * nchunk
-    int kp1, V, W, C, cpw, nchunk;
+    const int32_t *draft;     // [B, k]; nullptr when k = 0
+    float2 *bstats;           // [rows, C]
+    float *sx;                // [rows]: Sc of the draft's own block without the draft
+    uint64_t *out_counters;   // zeroed here, accumulated by finalize
+    uint32_t *status;         // zeroed here when given
+    uint32_t *dbg_flags;      // zeroed here when given
+    int64_t ntasks;           // rows * nchunk (chunked element kernel)
+    int64_t nblk;             // rows * C (vector kernel sweep)
+    int k, kp1, V, W, C, cpw, nchunk;
 };
 
-template <int G, int P>
+// Per-block statistics of a sampling row from one lane's values v (masked
+// tokens and tokens past V hold -inf): (Mc, Sc) with Mc = fp32(max l * c) and
+// Sc = sum 2^(l c - Mc).
+template <int NV>
 __device__ __forceinline__ float2 softmax_block(const float *v, float c) {
-    constexpr int NV = G * P;
     float m = v[0];
 #pragma unroll
     for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
@@ -161,8 +193,11 @@ __device__ __forceinline__ float2 softmax_block(const float *v, float c) {
     return make_float2(mc, wave_sum(s));
 }
 
+// Greedy rows: the block's largest logit and the lowest index holding it
+// (NaN when the block holds an allowed NaN).  Element (g, e) of a lane is
+// token blk_base + (g * 64 + lane) * P + e.
 template <int G, int P>
-__device__ __forceinline__ float2 greedy_block(const float *v, int64_t base) {
+__device__ __forceinline__ float2 greedy_block(const float *v, int64_t blk_base, int lane) {
     constexpr int NV = G * P;
     float m = -INFINITY;
     bool nan = false;
@@ -179,46 +214,306 @@ __device__ __forceinline__ float2 greedy_block(const float *v, int64_t base) {
     for (int g = G - 1; g >= 0; --g)
 #pragma unroll
         for (int e = P - 1; e >= 0; --e)
-            if (v[g * P + e] == m) idx = static_cast<int>(base + g * kWave * P + e);
+            if (v[g * P + e] == m) idx = static_cast<int>(blk_base + (g * kWave + lane) * P + e);
     return make_float2(m, __int_as_float(wave_min_i(idx)));
 }
 
-template <typename ET, bool MASKED, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(RowStatsArgs a) {
-    constexpr int P = Logit<ET>::kPer16;
-    constexpr int G = kBlock / (kWave * P);  // 16-byte groups per lane per block
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.ticket = 0u;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t task = int64_t(blockIdx.x) * (kThreads / kWave) + (threadIdx.x >> 6);
-    if (task >= a.ntasks) return;
-    const int row = static_cast<int>(task / a.nchunk);
-    const int chunk = static_cast<int>(task - int64_t(row) * a.nchunk);
-    const float T = a.temperature[row / a.kp1];
-    const bool greedy = (T == 0.0f);
-    if (!greedy && !(T > 0.0f && T <= FLT_MAX)) return;  // reported by finalize
-    const float c = greedy ? 0.0f : scale_of(T);
-    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;
-    const uint8_t *mrow =
-        MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
-    float2 *out = a.bstats + int64_t(row) * a.C;
-    const int c0 = chunk * a.cpw;
-    const int c1 = min(a.C, c0 + a.cpw);
-    for (int blk = c0; blk < c1; ++blk) {
-        const int64_t base = int64_t(blk) * kBlock + lane * P;
-        float v[G * P];
-#pragma unroll
-        for (int g = 0; g < G; ++g) load_group<ET, ALIGNED>(rowp, base + g * kWave * P, a.V, v + g * P);
-        if (MASKED) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint32_t bits = mask_bits<P>(mrow, base + g * kWave * P, a.V);
-#pragma unroll
-                for (int e = 0; e < P; ++e)
-                    if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
-            }
+__device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
+    if (blockIdx.x != 0) return;
+    if (threadIdx.x < 4) a.out_counters[threadIdx.x] = 0ull;
+    if (threadIdx.x == 0 && a.status) *a.status = 0u;
+    if (threadIdx.x < 2 && a.dbg_flags) a.dbg_flags[threadIdx.x] = 0u;
+}
+
+// Which row a wave works on, and its parameters (all wave-uniform).
+struct RowTask {
+    int row, c0, c1;
+    bool greedy, skip;
+    float c;
+    int xblk, xrel;  // the draft's block and offset in it (-1: none)
+};
+
+__device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task) {
+    RowTask t;
+    t.row = static_cast<int>(task / a.nchunk);
+    const int chunk = static_cast<int>(task - int64_t(t.row) * a.nchunk);
+    t.c0 = chunk * a.cpw;
+    t.c1 = min(a.C, t.c0 + a.cpw);
+    const int b = t.row / a.kp1, i = t.row - b * a.kp1;
+    const float T = a.temperature[b];
+    t.greedy = (T == 0.0f);
+    t.skip = !t.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
+    t.c = t.greedy ? 0.0f : scale_of(T);
+    t.xblk = t.xrel = -1;
+    if (!t.greedy && i < a.k) {
+        const int x = a.draft[int64_t(b) * a.k + i];
+        if (x >= 0 && x < a.V) {
+            t.xblk = x / kBlock;
+            t.xrel = x - t.xblk * kBlock;
         }
-        const float2 r = greedy ? greedy_block<G, P>(v, base) : softmax_block<G, P>(v, c);
-        if (lane == 0) out[blk] = r;
+    }
+    return t;
+}
+
+// Raw 16-byte groups and mask bytes of one block wholly inside the row: lane
+// l reads groups l, l + 64, ... (consecutive lanes, consecutive 16 bytes).
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void load_full_block(const ET *rowp, const uint8_t *mrow, int blk,
+                                                int lane, uint4 *r, uint32_t *m) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    const uint4 *bp = reinterpret_cast<const uint4 *>(rowp + int64_t(blk) * kBlock) + lane;
+#pragma unroll
+    for (int g = 0; g < G; ++g) r[g] = bp[g * kWave];
+    if (MASKED) {
+        // P tokens per group: the group's bits sit in byte (first token) / 8
+        const uint8_t *mb = mrow + int64_t(blk) * (kBlock / 8);
+#pragma unroll
+        for (int g = 0; g < G; ++g) m[g] = mb[((g * kWave + lane) * P) >> 3];
+    }
+}
+
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void unpack_full_block(const uint4 *r, const uint32_t *m, int lane,
+                                                  float *v) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        Logit<ET>::unpack(r[g], v + g * P);
+        if (MASKED) {
+            const uint32_t bits = (P == 8) ? m[g] : (m[g] >> ((lane & 1) * 4));
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
+        }
+    }
+}
+
+// Values of one lane for any block (used for the row's partial last block and
+// for re-reads): addresses clamped into the row, tokens past V and masked
+// tokens become -inf.
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void load_any_block(const ET *rowp, const uint8_t *mrow, int blk, int V,
+                                               int lane, float *v) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    uint4 r[G];
+    uint32_t m[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
+        const int64_t tc = tok < V ? tok : int64_t(V - P);
+        r[g] = *reinterpret_cast<const uint4 *>(rowp + tc);
+        m[g] = MASKED ? uint32_t(mrow[tc >> 3]) : 0xffu;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
+        Logit<ET>::unpack(r[g], v + g * P);
+        uint32_t bits = tok < V ? 0xffu : 0u;
+        if (MASKED) bits &= (P == 8) ? m[g] : (m[g] >> (uint32_t(tok) & 4u));
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+            if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
+    }
+}
+
+template <bool GREEDY, int G, int P>
+__device__ __forceinline__ void store_block(const RowStatsArgs &a, const RowTask &t, const float *v,
+                                            int blk, int lane) {
+    const float2 r = GREEDY ? greedy_block<G, P>(v, int64_t(blk) * kBlock, lane)
+                            : softmax_block<G * P>(v, t.c);
+    if (lane == 0) a.bstats[int64_t(t.row) * a.C + blk] = r;
+}
+
+// The sum of the draft's own block without the draft (the one-hot residual
+// mass of that block), relative to the same Mc as the block statistics.
+template <int G, int P>
+__device__ __forceinline__ void store_excluded_sum(const RowStatsArgs &a, int row, float c, int xrel,
+                                                   const float *v, int lane) {
+    constexpr int NV = G * P;
+    float m = v[0];
+#pragma unroll
+    for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
+    m = wave_max(m);
+    float s = 0.0f;
+    if (m > -INFINITY) {
+        const float mc = m * c;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if ((g * kWave + lane) * P + e != xrel)
+                    s += __builtin_amdgcn_exp2f(fmaf(v[g * P + e], c, -mc));
+    }
+    s = wave_sum(s);
+    if (lane == 0) a.sx[row] = s;
+}
+
+// One block's share of the sweep: where it lives and its row's parameters.
+struct SweepBlock {
+    int64_t gb;   // row * C + block
+    int row, blk;
+    bool full, greedy, skip;
+    float c;
+    int xrel;     // the draft's offset in this block, -1 if the draft is elsewhere
+};
+
+__device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t gb) {
+    SweepBlock s;
+    s.gb = gb;
+    s.row = static_cast<int>(gb / a.C);
+    s.blk = static_cast<int>(gb - int64_t(s.row) * a.C);
+    s.full = int64_t(s.blk + 1) * kBlock <= a.V;
+    const int b = s.row / a.kp1, i = s.row - b * a.kp1;
+    const float T = uniform_load(a.temperature + b);
+    s.greedy = (T == 0.0f);
+    s.skip = !s.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
+    s.c = s.greedy ? 0.0f : scale_of(T);
+    s.xrel = -1;
+    if (!s.greedy && i < a.k) {
+        const int x = uniform_load(a.draft + int64_t(b) * a.k + i);
+        if (x >= 0 && x < a.V && x / kBlock == s.blk) s.xrel = x - s.blk * kBlock;
+    }
+    return s;
+}
+
+// Issue the loads of one block through buffer resources spanning its row (and
+// its mask row): every block takes the same instructions, and the groups of a
+// partial block that lie past the row read zeros (they are replaced by -inf
+// when the block is reduced).
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void issue_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
+                                            uint4 *r, uint32_t *m) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    const __amdgpu_buffer_rsrc_t rs = buffer_of(
+        reinterpret_cast<const ET *>(a.logits) + int64_t(s.row) * a.V, uint32_t(a.V) * sizeof(ET));
+    const int base = s.blk * kBlock * int(sizeof(ET)) + lane * 16;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, 0);
+        r[g] = make_uint4(w.x, w.y, w.z, w.w);
+    }
+    if (MASKED) {
+        const __amdgpu_buffer_rsrc_t rm = buffer_of(a.mask + int64_t(s.row) * a.W, uint32_t(a.W) * 4u);
+        const int mbase = s.blk * (kBlock / 8) + ((lane * P) >> 3);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, mbase + g * kWave * P / 8, 0, 0);
+    }
+}
+
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
+                                             const uint4 *r, const uint32_t *m) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    if (s.skip) return;
+    float v[G * P];
+    if (s.full) {
+        unpack_full_block<ET, MASKED>(r, m, lane, v);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t tok = int64_t(s.blk) * kBlock + (g * kWave + lane) * P;
+            Logit<ET>::unpack(r[g], v + g * P);
+            uint32_t bits = tok < a.V ? 0xffu : 0u;
+            if (MASKED) bits &= (P == 8) ? m[g] : (m[g] >> (uint32_t(tok) & 4u));
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
+        }
+    }
+    float2 res;
+    if (s.greedy) {
+        res = greedy_block<G, P>(v, int64_t(s.blk) * kBlock, lane);
+    } else {
+        res = softmax_block<G * P>(v, s.c);
+        if (s.xrel >= 0) store_excluded_sum<G, P>(a, s.row, s.c, s.xrel, v, lane);
+    }
+    if (lane == 0) a.bstats[s.gb] = res;
+}
+
+// Rows 16-byte aligned with V a multiple of the group width.  The grid sweeps
+// the (row, block) pairs in memory order: wave w of the grid takes blocks
+// w, w + Wt, w + 2 Wt, ... (Wt = waves in the grid), so the whole grid reads
+// one contiguous window of the logits at a time.  Each wave keeps the loads of
+// its next block in flight while it reduces the current one; the next index
+// is clamped to the current block at the end of the sweep, so every path
+// reaches a reduction with the same loads outstanding.
+template <typename ET, bool MASKED>
+__global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    zero_call_outputs(a);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t stride = int64_t(gridDim.x) * (kThreads / kWave);
+    int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
+    if (g0 >= a.nblk) return;
+    uint4 ra[G], rb[G];
+    uint32_t ma[G], mb[G];
+    SweepBlock sa = sweep_block(a, g0);
+    issue_block<ET, MASKED>(a, sa, lane, ra, ma);
+    for (;;) {
+        const int64_t g1 = sa.gb + stride;
+        const bool more1 = g1 < a.nblk;
+        const SweepBlock sb = sweep_block(a, more1 ? g1 : sa.gb);
+        issue_block<ET, MASKED>(a, sb, lane, rb, mb);
+        reduce_block<ET, MASKED>(a, sa, lane, ra, ma);
+        if (!more1) break;
+        const int64_t g2 = sb.gb + stride;
+        const bool more2 = g2 < a.nblk;
+        sa = sweep_block(a, more2 ? g2 : sb.gb);
+        issue_block<ET, MASKED>(a, sa, lane, ra, ma);
+        reduce_block<ET, MASKED>(a, sb, lane, rb, mb);
+        if (!more2) break;
+    }
+}
+
+// Any alignment and any V: element loads clamped into the row.
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void load_block_elem(const ET *rowp, const uint8_t *mrow, int blk, int V,
+                                                int lane, float *v) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P + e;
+            const int64_t tc = tok < V ? tok : int64_t(V - 1);
+            const float x = Logit<ET>::to_float(rowp[tc]);
+            bool live = tok < V;
+            if (MASKED) live = live && ((mrow[tc >> 3] >> (tc & 7)) & 1u);
+            v[g * P + e] = live ? x : -INFINITY;
+        }
+}
+
+template <typename ET, bool MASKED>
+__global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    zero_call_outputs(a);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t task = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
+    if (task >= a.ntasks) return;
+    const RowTask t = row_task(a, task);
+    if (t.skip) return;
+    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(t.row) * a.V;
+    const uint8_t *mrow =
+        MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(t.row) * a.W) : nullptr;
+    float v[G * P];
+    for (int blk = t.c0; blk < t.c1; ++blk) {
+        load_block_elem<ET, MASKED>(rowp, mrow, blk, a.V, lane, v);
+        if (t.greedy) {
+            store_block<true, G, P>(a, t, v, blk, lane);
+        } else {
+            store_block<false, G, P>(a, t, v, blk, lane);
+            if (blk == t.xblk) store_excluded_sum<G, P>(a, t.row, t.c, t.xrel, v, lane);
+        }
     }
 }
 
@@ -240,30 +535,49 @@ struct FinalArgs {
     uint32_t *dbg_flags;
     uint32_t *status;
     const float2 *bstats;
-    int32_t *rec;  // [B, kRecordWords]
-    uint32_t *ticket;
+    const float *sx;
     int B, k, V, W, C;
 };
 
 enum SampleMode { kModeP = 0, kModeOneHot = 1, kModeDense = 2 };
 
+struct Level1 {
+    int c;     // winning block, -1 when no block has mass
+    int flag;  // 1 when the top-2 block keys are closer than the flag threshold
+};
+
 struct FinalShared {
-    float M[kMaxDraft + 1];   // per row: fp32 max (log2 units) or greedy max logit
-    double S[kMaxDraft + 1];  // per row: sum of 2^(t - M)
-    int G[kMaxDraft + 1];     // greedy argmax
+    float M[kMaxDraft + 1];     // per row: fp32 max (log2 units), or greedy max logit
+    double S[kMaxDraft + 1];    // per row: sum of 2^(t - M)
+    int G[kMaxDraft + 1];       // greedy argmax
+    Level1 l1p[kMaxDraft + 1];  // level-1 winner under p
+    Level1 l1x[kMaxDraft + 1];  // level-1 winner under p without the row's draft
     int X[kMaxDraft];
     double acc[kMaxDraft];
     unsigned char ok[kMaxDraft], flag[kMaxDraft], invalid[kMaxDraft];
     uint32_t status;
-    int nacc, flag_acc, ninvalid, last;
-    double red_d[4];
-    Top2 red_t[4];
-    unsigned long long red_u[4][4];
-    uint32_t red_s[4];
+    int nacc, flag_acc, ninvalid;
+    int staged_c;               // block of the sampled row held in blockv (-1: none)
+    double red_d[kFinalWaves];
+    Top2 red_t[kFinalWaves];
+    float blockv[kBlock];       // that block's logits, -inf where masked or past V
 };
 
-// Per-block residual masses of row `row` for dense q: W_c = sum_j max(p_j - q_j, 0)
-// with p_j = 2^(l_j c - M) / S, evaluated in fp32.  One wave per block.
+// Workgroup barrier that orders LDS only: global loads a wave has in flight
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ Level1 level1_of(const Top2 &t) {
+    if (t.k1 == -INFINITY) return Level1{-1, 0};
+    return Level1{t.i1, (t.k2 > -INFINITY && t.k1 - t.k2 < kGumbelFlagEps) ? 1 : 0};
+}
+
+// Residual masses W_c = sum_j max(p_j - q_j, 0) of one row for dense q, with
+// p_j = 2^(l_j c - M) / S in fp32.  One wave per block; clamped loads.
 template <typename ET, bool ALIGNED>
 __device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const float *qrow, int V,
                                    int C, float c, float M, double S, double *Wout) {
@@ -271,37 +585,40 @@ __device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const f
     constexpr int G = kBlock / (kWave * P);
     const int lane = threadIdx.x & (kWave - 1);
     const float invS = static_cast<float>(1.0 / S);
-    for (int blk = threadIdx.x >> 6; blk < C; blk += kThreads / kWave) {
-        const int64_t base = int64_t(blk) * kBlock + lane * P;
+    const uint8_t *mb = reinterpret_cast<const uint8_t *>(mrow);
+    for (int blk = wave_id(); blk < C; blk += kFinalWaves) {
         float acc = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const int64_t tok = base + g * kWave * P;
-            float lv[P];
-            load_group<ET, ALIGNED>(rowp, tok, V, lv);
-            float qv[P];
+            const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
+            float lv[P], qv[P];
+            if (ALIGNED) {
+                const int64_t tc = tok < V ? tok : int64_t(V - P);
+                Logit<ET>::unpack(*reinterpret_cast<const uint4 *>(rowp + tc), lv);
 #pragma unroll
-            for (int h = 0; h < P / 4; ++h) {
-                if (ALIGNED) {
-                    if (tok < V) {
-                        const float4 f = *reinterpret_cast<const float4 *>(qrow + tok + 4 * h);
-                        qv[4 * h] = f.x; qv[4 * h + 1] = f.y; qv[4 * h + 2] = f.z; qv[4 * h + 3] = f.w;
-                    } else {
-                        qv[4 * h] = qv[4 * h + 1] = qv[4 * h + 2] = qv[4 * h + 3] = 0.0f;
-                    }
-                } else {
+                for (int h = 0; h < P / 4; ++h) {
+                    const float4 f = *reinterpret_cast<const float4 *>(qrow + tc + 4 * h);
+                    qv[4 * h] = f.x;
+                    qv[4 * h + 1] = f.y;
+                    qv[4 * h + 2] = f.z;
+                    qv[4 * h + 3] = f.w;
+                }
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        qv[4 * h + e] = (tok + 4 * h + e < V) ? qrow[tok + 4 * h + e] : 0.0f;
+                for (int e = 0; e < P; ++e) {
+                    const int64_t tc = tok + e < V ? tok + e : int64_t(V - 1);
+                    lv[e] = Logit<ET>::to_float(rowp[tc]);
+                    qv[e] = qrow[tc];
                 }
             }
-            const uint32_t bits =
-                mrow ? mask_bits<P>(reinterpret_cast<const uint8_t *>(mrow), tok, V) : 0xffu;
 #pragma unroll
             for (int e = 0; e < P; ++e) {
-                const bool live = ((bits >> e) & 1u) && lv[e] > -INFINITY;
+                const int64_t j = tok + e;
+                const int64_t jc = j < V ? j : int64_t(V - 1);
+                bool live = j < V && lv[e] > -INFINITY;
+                if (mrow) live = live && ((mb[jc >> 3] >> (jc & 7)) & 1u);
                 const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[e], c, -M)) * invS : 0.0f;
-                acc += fmaxf(p - qv[e], 0.0f);
+                acc += live ? fmaxf(p - qv[e], 0.0f) : 0.0f;
             }
         }
         const double w = wave_sum_d(static_cast<double>(acc));
@@ -309,189 +626,250 @@ __device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const f
     }
 }
 
-// Draw the emitted token of sampled row n of request b; all threads call it
-// and all get the token.  Adds the number of near-tie flags to *flags.
+// Four consecutive tokens j0 .. j0+3 (j0 % 4 == 0) of a row, masked; tokens
+// past V read as -inf.
 template <typename ET, bool ALIGNED>
-__device__ int sample_row(const FinalArgs &a, FinalShared &sh, double *sW, int b, int n, float c,
-                          float T, int *flags) {
-    const int k = a.k, V = a.V, C = a.C;
+__device__ __forceinline__ void load4_masked(const ET *row, const uint32_t *mrow, int64_t j0, int V,
+                                             float *o) {
+    if (ALIGNED && j0 < V) {  // V is a multiple of 4 (fp32) or 8 (bf16): all four exist
+        if (sizeof(ET) == 2) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(row + j0);
+            o[0] = __uint_as_float(w.x << 16);
+            o[1] = __uint_as_float(w.x & 0xffff0000u);
+            o[2] = __uint_as_float(w.y << 16);
+            o[3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+            const float4 f = *reinterpret_cast<const float4 *>(row + j0);
+            o[0] = f.x;
+            o[1] = f.y;
+            o[2] = f.z;
+            o[3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (j0 + e < V) ? Logit<ET>::to_float(row[j0 + e]) : -INFINITY;
+    }
+    if (mrow != nullptr && j0 < V) {
+        const uint32_t bits = reinterpret_cast<const uint8_t *>(mrow)[j0 >> 3] >> (uint32_t(j0) & 4u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (!((bits >> e) & 1u)) o[e] = -INFINITY;
+    }
+}
+
+// Level 2: the token of block cb of row n drawn under the weights of `mode`
+// (4 tokens per thread; values from the staged LDS copy when `staged`).  All
+// threads call it; returns (token, near-tie flag), token -1 when the block
+// holds no positive weight.
+template <typename ET, bool ALIGNED>
+__device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb, int mode, float c,
+                       double invT, const float *qrow, bool staged) {
+    const int k = a.k, V = a.V;
     const int64_t row = int64_t(b) * (k + 1) + n;
-    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + row * V;
-    const uint32_t *mrow = a.mask ? a.mask + row * a.W : nullptr;
-    const float2 *st = a.bstats + row * C;
-    const PhiloxKey key = key_of(a.seed);
+    const int x = (n < k) ? sh.X[n] : -1;
+    const int64_t j0 = int64_t(cb) * kBlock + threadIdx.x * 4;
+    float lv[4];
+    if (staged) {
+        const float4 f = *reinterpret_cast<const float4 *>(&sh.blockv[threadIdx.x * 4]);
+        lv[0] = f.x;
+        lv[1] = f.y;
+        lv[2] = f.z;
+        lv[3] = f.w;
+    } else {
+        load4_masked<ET, ALIGNED>(reinterpret_cast<const ET *>(a.logits) + row * V,
+                                  a.mask ? a.mask + row * a.W : nullptr, j0, V, lv);
+    }
+    float g[4];
+    draw_token_gumbels4(key_of(a.seed), b, n, static_cast<uint32_t>(j0), g);
     const float M = sh.M[n];
     const double S = sh.S[n];
-    const int x = (n < k) ? sh.X[n] : -1;
-    const float *qrow = (n < k && a.q) ? a.q + (int64_t(b) * k + n) * V : nullptr;
-    int mode = (n == k) ? kModeP : (qrow ? kModeDense : kModeOneHot);
-    const int tid = threadIdx.x;
-
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        // ---- level 1: block masses and their Gumbel keys
-        int cx = -1;
-        double wx = 0.0;
-        if (mode == kModeOneHot) {  // the draft's own block, recomputed without the draft
-            cx = x / kBlock;
-            const int64_t j0 = int64_t(cx) * kBlock + tid * 8;
-            float lv[8];
-            load8_masked<ET, ALIGNED>(rowp, mrow, j0, V, lv);
-            double s = 0.0;
+    Top2 t = top2_empty();
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (lv[e] > -INFINITY && j0 + e != x)
-                    s += exp2(static_cast<double>(lv[e]) * c - static_cast<double>(M));
-            wx = block_sum_d(s, sh.red_d);
-        } else if (mode == kModeDense) {
-            dense_block_masses<ET, ALIGNED>(rowp, mrow, qrow, V, C, c, M, S, sW);
-            __syncthreads();
+    for (int e = 0; e < 4; ++e) {
+        const int64_t j = j0 + e;
+        if (!(lv[e] > -INFINITY)) continue;  // masked, -inf, or past V
+        double key2;
+        if (mode == kModeDense) {
+            const double p = exp2(static_cast<double>(lv[e]) * c - static_cast<double>(M)) / S;
+            const double r = p - static_cast<double>(qrow[j]);
+            if (!(r > 0.0)) continue;
+            key2 = log(r);
+        } else {
+            if (mode == kModeOneHot && j == x) continue;
+            key2 = static_cast<double>(lv[e]) * invT;
         }
-        Top2 t = top2_empty();
-        for (int cb = tid; cb < C; cb += kThreads) {
-            double w;
-            if (mode == kModeDense) {
-                w = sW[cb];
-            } else if (cb == cx) {
-                w = wx;
-            } else {
-                const float2 e = st[cb];
-                w = e.x > -INFINITY ? static_cast<double>(e.y) *
-                                          exp2(static_cast<double>(e.x) - static_cast<double>(M))
-                                    : 0.0;
-            }
-            if (w > 0.0) top2_push(t, log(w) + draw_block_gumbel(key, b, n, cb), cb);
-        }
-        t = block_top2(t, sh.red_t);
-        if (t.k1 == -INFINITY) {  // no residual mass: draw from p instead
-            mode = kModeP;
-            continue;
-        }
-        int nflag = (t.k2 > -INFINITY && t.k1 - t.k2 < kGumbelFlagEps) ? 1 : 0;
-
-        // ---- level 2: tokens of the winning block
-        const int64_t j0 = int64_t(t.i1) * kBlock + tid * 8;
-        float lv[8];
-        load8_masked<ET, ALIGNED>(rowp, mrow, j0, V, lv);
-        double g[8];
-        draw_token_gumbels8(key, b, n, static_cast<uint32_t>(j0), g);
-        Top2 t2 = top2_empty();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t j = j0 + e;
-            if (!(lv[e] > -INFINITY)) continue;  // masked, -inf, or beyond V
-            double kk;
-            if (mode == kModeDense) {
-                const double p = exp2(static_cast<double>(lv[e]) * c - static_cast<double>(M)) / S;
-                const double r = p - static_cast<double>(qrow[j]);
-                if (!(r > 0.0)) continue;
-                kk = log(r) + g[e];
-            } else {
-                if (mode == kModeOneHot && j == x) continue;
-                kk = static_cast<double>(lv[e]) / static_cast<double>(T) + g[e];
-            }
-            top2_push(t2, kk, static_cast<int>(j));
-        }
-        t2 = block_top2(t2, sh.red_t);
-        if (t2.k1 == -INFINITY) {  // the block lost its mass in double precision
-            mode = kModeP;
-            continue;
-        }
-        nflag += (t2.k2 > -INFINITY && t2.k1 - t2.k2 < kGumbelFlagEps) ? 1 : 0;
-        *flags += nflag;
-        return t2.i1;
+        top2_push(t, key2 + static_cast<double>(g[e]), static_cast<int>(j));
     }
-    return -1;  // unreachable: a row that passed validation has mass under p
+    t = block_top2<kFinalWaves>(t, sh.red_t);
+    if (t.k1 == -INFINITY) return make_int2(-1, 0);
+    return make_int2(t.i1, (t.k2 > -INFINITY && t.k1 - t.k2 < kGumbelFlagEps) ? 1 : 0);
+}
+
+// Fold one greedy row's block statistics (one wave): max and lowest argmax.
+__device__ __forceinline__ void fold_greedy_row(const float2 *st, int C, int i, FinalShared &sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    bool bad = false;
+    float best = -INFINITY;
+    int bidx = INT_MAX;
+    for (int cb = lane; cb < C; cb += kWave) {
+        const float2 e = st[cb];
+        if (e.x != e.x || e.x == INFINITY) bad = true;
+        if (e.x > best) {
+            best = e.x;
+            bidx = __float_as_int(e.y);
+        }
+    }
+    bad = wave_any(bad);
+    const float m = wave_max(best);
+    const int gi = wave_min_i(best == m ? bidx : INT_MAX);
+    if (lane == 0) {
+        sh.M[i] = m;
+        sh.G[i] = gi;
+        sh.S[i] = 1.0;
+        if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
+        else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+    }
+}
+
+// Fold one sampling row's block statistics (one wave) into its max and
+// normaliser, and run the row's level-1 Gumbel race over block masses, both
+// under p and under p without block cx's draft (mass sxi instead of Sc).
+__device__ __forceinline__ void fold_sampling_row(const float2 *st, int C, int i, int b, int cx,
+                                                  float sxi, PhiloxKey key, FinalShared &sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    bool bad = false;
+    float mx = -INFINITY;
+    for (int cb = lane; cb < C; cb += kWave) {
+        const float2 e = st[cb];
+        if (e.x != e.x || e.y != e.y || e.x == INFINITY) bad = true;
+        mx = fmaxf(mx, e.x);
+    }
+    bad = wave_any(bad);
+    const float m = wave_max(mx);
+    double s = 0.0;
+    Top2 tp = top2_empty(), tx = top2_empty();
+    if (!bad && m > -INFINITY) {
+        const int ngroups = (C + 3) >> 2;
+        for (int g4 = lane; g4 < ngroups; g4 += kWave) {
+            float gum[4];
+            draw_block_gumbels4(key, b, i, g4, gum);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int cb = 4 * g4 + q;
+                if (cb >= C) break;
+                const float2 e = st[cb];
+                if (!(e.x > -INFINITY) || !(e.y > 0.0f)) continue;
+                const double dm = static_cast<double>(e.x) - static_cast<double>(m);
+                s += static_cast<double>(e.y) * exp2(dm);
+                const double gq = static_cast<double>(gum[q]);
+                const double kp = static_cast<double>(logf(e.y)) + dm * kLn2 + gq;
+                top2_push(tp, kp, cb);
+                if (cb != cx) {
+                    top2_push(tx, kp, cb);
+                } else if (sxi > 0.0f) {
+                    top2_push(tx, static_cast<double>(logf(sxi)) + dm * kLn2 + gq, cb);
+                }
+            }
+        }
+    }
+    s = wave_sum_d(s);
+    tp = wave_top2(tp);
+    tx = wave_top2(tx);
+    if (lane == 0) {
+        sh.M[i] = m;
+        sh.S[i] = s;
+        sh.G[i] = -1;
+        sh.l1p[i] = level1_of(tp);
+        sh.l1x[i] = level1_of(tx);
+        if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
+        else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+    }
 }
 
 template <typename ET, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
+__global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
     __shared__ FinalShared sh;
     extern __shared__ double sW[];  // dense q: per-block residual mass [C]
     const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int k = a.k, kp1 = a.k + 1, V = a.V, C = a.C;
-    const float T = a.temperature[b];
+    const float T = uniform_load(a.temperature + b);
     const bool greedy = (T == 0.0f);
+    const bool bad_T = !greedy && !(T > 0.0f && T <= FLT_MAX);
     const PhiloxKey key = key_of(a.seed);
+    const float c = greedy || bad_T ? 0.0f : scale_of(T);
+    const bool one_hot = a.q == nullptr;
 
+    // ---- drafts, and the gathers at the drafts
+    int x = -1;
+    if (tid < k) x = a.draft[int64_t(b) * k + tid];
+    const bool xok = tid < k && x >= 0 && x < V;
+    float lx = 0.0f, qx = 1.0f;
+    uint32_t mw = 0xffffffffu;
+    if (xok && !bad_T) {
+        const int64_t rowi = int64_t(b) * kp1 + tid;
+        if (!greedy) lx = load_one<ET>(a.logits, rowi * V + x);
+        if (a.mask) mw = a.mask[rowi * a.W + (x >> 5)];
+        if (!greedy && !one_hot) qx = a.q[(int64_t(b) * k + tid) * V + x];
+    }
     if (tid == 0) {
-        sh.status = (greedy || (T > 0.0f && T <= FLT_MAX)) ? 0u : SD_STATUS_TEMPERATURE;
+        sh.status = bad_T ? SD_STATUS_TEMPERATURE : 0u;
         sh.nacc = 0;
         sh.flag_acc = 0;
         sh.ninvalid = 0;
+        sh.staged_c = -1;
     }
     __syncthreads();
     if (tid < k) {
-        const int x = a.draft[int64_t(b) * k + tid];
         sh.X[tid] = x;
-        if (x < 0 || x >= V) atomicOr(&sh.status, SD_STATUS_DRAFT_ID);
+        if (!xok) atomicOr(&sh.status, SD_STATUS_DRAFT_ID);
     }
     __syncthreads();
-    const float c = greedy ? 0.0f : scale_of(T);
 
-    // ---- fold block statistics into per-row max / normaliser / argmax
-    if (!(sh.status & SD_STATUS_TEMPERATURE)) {
-        for (int i = wave; i < kp1; i += kThreads / kWave) {
-            const float2 *st = a.bstats + (int64_t(b) * kp1 + i) * C;
-            bool bad = false;
+    // ---- one wave per row: fold the block statistics; sampling rows also run
+    //      their level-1 race and start loading the block they would sample
+    uint4 stage_r[G];
+    uint32_t stage_m[G];
+    int stage_row = -1, stage_c = -1;
+    if (!bad_T) {
+        for (int i = wave; i < kp1; i += kFinalWaves) {
+            const int64_t row = int64_t(b) * kp1 + i;
+            const float2 *st = a.bstats + row * C;
             if (greedy) {
-                float best = -INFINITY;
-                int bidx = INT_MAX;
-                for (int cb = lane; cb < C; cb += kWave) {
-                    const float2 e = st[cb];
-                    if (e.x != e.x || e.x == INFINITY) bad = true;
-                    if (e.x > best) {
-                        best = e.x;
-                        bidx = __float_as_int(e.y);
-                    }
-                }
-                bad = wave_any(bad);
-                const float m = wave_max(best);
-                const int gi = wave_min_i(best == m ? bidx : INT_MAX);
-                if (lane == 0) {
-                    sh.M[i] = m;
-                    sh.G[i] = gi;
-                    sh.S[i] = 1.0;
-                    if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
-                    else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
-                }
-            } else {
-                float mx = -INFINITY;
-                for (int cb = lane; cb < C; cb += kWave) {
-                    const float2 e = st[cb];
-                    if (e.x != e.x || e.y != e.y || e.x == INFINITY) bad = true;
-                    mx = fmaxf(mx, e.x);
-                }
-                bad = wave_any(bad);
-                const float m = wave_max(mx);
-                double s = 0.0;
-                if (!bad && m > -INFINITY) {
-                    for (int cb = lane; cb < C; cb += kWave) {
-                        const float2 e = st[cb];
-                        if (e.x > -INFINITY)
-                            s += static_cast<double>(e.y) *
-                                 exp2(static_cast<double>(e.x) - static_cast<double>(m));
-                    }
-                }
-                s = wave_sum_d(s);
-                if (lane == 0) {
-                    sh.M[i] = m;
-                    sh.S[i] = s;
-                    sh.G[i] = -1;
-                    if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
-                    else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+                fold_greedy_row(st, C, i, sh);
+                continue;
+            }
+            const int xi = (i < k) ? sh.X[i] : -1;
+            const int cx = (one_hot && xi >= 0 && xi < V) ? xi / kBlock : -1;
+            const float sxi = cx >= 0 ? uniform_load(a.sx + row) : 0.0f;
+            fold_sampling_row(st, C, i, b, cx, sxi, key, sh);
+            if (ALIGNED && kp1 <= kFinalWaves) {
+                const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
+                if (l1.c >= 0) {
+                    RowStatsArgs ra;  // only the fields issue_block reads
+                    ra.logits = a.logits;
+                    ra.mask = a.mask;
+                    ra.V = V;
+                    ra.W = a.W;
+                    SweepBlock sb;
+                    sb.row = static_cast<int>(row);
+                    sb.blk = l1.c;
+                    if (a.mask) issue_block<ET, true>(ra, sb, lane, stage_r, stage_m);
+                    else issue_block<ET, false>(ra, sb, lane, stage_r, stage_m);
+                    stage_row = i;
+                    stage_c = l1.c;
                 }
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- per-position accept probabilities and verdicts
     if (sh.status == 0 && tid < k) {
-        const int i = tid, x = sh.X[i];
-        const int64_t rowi = int64_t(b) * kp1 + i;
-        bool allowed = true;
-        if (a.mask) allowed = (a.mask[rowi * a.W + (x >> 5)] >> (x & 31)) & 1u;
+        const int i = tid;
+        const bool allowed = (mw >> (x & 31)) & 1u;
         sh.invalid[i] = !allowed;
         double acc;
         bool ok, flag = false;
@@ -499,16 +877,12 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
             ok = (x == sh.G[i]);
             acc = ok ? 1.0 : 0.0;
         } else {
-            const float lx = load_one<ET>(a.logits, rowi * V + x);
             double p = 0.0;
             if (allowed && lx > -INFINITY)
                 p = exp2(static_cast<double>(lx) * c - static_cast<double>(sh.M[i])) / sh.S[i];
-            double q = 1.0;
-            if (a.q) {
-                const float qf = a.q[(int64_t(b) * k + i) * V + x];
-                if (!(qf >= 0.0f && qf <= FLT_MAX)) atomicOr(&sh.status, SD_STATUS_BAD_DRAFT_PROB);
-                q = qf;
-            }
+            if (!one_hot && !(qx >= 0.0f && qx <= FLT_MAX))
+                atomicOr(&sh.status, SD_STATUS_BAD_DRAFT_PROB);
+            const double q = qx;
             acc = (p == 0.0) ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
             const double u = draw_accept(key, b, i);
             ok = u < acc;
@@ -518,7 +892,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
         sh.ok[i] = ok;
         sh.flag[i] = flag;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0 && sh.status == 0) {
         int n = 0, fa = 0, inv = 0;
         while (n < k && sh.ok[n]) fa += sh.flag[n++];
@@ -528,6 +902,28 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
         sh.flag_acc = fa;
         sh.ninvalid = inv;
     }
+    lds_barrier();
+
+    // ---- the wave that loaded the sampled row's block puts it in LDS
+    if (sh.status == 0 && stage_row >= 0 && stage_row == sh.nacc) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float v[P];
+            Logit<ET>::unpack(stage_r[g], v);
+            const int off = (g * kWave + lane) * P;  // token offset inside the block
+            const int64_t tok = int64_t(stage_c) * kBlock + off;
+            uint32_t bits = tok < V ? 0xffu : 0u;
+            if (a.mask) bits &= (P == 8) ? stage_m[g] : (stage_m[g] >> (uint32_t(tok) & 4u));
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if (!((bits >> e) & 1u)) v[e] = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < P / 4; ++h)
+                *reinterpret_cast<float4 *>(&sh.blockv[off + 4 * h]) =
+                    make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+        }
+        if (lane == 0) sh.staged_c = stage_c;
+    }
     __syncthreads();
 
     // ---- the emitted token
@@ -535,13 +931,49 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     int y = -1, fg = 0;
     if (st == 0) {
         const int n = sh.nacc;
-        if (greedy)
+        if (greedy) {
             y = sh.G[n];
-        else
-            y = sample_row<ET, ALIGNED>(a, sh, sW, b, n, c, T, &fg);
+        } else {
+            const double invT = 1.0 / static_cast<double>(T);
+            const float *qrow = (n < k && !one_hot) ? a.q + (int64_t(b) * k + n) * V : nullptr;
+            int mode = (n == k) ? kModeP : (one_hot ? kModeOneHot : kModeDense);
+            Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
+            if (mode == kModeDense) {
+                const int64_t row = int64_t(b) * kp1 + n;
+                dense_block_masses<ET, ALIGNED>(
+                    reinterpret_cast<const ET *>(a.logits) + row * V,
+                    a.mask ? a.mask + row * a.W : nullptr, qrow, V, C, c, sh.M[n], sh.S[n], sW);
+                __syncthreads();
+                Top2 t = top2_empty();
+                const int ngroups = (C + 3) >> 2;
+                for (int g4 = tid; g4 < ngroups; g4 += kFinalThreads) {
+                    float gum[4];
+                    draw_block_gumbels4(key, b, n, g4, gum);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int cb = 4 * g4 + q;
+                        if (cb < C && sW[cb] > 0.0)
+                            top2_push(t, log(sW[cb]) + static_cast<double>(gum[q]), cb);
+                    }
+                }
+                l1 = level1_of(block_top2<kFinalWaves>(t, sh.red_t));
+            }
+            if (l1.c < 0) {  // no residual mass: draw from p instead
+                mode = kModeP;
+                l1 = sh.l1p[n];
+            }
+            int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c);
+            if (r2.x < 0 && mode != kModeP) {  // the block lost its mass in double precision
+                mode = kModeP;
+                l1 = sh.l1p[n];
+                r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c);
+            }
+            y = r2.x;
+            fg = l1.flag + r2.y;
+        }
     }
 
-    // ---- outputs and the per-request record
+    // ---- outputs, and this request's share of the counters
     const int n = st ? -1 : sh.nacc;
     if (tid < kp1) {
         int tok = -1;
@@ -557,69 +989,21 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     if (tid < k && a.dbg_acc) a.dbg_acc[int64_t(b) * k + tid] = st ? NAN : sh.acc[tid];
     if (tid == 0) {
         a.out_num_accepted[b] = n;
-        int32_t *r = a.rec + int64_t(b) * kRecordWords;
-        r[0] = st ? 0 : k;
-        r[1] = st ? 0 : sh.ninvalid;
-        r[2] = st ? 0 : n;
-        r[3] = static_cast<int32_t>(st);
-        r[4] = st ? 0 : sh.flag_acc;
-        r[5] = st ? 0 : fg;
+        if (st) {
+            if (a.status) atomicOr(a.status, st);
+        } else {
+            // integer atomics: the sums do not depend on the order of arrival
+            atomicAdd(&a.out_counters[0], static_cast<unsigned long long>(k));
+            if (sh.ninvalid) atomicAdd(&a.out_counters[1], static_cast<unsigned long long>(sh.ninvalid));
+            atomicAdd(&a.out_counters[2], static_cast<unsigned long long>(k - sh.ninvalid));
+            if (n) atomicAdd(&a.out_counters[3], static_cast<unsigned long long>(n));
+            if (a.dbg_flags) {
+                if (sh.flag_acc) atomicAdd(&a.dbg_flags[0], static_cast<uint32_t>(sh.flag_acc));
+                if (fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
+            }
+        }
         if (a.dbg_req_flags)
             a.dbg_req_flags[b] = st ? 0u : (uint32_t(min(sh.flag_acc, 0xffff)) | (uint32_t(fg) << 16));
-    }
-
-    // ---- the last workgroup to finish sums the records in request order
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sh.last = (atomicAdd(a.ticket, 1u) == uint32_t(a.B - 1));
-    __syncthreads();
-    if (!sh.last) return;
-    __threadfence();
-    unsigned long long R = 0, I = 0, A = 0, FA = 0, FG = 0;
-    uint32_t S = 0;
-    for (int r = tid; r < a.B; r += kThreads) {
-        const int32_t *rr = a.rec + int64_t(r) * kRecordWords;
-        R += uint32_t(__hip_atomic_load(rr + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        I += uint32_t(__hip_atomic_load(rr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        A += uint32_t(__hip_atomic_load(rr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        S |= uint32_t(__hip_atomic_load(rr + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        FA += uint32_t(__hip_atomic_load(rr + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        FG += uint32_t(__hip_atomic_load(rr + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    }
-    R = wave_sum_u64(R);
-    I = wave_sum_u64(I);
-    A = wave_sum_u64(A);
-    FA = wave_sum_u64(FA);
-    FG = wave_sum_u64(FG);
-    S = wave_or_u32(S);
-    if (lane == 0) {
-        sh.red_u[wave][0] = R;
-        sh.red_u[wave][1] = I;
-        sh.red_u[wave][2] = A;
-        sh.red_u[wave][3] = (FA & 0xffffffffull) | (FG << 32);
-        sh.red_s[wave] = S;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        unsigned long long tr = 0, ti = 0, ta = 0, tfa = 0, tfg = 0;
-        uint32_t ts = 0;
-        for (int w = 0; w < kThreads / kWave; ++w) {
-            tr += sh.red_u[w][0];
-            ti += sh.red_u[w][1];
-            ta += sh.red_u[w][2];
-            tfa += sh.red_u[w][3] & 0xffffffffull;
-            tfg += sh.red_u[w][3] >> 32;
-            ts |= sh.red_s[w];
-        }
-        a.out_counters[0] = tr;
-        a.out_counters[1] = ti;
-        a.out_counters[2] = tr - ti;
-        a.out_counters[3] = ta;
-        if (a.status) *a.status = ts;
-        if (a.dbg_flags) {
-            a.dbg_flags[0] = static_cast<uint32_t>(tfa);
-            a.dbg_flags[1] = static_cast<uint32_t>(tfg);
-        }
     }
 }
 
@@ -637,8 +1021,8 @@ using FinalFn = void (*)(FinalArgs);
 
 template <typename ET>
 RowStatsFn pick_row_stats(bool masked, bool aligned) {
-    if (masked) return aligned ? row_stats_kernel<ET, true, true> : row_stats_kernel<ET, true, false>;
-    return aligned ? row_stats_kernel<ET, false, true> : row_stats_kernel<ET, false, false>;
+    if (aligned) return masked ? row_stats_vec_kernel<ET, true> : row_stats_vec_kernel<ET, false>;
+    return masked ? row_stats_elem_kernel<ET, true> : row_stats_elem_kernel<ET, false>;
 }
 
 template <typename ET>
@@ -649,7 +1033,7 @@ FinalFn pick_final(bool aligned) {
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_rec, off_ticket, total;
+    size_t off_bstats, off_sx, total;
 };
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -666,9 +1050,8 @@ inline Layout layout_of(const sd_params *p) {
     L.W = (p->vocab + 31) / 32;
     L.nchunk = (L.C + SDV_BLOCKS_PER_WAVE - 1) / SDV_BLOCKS_PER_WAVE;
     L.off_bstats = 0;
-    L.off_rec = align256(size_t(L.rows) * L.C * sizeof(float2));
-    L.off_ticket = L.off_rec + align256(size_t(p->batch) * kRecordWords * sizeof(int32_t));
-    L.total = L.off_ticket + 256;
+    L.off_sx = align256(size_t(L.rows) * L.C * sizeof(float2));
+    L.total = L.off_sx + align256(size_t(L.rows) * sizeof(float));
     return L;
 }
 
@@ -737,9 +1120,15 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.logits = target_logits;
     ra.mask = reinterpret_cast<const uint32_t *>(bitmask);
     ra.temperature = temperature;
+    ra.draft = draft_token_ids;
     ra.bstats = reinterpret_cast<float2 *>(ws + L.off_bstats);
-    ra.ticket = reinterpret_cast<uint32_t *>(ws + L.off_ticket);
+    ra.sx = reinterpret_cast<float *>(ws + L.off_sx);
+    ra.out_counters = out_counters;
+    ra.status = p->status;
+    ra.dbg_flags = p->dbg_flags;
     ra.ntasks = L.rows * L.nchunk;
+    ra.nblk = L.rows * L.C;
+    ra.k = k;
     ra.kp1 = k + 1;
     ra.V = V;
     ra.W = L.W;
@@ -747,7 +1136,9 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.cpw = SDV_BLOCKS_PER_WAVE;
     ra.nchunk = L.nchunk;
     const int64_t waves_per_wg = kThreads / kWave;
-    const int64_t grid1 = (ra.ntasks + waves_per_wg - 1) / waves_per_wg;
+    int64_t grid1 = aligned ? (ra.nblk + waves_per_wg - 1) / waves_per_wg
+                            : (ra.ntasks + waves_per_wg - 1) / waves_per_wg;
+    if (aligned) grid1 = std::min<int64_t>(grid1, SDV_ROW_STATS_GRID);
     if (grid1 > INT_MAX) return SD_ERR_UNSUPPORTED;
 
     FinalArgs fa;
@@ -766,8 +1157,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.dbg_flags = p->dbg_flags;
     fa.status = p->status;
     fa.bstats = ra.bstats;
-    fa.rec = reinterpret_cast<int32_t *>(ws + L.off_rec);
-    fa.ticket = ra.ticket;
+    fa.sx = ra.sx;
     fa.B = B;
     fa.k = k;
     fa.V = V;
@@ -786,7 +1176,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     if (p->row_stats_event_end &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_end), stream) != hipSuccess)
         return SD_ERR_HIP;
-    hipLaunchKernelGGL(k2, dim3(B), dim3(kThreads), dyn_lds, stream, fa);
+    hipLaunchKernelGGL(k2, dim3(B), dim3(kFinalThreads), dyn_lds, stream, fa);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     return SD_OK;
 }

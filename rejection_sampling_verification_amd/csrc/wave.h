@@ -1,10 +1,10 @@
 // Wave64 and workgroup reductions for gfx950.
 //
-// The float/int wave reductions run the classic GFX9 DPP ladder: row_shr 1, 2,
-// 4, 8 folds each row of 16 lanes into its lane 15, row_bcast:15 (rows 1 and 3)
-// and row_bcast:31 (rows 2 and 3) fold the rows into lane 63, which is then
-// read into a scalar.  Lanes whose DPP source is out of range keep the
-// identity.  Double-precision and pair reductions use cross-lane shuffles.
+// Wave reductions run the classic GFX9 DPP ladder: row_shr 1, 2, 4, 8 folds
+// each row of 16 lanes into its lane 15, row_bcast:15 (rows 1 and 3) and
+// row_bcast:31 (rows 2 and 3) fold the rows into lane 63, which is then read
+// into a scalar.  Lanes whose DPP source is out of range keep the identity.
+// Doubles move as two 32-bit halves.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -14,6 +14,12 @@
 namespace sdv {
 
 constexpr int kWave = 64;
+
+// Index of the calling wave in its workgroup, as a scalar (wave-uniform)
+// value, so that loops and branches over it stay on the scalar unit.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int dpp_i(int identity, int v) {
@@ -58,28 +64,29 @@ __device__ __forceinline__ int wave_min_i(int v) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_d(double identity, double v) {
+    const long long iv = __double_as_longlong(v), ii = __double_as_longlong(identity);
+    const int lo = dpp_i<CTRL, ROW_MASK>(static_cast<int>(ii), static_cast<int>(iv));
+    const int hi = dpp_i<CTRL, ROW_MASK>(static_cast<int>(ii >> 32), static_cast<int>(iv >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+    const long long iv = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(iv), lane);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(iv >> 32), lane);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-__device__ __forceinline__ double wave_max_d(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmax(v, __shfl_xor(v, m, kWave));
-    return v;
-}
-
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_d<0x111, 0xf>(0.0, v);
+    v += dpp_d<0x112, 0xf>(0.0, v);
+    v += dpp_d<0x114, 0xf>(0.0, v);
+    v += dpp_d<0x118, 0xf>(0.0, v);
+    v += dpp_d<0x142, 0xa>(0.0, v);
+    v += dpp_d<0x143, 0xc>(0.0, v);
+    return readlane_d(v, 63);
 }
 
 // Largest key with its index (lowest index on equal keys) and the runner-up key.
@@ -107,36 +114,47 @@ __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
     return Top2{a.k1, a.i1, fmax(b.k1, a.k2)};
 }
 
-__device__ __forceinline__ Top2 wave_top2(Top2 t) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        Top2 o{__shfl_xor(t.k1, m, kWave), __shfl_xor(t.i1, m, kWave), __shfl_xor(t.k2, m, kWave)};
-        t = top2_merge(t, o);
-    }
-    return t;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ Top2 top2_step(Top2 t) {
+    const Top2 o{dpp_d<CTRL, ROW_MASK>(-INFINITY, t.k1), dpp_i<CTRL, ROW_MASK>(INT_MAX, t.i1),
+                 dpp_d<CTRL, ROW_MASK>(-INFINITY, t.k2)};
+    return top2_merge(t, o);
 }
 
-// Workgroup-wide reductions for 256-thread workgroups (4 waves).  Every thread
-// gets the result.  `scratch` must hold 4 elements and is reused after return.
+// The wave's Top2, broadcast from lane 63 after the DPP ladder.
+__device__ __forceinline__ Top2 wave_top2(Top2 t) {
+    t = top2_step<0x111, 0xf>(t);
+    t = top2_step<0x112, 0xf>(t);
+    t = top2_step<0x114, 0xf>(t);
+    t = top2_step<0x118, 0xf>(t);
+    t = top2_step<0x142, 0xa>(t);
+    t = top2_step<0x143, 0xc>(t);
+    return Top2{readlane_d(t.k1, 63), __builtin_amdgcn_readlane(t.i1, 63), readlane_d(t.k2, 63)};
+}
+
+// Workgroup-wide reductions over NW waves.  Every thread gets the result.
+// `scratch` holds NW elements and may be reused once the call returns.
+template <int NW>
 __device__ __forceinline__ double block_sum_d(double v, double *scratch) {
     v = wave_sum_d(v);
-    const int w = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[w] = v;
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
     __syncthreads();
-    return scratch[0] + scratch[1] + scratch[2] + scratch[3];
+    double r = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) r += scratch[w];
+    return r;
 }
 
+template <int NW>
 __device__ __forceinline__ Top2 block_top2(Top2 t, Top2 *scratch) {
     t = wave_top2(t);
-    const int w = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[w] = t;
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = t;
     __syncthreads();
     Top2 r = scratch[0];
-    r = top2_merge(r, scratch[1]);
-    r = top2_merge(r, scratch[2]);
-    r = top2_merge(r, scratch[3]);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = top2_merge(r, scratch[w]);
     return r;
 }
 

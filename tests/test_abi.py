@@ -85,10 +85,10 @@ def test_workspace_size():
     assert sdv.sd_verify_workspace_size(4, -1, 100) == 0
     assert sdv.sd_verify_workspace_size(4, 65, 100) == 0
     assert sdv.sd_verify_workspace_size(4, 4, 0) == 0
-    # rows * blocks * 8 bytes of block statistics, per-request records, a ticket
+    # rows * blocks * 8 bytes of block statistics and 4 bytes per row
     ws = sdv.sd_verify_workspace_size(256, 4, 151936)
     rows, C = 256 * 5, -(-151936 // 2048)
-    assert ws >= rows * C * 8 + 256 * 32 and ws % 256 == 0
+    assert ws >= rows * C * 8 + rows * 4 and ws % 256 == 0
 
 
 def test_host_argument_checks_return_before_any_launch():

@@ -78,8 +78,8 @@ def test_stream_layout_matches_rocrand(rocrand_ref):
     w_tok = [r[0] for r in rocrand_ref(q_tok)]
     assert np.array_equal(philox.u_token(seed, b, a, js), philox.uniform_open(w_tok))
 
-    cs = [0, 1, 74]
-    q_blk = [(seed, b | (1 << 32), 4 * (c | (a << 32)), 1) for c in cs]
+    cs = [0, 1, 2, 3, 4, 74]
+    q_blk = [(seed, b | (1 << 32), 4 * ((c >> 2) | (a << 32)) + (c & 3), 1) for c in cs]
     w_blk = [r[0] for r in rocrand_ref(q_blk)]
     assert np.array_equal(philox.u_block(seed, b, a, cs), philox.uniform_open(w_blk))
 
