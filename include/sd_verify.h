@@ -20,10 +20,11 @@
  *   speculative decoding acceptance", "Name the three counters").
  *
  *   Every uniform comes from Philox4x32-10 (Salmon et al., SC'11) keyed by
- *   the 64-bit seed, with counters (0, i, b, 0) for the accept draw of
- *   position i, (c, a, b, 1) for block c and (j >> 2, a, b, 2) word j & 3 for
- *   token j of the sampled row a.  Sampling is two-level Gumbel-max over
- *   blocks of 2048 tokens.  Lowest index wins every tie.
+ *   the 64-bit seed: counter (0, i, b, 0) word 0 for the accept draw of
+ *   position i of request b; (c >> 2, a, b, 1) word c & 3 for block c and
+ *   (j >> 2, a, b, 2) word j & 3 for token j when row a is sampled.
+ *   Sampling is two-level Gumbel-max over blocks of 2048 tokens.  Lowest
+ *   index wins every tie.
  *
  * Conventions for every entry point:
  *   - "device" pointers address HIP device memory of the current device;
@@ -49,15 +50,16 @@ extern "C" {
 typedef enum {
     SD_OK = 0,
     SD_ERR_INVALID_ARG = -1, /* null required pointer, negative size, bad dtype */
-    SD_ERR_UNSUPPORTED = -2, /* k > SD_MAX_DRAFT or V > SD_MAX_VOCAB */
+    SD_ERR_UNSUPPORTED = -2, /* B > SD_MAX_BATCH, k > SD_MAX_DRAFT or V > SD_MAX_VOCAB */
     SD_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
     SD_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } sd_status;
 
 typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
 
+#define SD_MAX_BATCH 65535        /* largest supported B per call */
 #define SD_MAX_DRAFT 64           /* largest supported k */
-#define SD_MAX_VOCAB (1 << 23)    /* largest supported V (4096 blocks of 2048) */
+#define SD_MAX_VOCAB (1 << 22)    /* largest supported V (2048 blocks of 2048) */
 #define SD_BLOCK_TOKENS 2048      /* level-1 block of the two-level Gumbel-max */
 
 /* Data-error bits OR-ed into *params->status.  A request with any bit set
@@ -70,7 +72,7 @@ typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
 #define SD_STATUS_BAD_DRAFT_PROB 16u /* q at a draft token NaN, infinite or < 0 */
 
 typedef struct {
-    int32_t batch;      /* B >= 0 requests */
+    int32_t batch;      /* B, 0 <= B <= SD_MAX_BATCH requests */
     int32_t num_draft;  /* k, 0 <= k <= SD_MAX_DRAFT, the same for every request */
     int32_t vocab;      /* V, 1 <= V <= SD_MAX_VOCAB */
     sd_dtype logits_dtype;

@@ -22,8 +22,9 @@ LIBRARY_PATH = os.path.join(_PKG_DIR, "libsdverify.so")
 SD_OK = 0
 SD_DTYPE_F32 = 0
 SD_DTYPE_BF16 = 1
+SD_MAX_BATCH = 65535
 SD_MAX_DRAFT = 64
-SD_MAX_VOCAB = 1 << 23
+SD_MAX_VOCAB = 1 << 22
 SD_BLOCK_TOKENS = 2048
 
 SD_STATUS_DRAFT_ID = 1

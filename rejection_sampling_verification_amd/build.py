@@ -25,6 +25,9 @@ def compile_command(output=LIBRARY, extra=()):
         hipcc_path(), "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 VALU forms are kept out of every kernel
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # every atomic here is issued by one lane; the wave-combining rewrite
+        # would wait for an atomic's return right after issuing it
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", os.path.join(ROOT, "include"),
         *extra, "-o", output, SOURCE,
     ]

@@ -42,6 +42,9 @@
 #ifndef SDV_ROW_STATS_GRID
 #define SDV_ROW_STATS_GRID 2048 // vector kernel: workgroups of the block sweep
 #endif
+#ifndef SDV_LOGITS_CACHE_POLICY
+#define SDV_LOGITS_CACHE_POLICY 2  // logits loads: non-temporal (read once, kept out of the caches)
+#endif
 
 namespace sdv {
 
@@ -49,6 +52,10 @@ constexpr int kBlock = SD_BLOCK_TOKENS;
 constexpr int kThreads = 256;       // row statistics: 4 waves per workgroup
 constexpr int kFinalThreads = 512;  // finalize: 8 waves per request
 constexpr int kFinalWaves = kFinalThreads / 64;
+// s_waitcnt operand (GFX9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8) that waits for vmcnt = 0 only.
+constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kTallyStride = 32;  // 64-bit words between tally words: one 256-byte line each
 constexpr int kMaxDraft = SD_MAX_DRAFT;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kLn2 = 0.6931471805599453;
@@ -161,14 +168,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint3
 
 // ------------------------------------------------------------ row statistics
 
+// Statistics of one 2048-token block of a row.  Sampling rows: m = Mc =
+// fp32(max l * c), s = Sc = sum 2^(l c - Mc), key = ln Sc + Mc ln 2 + G_c, the
+// block's level-1 Gumbel key up to a per-row constant.  Greedy rows: m = the
+// largest logit, s = the lowest index holding it (int bits), key unused.
+struct BlockStat {
+    float m, s;
+    double key;
+};
+
+// What the sweep learns about the draft of row i < k, in the draft's block.
+struct DraftRec {
+    float sx;        // Sc of the draft's block without the draft
+    float lx;        // the draft's logit (-inf when masked)
+    float qx;        // the draft probability q_i(x), 1 for one-hot drafts
+    uint32_t allowed;  // the draft's mask bit
+    double keyx;     // level-1 key of the draft's block without the draft
+    double pad;
+};
+
 struct RowStatsArgs {
     const void *logits;
     const uint32_t *mask;     // nullptr = no bitmask
     const float *temperature;
     const int32_t *draft;     // [B, k]; nullptr when k = 0
-    float2 *bstats;           // [rows, C]
-    float *sx;                // [rows]: Sc of the draft's own block without the draft
-    uint64_t *out_counters;   // zeroed here, accumulated by finalize
+    const float *q;           // [B, k, V] or nullptr
+    uint64_t seed;
+    BlockStat *bstats;        // [rows, C]
+    DraftRec *drec;           // [rows]
+    unsigned long long *tally;  // counter tally, zeroed here, accumulated by finalize
+    int ntally;                 // words of the tally
     uint32_t *status;         // zeroed here when given
     uint32_t *dbg_flags;      // zeroed here when given
     int64_t ntasks;           // rows * nchunk (chunked element kernel)
@@ -191,6 +220,22 @@ __device__ __forceinline__ float2 softmax_block(const float *v, float c) {
 #pragma unroll
     for (int e = 0; e < NV; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mc));
     return make_float2(mc, wave_sum(s));
+}
+
+// The same sum without the token at offset xrel of the block (the one-hot
+// residual mass of the draft's block), against the same Mc.
+template <int G, int P>
+__device__ __forceinline__ float excluded_sum(const float *v, float c, float mc, int xrel, int lane) {
+    float s = 0.0f;
+    if (mc > -INFINITY) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if ((g * kWave + lane) * P + e != xrel)
+                    s += __builtin_amdgcn_exp2f(fmaf(v[g * P + e], c, -mc));
+    }
+    return wave_sum(s);
 }
 
 // Greedy rows: the block's largest logit and the lowest index holding it
@@ -218,19 +263,34 @@ __device__ __forceinline__ float2 greedy_block(const float *v, int64_t blk_base,
     return make_float2(m, __int_as_float(wave_min_i(idx)));
 }
 
+// The level-1 Gumbel variate of block blk of row i of request b.
+__device__ __forceinline__ float block_gumbel(PhiloxKey key, int b, int i, int blk) {
+    const uint4 w = philox4x32_10(make_uint4(uint32_t(blk) >> 2, uint32_t(i), uint32_t(b), 1u),
+                                  key.k0, key.k1);
+    const int q = blk & 3;
+    return gumbel_of(q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w)));
+}
+
+// ln(mass) + Mc ln 2 + G: a level-1 key up to the row's constant (-inf when
+// the mass is zero).
+__device__ __forceinline__ double key_of_mass(float mass, float mc, float g) {
+    if (!(mass > 0.0f) || !(mc > -INFINITY)) return -INFINITY;
+    return static_cast<double>(logf(mass)) + static_cast<double>(mc) * kLn2 + static_cast<double>(g);
+}
+
 __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
     if (blockIdx.x != 0) return;
-    if (threadIdx.x < 4) a.out_counters[threadIdx.x] = 0ull;
+    for (int w = threadIdx.x; w < a.ntally; w += blockDim.x) a.tally[w * kTallyStride] = 0ull;
     if (threadIdx.x == 0 && a.status) *a.status = 0u;
     if (threadIdx.x < 2 && a.dbg_flags) a.dbg_flags[threadIdx.x] = 0u;
 }
 
-// Which row a wave works on, and its parameters (all wave-uniform).
+// Which rows a chunked wave works on, and their parameters (wave-uniform).
 struct RowTask {
-    int row, c0, c1;
+    int row, b, i, c0, c1;
     bool greedy, skip;
     float c;
-    int xblk, xrel;  // the draft's block and offset in it (-1: none)
+    int x, xblk, xrel;  // the draft, its block and offset in it (-1: none)
 };
 
 __device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task) {
@@ -239,15 +299,17 @@ __device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task)
     const int chunk = static_cast<int>(task - int64_t(t.row) * a.nchunk);
     t.c0 = chunk * a.cpw;
     t.c1 = min(a.C, t.c0 + a.cpw);
-    const int b = t.row / a.kp1, i = t.row - b * a.kp1;
-    const float T = a.temperature[b];
+    t.b = t.row / a.kp1;
+    t.i = t.row - t.b * a.kp1;
+    const float T = uniform_load(a.temperature + t.b);
     t.greedy = (T == 0.0f);
     t.skip = !t.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     t.c = t.greedy ? 0.0f : scale_of(T);
-    t.xblk = t.xrel = -1;
-    if (!t.greedy && i < a.k) {
-        const int x = a.draft[int64_t(b) * a.k + i];
+    t.x = t.xblk = t.xrel = -1;
+    if (t.i < a.k) {
+        const int x = uniform_load(a.draft + int64_t(t.b) * a.k + t.i);
         if (x >= 0 && x < a.V) {
+            t.x = x;
             t.xblk = x / kBlock;
             t.xrel = x - t.xblk * kBlock;
         }
@@ -255,24 +317,34 @@ __device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task)
     return t;
 }
 
-// Raw 16-byte groups and mask bytes of one block wholly inside the row: lane
-// l reads groups l, l + 64, ... (consecutive lanes, consecutive 16 bytes).
-template <typename ET, bool MASKED>
-__device__ __forceinline__ void load_full_block(const ET *rowp, const uint8_t *mrow, int blk,
-                                                int lane, uint4 *r, uint32_t *m) {
-    constexpr int P = Logit<ET>::kPer16;
-    constexpr int G = kBlock / (kWave * P);
-    const uint4 *bp = reinterpret_cast<const uint4 *>(rowp + int64_t(blk) * kBlock) + lane;
+// The lane holding the draft writes its logit, its mask bit and q(x) into
+// the row's draft record.  v: the block's masked values; bits(g): the lane's
+// mask bits of group g.
+template <int G, int P, bool MASKED>
+__device__ __forceinline__ void record_draft(const RowStatsArgs &a, int row, int b, int i, int x,
+                                             int xrel, const float *v, const uint32_t *m, int lane,
+                                             float sx) {
+    const int xg = xrel / (kWave * P), xl = (xrel / P) & (kWave - 1), xe = xrel % P;
+    if (lane != xl) return;
+    float lx = -INFINITY;
+    uint32_t bits = 0xffu;
 #pragma unroll
-    for (int g = 0; g < G; ++g) r[g] = bp[g * kWave];
-    if (MASKED) {
-        // P tokens per group: the group's bits sit in byte (first token) / 8
-        const uint8_t *mb = mrow + int64_t(blk) * (kBlock / 8);
+    for (int g = 0; g < G; ++g)
+        if (g == xg) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) m[g] = mb[((g * kWave + lane) * P) >> 3];
-    }
+            for (int e = 0; e < P; ++e)
+                if (e == xe) lx = v[g * P + e];
+            if (MASKED) bits = (P == 8) ? m[g] : (m[g] >> ((lane & 1) * 4));
+        }
+    DraftRec &r = a.drec[row];
+    r.sx = sx;
+    r.lx = lx;
+    r.allowed = (bits >> xe) & 1u;
+    r.qx = a.q ? uniform_load(a.q + (int64_t(b) * a.k + i) * a.V + x) : 1.0f;
 }
 
+// Raw 16-byte groups and mask bytes of one block wholly inside the row: lane
+// l reads groups l, l + 64, ... (consecutive lanes, consecutive 16 bytes).
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void unpack_full_block(const uint4 *r, const uint32_t *m, int lane,
                                                   float *v) {
@@ -290,74 +362,13 @@ __device__ __forceinline__ void unpack_full_block(const uint4 *r, const uint32_t
     }
 }
 
-// Values of one lane for any block (used for the row's partial last block and
-// for re-reads): addresses clamped into the row, tokens past V and masked
-// tokens become -inf.
-template <typename ET, bool MASKED>
-__device__ __forceinline__ void load_any_block(const ET *rowp, const uint8_t *mrow, int blk, int V,
-                                               int lane, float *v) {
-    constexpr int P = Logit<ET>::kPer16;
-    constexpr int G = kBlock / (kWave * P);
-    uint4 r[G];
-    uint32_t m[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
-        const int64_t tc = tok < V ? tok : int64_t(V - P);
-        r[g] = *reinterpret_cast<const uint4 *>(rowp + tc);
-        m[g] = MASKED ? uint32_t(mrow[tc >> 3]) : 0xffu;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
-        Logit<ET>::unpack(r[g], v + g * P);
-        uint32_t bits = tok < V ? 0xffu : 0u;
-        if (MASKED) bits &= (P == 8) ? m[g] : (m[g] >> (uint32_t(tok) & 4u));
-#pragma unroll
-        for (int e = 0; e < P; ++e)
-            if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
-    }
-}
-
-template <bool GREEDY, int G, int P>
-__device__ __forceinline__ void store_block(const RowStatsArgs &a, const RowTask &t, const float *v,
-                                            int blk, int lane) {
-    const float2 r = GREEDY ? greedy_block<G, P>(v, int64_t(blk) * kBlock, lane)
-                            : softmax_block<G * P>(v, t.c);
-    if (lane == 0) a.bstats[int64_t(t.row) * a.C + blk] = r;
-}
-
-// The sum of the draft's own block without the draft (the one-hot residual
-// mass of that block), relative to the same Mc as the block statistics.
-template <int G, int P>
-__device__ __forceinline__ void store_excluded_sum(const RowStatsArgs &a, int row, float c, int xrel,
-                                                   const float *v, int lane) {
-    constexpr int NV = G * P;
-    float m = v[0];
-#pragma unroll
-    for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
-    m = wave_max(m);
-    float s = 0.0f;
-    if (m > -INFINITY) {
-        const float mc = m * c;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < P; ++e)
-                if ((g * kWave + lane) * P + e != xrel)
-                    s += __builtin_amdgcn_exp2f(fmaf(v[g * P + e], c, -mc));
-    }
-    s = wave_sum(s);
-    if (lane == 0) a.sx[row] = s;
-}
-
 // One block's share of the sweep: where it lives and its row's parameters.
 struct SweepBlock {
     int64_t gb;   // row * C + block
-    int row, blk;
+    int row, blk, b, i;
     bool full, greedy, skip;
     float c;
-    int xrel;     // the draft's offset in this block, -1 if the draft is elsewhere
+    int x, xrel;  // the draft and its offset in this block (-1: elsewhere)
 };
 
 __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t gb) {
@@ -366,15 +377,19 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t
     s.row = static_cast<int>(gb / a.C);
     s.blk = static_cast<int>(gb - int64_t(s.row) * a.C);
     s.full = int64_t(s.blk + 1) * kBlock <= a.V;
-    const int b = s.row / a.kp1, i = s.row - b * a.kp1;
-    const float T = uniform_load(a.temperature + b);
+    s.b = s.row / a.kp1;
+    s.i = s.row - s.b * a.kp1;
+    const float T = uniform_load(a.temperature + s.b);
     s.greedy = (T == 0.0f);
     s.skip = !s.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     s.c = s.greedy ? 0.0f : scale_of(T);
-    s.xrel = -1;
-    if (!s.greedy && i < a.k) {
-        const int x = uniform_load(a.draft + int64_t(b) * a.k + i);
-        if (x >= 0 && x < a.V && x / kBlock == s.blk) s.xrel = x - s.blk * kBlock;
+    s.x = s.xrel = -1;
+    if (s.i < a.k) {
+        const int x = uniform_load(a.draft + int64_t(s.b) * a.k + s.i);
+        if (x >= 0 && x < a.V && x / kBlock == s.blk) {
+            s.x = x;
+            s.xrel = x - s.blk * kBlock;
+        }
     }
     return s;
 }
@@ -394,7 +409,7 @@ __device__ __forceinline__ void issue_block(const RowStatsArgs &a, const SweepBl
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, 0);
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, SDV_LOGITS_CACHE_POLICY);
         r[g] = make_uint4(w.x, w.y, w.z, w.w);
     }
     if (MASKED) {
@@ -406,12 +421,38 @@ __device__ __forceinline__ void issue_block(const RowStatsArgs &a, const SweepBl
     }
 }
 
+// Per-lane record of one swept block, kept until the wave writes a batch of
+// up to 64 blocks: each lane then draws its block's level-1 Gumbel variate,
+// so one vector pass serves 64 blocks.
+struct Stash {
+    int64_t gb;
+    int row, b, i, blk;
+    float m, s, sx;
+    int kind;  // 0 none, 1 greedy, 2 sampling, 3 sampling with the draft in it
+};
+
+__device__ __forceinline__ void flush_stash(const RowStatsArgs &a, const Stash &st, PhiloxKey key,
+                                            int lane, int count) {
+    if (lane >= count || st.kind == 0) return;
+    BlockStat out;
+    out.m = st.m;
+    out.s = st.s;
+    out.key = -INFINITY;
+    if (st.kind >= 2 && st.m > -INFINITY) {
+        const float g = block_gumbel(key, st.b, st.i, st.blk);
+        out.key = key_of_mass(st.s, st.m, g);
+        if (st.kind == 3) a.drec[st.row].keyx = key_of_mass(st.sx, st.m, g);
+    } else if (st.kind == 3) {
+        a.drec[st.row].keyx = -INFINITY;
+    }
+    a.bstats[st.gb] = out;
+}
+
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
-                                             const uint4 *r, const uint32_t *m) {
+                                             const uint4 *r, const uint32_t *m, Stash &st, int slot) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
-    if (s.skip) return;
     float v[G * P];
     if (s.full) {
         unpack_full_block<ET, MASKED>(r, m, lane, v);
@@ -428,13 +469,25 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
         }
     }
     float2 res;
+    float sx = 0.0f;
     if (s.greedy) {
         res = greedy_block<G, P>(v, int64_t(s.blk) * kBlock, lane);
     } else {
         res = softmax_block<G * P>(v, s.c);
-        if (s.xrel >= 0) store_excluded_sum<G, P>(a, s.row, s.c, s.xrel, v, lane);
+        if (s.xrel >= 0) sx = excluded_sum<G, P>(v, s.c, res.x, s.xrel, lane);
     }
-    if (lane == 0) a.bstats[s.gb] = res;
+    if (s.xrel >= 0) record_draft<G, P, MASKED>(a, s.row, s.b, s.i, s.x, s.xrel, v, m, lane, sx);
+    if (lane == slot) {
+        st.gb = s.gb;
+        st.row = s.row;
+        st.b = s.b;
+        st.i = s.i;
+        st.blk = s.blk;
+        st.m = res.x;
+        st.s = res.y;
+        st.sx = sx;
+        st.kind = s.greedy ? 1 : (s.xrel >= 0 ? 3 : 2);
+    }
 }
 
 // Rows 16-byte aligned with V a multiple of the group width.  The grid sweeps
@@ -451,8 +504,12 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
     zero_call_outputs(a);
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t stride = int64_t(gridDim.x) * (kThreads / kWave);
-    int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
+    const int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
     if (g0 >= a.nblk) return;
+    const PhiloxKey key = key_of(a.seed);
+    Stash st;
+    st.kind = 0;
+    int count = 0;
     uint4 ra[G], rb[G];
     uint32_t ma[G], mb[G];
     SweepBlock sa = sweep_block(a, g0);
@@ -462,34 +519,52 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
         const bool more1 = g1 < a.nblk;
         const SweepBlock sb = sweep_block(a, more1 ? g1 : sa.gb);
         issue_block<ET, MASKED>(a, sb, lane, rb, mb);
-        reduce_block<ET, MASKED>(a, sa, lane, ra, ma);
+        if (!sa.skip) reduce_block<ET, MASKED>(a, sa, lane, ra, ma, st, count++);
+        if (count == kWave) {
+            flush_stash(a, st, key, lane, count);
+            st.kind = 0;
+            count = 0;
+        }
         if (!more1) break;
         const int64_t g2 = sb.gb + stride;
         const bool more2 = g2 < a.nblk;
         sa = sweep_block(a, more2 ? g2 : sb.gb);
         issue_block<ET, MASKED>(a, sa, lane, ra, ma);
-        reduce_block<ET, MASKED>(a, sb, lane, rb, mb);
+        if (!sb.skip) reduce_block<ET, MASKED>(a, sb, lane, rb, mb, st, count++);
+        if (count == kWave) {
+            flush_stash(a, st, key, lane, count);
+            st.kind = 0;
+            count = 0;
+        }
         if (!more2) break;
     }
+    flush_stash(a, st, key, lane, count);
 }
 
-// Any alignment and any V: element loads clamped into the row.
+// Any alignment and any V: element loads clamped into the row, one chunk of
+// blocks of one row per wave.
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void load_block_elem(const ET *rowp, const uint8_t *mrow, int blk, int V,
-                                                int lane, float *v) {
+                                                int lane, float *v, uint32_t *m) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+        uint32_t bits = 0u;
 #pragma unroll
         for (int e = 0; e < P; ++e) {
             const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P + e;
             const int64_t tc = tok < V ? tok : int64_t(V - 1);
             const float x = Logit<ET>::to_float(rowp[tc]);
             bool live = tok < V;
-            if (MASKED) live = live && ((mrow[tc >> 3] >> (tc & 7)) & 1u);
+            const bool mbit = MASKED ? ((mrow[tc >> 3] >> (tc & 7)) & 1u) : true;
+            live = live && mbit;
+            bits |= uint32_t(mbit) << e;
             v[g * P + e] = live ? x : -INFINITY;
         }
+        // bits already aligned to the group, as record_draft reads them for P == 8
+        m[g] = (P == 8) ? bits : (bits << ((lane & 1) * 4));
+    }
 }
 
 template <typename ET, bool MASKED>
@@ -502,18 +577,34 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
     if (task >= a.ntasks) return;
     const RowTask t = row_task(a, task);
     if (t.skip) return;
+    const PhiloxKey key = key_of(a.seed);
     const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(t.row) * a.V;
     const uint8_t *mrow =
         MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(t.row) * a.W) : nullptr;
     float v[G * P];
+    uint32_t m[G];
     for (int blk = t.c0; blk < t.c1; ++blk) {
-        load_block_elem<ET, MASKED>(rowp, mrow, blk, a.V, lane, v);
+        load_block_elem<ET, MASKED>(rowp, mrow, blk, a.V, lane, v, m);
+        BlockStat out;
+        out.key = -INFINITY;
+        float sx = 0.0f;
         if (t.greedy) {
-            store_block<true, G, P>(a, t, v, blk, lane);
+            const float2 r = greedy_block<G, P>(v, int64_t(blk) * kBlock, lane);
+            out.m = r.x;
+            out.s = r.y;
         } else {
-            store_block<false, G, P>(a, t, v, blk, lane);
-            if (blk == t.xblk) store_excluded_sum<G, P>(a, t.row, t.c, t.xrel, v, lane);
+            const float2 r = softmax_block<G * P>(v, t.c);
+            out.m = r.x;
+            out.s = r.y;
+            const float g = block_gumbel(key, t.b, t.i, blk);
+            out.key = key_of_mass(r.y, r.x, g);
+            if (blk == t.xblk) {
+                sx = excluded_sum<G, P>(v, t.c, r.x, t.xrel, lane);
+                if (lane == 0) a.drec[t.row].keyx = key_of_mass(sx, r.x, g);
+            }
         }
+        if (blk == t.xblk) record_draft<G, P, true>(a, t.row, t.b, t.i, t.x, t.xrel, v, m, lane, sx);
+        if (lane == 0) a.bstats[int64_t(t.row) * a.C + blk] = out;
     }
 }
 
@@ -529,13 +620,15 @@ struct FinalArgs {
     int32_t *out_tokens;
     int32_t *out_num_accepted;
     uint64_t *out_counters;
+    unsigned long long *tally;  // nslot slot words, then the two call words
+    int nslot;
     double *dbg_lse;
     double *dbg_acc;
     uint32_t *dbg_req_flags;
     uint32_t *dbg_flags;
     uint32_t *status;
-    const float2 *bstats;
-    const float *sx;
+    const BlockStat *bstats;
+    const DraftRec *drec;
     int B, k, V, W, C;
 };
 
@@ -553,27 +646,27 @@ struct FinalShared {
     Level1 l1p[kMaxDraft + 1];  // level-1 winner under p
     Level1 l1x[kMaxDraft + 1];  // level-1 winner under p without the row's draft
     int X[kMaxDraft];
+    float lx[kMaxDraft], qx[kMaxDraft];
+    double keyx[kMaxDraft];
     double acc[kMaxDraft];
     unsigned char ok[kMaxDraft], flag[kMaxDraft], invalid[kMaxDraft];
     uint32_t status;
     int nacc, flag_acc, ninvalid;
     int staged_c;               // block of the sampled row held in blockv (-1: none)
     double red_d[kFinalWaves];
-    Top2 red_t[kFinalWaves];
+    uint64_t red_u[kFinalWaves];
+    uint32_t red_b[kFinalWaves];
     float blockv[kBlock];       // that block's logits, -inf where masked or past V
 };
 
-// Workgroup barrier that orders LDS only: global loads a wave has in flight
-// stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+// Gumbel keys are compared in fp32 relative to a per-row constant, where
+// they stay within about 2e-6 of their exact values; packed with their index
+// (wave.h) one 64-bit maximum finds the winner, lowest index on ties, and a
+// ballot finds whether another key lies within the near-tie threshold.
+constexpr float kTieEps = static_cast<float>(kGumbelFlagEps);
 
-__device__ __forceinline__ Level1 level1_of(const Top2 &t) {
-    if (t.k1 == -INFINITY) return Level1{-1, 0};
-    return Level1{t.i1, (t.k2 > -INFINITY && t.k1 - t.k2 < kGumbelFlagEps) ? 1 : 0};
+__device__ __forceinline__ bool near_tie(float key, int idx, uint64_t best) {
+    return idx != packed_index(best) && key >= packed_key(best) - kTieEps;
 }
 
 // Residual masses W_c = sum_j max(p_j - q_j, 0) of one row for dense q, with
@@ -683,36 +776,42 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb
     draw_token_gumbels4(key_of(a.seed), b, n, static_cast<uint32_t>(j0), g);
     const float M = sh.M[n];
     const double S = sh.S[n];
-    Top2 t = top2_empty();
+    const double lref = static_cast<double>(M) / static_cast<double>(c);  // about the row's max logit
+    float keys[4];
+    uint64_t best = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t j = j0 + e;
+        keys[e] = -INFINITY;
         if (!(lv[e] > -INFINITY)) continue;  // masked, -inf, or past V
-        double key2;
         if (mode == kModeDense) {
             const double p = exp2(static_cast<double>(lv[e]) * c - static_cast<double>(M)) / S;
             const double r = p - static_cast<double>(qrow[j]);
             if (!(r > 0.0)) continue;
-            key2 = log(r);
+            keys[e] = static_cast<float>(log(r) + static_cast<double>(g[e]));
         } else {
             if (mode == kModeOneHot && j == x) continue;
-            key2 = static_cast<double>(lv[e]) * invT;
+            keys[e] = static_cast<float>((static_cast<double>(lv[e]) - lref) * invT + static_cast<double>(g[e]));
         }
-        top2_push(t, key2 + static_cast<double>(g[e]), static_cast<int>(j));
+        best = max_u64(best, pack_key(keys[e], static_cast<int>(j)));
     }
-    t = block_top2<kFinalWaves>(t, sh.red_t);
-    if (t.k1 == -INFINITY) return make_int2(-1, 0);
-    return make_int2(t.i1, (t.k2 > -INFINITY && t.k1 - t.k2 < kGumbelFlagEps) ? 1 : 0);
+    best = block_max_u64<kFinalWaves>(best, sh.red_u);
+    if (best == 0) return make_int2(-1, 0);
+    bool tie = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (keys[e] > -INFINITY) tie |= near_tie(keys[e], static_cast<int>(j0 + e), best);
+    return make_int2(packed_index(best), block_any<kFinalWaves>(tie, sh.red_b) ? 1 : 0);
 }
 
 // Fold one greedy row's block statistics (one wave): max and lowest argmax.
-__device__ __forceinline__ void fold_greedy_row(const float2 *st, int C, int i, FinalShared &sh) {
+__device__ __forceinline__ void fold_greedy_row(const BlockStat *st, int C, int i, FinalShared &sh) {
     const int lane = threadIdx.x & (kWave - 1);
     bool bad = false;
     float best = -INFINITY;
     int bidx = INT_MAX;
     for (int cb = lane; cb < C; cb += kWave) {
-        const float2 e = st[cb];
+        const float2 e = *reinterpret_cast<const float2 *>(&st[cb]);
         if (e.x != e.x || e.x == INFINITY) bad = true;
         if (e.x > best) {
             best = e.x;
@@ -731,62 +830,123 @@ __device__ __forceinline__ void fold_greedy_row(const float2 *st, int C, int i, 
     }
 }
 
+// 2^d for d <= 0 in double precision from an fp32 exp2 of the fractional
+// part (relative error of a few 1e-8).
+__device__ __forceinline__ double exp2_nonpos(double d) {
+    const double n = floor(d);
+    return ldexp(static_cast<double>(__builtin_amdgcn_exp2f(static_cast<float>(d - n))),
+                 static_cast<int>(n));
+}
+
 // Fold one sampling row's block statistics (one wave) into its max and
-// normaliser, and run the row's level-1 Gumbel race over block masses, both
-// under p and under p without block cx's draft (mass sxi instead of Sc).
-__device__ __forceinline__ void fold_sampling_row(const float2 *st, int C, int i, int b, int cx,
-                                                  float sxi, PhiloxKey key, FinalShared &sh) {
+// normaliser, and finish its level-1 races over the keys the sweep drew:
+// under p, and under p with block cx's key replaced by the draft-excluded
+// key keyx.
+__device__ __forceinline__ void fold_sampling_row(const BlockStat *st, int C, int i, int cx,
+                                                  double keyx, FinalShared &sh) {
     const int lane = threadIdx.x & (kWave - 1);
     bool bad = false;
     float mx = -INFINITY;
     for (int cb = lane; cb < C; cb += kWave) {
-        const float2 e = st[cb];
+        const float2 e = *reinterpret_cast<const float2 *>(&st[cb]);
         if (e.x != e.x || e.y != e.y || e.x == INFINITY) bad = true;
         mx = fmaxf(mx, e.x);
     }
     bad = wave_any(bad);
     const float m = wave_max(mx);
+    const double ref = static_cast<double>(m) * kLn2;  // keys relative to the row
     double s = 0.0;
-    Top2 tp = top2_empty(), tx = top2_empty();
+    uint64_t bp = 0, bx = 0;
     if (!bad && m > -INFINITY) {
-        const int ngroups = (C + 3) >> 2;
-        for (int g4 = lane; g4 < ngroups; g4 += kWave) {
-            float gum[4];
-            draw_block_gumbels4(key, b, i, g4, gum);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int cb = 4 * g4 + q;
-                if (cb >= C) break;
-                const float2 e = st[cb];
-                if (!(e.x > -INFINITY) || !(e.y > 0.0f)) continue;
-                const double dm = static_cast<double>(e.x) - static_cast<double>(m);
-                s += static_cast<double>(e.y) * exp2(dm);
-                const double gq = static_cast<double>(gum[q]);
-                const double kp = static_cast<double>(logf(e.y)) + dm * kLn2 + gq;
-                top2_push(tp, kp, cb);
-                if (cb != cx) {
-                    top2_push(tx, kp, cb);
-                } else if (sxi > 0.0f) {
-                    top2_push(tx, static_cast<double>(logf(sxi)) + dm * kLn2 + gq, cb);
-                }
-            }
+        for (int cb = lane; cb < C; cb += kWave) {
+            const BlockStat e = st[cb];
+            if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
+            s += static_cast<double>(e.s) * exp2_nonpos(static_cast<double>(e.m) - static_cast<double>(m));
+            const float kp = static_cast<float>(e.key - ref);
+            bp = max_u64(bp, pack_key(kp, cb));
+            if (cb != cx) bx = max_u64(bx, pack_key(kp, cb));
+            else if (keyx > -INFINITY) bx = max_u64(bx, pack_key(static_cast<float>(keyx - ref), cb));
         }
     }
     s = wave_sum_d(s);
-    tp = wave_top2(tp);
-    tx = wave_top2(tx);
+    bp = wave_max_u64(bp);
+    bx = wave_max_u64(bx);
+    bool tp = false, tx = false;
+    if (bp != 0) {
+        for (int cb = lane; cb < C; cb += kWave) {
+            const BlockStat e = st[cb];
+            if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
+            const float kp = static_cast<float>(e.key - ref);
+            tp |= near_tie(kp, cb, bp);
+            if (cb != cx) tx |= near_tie(kp, cb, bx);
+            else if (keyx > -INFINITY) tx |= near_tie(static_cast<float>(keyx - ref), cb, bx);
+        }
+    }
+    tp = wave_any(tp);
+    tx = wave_any(tx);
     if (lane == 0) {
         sh.M[i] = m;
         sh.S[i] = s;
         sh.G[i] = -1;
-        sh.l1p[i] = level1_of(tp);
-        sh.l1x[i] = level1_of(tx);
+        sh.l1p[i] = bp ? Level1{packed_index(bp), tp ? 1 : 0} : Level1{-1, 0};
+        sh.l1x[i] = bx ? Level1{packed_index(bx), tx ? 1 : 0} : Level1{-1, 0};
         if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
         else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
     }
 }
 
-template <typename ET, bool ALIGNED>
+// Counters of the call.  Every workgroup finishes at about the same time, so
+// one word hit by all of them would serialise their atomics; instead request
+// b adds to slot word b % nslot, and the request that completes a slot adds
+// the slot's sums to the two call words.  Each level packs the arrival count
+// with the sums into one 64-bit word, so the workgroup that completes a level
+// reads that level's totals in its own atomic's return value: no fence and
+// no ordering between different words is needed, and the integer sums do not
+// depend on the order of arrival.
+//   slot word:  arrivals [0,12)  accepted [12,30)  outside grammar [30,48)  errors [48,60)
+//   call word 0: slots [0,9)  accepted [9,33)  errors [33,50)   -> writes R and A
+//   call word 1: slots [0,9)  outside grammar [9,33)  errors [33,50)  -> writes I and D
+// Field widths hold B <= 65535 with at most 256 slots of at most 256 requests.
+__device__ __forceinline__ unsigned long long tally_share(int accepted, int invalid, bool error) {
+    return 1ull | (static_cast<unsigned long long>(accepted) << 12) |
+           (static_cast<unsigned long long>(invalid) << 30) | (error ? (1ull << 48) : 0ull);
+}
+
+// Adds request b's share to its slot word; returns the word's previous value.
+// The caller reads the result as late as it can, so that the atomic's round
+// trip overlaps other work.
+__device__ __forceinline__ unsigned long long tally_slot(const FinalArgs &a, int b,
+                                                         unsigned long long share) {
+    return atomicAdd(&a.tally[(b % a.nslot) * kTallyStride], share);
+}
+
+// `before` is what tally_slot returned for request b with `share`.
+__device__ __forceinline__ void tally_call(const FinalArgs &a, int b, unsigned long long before,
+                                           unsigned long long share) {
+    const unsigned long long slot = before + share;
+    const int S = a.nslot, s = b % S;
+    const int members = (a.B - s + S - 1) / S;  // requests b' < B with b' % S == s
+    if (static_cast<int>(slot & 0xfffull) != members) return;
+    const unsigned long long acc = (slot >> 12) & 0x3ffffull, inv = (slot >> 30) & 0x3ffffull,
+                             err = (slot >> 48) & 0xfffull;
+    unsigned long long *call = a.tally + S * kTallyStride;
+    const unsigned long long w0 = 1ull | (acc << 9) | (err << 33);
+    const unsigned long long w1 = 1ull | (inv << 9) | (err << 33);
+    const unsigned long long t0 = atomicAdd(&call[0], w0) + w0;
+    const unsigned long long t1 = atomicAdd(&call[kTallyStride], w1) + w1;
+    const uint64_t k = static_cast<uint64_t>(a.k), B = static_cast<uint64_t>(a.B);
+    if (static_cast<int>(t0 & 0x1ffull) == S) {
+        a.out_counters[0] = k * (B - ((t0 >> 33) & 0x1ffffull));
+        a.out_counters[3] = (t0 >> 9) & 0xffffffull;
+    }
+    if (static_cast<int>(t1 & 0x1ffull) == S) {
+        const uint64_t I = (t1 >> 9) & 0xffffffull;
+        a.out_counters[1] = I;
+        a.out_counters[2] = k * (B - ((t1 >> 33) & 0x1ffffull)) - I;
+    }
+}
+
+template <typename ET, bool ALIGNED, bool DENSE>
 __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -800,20 +960,14 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     const bool bad_T = !greedy && !(T > 0.0f && T <= FLT_MAX);
     const PhiloxKey key = key_of(a.seed);
     const float c = greedy || bad_T ? 0.0f : scale_of(T);
-    const bool one_hot = a.q == nullptr;
+    constexpr bool one_hot = !DENSE;
 
-    // ---- drafts, and the gathers at the drafts
+    // ---- drafts, and what the sweep recorded about them
     int x = -1;
     if (tid < k) x = a.draft[int64_t(b) * k + tid];
     const bool xok = tid < k && x >= 0 && x < V;
-    float lx = 0.0f, qx = 1.0f;
-    uint32_t mw = 0xffffffffu;
-    if (xok && !bad_T) {
-        const int64_t rowi = int64_t(b) * kp1 + tid;
-        if (!greedy) lx = load_one<ET>(a.logits, rowi * V + x);
-        if (a.mask) mw = a.mask[rowi * a.W + (x >> 5)];
-        if (!greedy && !one_hot) qx = a.q[(int64_t(b) * k + tid) * V + x];
-    }
+    DraftRec rec;
+    if (tid < k) rec = a.drec[int64_t(b) * kp1 + tid];  // read only when xok and T is valid
     if (tid == 0) {
         sh.status = bad_T ? SD_STATUS_TEMPERATURE : 0u;
         sh.nacc = 0;
@@ -825,6 +979,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     if (tid < k) {
         sh.X[tid] = x;
         if (!xok) atomicOr(&sh.status, SD_STATUS_DRAFT_ID);
+        sh.lx[tid] = rec.lx;
+        sh.qx[tid] = rec.qx;
+        sh.keyx[tid] = rec.keyx;
+        sh.invalid[tid] = !(rec.allowed & 1u);
     }
     __syncthreads();
 
@@ -836,15 +994,14 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     if (!bad_T) {
         for (int i = wave; i < kp1; i += kFinalWaves) {
             const int64_t row = int64_t(b) * kp1 + i;
-            const float2 *st = a.bstats + row * C;
+            const BlockStat *st = a.bstats + row * C;
             if (greedy) {
                 fold_greedy_row(st, C, i, sh);
                 continue;
             }
             const int xi = (i < k) ? sh.X[i] : -1;
             const int cx = (one_hot && xi >= 0 && xi < V) ? xi / kBlock : -1;
-            const float sxi = cx >= 0 ? uniform_load(a.sx + row) : 0.0f;
-            fold_sampling_row(st, C, i, b, cx, sxi, key, sh);
+            fold_sampling_row(st, C, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
             if (ALIGNED && kp1 <= kFinalWaves) {
                 const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
                 if (l1.c >= 0) {
@@ -866,41 +1023,42 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     }
     lds_barrier();
 
-    // ---- per-position accept probabilities and verdicts
-    if (sh.status == 0 && tid < k) {
-        const int i = tid;
-        const bool allowed = (mw >> (x & 31)) & 1u;
-        sh.invalid[i] = !allowed;
-        double acc;
-        bool ok, flag = false;
-        if (greedy) {
-            ok = (x == sh.G[i]);
-            acc = ok ? 1.0 : 0.0;
-        } else {
-            double p = 0.0;
-            if (allowed && lx > -INFINITY)
-                p = exp2(static_cast<double>(lx) * c - static_cast<double>(sh.M[i])) / sh.S[i];
-            if (!one_hot && !(qx >= 0.0f && qx <= FLT_MAX))
-                atomicOr(&sh.status, SD_STATUS_BAD_DRAFT_PROB);
-            const double q = qx;
-            acc = (p == 0.0) ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-            const double u = draw_accept(key, b, i);
-            ok = u < acc;
-            flag = fabs(u - acc) < kAcceptFlagEps;
+    // ---- per-position accept probabilities and verdicts; wave 0 holds the
+    //      k <= 64 positions and scans them with ballots
+    if (wave == 0 && sh.status == 0) {
+        bool ok = false, flag = false, inv = false;
+        double acc = 0.0;
+        if (lane < k) {
+            const int xi = sh.X[lane];
+            inv = sh.invalid[lane];
+            if (greedy) {
+                ok = (xi == sh.G[lane]);
+                acc = ok ? 1.0 : 0.0;
+            } else {
+                const float lx = sh.lx[lane], qx = sh.qx[lane];
+                double p = 0.0;
+                if (!inv && lx > -INFINITY)
+                    p = exp2(static_cast<double>(lx) * c - static_cast<double>(sh.M[lane])) / sh.S[lane];
+                if (!one_hot && !(qx >= 0.0f && qx <= FLT_MAX))
+                    atomicOr(&sh.status, SD_STATUS_BAD_DRAFT_PROB);
+                const double q = qx;
+                acc = (p == 0.0) ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                const double u = draw_accept(key, b, lane);
+                ok = u < acc;
+                flag = fabs(u - acc) < kAcceptFlagEps;
+            }
+            sh.acc[lane] = acc;
         }
-        sh.acc[i] = acc;
-        sh.ok[i] = ok;
-        sh.flag[i] = flag;
-    }
-    lds_barrier();
-    if (tid == 0 && sh.status == 0) {
-        int n = 0, fa = 0, inv = 0;
-        while (n < k && sh.ok[n]) fa += sh.flag[n++];
-        if (n < k) fa += sh.flag[n];
-        for (int i = 0; i < k; ++i) inv += sh.invalid[i];
-        sh.nacc = n;
-        sh.flag_acc = fa;
-        sh.ninvalid = inv;
+        const uint64_t okm = __ballot(ok), flm = __ballot(flag), invm = __ballot(inv);
+        const uint64_t kmask = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
+        const uint64_t rejected = ~okm & kmask;
+        const int n = rejected ? __builtin_ctzll(rejected) : k;      // first rejection
+        const uint64_t scanned = n < k ? ((2ull << n) - 1ull) : kmask;  // positions tested
+        if (lane == 0) {
+            sh.nacc = n;
+            sh.flag_acc = __popcll(flm & scanned);
+            sh.ninvalid = __popcll(invm);
+        }
     }
     lds_barrier();
 
@@ -924,7 +1082,20 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
         }
         if (lane == 0) sh.staged_c = stage_c;
     }
-    __syncthreads();
+    // The request's share of the counters is known now: its atomic is issued
+    // here and completes while the emitted token is drawn (every barrier from
+    // here on waits for LDS traffic only).
+    unsigned long long share = 0, before = 0;
+    // Loads still in flight finish first (they were issued long ago): the
+    // memory counter retires in order, so a later wait for one of them would
+    // also wait for the atomic.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (tid == 0) {
+        const bool err = sh.status != 0;
+        share = tally_share(err ? 0 : sh.nacc, err ? 0 : sh.ninvalid, err);
+        before = tally_slot(a, b, share);
+    }
+    lds_barrier();
 
     // ---- the emitted token
     const uint32_t st = sh.status;
@@ -935,41 +1106,56 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             y = sh.G[n];
         } else {
             const double invT = 1.0 / static_cast<double>(T);
-            const float *qrow = (n < k && !one_hot) ? a.q + (int64_t(b) * k + n) * V : nullptr;
-            int mode = (n == k) ? kModeP : (one_hot ? kModeOneHot : kModeDense);
+            const float *qrow = (DENSE && n < k) ? a.q + (int64_t(b) * k + n) * V : nullptr;
+            int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
-            if (mode == kModeDense) {
+            if (DENSE && mode == kModeDense) {
                 const int64_t row = int64_t(b) * kp1 + n;
                 dense_block_masses<ET, ALIGNED>(
                     reinterpret_cast<const ET *>(a.logits) + row * V,
                     a.mask ? a.mask + row * a.W : nullptr, qrow, V, C, c, sh.M[n], sh.S[n], sW);
-                __syncthreads();
-                Top2 t = top2_empty();
+                lds_barrier();
+                // residual masses are <= 1, so their keys need no reference
                 const int ngroups = (C + 3) >> 2;
-                for (int g4 = tid; g4 < ngroups; g4 += kFinalThreads) {
+                float kq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                const int g4 = tid;  // one group of four blocks per thread
+                uint64_t best = 0;
+                if (g4 < ngroups) {
                     float gum[4];
                     draw_block_gumbels4(key, b, n, g4, gum);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int cb = 4 * g4 + q;
-                        if (cb < C && sW[cb] > 0.0)
-                            top2_push(t, log(sW[cb]) + static_cast<double>(gum[q]), cb);
+                        if (cb < C && sW[cb] > 0.0) {
+                            kq[q] = static_cast<float>(log(sW[cb]) + static_cast<double>(gum[q]));
+                            best = max_u64(best, pack_key(kq[q], cb));
+                        }
                     }
                 }
-                l1 = level1_of(block_top2<kFinalWaves>(t, sh.red_t));
+                best = block_max_u64<kFinalWaves>(best, sh.red_u);
+                bool tie = false;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (kq[q] > -INFINITY) tie |= near_tie(kq[q], 4 * g4 + q, best);
+                tie = block_any<kFinalWaves>(tie, sh.red_b);
+                l1 = best ? Level1{packed_index(best), tie ? 1 : 0} : Level1{-1, 0};
             }
-            if (l1.c < 0) {  // no residual mass: draw from p instead
-                mode = kModeP;
-                l1 = sh.l1p[n];
+            // A zero residual mass, or a block that lost its mass in double
+            // precision, falls back to drawing from p.
+            for (int attempt = 0; attempt < 2; ++attempt) {
+                if (l1.c < 0) {
+                    mode = kModeP;
+                    l1 = sh.l1p[n];
+                }
+                const int2 r2 =
+                    level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c);
+                if (r2.x >= 0) {
+                    y = r2.x;
+                    fg = l1.flag + r2.y;
+                    break;
+                }
+                l1.c = -1;
             }
-            int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c);
-            if (r2.x < 0 && mode != kModeP) {  // the block lost its mass in double precision
-                mode = kModeP;
-                l1 = sh.l1p[n];
-                r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c);
-            }
-            y = r2.x;
-            fg = l1.flag + r2.y;
         }
     }
 
@@ -989,21 +1175,15 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     if (tid < k && a.dbg_acc) a.dbg_acc[int64_t(b) * k + tid] = st ? NAN : sh.acc[tid];
     if (tid == 0) {
         a.out_num_accepted[b] = n;
-        if (st) {
-            if (a.status) atomicOr(a.status, st);
-        } else {
-            // integer atomics: the sums do not depend on the order of arrival
-            atomicAdd(&a.out_counters[0], static_cast<unsigned long long>(k));
-            if (sh.ninvalid) atomicAdd(&a.out_counters[1], static_cast<unsigned long long>(sh.ninvalid));
-            atomicAdd(&a.out_counters[2], static_cast<unsigned long long>(k - sh.ninvalid));
-            if (n) atomicAdd(&a.out_counters[3], static_cast<unsigned long long>(n));
-            if (a.dbg_flags) {
-                if (sh.flag_acc) atomicAdd(&a.dbg_flags[0], static_cast<uint32_t>(sh.flag_acc));
-                if (fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
-            }
-        }
         if (a.dbg_req_flags)
             a.dbg_req_flags[b] = st ? 0u : (uint32_t(min(sh.flag_acc, 0xffff)) | (uint32_t(fg) << 16));
+        if (st) {
+            if (a.status) atomicOr(a.status, st);
+        } else if (a.dbg_flags) {
+            if (sh.flag_acc) atomicAdd(&a.dbg_flags[0], static_cast<uint32_t>(sh.flag_acc));
+            if (fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
+        }
+        tally_call(a, b, before, share);
     }
 }
 
@@ -1026,21 +1206,31 @@ RowStatsFn pick_row_stats(bool masked, bool aligned) {
 }
 
 template <typename ET>
-FinalFn pick_final(bool aligned) {
-    return aligned ? finalize_kernel<ET, true> : finalize_kernel<ET, false>;
+FinalFn pick_final(bool aligned, bool dense) {
+    if (dense) return aligned ? finalize_kernel<ET, true, true> : finalize_kernel<ET, false, true>;
+    return aligned ? finalize_kernel<ET, true, false> : finalize_kernel<ET, false, false>;
 }
 
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_sx, total;
+    size_t off_bstats, off_drec, off_tally, total;
+    int nslot;
 };
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 inline bool sizes_ok(const sd_params *p) {
-    return p && p->batch >= 0 && p->num_draft >= 0 && p->num_draft <= SD_MAX_DRAFT &&
+    return p && p->batch >= 0 && p->batch <= SD_MAX_BATCH && p->num_draft >= 0 &&
+           p->num_draft <= SD_MAX_DRAFT &&
            p->vocab >= 1 && p->vocab <= SD_MAX_VOCAB;
+}
+
+// Slots of the counter tally: about sqrt(B), at most 256.
+inline int tally_slots(int B) {
+    int s = 1;
+    while (s < 256 && s * s < B) ++s;
+    return s;
 }
 
 inline Layout layout_of(const sd_params *p) {
@@ -1050,8 +1240,10 @@ inline Layout layout_of(const sd_params *p) {
     L.W = (p->vocab + 31) / 32;
     L.nchunk = (L.C + SDV_BLOCKS_PER_WAVE - 1) / SDV_BLOCKS_PER_WAVE;
     L.off_bstats = 0;
-    L.off_sx = align256(size_t(L.rows) * L.C * sizeof(float2));
-    L.total = L.off_sx + align256(size_t(L.rows) * sizeof(float));
+    L.off_drec = align256(size_t(L.rows) * L.C * sizeof(BlockStat));
+    L.off_tally = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
+    L.nslot = tally_slots(p->batch);
+    L.total = L.off_tally + align256(size_t(L.nslot + 2) * kTallyStride * sizeof(uint64_t));
     return L;
 }
 
@@ -1121,9 +1313,12 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.mask = reinterpret_cast<const uint32_t *>(bitmask);
     ra.temperature = temperature;
     ra.draft = draft_token_ids;
-    ra.bstats = reinterpret_cast<float2 *>(ws + L.off_bstats);
-    ra.sx = reinterpret_cast<float *>(ws + L.off_sx);
-    ra.out_counters = out_counters;
+    ra.q = draft_probs;
+    ra.seed = seed;
+    ra.bstats = reinterpret_cast<BlockStat *>(ws + L.off_bstats);
+    ra.drec = reinterpret_cast<DraftRec *>(ws + L.off_drec);
+    ra.tally = reinterpret_cast<unsigned long long *>(ws + L.off_tally);
+    ra.ntally = L.nslot + 2;
     ra.status = p->status;
     ra.dbg_flags = p->dbg_flags;
     ra.ntasks = L.rows * L.nchunk;
@@ -1151,13 +1346,15 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.out_tokens = out_tokens;
     fa.out_num_accepted = out_num_accepted;
     fa.out_counters = out_counters;
+    fa.tally = ra.tally;
+    fa.nslot = L.nslot;
     fa.dbg_lse = p->dbg_row_lse;
     fa.dbg_acc = p->dbg_accept_prob;
     fa.dbg_req_flags = p->dbg_request_flags;
     fa.dbg_flags = p->dbg_flags;
     fa.status = p->status;
     fa.bstats = ra.bstats;
-    fa.sx = ra.sx;
+    fa.drec = ra.drec;
     fa.B = B;
     fa.k = k;
     fa.V = V;
@@ -1166,7 +1363,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     const size_t dyn_lds = draft_probs ? size_t(L.C) * sizeof(double) : 0;
 
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned) : pick_row_stats<float>(masked, aligned);
-    FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned) : pick_final<float>(aligned);
+    FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr)
+                      : pick_final<float>(aligned, draft_probs != nullptr);
 
     if (p->row_stats_event_begin &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_begin), stream) != hipSuccess)

@@ -89,57 +89,68 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return readlane_d(v, 63);
 }
 
-// Largest key with its index (lowest index on equal keys) and the runner-up key.
-struct Top2 {
-    double k1;
-    int i1;
-    double k2;
-};
-
-__device__ __forceinline__ Top2 top2_empty() { return Top2{-INFINITY, INT_MAX, -INFINITY}; }
-
-__device__ __forceinline__ void top2_push(Top2 &t, double key, int idx) {
-    if (key > t.k1 || (key == t.k1 && idx < t.i1)) {
-        t.k2 = t.k1;
-        t.k1 = key;
-        t.i1 = idx;
-    } else if (key > t.k2) {
-        t.k2 = key;
-    }
+// Order-preserving unsigned code of a float: for non-NaN a, b,
+// a > b  <=>  code(a) > code(b).
+__device__ __forceinline__ uint32_t ordered_code(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
-    if (b.k1 > a.k1 || (b.k1 == a.k1 && b.i1 < a.i1))
-        return Top2{b.k1, b.i1, fmax(a.k1, b.k2)};
-    return Top2{a.k1, a.i1, fmax(b.k1, a.k2)};
+__device__ __forceinline__ float float_of_code(uint32_t c) {
+    return __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
+}
+
+// A key and its index in one word: the larger word holds the larger key, and
+// the lower index among equal keys.  0 stands for "no candidate".
+__device__ __forceinline__ uint64_t pack_key(float key, int idx) {
+    return (static_cast<uint64_t>(ordered_code(key)) << 32) | (0xffffffffu - static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ float packed_key(uint64_t p) { return float_of_code(static_cast<uint32_t>(p >> 32)); }
+
+__device__ __forceinline__ int packed_index(uint64_t p) {
+    return static_cast<int>(0xffffffffu - static_cast<uint32_t>(p));
 }
 
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ Top2 top2_step(Top2 t) {
-    const Top2 o{dpp_d<CTRL, ROW_MASK>(-INFINITY, t.k1), dpp_i<CTRL, ROW_MASK>(INT_MAX, t.i1),
-                 dpp_d<CTRL, ROW_MASK>(-INFINITY, t.k2)};
-    return top2_merge(t, o);
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {  // out-of-range lanes read 0
+    const int lo = dpp_i<CTRL, ROW_MASK>(0, static_cast<int>(static_cast<uint32_t>(v)));
+    const int hi = dpp_i<CTRL, ROW_MASK>(0, static_cast<int>(static_cast<uint32_t>(v >> 32)));
+    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
 }
 
-// The wave's Top2, broadcast from lane 63 after the DPP ladder.
-__device__ __forceinline__ Top2 wave_top2(Top2 t) {
-    t = top2_step<0x111, 0xf>(t);
-    t = top2_step<0x112, 0xf>(t);
-    t = top2_step<0x114, 0xf>(t);
-    t = top2_step<0x118, 0xf>(t);
-    t = top2_step<0x142, 0xa>(t);
-    t = top2_step<0x143, 0xc>(t);
-    return Top2{readlane_d(t.k1, 63), __builtin_amdgcn_readlane(t.i1, 63), readlane_d(t.k2, 63)};
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<0x111, 0xf>(v));
+    v = max_u64(v, dpp_u64<0x112, 0xf>(v));
+    v = max_u64(v, dpp_u64<0x114, 0xf>(v));
+    v = max_u64(v, dpp_u64<0x118, 0xf>(v));
+    v = max_u64(v, dpp_u64<0x142, 0xa>(v));
+    v = max_u64(v, dpp_u64<0x143, 0xc>(v));
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Workgroup-wide reductions over NW waves.  Every thread gets the result.
-// `scratch` holds NW elements and may be reused once the call returns.
+// Workgroup barrier that orders LDS traffic only: unlike __syncthreads it
+// does not wait for the calling wave's outstanding global loads, stores and
+// atomics.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup-wide reductions over NW waves through LDS; every thread gets the
+// result.  `scratch` holds NW elements.  Each call starts with a barrier, so
+// a scratch array may be reused by the next call.
 template <int NW>
 __device__ __forceinline__ double block_sum_d(double v, double *scratch) {
     v = wave_sum_d(v);
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     double r = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) r += scratch[w];
@@ -147,15 +158,27 @@ __device__ __forceinline__ double block_sum_d(double v, double *scratch) {
 }
 
 template <int NW>
-__device__ __forceinline__ Top2 block_top2(Top2 t, Top2 *scratch) {
-    t = wave_top2(t);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = t;
-    __syncthreads();
-    Top2 r = scratch[0];
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch) {
+    v = wave_max_u64(v);
+    lds_barrier();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    lds_barrier();
+    uint64_t r = scratch[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) r = top2_merge(r, scratch[w]);
+    for (int w = 1; w < NW; ++w) r = max_u64(r, scratch[w]);
     return r;
+}
+
+template <int NW>
+__device__ __forceinline__ bool block_any(bool p, uint32_t *scratch) {
+    const bool w = wave_any(p);
+    lds_barrier();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = w ? 1u : 0u;
+    lds_barrier();
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) r |= scratch[i];
+    return r != 0;
 }
 
 }  // namespace sdv

@@ -106,8 +106,11 @@ def test_host_argument_checks_return_before_any_launch():
     assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -1
     p.logits_dtype, p.num_draft = 1, 65
     assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -2
-    p.num_draft, p.vocab = 3, (1 << 23) + 1
+    p.num_draft, p.vocab = 3, (1 << 22) + 1
     assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -2
+    p.vocab, p.batch = 100, 65536
+    assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -2
+    p.batch = 4
     # missing required tensors
     p.vocab = 100
     assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -1
