@@ -11,10 +11,16 @@ Printed as one JSON line, with
   roofline      the row-statistics kernel's algorithmic bytes (logits + mask)
                 over its average duration, timed with HIP events recorded
                 around that kernel on the launch stream, against 8 TB/s HBM;
-  cpu_baseline  the CPU oracle timed on the host over the same workload.
+                `traffic` is the HBM bytes per launch that rocprofv3's
+                FETCH_SIZE and WRITE_SIZE counters measured on the current
+                kernel sources (null when the sources changed since);
+  cpu_baseline  the CPU oracle timed on the host over a sample of the same
+                workload.
 
   python bench.py [--steps K] [--warmup W] [--workload ngram]
   python bench.py --copy-calibration    # plain 1 GiB device copy, for PMC scaling
+  python bench.py --summarize-pmc FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
+      # turns four `rocprofv3 --pmc` counter files into the traffic summary
 """
 import argparse
 import hashlib
@@ -48,7 +54,7 @@ def measured_traffic(digest):
     if it was taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
-            kv = dict(line.split(":", 1) for line in f if ":" in line)
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
@@ -60,19 +66,89 @@ def measured_traffic(digest):
         return None
 
 
+COPY_BYTES = 1 << 30
+
+
 def copy_calibration():
+    """A plain device copy of COPY_BYTES: reads and writes exactly that many
+    bytes per launch, which scales the PMC byte counters."""
     import torch
-    n = 1 << 30
-    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
-                      "launches": 5}), flush=True)
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES,
+                      "copy_calibration_bytes_written": COPY_BYTES, "launches": 5}), flush=True)
 
 
-def cpu_baseline(wl, n_requests):
+def copy_ceiling_gbps():
+    """Read+write GB/s of a plain 1 GiB device copy: a practical ceiling."""
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * COPY_BYTES * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def _pmc_rows(path, counter):
+    import csv
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                yield row.get("Kernel_Name", ""), float(row["Counter_Value"])
+
+
+def _mean_kib(path, counter, match):
+    vals = [v for name, v in _pmc_rows(path, counter) if match(name)]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for the kernel in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per row-statistics launch: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled by what the same counter reads for the plain
+    copy of COPY_BYTES."""
+    is_k1 = lambda n: "row_stats" in n
+    is_copy = lambda n: "copy" in n.lower()  # the copy itself, not the fill before it
+    f_k1, n_f = _mean_kib(fetch_csv, "FETCH_SIZE", is_k1)
+    w_k1, n_w = _mean_kib(write_csv, "WRITE_SIZE", is_k1)
+    f_cp, _ = _mean_kib(copy_fetch_csv, "FETCH_SIZE", is_copy)
+    w_cp, _ = _mean_kib(copy_write_csv, "WRITE_SIZE", is_copy)
+    f_scale = COPY_BYTES / (f_cp * 1024.0)
+    w_scale = COPY_BYTES / (w_cp * 1024.0)
+    fetch_b = f_k1 * 1024.0 * f_scale
+    write_b = w_k1 * 1024.0 * w_scale
+    lines = [
+        f"source_digest: {source_digest()}",
+        f"row_stats_dispatches: {n_f} (FETCH_SIZE run), {n_w} (WRITE_SIZE run)",
+        f"row_stats_fetch_kib_per_dispatch: {f_k1:.1f}",
+        f"row_stats_write_kib_per_dispatch: {w_k1:.1f}",
+        f"copy_fetch_kib_per_dispatch: {f_cp:.1f} (plain copy of {COPY_BYTES} bytes)",
+        f"copy_write_kib_per_dispatch: {w_cp:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"hbm_write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]
+    print("\n".join(lines))
+
+
+def cpu_baseline(wl, n_requests, min_seconds=10.0):
+    """The oracle on one host thread, repeated over the first n_requests
+    requests of the workload until at least min_seconds have passed."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -80,17 +156,22 @@ def cpu_baseline(wl, n_requests):
     from workloads import to_numpy
     req = list(range(n_requests))
     host = to_numpy(wl, req)
+    passes = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.sd_verify(host["logits"], host["draft_token_ids"], host["draft_probs"],
-                         host["bitmask"], host["temperature"], seed=wl["seed"],
-                         top_k=host["top_k"], request_ids=req)
-        dt = time.perf_counter() - t0
+        while True:
+            oracle.sd_verify(host["logits"], host["draft_token_ids"], host["draft_probs"],
+                             host["bitmask"], host["temperature"], seed=wl["seed"],
+                             top_k=host["top_k"], request_ids=req)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
     k = host["draft_token_ids"].shape[1]
-    return {"value": n_requests * k / dt, "unit": "verified draft positions/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n_requests} of {wl['logits'].shape[0]} requests of the same workload, "
-                      f"float64 NumPy, one thread, {dt:.2f} s",
+    return {"value": passes * n_requests * k / dt, "unit": "verified draft positions/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over {n_requests} of the {wl['logits'].shape[0]} requests "
+                      f"of the same workload, float64 NumPy on one thread, {dt:.1f} s",
             "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
 
 
@@ -98,13 +179,20 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # the clocks settle only after some hundreds of calls
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="ngram")
-    ap.add_argument("--copies", type=int, default=3)
+    # input copies rotated over: 4 x 389 MB keeps the 256 MB cache cold
+    ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-requests", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar="CSV")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this verifier build runs on "
@@ -151,6 +239,15 @@ def main():
     value = B * k / step_s
     print(f"[bench] timed {args.steps} steps: {step_s * 1e6:.1f} us/step", file=sys.stderr, flush=True)
 
+    # ---- per-call distribution: HIP events between consecutive calls
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for s in range(args.steps):
+        v(copies[s % len(copies)], *call_args)
+        marks[s + 1].record()
+    torch.cuda.synchronize()
+    call_us = sorted(marks[s].elapsed_time(marks[s + 1]) * 1e3 for s in range(args.steps))
+
     # ---- timed region: row-statistics kernel alone, HIP events around it
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)]
@@ -177,6 +274,7 @@ def main():
     algo = algorithmic_bytes(wl, n_res)
     flags = [int(f) for f in r.flags.cpu().tolist()]
 
+    ceiling = copy_ceiling_gbps()
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -199,7 +297,10 @@ def main():
                                f"{'bf16' if lg.dtype == torch.bfloat16 else 'fp32'} logits, "
                                f"{'one-hot' if wl['draft_probs'] is None else 'dense'} drafts",
                    "batch": B, "num_draft": k, "vocab": V, "input_copies": len(copies)},
+        "call_us": {"p10": call_us[len(call_us) // 10], "p50": call_us[len(call_us) // 2],
+                    "p90": call_us[(9 * len(call_us)) // 10]},
         "hbm_gbps_whole_call": algo / step_s / 1e9,
+        "plain_copy_gbps": ceiling,
         "algorithmic_bytes_per_call": algo,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

@@ -161,6 +161,9 @@ __device__ __forceinline__ T uniform_load(const T *p) {
 // format).  Loads at offsets >= bytes return zero instead of faulting.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Byte offset beyond every buffer_of range (rows are at most 16 MiB).
+constexpr int kPastAnyBuffer = 0x40000000;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
                                              kBufferWord3);
@@ -400,12 +403,14 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t
 // when the block is reduced).
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void issue_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
-                                            uint4 *r, uint32_t *m) {
+                                            uint4 *r, uint32_t *m, bool live = true) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     const __amdgpu_buffer_rsrc_t rs = buffer_of(
         reinterpret_cast<const ET *>(a.logits) + int64_t(s.row) * a.V, uint32_t(a.V) * sizeof(ET));
-    const int base = s.blk * kBlock * int(sizeof(ET)) + lane * 16;
+    // A dead issue (the sweep's look-ahead past its last block) points past
+    // the end of the buffer: such loads return zeros and touch no memory.
+    const int base = live ? s.blk * kBlock * int(sizeof(ET)) + lane * 16 : kPastAnyBuffer;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -414,7 +419,7 @@ __device__ __forceinline__ void issue_block(const RowStatsArgs &a, const SweepBl
     }
     if (MASKED) {
         const __amdgpu_buffer_rsrc_t rm = buffer_of(a.mask + int64_t(s.row) * a.W, uint32_t(a.W) * 4u);
-        const int mbase = s.blk * (kBlock / 8) + ((lane * P) >> 3);
+        const int mbase = live ? s.blk * (kBlock / 8) + ((lane * P) >> 3) : kPastAnyBuffer;
 #pragma unroll
         for (int g = 0; g < G; ++g)
             m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, mbase + g * kWave * P / 8, 0, 0);
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
         const int64_t g1 = sa.gb + stride;
         const bool more1 = g1 < a.nblk;
         const SweepBlock sb = sweep_block(a, more1 ? g1 : sa.gb);
-        issue_block<ET, MASKED>(a, sb, lane, rb, mb);
+        issue_block<ET, MASKED>(a, sb, lane, rb, mb, more1);
         if (!sa.skip) reduce_block<ET, MASKED>(a, sa, lane, ra, ma, st, count++);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
         const int64_t g2 = sb.gb + stride;
         const bool more2 = g2 < a.nblk;
         sa = sweep_block(a, more2 ? g2 : sb.gb);
-        issue_block<ET, MASKED>(a, sa, lane, ra, ma);
+        issue_block<ET, MASKED>(a, sa, lane, ra, ma, more2);
         if (!sb.skip) reduce_block<ET, MASKED>(a, sb, lane, rb, mb, st, count++);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
