@@ -197,6 +197,7 @@ struct RowStatsArgs {
     const int32_t *draft;     // [B, k]; nullptr when k = 0
     const float *q;           // [B, k, V] or nullptr
     uint64_t seed;
+    const float *tau;         // [rows] top-k thresholds, or nullptr (no top-k)
     BlockStat *bstats;        // [rows, C]
     DraftRec *drec;           // [rows]
     unsigned long long *tally;  // counter tally, zeroed here, accumulated by finalize
@@ -266,6 +267,15 @@ __device__ __forceinline__ float2 greedy_block(const float *v, int64_t blk_base,
     return make_float2(m, __int_as_float(wave_min_i(idx)));
 }
 
+// Tokens below the row's top-k threshold leave the support like masked ones
+// (NaN stays NaN, so that a bad logit is still reported).
+template <int NV>
+__device__ __forceinline__ void apply_tau(float *v, float tau) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e)
+        if (v[e] < tau) v[e] = -INFINITY;
+}
+
 // The level-1 Gumbel variate of block blk of row i of request b.
 __device__ __forceinline__ float block_gumbel(PhiloxKey key, int b, int i, int blk) {
     const uint4 w = philox4x32_10(make_uint4(uint32_t(blk) >> 2, uint32_t(i), uint32_t(b), 1u),
@@ -292,7 +302,7 @@ __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
 struct RowTask {
     int row, b, i, c0, c1;
     bool greedy, skip;
-    float c;
+    float c, tau;
     int x, xblk, xrel;  // the draft, its block and offset in it (-1: none)
 };
 
@@ -308,6 +318,7 @@ __device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task)
     t.greedy = (T == 0.0f);
     t.skip = !t.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     t.c = t.greedy ? 0.0f : scale_of(T);
+    t.tau = a.tau ? uniform_load(a.tau + t.row) : -INFINITY;
     t.x = t.xblk = t.xrel = -1;
     if (t.i < a.k) {
         const int x = uniform_load(a.draft + int64_t(t.b) * a.k + t.i);
@@ -370,7 +381,7 @@ struct SweepBlock {
     int64_t gb;   // row * C + block
     int row, blk, b, i;
     bool full, greedy, skip;
-    float c;
+    float c, tau;
     int x, xrel;  // the draft and its offset in this block (-1: elsewhere)
 };
 
@@ -386,6 +397,7 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t
     s.greedy = (T == 0.0f);
     s.skip = !s.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     s.c = s.greedy ? 0.0f : scale_of(T);
+    s.tau = a.tau ? uniform_load(a.tau + s.row) : -INFINITY;
     s.x = s.xrel = -1;
     if (s.i < a.k) {
         const int x = uniform_load(a.draft + int64_t(s.b) * a.k + s.i);
@@ -453,7 +465,7 @@ __device__ __forceinline__ void flush_stash(const RowStatsArgs &a, const Stash &
     a.bstats[st.gb] = out;
 }
 
-template <typename ET, bool MASKED>
+template <typename ET, bool MASKED, bool TOPK>
 __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
                                              const uint4 *r, const uint32_t *m, Stash &st, int slot) {
     constexpr int P = Logit<ET>::kPer16;
@@ -473,6 +485,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
                 if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
         }
     }
+    if (TOPK) apply_tau<G * P>(v, s.tau);
     float2 res;
     float sx = 0.0f;
     if (s.greedy) {
@@ -502,7 +515,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
 // its next block in flight while it reduces the current one; the next index
 // is clamped to the current block at the end of the sweep, so every path
 // reaches a reduction with the same loads outstanding.
-template <typename ET, bool MASKED>
+template <typename ET, bool MASKED, bool TOPK>
 __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
         const bool more1 = g1 < a.nblk;
         const SweepBlock sb = sweep_block(a, more1 ? g1 : sa.gb);
         issue_block<ET, MASKED>(a, sb, lane, rb, mb, more1);
-        if (!sa.skip) reduce_block<ET, MASKED>(a, sa, lane, ra, ma, st, count++);
+        if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
             st.kind = 0;
@@ -535,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
         const bool more2 = g2 < a.nblk;
         sa = sweep_block(a, more2 ? g2 : sb.gb);
         issue_block<ET, MASKED>(a, sa, lane, ra, ma, more2);
-        if (!sb.skip) reduce_block<ET, MASKED>(a, sb, lane, rb, mb, st, count++);
+        if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
             st.kind = 0;
@@ -572,7 +585,7 @@ __device__ __forceinline__ void load_block_elem(const ET *rowp, const uint8_t *m
     }
 }
 
-template <typename ET, bool MASKED>
+template <typename ET, bool MASKED, bool TOPK>
 __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -590,6 +603,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
     uint32_t m[G];
     for (int blk = t.c0; blk < t.c1; ++blk) {
         load_block_elem<ET, MASKED>(rowp, mrow, blk, a.V, lane, v, m);
+        if (TOPK) apply_tau<G * P>(v, t.tau);
         BlockStat out;
         out.key = -INFINITY;
         float sx = 0.0f;
@@ -613,6 +627,220 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
     }
 }
 
+// ------------------------------------------------------------------ top-k
+
+// Per row of a sampling request with top_k = K > 0: tau = the K-th largest
+// allowed finite logit, counted with multiplicity, or -inf when the row holds
+// at most K such logits (pyshine "vLLM, part 2", "Verification: rejection
+// sampling on the GPU": top-k is applied to the logits before the accept
+// test).  The kept set is {allowed, finite, l >= tau}: every tie at the K-th
+// value stays.  Greedy rows, rows with top-k off and rows of requests with a
+// bad temperature get -inf.  The row statistics and the sampler then treat
+// l < tau like a masked token.
+//
+// Selection runs on order-preserving 32-bit codes of the values.  The top 16
+// bits (the bf16 value itself) are counted in a histogram over a window of
+// 1024 consecutive codes placed just above the largest code of the row's first
+// 16 KB; elements above the window are only counted.  When the K-th largest
+// lies outside the window, the window moves (another pass over the row) in the
+// one direction that can hold it.  For fp32 rows two more passes pick the low
+// two bytes among the elements that share the selected top half.
+struct TopkArgs {
+    const void *logits;
+    const uint32_t *mask;
+    const float *temperature;
+    const int32_t *top_k;
+    float *tau;  // [rows]
+    int kp1, V, W;
+};
+
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kTopkWindow = 1024;
+
+struct TopkShared {
+    uint32_t hist[kTopkWindow];
+    uint32_t part[kTopkThreads];  // per-thread sums of 4 bins, scanned in place
+    uint32_t red[kTopkWaves];
+    uint32_t found_digit, found_rank;
+};
+
+// The P values of one 16-byte group of the row at token `tok` with excluded
+// tokens (masked, past V, NaN, +-inf) as NaN.
+template <typename ET, bool ALIGNED>
+__device__ __forceinline__ void topk_group(const ET *rowp, const uint8_t *mrow, int V, int64_t tok,
+                                           float *v) {
+    constexpr int P = Logit<ET>::kPer16;
+    load_group<ET, ALIGNED>(rowp, tok, V, v);
+    uint32_t bits = 0xffu;
+    if (mrow != nullptr && tok < V) {
+        if (ALIGNED) {
+            const uint32_t byte = mrow[tok >> 3];
+            bits = (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
+        } else {
+            bits = 0u;
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                const int64_t j = tok + e < V ? tok + e : int64_t(V - 1);
+                bits |= ((mrow[j >> 3] >> (j & 7)) & 1u) << e;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        const bool live = ((bits >> e) & 1u) && fabsf(v[e]) <= FLT_MAX;  // finite
+        if (!live) v[e] = NAN;
+    }
+}
+
+// Finds, in a histogram of `nbins` bins (bin i = digit lo + i), the bin that
+// holds the need-th largest element counted from the top.  Returns false
+// when the histogram holds fewer than `need` elements.  All threads call it.
+__device__ bool topk_pick(TopkShared &sh, int nbins, uint32_t lo, uint32_t need, uint32_t &digit,
+                          uint32_t &rank) {
+    const int tid = threadIdx.x;
+    const int per = nbins / kTopkThreads;  // 4 or 1
+    uint32_t own = 0;
+    for (int i = 0; i < per; ++i) own += sh.hist[tid * per + i];
+    sh.part[tid] = own;
+    // inclusive suffix sums: part[t] = sum of part[t'] for t' >= t
+    for (int d = 1; d < kTopkThreads; d <<= 1) {
+        lds_barrier();
+        const uint32_t add = (tid + d < kTopkThreads) ? sh.part[tid + d] : 0u;
+        lds_barrier();
+        sh.part[tid] += add;
+    }
+    lds_barrier();
+    const uint32_t incl = sh.part[tid];
+    if (tid == 0) sh.found_digit = 0xffffffffu;
+    lds_barrier();
+    if (incl >= need && incl - own < need) {
+        uint32_t acc = incl - own;
+        for (int i = per - 1; i >= 0; --i) {
+            const uint32_t h = sh.hist[tid * per + i];
+            if (acc + h >= need) {
+                sh.found_digit = lo + uint32_t(tid * per + i);
+                sh.found_rank = need - acc;
+                break;
+            }
+            acc += h;
+        }
+    }
+    lds_barrier();
+    digit = sh.found_digit;
+    rank = sh.found_rank;
+    return digit != 0xffffffffu;
+}
+
+template <typename ET, bool ALIGNED>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int64_t kStep = int64_t(kTopkThreads) * P;
+    __shared__ TopkShared sh;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int b = row / a.kp1;
+    const float T = uniform_load(a.temperature + b);
+    const int K = uniform_load(a.top_k + b);
+    if (!(T > 0.0f && T <= FLT_MAX) || K <= 0) {
+        if (tid == 0) a.tau[row] = -INFINITY;
+        return;
+    }
+    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;
+    const uint8_t *mrow =
+        a.mask ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
+    const int64_t V = a.V;
+
+    // anchor: the largest top-half code among the first 16 KB of the row
+    uint32_t anchor = 0;
+    for (int64_t tok = int64_t(tid) * P; tok < V && tok < 4 * kStep; tok += kStep) {
+        float v[P];
+        topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok, v);
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+            if (v[e] == v[e]) anchor = max(anchor, ordered_code(v[e]) >> 16);
+    }
+    anchor = block_max_u<kTopkWaves>(anchor, sh.red);
+
+    uint32_t hi = min(anchor + 128u, 0xffffu);
+    uint32_t need = static_cast<uint32_t>(K);
+    uint32_t digit = 0, rank = 0;
+    bool first = true, found = false;
+    // The window only ever moves one way (up while the K-th largest lies above
+    // it, down while it lies below), so at most 65536 / kTopkWindow + 1 passes
+    // run; the bound below is never reached.
+    for (int pass = 0; pass < 0x10000 / kTopkWindow + 2; ++pass) {
+        const uint32_t lo = hi >= kTopkWindow - 1 ? hi - (kTopkWindow - 1) : 0u;
+        for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.hist[i] = 0u;
+        lds_barrier();
+        uint32_t above = 0, support = 0;
+        for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
+            float v[P];
+            topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok, v);
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                if (v[e] != v[e]) continue;
+                ++support;
+                const uint32_t d = ordered_code(v[e]) >> 16;
+                if (d > hi) ++above;
+                else if (d >= lo) atomicAdd(&sh.hist[d - lo], 1u);
+            }
+        }
+        above = block_sum_u<kTopkWaves>(above, sh.red);
+        if (first) {
+            support = block_sum_u<kTopkWaves>(support, sh.red);
+            if (support <= static_cast<uint32_t>(K)) {  // every supported token stays
+                if (tid == 0) a.tau[row] = -INFINITY;
+                return;
+            }
+            first = false;
+        }
+        if (above >= need) {  // the K-th largest lies above the window
+            hi = min(hi + kTopkWindow, 0xffffu);
+            continue;
+        }
+        if (topk_pick(sh, kTopkWindow, lo, need - above, digit, rank)) {
+            found = true;
+            break;
+        }
+        if (lo == 0u) break;  // cannot happen: the row holds more than K
+        hi = lo - 1u;         // the K-th largest lies below the window
+    }
+    if (!found) {
+        if (tid == 0) a.tau[row] = -INFINITY;
+        return;
+    }
+
+    uint32_t code;
+    if (sizeof(ET) == 2) {
+        // a bf16 value's code has all-zero (positive) or all-one (negative) low half
+        code = (digit << 16) | ((digit & 0x8000u) ? 0u : 0xffffu);
+    } else {
+        uint32_t prefix = digit;  // selected high bits so far
+        uint32_t want = rank;
+        for (int shift = 8; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0u;
+            lds_barrier();
+            for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
+                float v[P];
+                topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok, v);
+#pragma unroll
+                for (int e = 0; e < P; ++e) {
+                    if (v[e] != v[e]) continue;
+                    const uint32_t c = ordered_code(v[e]);
+                    if ((c >> (shift + 8)) == prefix) atomicAdd(&sh.hist[(c >> shift) & 0xffu], 1u);
+                }
+            }
+            lds_barrier();
+            uint32_t byte = 0, r = 0;
+            topk_pick(sh, 256, 0u, want, byte, r);  // holds `want` elements by construction
+            prefix = (prefix << 8) | byte;
+            want = r;
+        }
+        code = prefix;
+    }
+    if (tid == 0) a.tau[row] = float_of_code(code);
+}
+
 // ------------------------------------------------------------------ finalize
 
 struct FinalArgs {
@@ -634,6 +862,7 @@ struct FinalArgs {
     uint32_t *status;
     const BlockStat *bstats;
     const DraftRec *drec;
+    const float *tau;  // [rows] top-k thresholds, or nullptr
     int B, k, V, W, C;
 };
 
@@ -678,7 +907,7 @@ __device__ __forceinline__ bool near_tie(float key, int idx, uint64_t best) {
 // p_j = 2^(l_j c - M) / S in fp32.  One wave per block; clamped loads.
 template <typename ET, bool ALIGNED>
 __device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const float *qrow, int V,
-                                   int C, float c, float M, double S, double *Wout) {
+                                   int C, float c, float M, double S, float tau, double *Wout) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     const int lane = threadIdx.x & (kWave - 1);
@@ -713,7 +942,7 @@ __device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const f
             for (int e = 0; e < P; ++e) {
                 const int64_t j = tok + e;
                 const int64_t jc = j < V ? j : int64_t(V - 1);
-                bool live = j < V && lv[e] > -INFINITY;
+                bool live = j < V && lv[e] > -INFINITY && !(lv[e] < tau);
                 if (mrow) live = live && ((mb[jc >> 3] >> (jc & 7)) & 1u);
                 const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[e], c, -M)) * invS : 0.0f;
                 acc += live ? fmaxf(p - qv[e], 0.0f) : 0.0f;
@@ -776,6 +1005,7 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb
     } else {
         load4_masked<ET, ALIGNED>(reinterpret_cast<const ET *>(a.logits) + row * V,
                                   a.mask ? a.mask + row * a.W : nullptr, j0, V, lv);
+        if (a.tau) apply_tau<4>(lv, a.tau[row]);
     }
     float g[4];
     draw_token_gumbels4(key_of(a.seed), b, n, static_cast<uint32_t>(j0), g);
@@ -1080,6 +1310,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
 #pragma unroll
             for (int e = 0; e < P; ++e)
                 if (!((bits >> e) & 1u)) v[e] = -INFINITY;
+            if (a.tau) apply_tau<P>(v, a.tau[int64_t(b) * kp1 + stage_row]);
 #pragma unroll
             for (int h = 0; h < P / 4; ++h)
                 *reinterpret_cast<float4 *>(&sh.blockv[off + 4 * h]) =
@@ -1118,7 +1349,8 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 const int64_t row = int64_t(b) * kp1 + n;
                 dense_block_masses<ET, ALIGNED>(
                     reinterpret_cast<const ET *>(a.logits) + row * V,
-                    a.mask ? a.mask + row * a.W : nullptr, qrow, V, C, c, sh.M[n], sh.S[n], sW);
+                    a.mask ? a.mask + row * a.W : nullptr, qrow, V, C, c, sh.M[n], sh.S[n],
+                    a.tau ? a.tau[row] : -INFINITY, sW);
                 lds_barrier();
                 // residual masses are <= 1, so their keys need no reference
                 const int ngroups = (C + 3) >> 2;
@@ -1205,9 +1437,20 @@ using RowStatsFn = void (*)(RowStatsArgs);
 using FinalFn = void (*)(FinalArgs);
 
 template <typename ET>
-RowStatsFn pick_row_stats(bool masked, bool aligned) {
-    if (aligned) return masked ? row_stats_vec_kernel<ET, true> : row_stats_vec_kernel<ET, false>;
-    return masked ? row_stats_elem_kernel<ET, true> : row_stats_elem_kernel<ET, false>;
+RowStatsFn pick_row_stats(bool masked, bool aligned, bool topk) {
+    if (aligned) {
+        if (topk) return masked ? row_stats_vec_kernel<ET, true, true> : row_stats_vec_kernel<ET, false, true>;
+        return masked ? row_stats_vec_kernel<ET, true, false> : row_stats_vec_kernel<ET, false, false>;
+    }
+    if (topk) return masked ? row_stats_elem_kernel<ET, true, true> : row_stats_elem_kernel<ET, false, true>;
+    return masked ? row_stats_elem_kernel<ET, true, false> : row_stats_elem_kernel<ET, false, false>;
+}
+
+using TopkFn = void (*)(TopkArgs);
+
+template <typename ET>
+TopkFn pick_topk(bool aligned) {
+    return aligned ? topk_kernel<ET, true> : topk_kernel<ET, false>;
 }
 
 template <typename ET>
@@ -1219,7 +1462,7 @@ FinalFn pick_final(bool aligned, bool dense) {
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_drec, off_tally, total;
+    size_t off_bstats, off_drec, off_tau, off_tally, total;
     int nslot;
 };
 
@@ -1246,7 +1489,8 @@ inline Layout layout_of(const sd_params *p) {
     L.nchunk = (L.C + SDV_BLOCKS_PER_WAVE - 1) / SDV_BLOCKS_PER_WAVE;
     L.off_bstats = 0;
     L.off_drec = align256(size_t(L.rows) * L.C * sizeof(BlockStat));
-    L.off_tally = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
+    L.off_tau = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
+    L.off_tally = L.off_tau + align256(size_t(L.rows) * sizeof(float));
     L.nslot = tally_slots(p->batch);
     L.total = L.off_tally + align256(size_t(L.nslot + 2) * kTallyStride * sizeof(uint64_t));
     return L;
@@ -1294,7 +1538,6 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     if (p->logits_dtype != SD_DTYPE_F32 && p->logits_dtype != SD_DTYPE_BF16) return SD_ERR_INVALID_ARG;
     if (!sizes_ok(p)) return SD_ERR_UNSUPPORTED;
     const int B = p->batch, k = p->num_draft, V = p->vocab;
-    if (p->top_k) return SD_ERR_UNSUPPORTED;  // top-k path not built yet
     if (B == 0) {
         hipLaunchKernelGGL(empty_batch_kernel, dim3(1), dim3(64), 0, stream, out_counters, p->status,
                            p->dbg_flags);
@@ -1320,6 +1563,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.draft = draft_token_ids;
     ra.q = draft_probs;
     ra.seed = seed;
+    ra.tau = p->top_k ? reinterpret_cast<float *>(ws + L.off_tau) : nullptr;
     ra.bstats = reinterpret_cast<BlockStat *>(ws + L.off_bstats);
     ra.drec = reinterpret_cast<DraftRec *>(ws + L.off_drec);
     ra.tally = reinterpret_cast<unsigned long long *>(ws + L.off_tally);
@@ -1360,6 +1604,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.status = p->status;
     fa.bstats = ra.bstats;
     fa.drec = ra.drec;
+    fa.tau = ra.tau;
     fa.B = B;
     fa.k = k;
     fa.V = V;
@@ -1367,10 +1612,26 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.C = L.C;
     const size_t dyn_lds = draft_probs ? size_t(L.C) * sizeof(double) : 0;
 
-    RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned) : pick_row_stats<float>(masked, aligned);
+    const bool topk = p->top_k != nullptr;
+    RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
+                         : pick_row_stats<float>(masked, aligned, topk);
     FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr)
                       : pick_final<float>(aligned, draft_probs != nullptr);
 
+    if (topk) {
+        TopkArgs ta;
+        ta.logits = target_logits;
+        ta.mask = ra.mask;
+        ta.temperature = temperature;
+        ta.top_k = p->top_k;
+        ta.tau = const_cast<float *>(ra.tau);
+        ta.kp1 = k + 1;
+        ta.V = V;
+        ta.W = L.W;
+        const TopkFn k0 = bf16 ? pick_topk<uint16_t>(aligned) : pick_topk<float>(aligned);
+        hipLaunchKernelGGL(k0, dim3(static_cast<unsigned>(L.rows)), dim3(kTopkThreads), 0, stream, ta);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    }
     if (p->row_stats_event_begin &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_begin), stream) != hipSuccess)
         return SD_ERR_HIP;

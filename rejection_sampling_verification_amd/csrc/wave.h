@@ -62,6 +62,27 @@ __device__ __forceinline__ int wave_min_i(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+__device__ __forceinline__ uint32_t wave_sum_u(uint32_t v) {
+    int x = static_cast<int>(v);
+    x += dpp_i<0x111, 0xf>(0, x);
+    x += dpp_i<0x112, 0xf>(0, x);
+    x += dpp_i<0x114, 0xf>(0, x);
+    x += dpp_i<0x118, 0xf>(0, x);
+    x += dpp_i<0x142, 0xa>(0, x);
+    x += dpp_i<0x143, 0xc>(0, x);
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(dpp_i<0x111, 0xf>(0, static_cast<int>(v))));
+    v = max(v, static_cast<uint32_t>(dpp_i<0x112, 0xf>(0, static_cast<int>(v))));
+    v = max(v, static_cast<uint32_t>(dpp_i<0x114, 0xf>(0, static_cast<int>(v))));
+    v = max(v, static_cast<uint32_t>(dpp_i<0x118, 0xf>(0, static_cast<int>(v))));
+    v = max(v, static_cast<uint32_t>(dpp_i<0x142, 0xa>(0, static_cast<int>(v))));
+    v = max(v, static_cast<uint32_t>(dpp_i<0x143, 0xc>(0, static_cast<int>(v))));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
 template <int CTRL, int ROW_MASK>
@@ -166,6 +187,30 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
     uint64_t r = scratch[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) r = max_u64(r, scratch[w]);
+    return r;
+}
+
+template <int NW>
+__device__ __forceinline__ uint32_t block_sum_u(uint32_t v, uint32_t *scratch) {
+    v = wave_sum_u(v);
+    lds_barrier();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    lds_barrier();
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) r += scratch[w];
+    return r;
+}
+
+template <int NW>
+__device__ __forceinline__ uint32_t block_max_u(uint32_t v, uint32_t *scratch) {
+    v = wave_max_u(v);
+    lds_barrier();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    lds_barrier();
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) r = max(r, scratch[w]);
     return r;
 }
 

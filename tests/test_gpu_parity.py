@@ -24,7 +24,7 @@ def _needs_gpu():
 
 
 def _custom(B, k, V, dtype=torch.bfloat16, dense=True, masked=False, greedy_frac=0.0,
-            std=3.0, density=0.3, seed=0, x_argmax_frac=0.3, integer_logits=False):
+            std=3.0, density=0.3, seed=0, x_argmax_frac=0.3, integer_logits=False, top_k=None):
     """Small synthetic case with any shape (inputs only)."""
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
@@ -52,8 +52,12 @@ def _custom(B, k, V, dtype=torch.bfloat16, dense=True, masked=False, greedy_frac
     x = torch.where(pick, amax, x)
     T = 0.5 + torch.rand(B, generator=g, device=DEV)
     T = torch.where(torch.rand(B, generator=g, device=DEV) < greedy_frac, torch.zeros_like(T), T)
+    tk = None
+    if top_k is not None:  # per request, drawn from the given choices
+        choice = torch.tensor(list(top_k), dtype=torch.int32, device=DEV)
+        tk = choice[torch.randint(0, len(top_k), (B,), generator=g, device=DEV)].contiguous()
     return {"name": "custom", "logits": lg.contiguous(), "draft_token_ids": x.to(torch.int32).contiguous(),
-            "draft_probs": q, "bitmask": mask, "temperature": T.float().contiguous(), "top_k": None,
+            "draft_probs": q, "bitmask": mask, "temperature": T.float().contiguous(), "top_k": tk,
             "seed": 12345 + seed}
 
 
@@ -125,6 +129,81 @@ def test_structured_full_sampled():
     R, I, D, A = (int(v) for v in gpu["counters"])
     assert (R, I, D) == (640, 128, 512)           # survival exactly 80%
     assert A == int(gpu["out_num_accepted"].sum()) and A <= D
+
+
+def test_long_k_scaled():
+    announce("long_k B=12 k=12 V=151936 top-k 50, greedy and masked mix")
+    wl = make_workload("long_k", device=DEV, batch=12)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_long_k_full_sampled():
+    announce("long_k full B=512 k=12 V=151936, 10 requests rechecked by the oracle")
+    wl = make_workload("long_k", device=DEV)
+    gpu = run_gpu(wl)
+    B, k = 512, 12
+    tk = wl["top_k"].cpu().numpy()
+    T = wl["temperature"].cpu().numpy()
+    greedy = np.nonzero(T == 0)[0]
+    sampled = np.nonzero(T > 0)[0]
+    req = sorted(set([0, 511, int(greedy[0]), int(greedy[-1])] + [int(v) for v in sampled[:3]]
+                     + [int(v) for v in sampled[-3:]]))
+    orc = run_oracle(wl, requests=req)
+    assert_parity(gpu, orc, requests=req, max_flagged=1)
+    R, I, D, A = (int(v) for v in gpu["counters"])
+    na = gpu["out_num_accepted"]
+    assert R == B * k and D == R - I and A == int(na.sum()) and gpu["status"] == 0
+    # every sampled token of a top-k request lies in its row's top-50 allowed set
+    lg = wl["logits"]
+    tok = gpu["out_tokens"]
+    j = torch.arange(151936, device=DEV)
+    for b in [int(v) for v in sampled[:40]]:
+        n = int(na[b])
+        words = wl["bitmask"][b, n].to(torch.int64) & 0xFFFFFFFF
+        allowed = ((words[j >> 5] >> (j & 31)) & 1).bool()
+        row = torch.where(allowed, lg[b, n].float(), torch.full_like(j, -np.inf, dtype=torch.float32))
+        y = int(tok[b, n])
+        assert tk[b] == 50 and bool(allowed[y])
+        assert float(row[y]) >= float(torch.topk(row, 50).values[-1])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [7, 1001, 2049, 6150, 20000])
+def test_top_k_sizes(V, dtype):
+    announce(f"top-k custom V={V} dtype={dtype}")
+    for dense, masked in [(True, False), (False, True), (True, True)]:
+        wl = _custom(10, 3, V, dtype=dtype, dense=dense, masked=masked, greedy_frac=0.2,
+                     seed=V + 3 * dense + masked, top_k=(0, 1, 2, 5, 50, V + 5))
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_top_k_ties():
+    announce("top-k with integer logits: many ties at the threshold")
+    for dtype in (torch.bfloat16, torch.float32):
+        wl = _custom(24, 4, 5000, dtype=dtype, dense=True, integer_logits=True, seed=21,
+                     top_k=(1, 3, 10, 700))
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_top_k_threshold_far_from_the_first_tokens():
+    """The threshold lies far above the first 16 KB of the row (the window
+    moves up) or far below it among widely spread magnitudes (it moves down)."""
+    announce("top-k window moves")
+    B, k, V = 6, 2, 20000
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    for dtype in (torch.float32, torch.bfloat16):
+        lg = torch.randn((B, k + 1, V), generator=g, device=DEV)
+        lg[:3, :, 4096:] += 60.0                          # far above the first tokens
+        mag = torch.exp(torch.rand((3, k + 1, V), generator=g, device=DEV) * 40 - 20)
+        lg[3:] = mag * torch.sign(torch.randn((3, k + 1, V), generator=g, device=DEV))
+        lg = lg.to(dtype).contiguous()
+        x = torch.randint(0, V, (B, k), generator=g, device=DEV).to(torch.int32)
+        wl = {"name": "custom", "logits": lg, "draft_token_ids": x, "draft_probs": None,
+              "bitmask": None, "temperature": torch.full((B,), 1.5, device=DEV),
+              "top_k": torch.tensor([40, 3000, 15000, 40, 3000, 15000], dtype=torch.int32, device=DEV),
+              "seed": 77}
+        assert_parity(run_gpu(wl), run_oracle(wl))
 
 
 # ------------------------------------------------------- shapes and variants
@@ -231,7 +310,7 @@ def test_counter_example_on_gpu():
     assert [int(v) for v in gpu["counters"]] == [1000, 200, 800, 600]
 
 
-@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked"])
+@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked", "top_k"])
 def test_chi_square_on_gpu(mode):
     """Emitted tokens follow the target law (pyshine, "Verification": the output
     is statistically indistinguishable from undrafted decoding)."""
@@ -247,7 +326,8 @@ def test_chi_square_on_gpu(mode):
         allowed = torch.rand((k + 1, V), generator=g) < 0.7
         allowed[:, :2] = True
     T = 0.9
-    p = np.array([ov.target_distribution(l1[i].double().numpy(), allowed[i].numpy(), T, 0)[0]
+    top_k = 4 if mode == "top_k" else 0
+    p = np.array([ov.target_distribution(l1[i].double().numpy(), allowed[i].numpy(), T, top_k)[0]
                   for i in range(k + 1)])
     q1 = torch.softmax(torch.randn((k, V), generator=g), -1)
     x = torch.stack([torch.multinomial(q1[i], B, replacement=True, generator=g) for i in range(k)], 1)
@@ -255,7 +335,9 @@ def test_chi_square_on_gpu(mode):
           "draft_token_ids": x.to(torch.int32).to(DEV),
           "draft_probs": None if mode == "one_hot" else q1.expand(B, k, V).contiguous().to(DEV),
           "bitmask": None if mode != "masked" else pack_bitmask(allowed).expand(B, k + 1, 1).contiguous().to(DEV),
-          "temperature": torch.full((B,), T, device=DEV), "top_k": None, "seed": 2024}
+          "temperature": torch.full((B,), T, device=DEV),
+          "top_k": torch.full((B,), top_k, dtype=torch.int32, device=DEV) if top_k else None,
+          "seed": 2024}
     runs = [run_gpu(wl, seed=2024 + r) for r in range(4)]
     tok = np.concatenate([g["out_tokens"] for g in runs])
     na = np.concatenate([g["out_num_accepted"] for g in runs])
