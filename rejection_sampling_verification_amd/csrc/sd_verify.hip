@@ -55,7 +55,8 @@ constexpr int kFinalWaves = kFinalThreads / 64;
 // s_waitcnt operand (GFX9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8) that waits for vmcnt = 0 only.
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kTallyStride = 32;  // 64-bit words between tally words: one 256-byte line each
+constexpr int kTallyStride = 32;
+constexpr int kDenseSplitBlocks = 32;  // dense q rows of at least this many blocks use the grid  // 64-bit words between tally words: one 256-byte line each
 constexpr int kMaxDraft = SD_MAX_DRAFT;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kLn2 = 0.6931471805599453;
@@ -657,6 +658,7 @@ struct TopkArgs {
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kTopkWindow = 1024;
+constexpr int kTopkUnroll = 4;
 
 struct TopkShared {
     uint32_t hist[kTopkWindow];
@@ -773,17 +775,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.hist[i] = 0u;
         lds_barrier();
         uint32_t above = 0, support = 0;
-        for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
-            float v[P];
-            topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok, v);
+        // kTopkUnroll groups per thread in flight per iteration
+        for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
+            float v[kTopkUnroll][P];
 #pragma unroll
-            for (int e = 0; e < P; ++e) {
-                if (v[e] != v[e]) continue;
-                ++support;
-                const uint32_t d = ordered_code(v[e]) >> 16;
-                if (d > hi) ++above;
-                else if (d >= lo) atomicAdd(&sh.hist[d - lo], 1u);
-            }
+            for (int u = 0; u < kTopkUnroll; ++u)
+                topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok0 + u * kStep, v[u]);
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < P; ++e) {
+                    if (v[u][e] != v[u][e]) continue;
+                    ++support;
+                    const uint32_t d = ordered_code(v[u][e]) >> 16;
+                    if (d > hi) ++above;
+                    else if (d >= lo) atomicAdd(&sh.hist[d - lo], 1u);
+                }
         }
         above = block_sum_u<kTopkWaves>(above, sh.red);
         if (first) {
@@ -843,6 +850,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
 // ------------------------------------------------------------------ finalize
 
+struct Level1 {
+    int c;     // winning block, -1 when no block has mass
+    int flag;  // 1 when the top-2 block keys are closer than the flag threshold
+};
+
+// A request whose draw comes from the dense residual max(p - q, 0): the
+// finalize kernel leaves it to the residual-mass and residual-draw kernels.
+struct DenseJob {
+    double S;      // the row's sum of 2^(l c - M) over the support
+    double invT;   // 1 / T in fp64
+    float c, M;    // log2(e) / T and the row's fp32 max (log2 units)
+    float tau;     // the row's top-k threshold (-inf: none)
+    int row;       // b * (k + 1) + n, or -1: no dense draw for this request
+    int n;         // the rejected position
+    Level1 l1p;    // level-1 winner under p, for the fallback
+};
+
 struct FinalArgs {
     const void *logits;
     const int32_t *draft;
@@ -863,15 +887,13 @@ struct FinalArgs {
     const BlockStat *bstats;
     const DraftRec *drec;
     const float *tau;  // [rows] top-k thresholds, or nullptr
+    DenseJob *jobs;    // [B] dense q only
+    double *wmass;     // [B, C] dense q only: residual mass per block
+    int split_dense;   // dense q: 1 = residual masses by the grid-wide kernels
     int B, k, V, W, C;
 };
 
 enum SampleMode { kModeP = 0, kModeOneHot = 1, kModeDense = 2 };
-
-struct Level1 {
-    int c;     // winning block, -1 when no block has mass
-    int flag;  // 1 when the top-2 block keys are closer than the flag threshold
-};
 
 struct FinalShared {
     float M[kMaxDraft + 1];     // per row: fp32 max (log2 units), or greedy max logit
@@ -1186,7 +1208,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     __shared__ FinalShared sh;
-    extern __shared__ double sW[];  // dense q: per-block residual mass [C]
+    extern __shared__ double sW[];  // dense q, short rows: per-block residual mass [C]
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int k = a.k, kp1 = a.k + 1, V = a.V, C = a.C;
@@ -1336,6 +1358,8 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     // ---- the emitted token
     const uint32_t st = sh.status;
     int y = -1, fg = 0;
+    bool deferred = false;
+    if (DENSE && tid == 0) a.jobs[b].row = -1;  // overwritten below for a dense draw
     if (st == 0) {
         const int n = sh.nacc;
         if (greedy) {
@@ -1345,7 +1369,23 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             const float *qrow = (DENSE && n < k) ? a.q + (int64_t(b) * k + n) * V : nullptr;
             int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
-            if (DENSE && mode == kModeDense) {
+            if (DENSE && mode == kModeDense && a.split_dense) {
+                // left to the residual kernels; -1 stands in until they write y
+                if (tid == 0) {
+                    DenseJob j;
+                    j.row = b * kp1 + n;
+                    j.n = n;
+                    j.c = c;
+                    j.M = sh.M[n];
+                    j.S = sh.S[n];
+                    j.tau = a.tau ? a.tau[int64_t(b) * kp1 + n] : -INFINITY;
+                    j.l1p = sh.l1p[n];
+                    j.invT = invT;
+                    a.jobs[b] = j;
+                }
+                deferred = true;
+            }
+            if (DENSE && mode == kModeDense && !a.split_dense) {
                 const int64_t row = int64_t(b) * kp1 + n;
                 dense_block_masses<ET, ALIGNED>(
                     reinterpret_cast<const ET *>(a.logits) + row * V,
@@ -1379,7 +1419,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             }
             // A zero residual mass, or a block that lost its mass in double
             // precision, falls back to drawing from p.
-            for (int attempt = 0; attempt < 2; ++attempt) {
+            for (int attempt = 0; attempt < 2 && !deferred; ++attempt) {
                 if (l1.c < 0) {
                     mode = kModeP;
                     l1 = sh.l1p[n];
@@ -1424,6 +1464,143 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     }
 }
 
+// Residual masses W_c = sum_j max(p_j - q_j, 0) of the rejected rows of the
+// deferred requests (pyshine "vLLM, part 2", "Verification": the rejected
+// position is resampled from the clamped difference of the target and draft
+// distributions).  Grid (ceil(C / 4), B); one wave per block, per-lane fp32
+// partial sums added in fp64.
+template <typename ET, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void dense_mass_kernel(FinalArgs a) {
+    const int b = blockIdx.y;
+    const int blk = blockIdx.x * (kThreads / kWave) + wave_id();
+    const DenseJob j = a.jobs[b];
+    if (j.row < 0 || blk >= a.C) return;
+    const int V = a.V, lane = threadIdx.x & (kWave - 1);
+    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(j.row) * V;
+    const uint8_t *mb = a.mask ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(j.row) * a.W) : nullptr;
+    const float *qrow = a.q + (int64_t(b) * a.k + j.n) * V;
+    const float invS = static_cast<float>(1.0 / j.S);
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    float lv[G][P], qv[G][P];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
+        if (ALIGNED) {
+            const int64_t tc = tok < V ? tok : int64_t(V - P);
+            Logit<ET>::unpack(*reinterpret_cast<const uint4 *>(rowp + tc), lv[g]);
+#pragma unroll
+            for (int h = 0; h < P / 4; ++h) {
+                const float4 f = *reinterpret_cast<const float4 *>(qrow + tc + 4 * h);
+                qv[g][4 * h] = f.x;
+                qv[g][4 * h + 1] = f.y;
+                qv[g][4 * h + 2] = f.z;
+                qv[g][4 * h + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                const int64_t tc = tok + e < V ? tok + e : int64_t(V - 1);
+                lv[g][e] = Logit<ET>::to_float(rowp[tc]);
+                qv[g][e] = qrow[tc];
+            }
+        }
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
+        uint32_t bits = 0xffu;
+        if (mb != nullptr) {
+            const int64_t tc = tok < V ? tok : int64_t(V - 1);
+            if (ALIGNED) {
+                const uint32_t byte = mb[tc >> 3];
+                bits = (P == 8) ? byte : (byte >> (uint32_t(tc) & 4u));
+            } else {
+                bits = 0u;
+#pragma unroll
+                for (int e = 0; e < P; ++e) {
+                    const int64_t je = tok + e < V ? tok + e : int64_t(V - 1);
+                    bits |= ((mb[je >> 3] >> (je & 7)) & 1u) << e;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const bool live = tok + e < V && ((bits >> e) & 1u) && lv[g][e] > -INFINITY && !(lv[g][e] < j.tau);
+            const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[g][e], j.c, -j.M)) * invS : 0.0f;
+            acc += live ? fmaxf(p - qv[g][e], 0.0f) : 0.0f;
+        }
+    }
+    const double w = wave_sum_d(static_cast<double>(acc));
+    if (lane == 0) a.wmass[int64_t(b) * a.C + blk] = w;
+}
+
+// The token of each deferred request: level 1 over the residual masses, then
+// level 2 inside the winning block (the same draws the finalize kernel makes
+// for the other sampling modes); a zero residual falls back to p.
+template <typename ET, bool ALIGNED>
+__global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) {
+    __shared__ FinalShared sh;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const DenseJob j = a.jobs[b];
+    if (j.row < 0) return;
+    const int k = a.k, kp1 = k + 1, C = a.C, n = j.n;
+    const PhiloxKey key = key_of(a.seed);
+    if (tid == 0) {
+        sh.M[n] = j.M;
+        sh.S[n] = j.S;
+        sh.X[n] = a.draft[int64_t(b) * k + n];
+    }
+    lds_barrier();
+    const double *W = a.wmass + int64_t(b) * C;
+    const float *qrow = a.q + (int64_t(b) * k + n) * a.V;
+    // residual masses are <= 1, so their keys need no reference
+    const int ngroups = (C + 3) >> 2;
+    float kq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    const int g4 = tid;  // one group of four blocks per thread
+    uint64_t best = 0;
+    if (g4 < ngroups) {
+        float gum[4];
+        draw_block_gumbels4(key, b, n, g4, gum);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int cb = 4 * g4 + q;
+            if (cb < C && W[cb] > 0.0) {
+                kq[q] = static_cast<float>(log(W[cb]) + static_cast<double>(gum[q]));
+                best = max_u64(best, pack_key(kq[q], cb));
+            }
+        }
+    }
+    best = block_max_u64<kFinalWaves>(best, sh.red_u);
+    bool tie = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (kq[q] > -INFINITY) tie |= near_tie(kq[q], 4 * g4 + q, best);
+    tie = block_any<kFinalWaves>(tie, sh.red_b);
+    Level1 l1 = best ? Level1{packed_index(best), tie ? 1 : 0} : Level1{-1, 0};
+    int mode = kModeDense, y = -1, fg = 0;
+    const double invT = j.invT;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        if (l1.c < 0) {
+            mode = kModeP;
+            l1 = j.l1p;
+        }
+        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, j.c, invT, qrow, false);
+        if (r2.x >= 0) {
+            y = r2.x;
+            fg = l1.flag + r2.y;
+            break;
+        }
+        l1.c = -1;
+    }
+    if (tid == 0) {
+        a.out_tokens[int64_t(b) * kp1 + n] = y;
+        if (a.dbg_req_flags) a.dbg_req_flags[b] += static_cast<uint32_t>(fg) << 16;
+        if (a.dbg_flags && fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
+    }
+}
+
 // Outputs of an empty batch: zero counters, status and flags.
 __global__ void empty_batch_kernel(uint64_t *counters, uint32_t *status, uint32_t *flags) {
     if (threadIdx.x < 4) counters[threadIdx.x] = 0ull;
@@ -1447,6 +1624,17 @@ RowStatsFn pick_row_stats(bool masked, bool aligned, bool topk) {
 }
 
 using TopkFn = void (*)(TopkArgs);
+using DenseFn = void (*)(FinalArgs);
+
+template <typename ET>
+DenseFn pick_dense_mass(bool aligned) {
+    return aligned ? dense_mass_kernel<ET, true> : dense_mass_kernel<ET, false>;
+}
+
+template <typename ET>
+DenseFn pick_dense_draw(bool aligned) {
+    return aligned ? dense_draw_kernel<ET, true> : dense_draw_kernel<ET, false>;
+}
 
 template <typename ET>
 TopkFn pick_topk(bool aligned) {
@@ -1462,7 +1650,7 @@ FinalFn pick_final(bool aligned, bool dense) {
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_drec, off_tau, off_tally, total;
+    size_t off_bstats, off_drec, off_tau, off_jobs, off_wmass, off_tally, total;
     int nslot;
 };
 
@@ -1490,7 +1678,9 @@ inline Layout layout_of(const sd_params *p) {
     L.off_bstats = 0;
     L.off_drec = align256(size_t(L.rows) * L.C * sizeof(BlockStat));
     L.off_tau = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
-    L.off_tally = L.off_tau + align256(size_t(L.rows) * sizeof(float));
+    L.off_jobs = L.off_tau + align256(size_t(L.rows) * sizeof(float));
+    L.off_wmass = L.off_jobs + align256(size_t(p->batch) * sizeof(DenseJob));
+    L.off_tally = L.off_wmass + align256(size_t(p->batch) * L.C * sizeof(double));
     L.nslot = tally_slots(p->batch);
     L.total = L.off_tally + align256(size_t(L.nslot + 2) * kTallyStride * sizeof(uint64_t));
     return L;
@@ -1605,12 +1795,17 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.bstats = ra.bstats;
     fa.drec = ra.drec;
     fa.tau = ra.tau;
+    fa.jobs = reinterpret_cast<DenseJob *>(ws + L.off_jobs);
+    fa.wmass = reinterpret_cast<double *>(ws + L.off_wmass);
+    // Long rows: the residual masses of the rejected rows are summed by a
+    // grid over (request, block); short rows are summed inside the finalize
+    // kernel, which saves two launches.
+    fa.split_dense = (draft_probs && L.C >= kDenseSplitBlocks) ? 1 : 0;
     fa.B = B;
     fa.k = k;
     fa.V = V;
     fa.W = L.W;
     fa.C = L.C;
-    const size_t dyn_lds = draft_probs ? size_t(L.C) * sizeof(double) : 0;
 
     const bool topk = p->top_k != nullptr;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
@@ -1640,7 +1835,17 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     if (p->row_stats_event_end &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_end), stream) != hipSuccess)
         return SD_ERR_HIP;
+    const size_t dyn_lds = (draft_probs && !fa.split_dense) ? size_t(L.C) * sizeof(double) : 0;
     hipLaunchKernelGGL(k2, dim3(B), dim3(kFinalThreads), dyn_lds, stream, fa);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    if (fa.split_dense) {
+        const DenseFn k3 = bf16 ? pick_dense_mass<uint16_t>(aligned) : pick_dense_mass<float>(aligned);
+        const DenseFn k4 = bf16 ? pick_dense_draw<uint16_t>(aligned) : pick_dense_draw<float>(aligned);
+        const unsigned gx = static_cast<unsigned>((L.C + kThreads / kWave - 1) / (kThreads / kWave));
+        hipLaunchKernelGGL(k3, dim3(gx, static_cast<unsigned>(B)), dim3(kThreads), 0, stream, fa);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+        hipLaunchKernelGGL(k4, dim3(B), dim3(kFinalThreads), 0, stream, fa);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    }
     return SD_OK;
 }

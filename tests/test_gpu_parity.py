@@ -218,6 +218,17 @@ def test_vocab_sizes_and_alignment(V, dtype):
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+@pytest.mark.parametrize("V", [65536, 70001])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_dense_long_rows(V, dtype):
+    """Rows of 32 blocks or more: the residual masses come from the grid-wide
+    kernels (vector path at V = 65536, element path at V = 70001)."""
+    announce(f"dense long rows V={V} dtype={dtype}")
+    wl = _custom(12, 3, V, dtype=dtype, dense=True, masked=True, greedy_frac=0.2, density=0.5,
+                 seed=V % 97, top_k=(0, 0, 20))
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
 def test_masked_dense_one_hot_and_greedy_mix():
     announce("custom B=24 k=6 V=40000 masked dense greedy mix")
     wl = _custom(24, 6, 40000, dense=True, masked=True, greedy_frac=0.4, density=0.1, seed=3)
