@@ -641,8 +641,9 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
 //
 // Selection runs on order-preserving 32-bit codes of the values.  The top 16
 // bits (the bf16 value itself) are counted in a histogram over a window of
-// 1024 consecutive codes placed just above the largest code of the row's first
-// 16 KB; elements above the window are only counted.  When the K-th largest
+// consecutive codes (256 for the first pass, 1024 after) placed around the
+// largest code of the row's first 16 KB; elements above the window are only
+// counted.  When the K-th largest
 // lies outside the window, the window moves (another pass over the row) in the
 // one direction that can hold it.  For fp32 rows two more passes pick the low
 // two bytes among the elements that share the selected top half.
@@ -659,6 +660,10 @@ constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kTopkWindow = 1024;
 constexpr int kTopkUnroll = 4;
+// The first window spans one binade of bf16 codes on either side of the
+// anchor: for top-k of a few percent of the vocabulary or less it holds the
+// K-th largest, and it draws few of the row's elements into the histogram.
+constexpr uint32_t kTopkFirstSpan = 256;
 
 struct TopkShared {
     uint32_t hist[kTopkWindow];
@@ -693,6 +698,38 @@ __device__ __forceinline__ void topk_group(const ET *rowp, const uint8_t *mrow, 
         const bool live = ((bits >> e) & 1u) && fabsf(v[e]) <= FLT_MAX;  // finite
         if (!live) v[e] = NAN;
     }
+}
+
+// The same for 16-byte aligned rows with V a multiple of P, through buffer
+// loads: a group past V reads zeros (no memory access) and is excluded by
+// its index, so no branch guards a load and the loads of several groups stay
+// in flight together.
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void topk_group_vec(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rm,
+                                               int V, int64_t tok, float *v) {
+    constexpr int P = Logit<ET>::kPer16;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(tok * int64_t(sizeof(ET))), 0, 0);
+    Logit<ET>::unpack(make_uint4(w.x, w.y, w.z, w.w), v);
+    uint32_t bits = tok < V ? 0xffu : 0u;
+    if (MASKED) {
+        const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rm, static_cast<int>(tok >> 3), 0, 0);
+        bits &= (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
+    }
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        const bool live = ((bits >> e) & 1u) && fabsf(v[e]) <= FLT_MAX;
+        v[e] = live ? v[e] : NAN;
+    }
+}
+
+// One group of the row for the top-k passes, through the path the row allows.
+template <typename ET, bool ALIGNED, bool MASKED>
+__device__ __forceinline__ void topk_load(const ET *rowp, const uint8_t *mrow,
+                                          __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rm, int V,
+                                          int64_t tok, float *v) {
+    if (ALIGNED) topk_group_vec<ET, MASKED>(rs, rm, V, tok, v);
+    else topk_group<ET, false>(rowp, MASKED ? mrow : nullptr, V, tok, v);
 }
 
 // Finds, in a histogram of `nbins` bins (bin i = digit lo + i), the bin that
@@ -734,7 +771,7 @@ __device__ bool topk_pick(TopkShared &sh, int nbins, uint32_t lo, uint32_t need,
     return digit != 0xffffffffu;
 }
 
-template <typename ET, bool ALIGNED>
+template <typename ET, bool ALIGNED, bool MASKED>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int64_t kStep = int64_t(kTopkThreads) * P;
@@ -749,14 +786,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
     const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;
     const uint8_t *mrow =
-        a.mask ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
+        MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
     const int64_t V = a.V;
+    const __amdgpu_buffer_rsrc_t rs = buffer_of(rowp, uint32_t(a.V) * sizeof(ET));
+    const __amdgpu_buffer_rsrc_t rm = buffer_of(MASKED ? static_cast<const void *>(mrow) : static_cast<const void *>(rowp),
+                                                MASKED ? uint32_t(a.W) * 4u : 0u);
 
     // anchor: the largest top-half code among the first 16 KB of the row
     uint32_t anchor = 0;
     for (int64_t tok = int64_t(tid) * P; tok < V && tok < 4 * kStep; tok += kStep) {
         float v[P];
-        topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok, v);
+        topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, a.V, tok, v);
 #pragma unroll
         for (int e = 0; e < P; ++e)
             if (v[e] == v[e]) anchor = max(anchor, ordered_code(v[e]) >> 16);
@@ -764,6 +804,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     anchor = block_max_u<kTopkWaves>(anchor, sh.red);
 
     uint32_t hi = min(anchor + 128u, 0xffffu);
+    uint32_t span = kTopkFirstSpan;  // the first window is narrow: fewer LDS atomics
     uint32_t need = static_cast<uint32_t>(K);
     uint32_t digit = 0, rank = 0;
     bool first = true, found = false;
@@ -771,7 +812,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     // it, down while it lies below), so at most 65536 / kTopkWindow + 1 passes
     // run; the bound below is never reached.
     for (int pass = 0; pass < 0x10000 / kTopkWindow + 2; ++pass) {
-        const uint32_t lo = hi >= kTopkWindow - 1 ? hi - (kTopkWindow - 1) : 0u;
+        const uint32_t lo = hi >= span - 1 ? hi - (span - 1) : 0u;
         for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.hist[i] = 0u;
         lds_barrier();
         uint32_t above = 0, support = 0;
@@ -780,7 +821,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             float v[kTopkUnroll][P];
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u)
-                topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok0 + u * kStep, v[u]);
+                topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, a.V, tok0 + u * kStep, v[u]);
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u)
 #pragma unroll
@@ -802,7 +843,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             first = false;
         }
         if (above >= need) {  // the K-th largest lies above the window
-            hi = min(hi + kTopkWindow, 0xffffu);
+            hi = min(hi + span, 0xffffu);
+            span = kTopkWindow;
             continue;
         }
         if (topk_pick(sh, kTopkWindow, lo, need - above, digit, rank)) {
@@ -811,6 +853,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         }
         if (lo == 0u) break;  // cannot happen: the row holds more than K
         hi = lo - 1u;         // the K-th largest lies below the window
+        span = kTopkWindow;
     }
     if (!found) {
         if (tid == 0) a.tau[row] = -INFINITY;
@@ -829,7 +872,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             lds_barrier();
             for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
                 float v[P];
-                topk_group<ET, ALIGNED>(rowp, mrow, a.V, tok, v);
+                topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, a.V, tok, v);
 #pragma unroll
                 for (int e = 0; e < P; ++e) {
                     if (v[e] != v[e]) continue;
@@ -1637,8 +1680,9 @@ DenseFn pick_dense_draw(bool aligned) {
 }
 
 template <typename ET>
-TopkFn pick_topk(bool aligned) {
-    return aligned ? topk_kernel<ET, true> : topk_kernel<ET, false>;
+TopkFn pick_topk(bool aligned, bool masked) {
+    if (aligned) return masked ? topk_kernel<ET, true, true> : topk_kernel<ET, true, false>;
+    return masked ? topk_kernel<ET, false, true> : topk_kernel<ET, false, false>;
 }
 
 template <typename ET>
@@ -1823,7 +1867,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         ta.kp1 = k + 1;
         ta.V = V;
         ta.W = L.W;
-        const TopkFn k0 = bf16 ? pick_topk<uint16_t>(aligned) : pick_topk<float>(aligned);
+        const TopkFn k0 = bf16 ? pick_topk<uint16_t>(aligned, masked) : pick_topk<float>(aligned, masked);
         hipLaunchKernelGGL(k0, dim3(static_cast<unsigned>(L.rows)), dim3(kTopkThreads), 0, stream, ta);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }
