@@ -955,6 +955,7 @@ struct FinalShared {
     double red_d[kFinalWaves];
     uint64_t red_u[kFinalWaves];
     uint32_t red_b[kFinalWaves];
+    uint64_t red2[2][2 * kFinalWaves];  // top-2 scratch of level-2 draws, by attempt
     float blockv[kBlock];       // that block's logits, -inf where masked or past V
 };
 
@@ -1055,7 +1056,7 @@ __device__ __forceinline__ void load4_masked(const ET *row, const uint32_t *mrow
 // holds no positive weight.
 template <typename ET, bool ALIGNED>
 __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb, int mode, float c,
-                       double invT, const float *qrow, bool staged) {
+                       double invT, const float *qrow, bool staged, int attempt) {
     const int k = a.k, V = a.V;
     const int64_t row = int64_t(b) * (k + 1) + n;
     const int x = (n < k) ? sh.X[n] : -1;
@@ -1078,7 +1079,7 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb
     const double S = sh.S[n];
     const double lref = static_cast<double>(M) / static_cast<double>(c);  // about the row's max logit
     float keys[4];
-    uint64_t best = 0;
+    uint64_t best = 0, second = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t j = j0 + e;
@@ -1093,29 +1094,66 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb
             if (mode == kModeOneHot && j == x) continue;
             keys[e] = static_cast<float>((static_cast<double>(lv[e]) - lref) * invT + static_cast<double>(g[e]));
         }
-        best = max_u64(best, pack_key(keys[e], static_cast<int>(j)));
+        merge_top2(best, second, pack_key(keys[e], static_cast<int>(j)), 0ull);
     }
-    best = block_max_u64<kFinalWaves>(best, sh.red_u);
+    // one reduction finds the winner and the runner-up (a near tie when its
+    // key is within the flag threshold); consecutive attempts use different
+    // scratch, so no barrier is needed between them
+    block_top2_u64<kFinalWaves>(best, second, sh.red2[attempt & 1]);
     if (best == 0) return make_int2(-1, 0);
-    bool tie = false;
+    const bool tie = second != 0 && packed_key(second) >= packed_key(best) - kTieEps;
+    return make_int2(packed_index(best), tie ? 1 : 0);
+}
+
+// A lane's share of one row's block statistics, blocks lane + 64 j for
+// j < kFoldCache, loaded once (absent blocks read as empty).  Rows of more
+// than 64 kFoldCache blocks fold the rest straight from memory.
+constexpr int kFoldCache = 2;
+
+struct FoldCache {
+    BlockStat e[kFoldCache];
+};
+
+__device__ __forceinline__ void load_fold_cache(const BlockStat *st, int C, int lane, FoldCache &fc) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (keys[e] > -INFINITY) tie |= near_tie(keys[e], static_cast<int>(j0 + e), best);
-    return make_int2(packed_index(best), block_any<kFinalWaves>(tie, sh.red_b) ? 1 : 0);
+    for (int j = 0; j < kFoldCache; ++j) {
+        const int cb = lane + kWave * j;
+        const int cc = cb < C ? cb : C - 1;  // clamped: every lane loads, no branch
+        fc.e[j] = st[cc];
+        if (cb >= C) {
+            fc.e[j].m = -INFINITY;
+            fc.e[j].s = 0.0f;
+            fc.e[j].key = -INFINITY;
+        }
+    }
+}
+
+// Block cb's statistics for the fold: from the cache when it holds them.
+__device__ __forceinline__ BlockStat fold_entry(const BlockStat *st, const FoldCache &fc, int j,
+                                                int cb) {
+    if (j < kFoldCache) {
+        BlockStat r = fc.e[0];
+#pragma unroll
+        for (int q = 1; q < kFoldCache; ++q)
+            if (j == q) r = fc.e[q];
+        return r;
+    }
+    return st[cb];
 }
 
 // Fold one greedy row's block statistics (one wave): max and lowest argmax.
-__device__ __forceinline__ void fold_greedy_row(const BlockStat *st, int C, int i, FinalShared &sh) {
+__device__ __forceinline__ void fold_greedy_row(const BlockStat *st, const FoldCache &fc, int C, int i,
+                                                FinalShared &sh) {
     const int lane = threadIdx.x & (kWave - 1);
     bool bad = false;
     float best = -INFINITY;
     int bidx = INT_MAX;
-    for (int cb = lane; cb < C; cb += kWave) {
-        const float2 e = *reinterpret_cast<const float2 *>(&st[cb]);
-        if (e.x != e.x || e.x == INFINITY) bad = true;
-        if (e.x > best) {
-            best = e.x;
-            bidx = __float_as_int(e.y);
+    for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
+        const BlockStat e = fold_entry(st, fc, j, cb);
+        if (e.m != e.m || e.m == INFINITY) bad = true;
+        if (e.m > best) {
+            best = e.m;
+            bidx = __float_as_int(e.s);
         }
     }
     bad = wave_any(bad);
@@ -1142,15 +1180,15 @@ __device__ __forceinline__ double exp2_nonpos(double d) {
 // normaliser, and finish its level-1 races over the keys the sweep drew:
 // under p, and under p with block cx's key replaced by the draft-excluded
 // key keyx.
-__device__ __forceinline__ void fold_sampling_row(const BlockStat *st, int C, int i, int cx,
-                                                  double keyx, FinalShared &sh) {
+__device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const FoldCache &fc, int C,
+                                                  int i, int cx, double keyx, FinalShared &sh) {
     const int lane = threadIdx.x & (kWave - 1);
     bool bad = false;
     float mx = -INFINITY;
-    for (int cb = lane; cb < C; cb += kWave) {
-        const float2 e = *reinterpret_cast<const float2 *>(&st[cb]);
-        if (e.x != e.x || e.y != e.y || e.x == INFINITY) bad = true;
-        mx = fmaxf(mx, e.x);
+    for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
+        const BlockStat e = fold_entry(st, fc, j, cb);
+        if (e.m != e.m || e.s != e.s || e.m == INFINITY) bad = true;
+        mx = fmaxf(mx, e.m);
     }
     bad = wave_any(bad);
     const float m = wave_max(mx);
@@ -1158,8 +1196,8 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, int C, in
     double s = 0.0;
     uint64_t bp = 0, bx = 0;
     if (!bad && m > -INFINITY) {
-        for (int cb = lane; cb < C; cb += kWave) {
-            const BlockStat e = st[cb];
+        for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
+            const BlockStat e = fold_entry(st, fc, j, cb);
             if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
             s += static_cast<double>(e.s) * exp2_nonpos(static_cast<double>(e.m) - static_cast<double>(m));
             const float kp = static_cast<float>(e.key - ref);
@@ -1173,8 +1211,8 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, int C, in
     bx = wave_max_u64(bx);
     bool tp = false, tx = false;
     if (bp != 0) {
-        for (int cb = lane; cb < C; cb += kWave) {
-            const BlockStat e = st[cb];
+        for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
+            const BlockStat e = fold_entry(st, fc, j, cb);
             if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
             const float kp = static_cast<float>(e.key - ref);
             tp |= near_tie(kp, cb, bp);
@@ -1262,6 +1300,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     const float c = greedy || bad_T ? 0.0f : scale_of(T);
     constexpr bool one_hot = !DENSE;
 
+    // ---- this wave's first row's block statistics, in flight with the drafts
+    FoldCache fc;
+    if (!bad_T && wave < kp1) load_fold_cache(a.bstats + (int64_t(b) * kp1 + wave) * C, C, lane, fc);
+
     // ---- drafts, and what the sweep recorded about them
     int x = -1;
     if (tid < k) x = a.draft[int64_t(b) * k + tid];
@@ -1295,13 +1337,14 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
         for (int i = wave; i < kp1; i += kFinalWaves) {
             const int64_t row = int64_t(b) * kp1 + i;
             const BlockStat *st = a.bstats + row * C;
+            if (i != wave) load_fold_cache(st, C, lane, fc);  // rows past the first wave of rows
             if (greedy) {
-                fold_greedy_row(st, C, i, sh);
+                fold_greedy_row(st, fc, C, i, sh);
                 continue;
             }
             const int xi = (i < k) ? sh.X[i] : -1;
             const int cx = (one_hot && xi >= 0 && xi < V) ? xi / kBlock : -1;
-            fold_sampling_row(st, C, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
+            fold_sampling_row(st, fc, C, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
             if (ALIGNED && kp1 <= kFinalWaves) {
                 const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
                 if (l1.c >= 0) {
@@ -1468,7 +1511,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                     l1 = sh.l1p[n];
                 }
                 const int2 r2 =
-                    level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c);
+                    level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c, attempt);
                 if (r2.x >= 0) {
                     y = r2.x;
                     fg = l1.flag + r2.y;
@@ -1629,7 +1672,7 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
             mode = kModeP;
             l1 = j.l1p;
         }
-        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, j.c, invT, qrow, false);
+        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, j.c, invT, qrow, false, attempt);
         if (r2.x >= 0) {
             y = r2.x;
             fg = l1.flag + r2.y;
