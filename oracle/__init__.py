@@ -33,5 +33,5 @@ the accept/resample law at V=8, and chi-square tests of the sampled tokens.
 """
 
 from . import philox, rates, verify  # noqa: F401
-from .verify import sd_verify  # noqa: F401
+from .verify import sd_verify, sd_verify_ragged  # noqa: F401
 from .rates import sd_rates  # noqa: F401

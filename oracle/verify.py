@@ -58,6 +58,7 @@ ST_TEMPERATURE = 2      # temperature negative, NaN or infinite
 ST_EMPTY_ROW = 4        # a row with no allowed token of finite logit
 ST_BAD_LOGIT = 8        # NaN or +inf logit at an allowed position
 ST_BAD_DRAFT_PROB = 16  # draft probability of a draft token NaN, inf or < 0
+ST_BAD_OFFSETS = 32     # ragged drafts: the request's draft offsets are inconsistent
 
 
 def unpack_bitmask(words, V):
@@ -288,4 +289,103 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
         A += r["A"]
     out["counters"] = np.array([R, I, R - I, A], dtype=np.uint64)
     out["status"] = status
+    out["accept_histogram"] = accept_histogram(out["num_accepted"], out["request_status"], k)
+    return out
+
+
+def accept_histogram(num_accepted, request_status, kmax):
+    """Requests per accepted draft length 0 .. kmax, requests in error left
+    out (fanout, "Mean acceptance length uses another denominator": one bucket
+    for every possible accepted length, the bonus token not counted)."""
+    h = np.zeros(kmax + 1, dtype=np.int64)
+    for n, st in zip(num_accepted, request_status):
+        if st == 0:
+            h[int(n)] += 1
+    return h
+
+
+def sd_verify_ragged(logits, draft_token_ids, draft_offsets, draft_probs=None, bitmask=None,
+                     temperature=None, seed=0, top_k=None, max_draft=None, total_drafts=None,
+                     block=BLOCK):
+    """Requests with their own draft lengths (a drafter that proposes a
+    variable number of tokens per request, infra-guide 5.2, dynamic draft
+    length).  Request b has k_b = off[b+1] - off[b] drafts; its rows are
+    logits[off[b] + b : off[b+1] + b + 1] (k_b draft positions, then the bonus
+    position), its drafts draft_token_ids[off[b] : off[b+1]].
+
+    logits:          [rows, V] with rows = off[B] + B
+    draft_token_ids: [off[B]] integer
+    draft_offsets:   [B + 1] integer
+    draft_probs:     [off[B], V] float or None
+    bitmask:         [rows, ceil(V/32)] int32 or None
+    temperature:     [B]; top_k: [B] or None
+    max_draft:       the largest allowed k_b (default: the largest given)
+    total_drafts:    the number of drafts the caller declares (default off[B])
+
+    The offsets must start at 0, never decrease, end at total_drafts, and give
+    every request at most max_draft drafts.  Otherwise the rows of the call
+    cannot be located: every request gets status ST_BAD_OFFSETS and
+    num_accepted -1, no output slot is written and the counters stay 0.
+    Returns out_tokens [rows] (each request's k_b + 1 slots), num_accepted [B],
+    counters, status, request_status, row_lse [rows], accept_prob [off[B]],
+    flag counts and the accepted-length histogram [max_draft + 1].
+    """
+    off = np.asarray(draft_offsets, dtype=np.int64).reshape(-1)
+    B = off.shape[0] - 1
+    total = int(off[B]) if total_drafts is None else int(total_drafts)
+    logits = np.asarray(logits)
+    rows, V = logits.shape
+    if rows != total + B:
+        raise ValueError("logits must hold total_drafts + B rows")
+    if total < 0:
+        raise ValueError("total_drafts must be >= 0")
+    x_all = np.asarray(draft_token_ids, dtype=np.int64).reshape(-1)
+    T_all = np.asarray(temperature, dtype=np.float64).reshape(B)
+    tk_all = np.zeros(B, dtype=np.int64) if top_k is None else \
+        np.asarray(top_k, dtype=np.int64).reshape(B)
+    kb = off[1:] - off[:-1]
+    kmax = int(max(kb.max(), 0)) if max_draft is None and B > 0 else int(max_draft or 0)
+    out = {
+        "out_tokens": np.full(rows, -1, dtype=np.int64),
+        "num_accepted": np.full(B, -1, dtype=np.int64),
+        "request_status": np.zeros(B, dtype=np.int64),
+        "row_lse": np.full(rows, np.nan),
+        "accept_prob": np.full(total, np.nan),
+        "flag_accept": np.zeros(B, dtype=np.int64),
+        "flag_gumbel": np.zeros(B, dtype=np.int64),
+    }
+    R = I = A = 0
+    status = 0
+    consistent = B >= 0 and int(off[0]) == 0 and int(off[B]) == total and \
+        bool(np.all(kb >= 0)) and bool(np.all(kb <= kmax))
+    for b in range(B):
+        o0, o1 = int(off[b]), int(off[b + 1])
+        if not consistent:
+            out["request_status"][b] = ST_BAD_OFFSETS
+            status |= ST_BAD_OFFSETS
+            continue
+        k = o1 - o0
+        r0 = o0 + b
+        l = logits[r0:r0 + k + 1].astype(np.float64)
+        if bitmask is None:
+            allowed = np.ones((k + 1, V), dtype=bool)
+        else:
+            allowed = unpack_bitmask(np.asarray(bitmask[r0:r0 + k + 1]), V)
+        q = None if draft_probs is None else np.asarray(draft_probs[o0:o1], dtype=np.float64)
+        r = _verify_request(l, x_all[o0:o1], q, allowed, float(T_all[b]), int(tk_all[b]),
+                            seed, b, block)
+        out["out_tokens"][r0:r0 + k + 1] = r["tokens"]
+        out["num_accepted"][b] = r["num_accepted"]
+        out["request_status"][b] = r["status"]
+        out["row_lse"][r0:r0 + k + 1] = r["row_lse"]
+        out["accept_prob"][o0:o1] = r["accept_prob"]
+        out["flag_accept"][b] = r["flag_accept"]
+        out["flag_gumbel"][b] = r["flag_gumbel"]
+        status |= r["status"]
+        R += r["R"]
+        I += r["I"]
+        A += r["A"]
+    out["counters"] = np.array([R, I, R - I, A], dtype=np.uint64)
+    out["status"] = status
+    out["accept_histogram"] = accept_histogram(out["num_accepted"], out["request_status"], kmax)
     return out
