@@ -70,6 +70,8 @@ typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
 #define SD_STATUS_EMPTY_ROW 4u      /* a row without an allowed finite logit */
 #define SD_STATUS_BAD_LOGIT 8u      /* NaN or +inf logit at an allowed token */
 #define SD_STATUS_BAD_DRAFT_PROB 16u /* q at a draft token NaN, infinite or < 0 */
+#define SD_STATUS_BAD_OFFSETS 32u   /* ragged call whose draft offsets are inconsistent:
+                                       set on every request (see draft_offsets) */
 
 typedef struct {
     int32_t batch;      /* B, 0 <= B <= SD_MAX_BATCH requests */
@@ -100,13 +102,36 @@ typedef struct {
      * after the row-statistics kernel (NULL = none); for timing only. */
     void *row_stats_event_begin;
     void *row_stats_event_end;
+    /* Ragged draft lengths (infra-guide 5.2, drafters that propose a variable
+     * number of tokens), or NULL for k drafts per request.  device [B + 1]
+     * int32 cumulative offsets: request b verifies k_b = off[b+1] - off[b]
+     * drafts, 0 <= k_b <= num_draft.  Every per-row and per-draft array is
+     * then packed without padding: logits and bitmask [total_drafts + B, ...]
+     * with request b's k_b + 1 rows from row off[b] + b, draft_token_ids
+     * [total_drafts] and draft_probs [total_drafts, V] from draft off[b],
+     * out_tokens [total_drafts + B] (k_b + 1 slots from off[b] + b),
+     * dbg_row_lse [total_drafts + B], dbg_accept_prob [total_drafts].  The
+     * offsets must start at 0, never decrease and end at total_drafts;
+     * otherwise every request gets SD_STATUS_BAD_OFFSETS and
+     * out_num_accepted = -1, no out_tokens slot is written and the counters
+     * are 0. */
+    const int32_t *draft_offsets;
+    int64_t total_drafts;  /* host: off[B] of a ragged call, 0 <= total_drafts <= B * num_draft */
+    /* device [num_draft + 1] or NULL: requests per accepted draft length
+     * (fanout, "Mean acceptance length uses another denominator": one bucket
+     * per possible accepted length), requests in error left out; overwritten
+     * by every call.  Accepted drafts per position i follow as the sum of
+     * the buckets above i. */
+    uint32_t *accept_histogram;
 } sd_params;
 
-/* Bytes of device workspace sd_verify needs for these sizes (0 for B = 0).
- * Host-only; never fails (returns 0 for invalid sizes). */
+/* Bytes of device workspace sd_verify needs for these sizes (0 for B = 0),
+ * including total_drafts for a ragged call.  Host-only; never fails (returns
+ * 0 for invalid sizes). */
 size_t sd_verify_workspace_size(const sd_params *p);
 
-/* Verify one batch.
+/* Verify one batch (shapes below for k drafts per request; see
+ * sd_params.draft_offsets for ragged calls).
  *   target_logits     device [B, k+1, V] bf16 or fp32 (p->logits_dtype).
  *                     Rows 16-byte aligned take the vector path, others a
  *                     slower element path.

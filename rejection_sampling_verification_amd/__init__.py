@@ -32,6 +32,7 @@ SD_STATUS_TEMPERATURE = 2
 SD_STATUS_EMPTY_ROW = 4
 SD_STATUS_BAD_LOGIT = 8
 SD_STATUS_BAD_DRAFT_PROB = 16
+SD_STATUS_BAD_OFFSETS = 32
 
 # every symbol include/sd_verify.h declares
 EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates")
@@ -51,6 +52,9 @@ class SdParams(ctypes.Structure):
         ("status", ctypes.c_void_p),
         ("row_stats_event_begin", ctypes.c_void_p),
         ("row_stats_event_end", ctypes.c_void_p),
+        ("draft_offsets", ctypes.c_void_p),
+        ("total_drafts", ctypes.c_int64),
+        ("accept_histogram", ctypes.c_void_p),
     ]
 
 
@@ -98,10 +102,14 @@ def _params(batch, num_draft, vocab, dtype_code):
     return p
 
 
-def sd_verify_workspace_size(batch, num_draft, vocab, logits_dtype=torch.bfloat16):
-    """Device workspace bytes for these sizes."""
-    return int(_lib.sd_verify_workspace_size(
-        ctypes.byref(_params(batch, num_draft, vocab, _dtype_code(logits_dtype)))))
+def sd_verify_workspace_size(batch, num_draft, vocab, logits_dtype=torch.bfloat16,
+                             total_drafts=None):
+    """Device workspace bytes for these sizes (total_drafts: a ragged call)."""
+    p = _params(batch, num_draft, vocab, _dtype_code(logits_dtype))
+    if total_drafts is not None:
+        p.draft_offsets = 1  # any non-null value: the size only depends on the mode
+        p.total_drafts = int(total_drafts)
+    return int(_lib.sd_verify_workspace_size(ctypes.byref(p)))
 
 
 def sd_status_string(code):
@@ -128,6 +136,7 @@ class VerifyResult(NamedTuple):
     accept_prob: Optional[torch.Tensor] = None     # [B, k] float64
     request_flags: Optional[torch.Tensor] = None   # [B] int32 (uint32 bits)
     flags: Optional[torch.Tensor] = None           # [2] int32 (uint32 counts)
+    accept_histogram: Optional[torch.Tensor] = None  # [k+1] int32 (uint32 counts)
 
 
 def _ptr(t):
@@ -156,7 +165,7 @@ class Verifier:
     """
 
     def __init__(self, batch, num_draft, vocab, logits_dtype=torch.bfloat16, device=None,
-                 debug=False):
+                 debug=False, histogram=False, total_drafts=None):
         dev = torch.device(device) if device is not None else torch.device("cuda")
         if dev.type != "cuda":
             raise ValueError("the verifier runs on a HIP device")
@@ -166,19 +175,34 @@ class Verifier:
         self.B, self.k, self.V = int(batch), int(num_draft), int(vocab)
         self.dtype = logits_dtype
         self.params = _params(self.B, self.k, self.V, _dtype_code(logits_dtype))
+        # ragged calls: draft counts differ per request, total_drafts in all
+        self.ragged = total_drafts is not None
+        self.T = int(total_drafts) if self.ragged else self.B * self.k
+        self.rows = self.T + self.B if self.ragged else self.B * (self.k + 1)
+        if self.ragged:
+            self.params.draft_offsets = 1  # placeholder until a call supplies the offsets
+            self.params.total_drafts = self.T
         ws = int(_lib.sd_verify_workspace_size(ctypes.byref(self.params)))
+        self.params.draft_offsets = None
         dev = self.device
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.workspace_bytes = ws
-        self.out_tokens = torch.empty((self.B, self.k + 1), dtype=torch.int32, device=dev)
+        tok_shape = (self.rows,) if self.ragged else (self.B, self.k + 1)
+        self.out_tokens = torch.empty(tok_shape, dtype=torch.int32, device=dev)
         self.out_num_accepted = torch.empty(self.B, dtype=torch.int32, device=dev)
         self.out_counters = torch.empty(4, dtype=torch.int64, device=dev)
         self.status = torch.empty(1, dtype=torch.int32, device=dev)
         self.params.status = self.status.data_ptr()
         self.debug = debug
+        self.accept_histogram = None
+        if histogram:
+            self.accept_histogram = torch.empty(self.k + 1, dtype=torch.int32, device=dev)
+            self.params.accept_histogram = self.accept_histogram.data_ptr()
         if debug:
-            self.row_lse = torch.empty((self.B, self.k + 1), dtype=torch.float64, device=dev)
-            self.accept_prob = torch.empty((self.B, self.k), dtype=torch.float64, device=dev)
+            lse_shape = (self.rows,) if self.ragged else (self.B, self.k + 1)
+            acc_shape = (self.T,) if self.ragged else (self.B, self.k)
+            self.row_lse = torch.empty(lse_shape, dtype=torch.float64, device=dev)
+            self.accept_prob = torch.empty(acc_shape, dtype=torch.float64, device=dev)
             self.request_flags = torch.empty(self.B, dtype=torch.int32, device=dev)
             self.flags = torch.empty(2, dtype=torch.int32, device=dev)
             self.params.dbg_row_lse = self.row_lse.data_ptr()
@@ -187,13 +211,28 @@ class Verifier:
             self.params.dbg_flags = self.flags.data_ptr()
 
     def __call__(self, target_logits, draft_token_ids, draft_probs=None, bitmask=None,
-                 temperature=None, seed=0, top_k=None, stream=None, row_stats_events=None):
+                 temperature=None, seed=0, top_k=None, stream=None, row_stats_events=None,
+                 draft_offsets=None):
         B, k, V, dev = self.B, self.k, self.V, self.device
-        _check(target_logits, "target_logits", self.dtype, (B, k + 1, V), dev)
-        if k > 0 or draft_token_ids is not None:
-            _check(draft_token_ids, "draft_token_ids", torch.int32, (B, k), dev)
-        _check(draft_probs, "draft_probs", torch.float32, (B, k, V), dev)
-        _check(bitmask, "bitmask", torch.int32, (B, k + 1, (V + 31) // 32), dev)
+        W = (V + 31) // 32
+        if self.ragged:
+            if draft_offsets is None:
+                raise ValueError("a ragged verifier needs draft_offsets ([B+1] int32)")
+            _check(draft_offsets, "draft_offsets", torch.int32, (B + 1,), dev)
+            _check(target_logits, "target_logits", self.dtype, (self.rows, V), dev)
+            if self.T > 0 or draft_token_ids is not None:
+                _check(draft_token_ids, "draft_token_ids", torch.int32, (self.T,), dev)
+            _check(draft_probs, "draft_probs", torch.float32, (self.T, V), dev)
+            _check(bitmask, "bitmask", torch.int32, (self.rows, W), dev)
+            self.params.draft_offsets = draft_offsets.data_ptr()
+        else:
+            if draft_offsets is not None:
+                raise ValueError("draft_offsets needs a verifier built with total_drafts")
+            _check(target_logits, "target_logits", self.dtype, (B, k + 1, V), dev)
+            if k > 0 or draft_token_ids is not None:
+                _check(draft_token_ids, "draft_token_ids", torch.int32, (B, k), dev)
+            _check(draft_probs, "draft_probs", torch.float32, (B, k, V), dev)
+            _check(bitmask, "bitmask", torch.int32, (B, k + 1, W), dev)
         if temperature is None:
             raise ValueError("temperature is required ([B] float32, 0 = greedy)")
         _check(temperature, "temperature", torch.float32, (B,), dev)
@@ -216,8 +255,9 @@ class Verifier:
         if self.debug:
             return VerifyResult(self.out_tokens, self.out_num_accepted, self.out_counters,
                                 self.status, self.row_lse, self.accept_prob,
-                                self.request_flags, self.flags)
-        return VerifyResult(self.out_tokens, self.out_num_accepted, self.out_counters, self.status)
+                                self.request_flags, self.flags, self.accept_histogram)
+        return VerifyResult(self.out_tokens, self.out_num_accepted, self.out_counters, self.status,
+                            accept_histogram=self.accept_histogram)
 
 
 def sd_verify(target_logits, draft_token_ids, draft_probs=None, bitmask=None, temperature=None,
@@ -234,6 +274,27 @@ def sd_verify(target_logits, draft_token_ids, draft_probs=None, bitmask=None, te
     B, kp1, V = target_logits.shape
     v = Verifier(B, kp1 - 1, V, target_logits.dtype, target_logits.device, debug=debug)
     return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream)
+
+
+def sd_verify_ragged(target_logits, draft_token_ids, draft_offsets, draft_probs=None,
+                     bitmask=None, temperature=None, seed=0, top_k=None, max_draft=None,
+                     debug=False, histogram=False, stream=None):
+    """Verify requests with their own draft counts; returns fresh outputs.
+
+    draft_offsets [B+1] int32 on the device (cumulative: request b has
+    off[b+1] - off[b] drafts), target_logits [total + B, V], draft_token_ids
+    [total], draft_probs [total, V] or None, bitmask [total + B, ceil(V/32)]
+    or None, temperature [B]; out_tokens come back as [total + B] (request b's
+    k_b + 1 slots from off[b] + b).  max_draft defaults to 64.
+    """
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be [total_drafts + B, V]")
+    B = draft_offsets.shape[0] - 1
+    rows, V = target_logits.shape
+    v = Verifier(B, SD_MAX_DRAFT if max_draft is None else max_draft, V, target_logits.dtype,
+                 target_logits.device, debug=debug, histogram=histogram, total_drafts=rows - B)
+    return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream,
+             draft_offsets=draft_offsets)
 
 
 def rates_from_counters(counters, steps):

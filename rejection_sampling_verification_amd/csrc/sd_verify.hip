@@ -170,6 +170,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint3
                                              kBufferWord3);
 }
 
+// ------------------------------------------------------------ request geometry
+
+// Where request b's rows, drafts and output slots sit.  Uniform calls: k
+// drafts per request, rows b (k + 1) ..; ragged calls (a cumulative draft
+// offset table off[B + 1]): k_b = off[b+1] - off[b] drafts, rows off[b] + b ..
+// and drafts off[b] ..  (infra-guide 5.2: drafters that propose a variable
+// number of tokens).  `ok` is false for every request of a ragged call whose
+// offsets the prep kernel found inconsistent; nothing is then read through
+// them.
+struct ReqGeom {
+    int k;          // drafts of the request
+    int64_t row0;   // its first row (and first output slot)
+    int64_t draft0; // its first draft
+    bool ok;
+};
+
+__device__ __forceinline__ ReqGeom req_geom(const int32_t *off, const uint32_t *off_ok, int b,
+                                            int k_uniform) {
+    ReqGeom g;
+    if (off == nullptr) {
+        g.k = k_uniform;
+        g.row0 = int64_t(b) * (k_uniform + 1);
+        g.draft0 = int64_t(b) * k_uniform;
+        g.ok = true;
+        return g;
+    }
+    g.ok = uniform_load(off_ok) != 0u;
+    const int o0 = uniform_load(off + b), o1 = uniform_load(off + b + 1);
+    g.k = g.ok ? o1 - o0 : 0;
+    g.row0 = g.ok ? int64_t(o0) + b : 0;
+    g.draft0 = g.ok ? o0 : 0;
+    return g;
+}
+
+// The request and position of a row (ragged calls: through the row table the
+// prep kernel wrote; only read when the offsets are consistent).
+__device__ __forceinline__ void row_owner(const int32_t *off, const int32_t *row_req, int row,
+                                          int kp1_uniform, int &b, int &i, int &k, int64_t &draft0) {
+    if (off == nullptr) {
+        b = row / kp1_uniform;
+        i = row - b * kp1_uniform;
+        k = kp1_uniform - 1;
+        draft0 = int64_t(b) * k;
+        return;
+    }
+    b = uniform_load(row_req + row);
+    const int o0 = uniform_load(off + b);
+    k = uniform_load(off + b + 1) - o0;
+    i = row - o0 - b;
+    draft0 = o0;
+}
+
 // ------------------------------------------------------------ row statistics
 
 // Statistics of one 2048-token block of a row.  Sampling rows: m = Mc =
@@ -205,6 +257,9 @@ struct RowStatsArgs {
     int ntally;                 // words of the tally
     uint32_t *status;         // zeroed here when given
     uint32_t *dbg_flags;      // zeroed here when given
+    const int32_t *off;       // ragged: [B + 1] draft offsets, or nullptr
+    const int32_t *row_req;   // ragged: [rows] request of each row
+    const uint32_t *off_ok;   // ragged: 1 when the offsets are consistent
     int64_t ntasks;           // rows * nchunk (chunked element kernel)
     int64_t nblk;             // rows * C (vector kernel sweep)
     int k, kp1, V, W, C, cpw, nchunk;
@@ -302,6 +357,7 @@ __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
 // Which rows a chunked wave works on, and their parameters (wave-uniform).
 struct RowTask {
     int row, b, i, c0, c1;
+    int64_t dpos;  // the row's draft index (draft rows)
     bool greedy, skip;
     float c, tau;
     int x, xblk, xrel;  // the draft, its block and offset in it (-1: none)
@@ -313,16 +369,18 @@ __device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task)
     const int chunk = static_cast<int>(task - int64_t(t.row) * a.nchunk);
     t.c0 = chunk * a.cpw;
     t.c1 = min(a.C, t.c0 + a.cpw);
-    t.b = t.row / a.kp1;
-    t.i = t.row - t.b * a.kp1;
+    int kb;
+    int64_t d0;
+    row_owner(a.off, a.row_req, t.row, a.kp1, t.b, t.i, kb, d0);
+    t.dpos = d0 + t.i;
     const float T = uniform_load(a.temperature + t.b);
     t.greedy = (T == 0.0f);
     t.skip = !t.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     t.c = t.greedy ? 0.0f : scale_of(T);
     t.tau = a.tau ? uniform_load(a.tau + t.row) : -INFINITY;
     t.x = t.xblk = t.xrel = -1;
-    if (t.i < a.k) {
-        const int x = uniform_load(a.draft + int64_t(t.b) * a.k + t.i);
+    if (t.i < kb) {
+        const int x = uniform_load(a.draft + t.dpos);
         if (x >= 0 && x < a.V) {
             t.x = x;
             t.xblk = x / kBlock;
@@ -336,7 +394,7 @@ __device__ __forceinline__ RowTask row_task(const RowStatsArgs &a, int64_t task)
 // the row's draft record.  v: the block's masked values; bits(g): the lane's
 // mask bits of group g.
 template <int G, int P, bool MASKED>
-__device__ __forceinline__ void record_draft(const RowStatsArgs &a, int row, int b, int i, int x,
+__device__ __forceinline__ void record_draft(const RowStatsArgs &a, int row, int64_t dpos, int x,
                                              int xrel, const float *v, const uint32_t *m, int lane,
                                              float sx) {
     const int xg = xrel / (kWave * P), xl = (xrel / P) & (kWave - 1), xe = xrel % P;
@@ -355,7 +413,7 @@ __device__ __forceinline__ void record_draft(const RowStatsArgs &a, int row, int
     r.sx = sx;
     r.lx = lx;
     r.allowed = (bits >> xe) & 1u;
-    r.qx = a.q ? uniform_load(a.q + (int64_t(b) * a.k + i) * a.V + x) : 1.0f;
+    r.qx = a.q ? uniform_load(a.q + dpos * a.V + x) : 1.0f;
 }
 
 // Raw 16-byte groups and mask bytes of one block wholly inside the row: lane
@@ -384,6 +442,7 @@ struct SweepBlock {
     bool full, greedy, skip;
     float c, tau;
     int x, xrel;  // the draft and its offset in this block (-1: elsewhere)
+    int64_t dpos; // the row's draft index (draft rows)
 };
 
 __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t gb) {
@@ -392,16 +451,18 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t
     s.row = static_cast<int>(gb / a.C);
     s.blk = static_cast<int>(gb - int64_t(s.row) * a.C);
     s.full = int64_t(s.blk + 1) * kBlock <= a.V;
-    s.b = s.row / a.kp1;
-    s.i = s.row - s.b * a.kp1;
+    int kb;
+    int64_t d0;
+    row_owner(a.off, a.row_req, s.row, a.kp1, s.b, s.i, kb, d0);
+    s.dpos = d0 + s.i;
     const float T = uniform_load(a.temperature + s.b);
     s.greedy = (T == 0.0f);
     s.skip = !s.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     s.c = s.greedy ? 0.0f : scale_of(T);
     s.tau = a.tau ? uniform_load(a.tau + s.row) : -INFINITY;
     s.x = s.xrel = -1;
-    if (s.i < a.k) {
-        const int x = uniform_load(a.draft + int64_t(s.b) * a.k + s.i);
+    if (s.i < kb) {
+        const int x = uniform_load(a.draft + s.dpos);
         if (x >= 0 && x < a.V && x / kBlock == s.blk) {
             s.x = x;
             s.xrel = x - s.blk * kBlock;
@@ -495,7 +556,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
         res = softmax_block<G * P>(v, s.c);
         if (s.xrel >= 0) sx = excluded_sum<G, P>(v, s.c, res.x, s.xrel, lane);
     }
-    if (s.xrel >= 0) record_draft<G, P, MASKED>(a, s.row, s.b, s.i, s.x, s.xrel, v, m, lane, sx);
+    if (s.xrel >= 0) record_draft<G, P, MASKED>(a, s.row, s.dpos, s.x, s.xrel, v, m, lane, sx);
     if (lane == slot) {
         st.gb = s.gb;
         st.row = s.row;
@@ -521,6 +582,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     zero_call_outputs(a);
+    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t stride = int64_t(gridDim.x) * (kThreads / kWave);
     const int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
@@ -591,6 +653,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     zero_call_outputs(a);
+    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t task = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
     if (task >= a.ntasks) return;
@@ -623,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
                 if (lane == 0) a.drec[t.row].keyx = key_of_mass(sx, r.x, g);
             }
         }
-        if (blk == t.xblk) record_draft<G, P, true>(a, t.row, t.b, t.i, t.x, t.xrel, v, m, lane, sx);
+        if (blk == t.xblk) record_draft<G, P, true>(a, t.row, t.dpos, t.x, t.xrel, v, m, lane, sx);
         if (lane == 0) a.bstats[int64_t(t.row) * a.C + blk] = out;
     }
 }
@@ -653,6 +716,9 @@ struct TopkArgs {
     const float *temperature;
     const int32_t *top_k;
     float *tau;  // [rows]
+    const int32_t *off;      // ragged: draft offsets, or nullptr
+    const int32_t *row_req;  // ragged: request of each row
+    const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
     int kp1, V, W;
 };
 
@@ -777,7 +843,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     constexpr int64_t kStep = int64_t(kTopkThreads) * P;
     __shared__ TopkShared sh;
     const int row = blockIdx.x, tid = threadIdx.x;
-    const int b = row / a.kp1;
+    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call
+    int b, i, kb;
+    int64_t d0;
+    row_owner(a.off, a.row_req, row, a.kp1, b, i, kb, d0);
     const float T = uniform_load(a.temperature + b);
     const int K = uniform_load(a.top_k + b);
     if (!(T > 0.0f && T <= FLT_MAX) || K <= 0) {
@@ -905,7 +974,8 @@ struct DenseJob {
     double invT;   // 1 / T in fp64
     float c, M;    // log2(e) / T and the row's fp32 max (log2 units)
     float tau;     // the row's top-k threshold (-inf: none)
-    int row;       // b * (k + 1) + n, or -1: no dense draw for this request
+    int64_t dpos;  // the rejected draft's index (its q row)
+    int row;       // the rejected row (and output slot), or -1: no dense draw
     int n;         // the rejected position
     Level1 l1p;    // level-1 winner under p, for the fallback
 };
@@ -933,7 +1003,9 @@ struct FinalArgs {
     DenseJob *jobs;    // [B] dense q only
     double *wmass;     // [B, C] dense q only: residual mass per block
     int split_dense;   // dense q: 1 = residual masses by the grid-wide kernels
-    int B, k, V, W, C;
+    const int32_t *off;      // ragged: [B + 1] draft offsets, or nullptr
+    const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
+    int B, k, V, W, C;       // k: the uniform draft count, or the largest k_b
 };
 
 enum SampleMode { kModeP = 0, kModeOneHot = 1, kModeDense = 2 };
@@ -1055,11 +1127,9 @@ __device__ __forceinline__ void load4_masked(const ET *row, const uint32_t *mrow
 // threads call it; returns (token, near-tie flag), token -1 when the block
 // holds no positive weight.
 template <typename ET, bool ALIGNED>
-__device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int cb, int mode, float c,
-                       double invT, const float *qrow, bool staged, int attempt) {
-    const int k = a.k, V = a.V;
-    const int64_t row = int64_t(b) * (k + 1) + n;
-    const int x = (n < k) ? sh.X[n] : -1;
+__device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_t row, int x, int cb,
+                       int mode, float c, double invT, const float *qrow, bool staged, int attempt) {
+    const int V = a.V;
     const int64_t j0 = int64_t(cb) * kBlock + threadIdx.x * 4;
     float lv[4];
     if (staged) {
@@ -1240,14 +1310,16 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
 // with the sums into one 64-bit word, so the workgroup that completes a level
 // reads that level's totals in its own atomic's return value: no fence and
 // no ordering between different words is needed, and the integer sums do not
-// depend on the order of arrival.
-//   slot word:  arrivals [0,12)  accepted [12,30)  outside grammar [30,48)  errors [48,60)
-//   call word 0: slots [0,9)  accepted [9,33)  errors [33,50)   -> writes R and A
-//   call word 1: slots [0,9)  outside grammar [9,33)  errors [33,50)  -> writes I and D
-// Field widths hold B <= 65535 with at most 256 slots of at most 256 requests.
-__device__ __forceinline__ unsigned long long tally_share(int accepted, int invalid, bool error) {
-    return 1ull | (static_cast<unsigned long long>(accepted) << 12) |
-           (static_cast<unsigned long long>(invalid) << 30) | (error ? (1ull << 48) : 0ull);
+// depend on the order of arrival.  A request in error adds only its arrival.
+//   slot word:   arrivals [0,9)  accepted [9,24)  outside grammar [24,39)  drafts [39,54)
+//   call word 0: slots [0,9)  accepted [9,31)  drafts [31,53)          -> writes R and A
+//   call word 1: slots [0,9)  outside grammar [9,31)  drafts [31,53)   -> writes I and D
+// Field widths hold B <= 65535 requests of at most 64 drafts, with at most
+// 256 slots of at most 256 requests.
+__device__ __forceinline__ unsigned long long tally_share(int accepted, int invalid, int drafts) {
+    return 1ull | (static_cast<unsigned long long>(accepted) << 9) |
+           (static_cast<unsigned long long>(invalid) << 24) |
+           (static_cast<unsigned long long>(drafts) << 39);
 }
 
 // Adds request b's share to its slot word; returns the word's previous value.
@@ -1264,23 +1336,22 @@ __device__ __forceinline__ void tally_call(const FinalArgs &a, int b, unsigned l
     const unsigned long long slot = before + share;
     const int S = a.nslot, s = b % S;
     const int members = (a.B - s + S - 1) / S;  // requests b' < B with b' % S == s
-    if (static_cast<int>(slot & 0xfffull) != members) return;
-    const unsigned long long acc = (slot >> 12) & 0x3ffffull, inv = (slot >> 30) & 0x3ffffull,
-                             err = (slot >> 48) & 0xfffull;
+    if (static_cast<int>(slot & 0x1ffull) != members) return;
+    const unsigned long long acc = (slot >> 9) & 0x7fffull, inv = (slot >> 24) & 0x7fffull,
+                             drafts = (slot >> 39) & 0x7fffull;
     unsigned long long *call = a.tally + S * kTallyStride;
-    const unsigned long long w0 = 1ull | (acc << 9) | (err << 33);
-    const unsigned long long w1 = 1ull | (inv << 9) | (err << 33);
+    const unsigned long long w0 = 1ull | (acc << 9) | (drafts << 31);
+    const unsigned long long w1 = 1ull | (inv << 9) | (drafts << 31);
     const unsigned long long t0 = atomicAdd(&call[0], w0) + w0;
     const unsigned long long t1 = atomicAdd(&call[kTallyStride], w1) + w1;
-    const uint64_t k = static_cast<uint64_t>(a.k), B = static_cast<uint64_t>(a.B);
     if (static_cast<int>(t0 & 0x1ffull) == S) {
-        a.out_counters[0] = k * (B - ((t0 >> 33) & 0x1ffffull));
-        a.out_counters[3] = (t0 >> 9) & 0xffffffull;
+        a.out_counters[0] = (t0 >> 31) & 0x3fffffull;
+        a.out_counters[3] = (t0 >> 9) & 0x3fffffull;
     }
     if (static_cast<int>(t1 & 0x1ffull) == S) {
-        const uint64_t I = (t1 >> 9) & 0xffffffull;
+        const uint64_t R = (t1 >> 31) & 0x3fffffull, I = (t1 >> 9) & 0x3fffffull;
         a.out_counters[1] = I;
-        a.out_counters[2] = k * (B - ((t1 >> 33) & 0x1ffffull)) - I;
+        a.out_counters[2] = R - I;
     }
 }
 
@@ -1292,26 +1363,28 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     extern __shared__ double sW[];  // dense q, short rows: per-block residual mass [C]
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
-    const int k = a.k, kp1 = a.k + 1, V = a.V, C = a.C;
+    const ReqGeom geo = req_geom(a.off, a.off_ok, b, a.k);
+    const int k = geo.k, kp1 = geo.k + 1, V = a.V, C = a.C;
     const float T = uniform_load(a.temperature + b);
     const bool greedy = (T == 0.0f);
     const bool bad_T = !greedy && !(T > 0.0f && T <= FLT_MAX);
+    const bool skip_rows = bad_T || !geo.ok;  // nothing of the request's rows is read
     const PhiloxKey key = key_of(a.seed);
     const float c = greedy || bad_T ? 0.0f : scale_of(T);
     constexpr bool one_hot = !DENSE;
 
     // ---- this wave's first row's block statistics, in flight with the drafts
     FoldCache fc;
-    if (!bad_T && wave < kp1) load_fold_cache(a.bstats + (int64_t(b) * kp1 + wave) * C, C, lane, fc);
+    if (!skip_rows && wave < kp1) load_fold_cache(a.bstats + (geo.row0 + wave) * C, C, lane, fc);
 
     // ---- drafts, and what the sweep recorded about them
     int x = -1;
-    if (tid < k) x = a.draft[int64_t(b) * k + tid];
+    if (tid < k) x = a.draft[geo.draft0 + tid];
     const bool xok = tid < k && x >= 0 && x < V;
     DraftRec rec;
-    if (tid < k) rec = a.drec[int64_t(b) * kp1 + tid];  // read only when xok and T is valid
+    if (tid < k) rec = a.drec[geo.row0 + tid];  // read only when xok and T is valid
     if (tid == 0) {
-        sh.status = bad_T ? SD_STATUS_TEMPERATURE : 0u;
+        sh.status = (bad_T ? SD_STATUS_TEMPERATURE : 0u) | (geo.ok ? 0u : SD_STATUS_BAD_OFFSETS);
         sh.nacc = 0;
         sh.flag_acc = 0;
         sh.ninvalid = 0;
@@ -1333,9 +1406,9 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     uint4 stage_r[G];
     uint32_t stage_m[G];
     int stage_row = -1, stage_c = -1;
-    if (!bad_T) {
+    if (!skip_rows) {
         for (int i = wave; i < kp1; i += kFinalWaves) {
-            const int64_t row = int64_t(b) * kp1 + i;
+            const int64_t row = geo.row0 + i;
             const BlockStat *st = a.bstats + row * C;
             if (i != wave) load_fold_cache(st, C, lane, fc);  // rows past the first wave of rows
             if (greedy) {
@@ -1418,7 +1491,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
 #pragma unroll
             for (int e = 0; e < P; ++e)
                 if (!((bits >> e) & 1u)) v[e] = -INFINITY;
-            if (a.tau) apply_tau<P>(v, a.tau[int64_t(b) * kp1 + stage_row]);
+            if (a.tau) apply_tau<P>(v, a.tau[geo.row0 + stage_row]);
 #pragma unroll
             for (int h = 0; h < P / 4; ++h)
                 *reinterpret_cast<float4 *>(&sh.blockv[off + 4 * h]) =
@@ -1436,7 +1509,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (tid == 0) {
         const bool err = sh.status != 0;
-        share = tally_share(err ? 0 : sh.nacc, err ? 0 : sh.ninvalid, err);
+        share = tally_share(err ? 0 : sh.nacc, err ? 0 : sh.ninvalid, err ? 0 : k);
         before = tally_slot(a, b, share);
     }
     lds_barrier();
@@ -1452,19 +1525,20 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             y = sh.G[n];
         } else {
             const double invT = 1.0 / static_cast<double>(T);
-            const float *qrow = (DENSE && n < k) ? a.q + (int64_t(b) * k + n) * V : nullptr;
+            const float *qrow = (DENSE && n < k) ? a.q + (geo.draft0 + n) * V : nullptr;
             int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
             if (DENSE && mode == kModeDense && a.split_dense) {
                 // left to the residual kernels; -1 stands in until they write y
                 if (tid == 0) {
                     DenseJob j;
-                    j.row = b * kp1 + n;
+                    j.row = static_cast<int>(geo.row0 + n);
+                    j.dpos = geo.draft0 + n;
                     j.n = n;
                     j.c = c;
                     j.M = sh.M[n];
                     j.S = sh.S[n];
-                    j.tau = a.tau ? a.tau[int64_t(b) * kp1 + n] : -INFINITY;
+                    j.tau = a.tau ? a.tau[geo.row0 + n] : -INFINITY;
                     j.l1p = sh.l1p[n];
                     j.invT = invT;
                     a.jobs[b] = j;
@@ -1472,7 +1546,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 deferred = true;
             }
             if (DENSE && mode == kModeDense && !a.split_dense) {
-                const int64_t row = int64_t(b) * kp1 + n;
+                const int64_t row = geo.row0 + n;
                 dense_block_masses<ET, ALIGNED>(
                     reinterpret_cast<const ET *>(a.logits) + row * V,
                     a.mask ? a.mask + row * a.W : nullptr, qrow, V, C, c, sh.M[n], sh.S[n],
@@ -1511,7 +1585,8 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                     l1 = sh.l1p[n];
                 }
                 const int2 r2 =
-                    level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, c, invT, qrow, sh.staged_c == l1.c, attempt);
+                    level2<ET, ALIGNED>(a, sh, b, n, geo.row0 + n, n < k ? sh.X[n] : -1, l1.c, mode, c,
+                                        invT, qrow, sh.staged_c == l1.c, attempt);
                 if (r2.x >= 0) {
                     y = r2.x;
                     fg = l1.flag + r2.y;
@@ -1524,18 +1599,18 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
 
     // ---- outputs, and this request's share of the counters
     const int n = st ? -1 : sh.nacc;
-    if (tid < kp1) {
+    if (tid < kp1 && geo.ok) {  // a malformed ragged call has no slots to write
         int tok = -1;
         if (!st) tok = tid < n ? sh.X[tid] : (tid == n ? y : -1);
-        a.out_tokens[int64_t(b) * kp1 + tid] = tok;
+        a.out_tokens[geo.row0 + tid] = tok;
         if (a.dbg_lse) {
             double v = NAN;
             if (!st) v = greedy ? static_cast<double>(sh.M[tid])
                                 : kLn2 * (static_cast<double>(sh.M[tid]) + log2(sh.S[tid]));
-            a.dbg_lse[int64_t(b) * kp1 + tid] = v;
+            a.dbg_lse[geo.row0 + tid] = v;
         }
     }
-    if (tid < k && a.dbg_acc) a.dbg_acc[int64_t(b) * k + tid] = st ? NAN : sh.acc[tid];
+    if (tid < k && a.dbg_acc) a.dbg_acc[geo.draft0 + tid] = st ? NAN : sh.acc[tid];
     if (tid == 0) {
         a.out_num_accepted[b] = n;
         if (a.dbg_req_flags)
@@ -1564,7 +1639,7 @@ __global__ __launch_bounds__(kThreads) void dense_mass_kernel(FinalArgs a) {
     const int V = a.V, lane = threadIdx.x & (kWave - 1);
     const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(j.row) * V;
     const uint8_t *mb = a.mask ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(j.row) * a.W) : nullptr;
-    const float *qrow = a.q + (int64_t(b) * a.k + j.n) * V;
+    const float *qrow = a.q + j.dpos * V;
     const float invS = static_cast<float>(1.0 / j.S);
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -1631,16 +1706,16 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
     const int b = blockIdx.x, tid = threadIdx.x;
     const DenseJob j = a.jobs[b];
     if (j.row < 0) return;
-    const int k = a.k, kp1 = k + 1, C = a.C, n = j.n;
+    const int C = a.C, n = j.n;
     const PhiloxKey key = key_of(a.seed);
     if (tid == 0) {
         sh.M[n] = j.M;
         sh.S[n] = j.S;
-        sh.X[n] = a.draft[int64_t(b) * k + n];
+        sh.X[n] = a.draft[j.dpos];
     }
     lds_barrier();
     const double *W = a.wmass + int64_t(b) * C;
-    const float *qrow = a.q + (int64_t(b) * k + n) * a.V;
+    const float *qrow = a.q + j.dpos * a.V;
     // residual masses are <= 1, so their keys need no reference
     const int ngroups = (C + 3) >> 2;
     float kq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -1672,7 +1747,8 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
             mode = kModeP;
             l1 = j.l1p;
         }
-        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, l1.c, mode, j.c, invT, qrow, false, attempt);
+        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, j.row, sh.X[n], l1.c, mode, j.c, invT, qrow,
+                                            false, attempt);
         if (r2.x >= 0) {
             y = r2.x;
             fg = l1.flag + r2.y;
@@ -1681,17 +1757,65 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
         l1.c = -1;
     }
     if (tid == 0) {
-        a.out_tokens[int64_t(b) * kp1 + n] = y;
+        a.out_tokens[j.row] = y;
         if (a.dbg_req_flags) a.dbg_req_flags[b] += static_cast<uint32_t>(fg) << 16;
         if (a.dbg_flags && fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
     }
 }
 
-// Outputs of an empty batch: zero counters, status and flags.
-__global__ void empty_batch_kernel(uint64_t *counters, uint32_t *status, uint32_t *flags) {
+// Outputs of an empty batch: zero counters, status, flags and histogram.
+__global__ void empty_batch_kernel(uint64_t *counters, uint32_t *status, uint32_t *flags,
+                                   uint32_t *hist, int kmax) {
     if (threadIdx.x < 4) counters[threadIdx.x] = 0ull;
     if (threadIdx.x == 0 && status) *status = 0u;
     if (threadIdx.x < 2 && flags) flags[threadIdx.x] = 0u;
+    if (hist)
+        for (int i = threadIdx.x; i <= kmax; i += blockDim.x) hist[i] = 0u;
+}
+
+// Ragged calls: checks the draft offsets (start at 0, never decrease, end at
+// total, no request above kmax drafts) and, when they hold, writes the
+// request of every row; one workgroup, so the check and the table need no
+// ordering between workgroups.  Nothing is written through offsets that fail.
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t *off, int B, int kmax,
+                                                                  int64_t total, int32_t *row_req,
+                                                                  uint32_t *off_ok) {
+    __shared__ uint32_t bad_any;
+    if (threadIdx.x == 0) bad_any = 0u;
+    __syncthreads();
+    bool bad = threadIdx.x == 0 && (off[0] != 0 || int64_t(off[B]) != total);
+    for (int b = threadIdx.x; b < B; b += kPrepThreads) {
+        const int64_t d = int64_t(off[b + 1]) - int64_t(off[b]);
+        bad |= d < 0 || d > kmax;
+    }
+    if (bad) atomicOr(&bad_any, 1u);
+    __syncthreads();
+    const bool ok = bad_any == 0u;
+    if (threadIdx.x == 0) *off_ok = ok ? 1u : 0u;
+    if (!ok) return;
+    // the offsets now partition rows [0, total + B): request b owns k_b + 1
+    // rows from off[b] + b
+    for (int b = threadIdx.x; b < B; b += kPrepThreads) {
+        const int64_t r0 = int64_t(off[b]) + b, kb = int64_t(off[b + 1]) - off[b];
+        for (int64_t i = 0; i <= kb; ++i) row_req[r0 + i] = b;
+    }
+}
+
+// Requests per accepted draft length 0 .. kmax (requests in error, with
+// num_accepted = -1, left out); one workgroup, after the finalize kernels.
+__global__ __launch_bounds__(1024) void histogram_kernel(const int32_t *num_accepted, int B, int kmax,
+                                                         uint32_t *hist) {
+    __shared__ uint32_t h[kMaxDraft + 1];
+    for (int i = threadIdx.x; i <= kmax; i += blockDim.x) h[i] = 0u;
+    __syncthreads();
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int n = num_accepted[b];
+        if (n >= 0 && n <= kmax) atomicAdd(&h[n], 1u);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i <= kmax; i += blockDim.x) hist[i] = h[i];
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1737,7 +1861,7 @@ FinalFn pick_final(bool aligned, bool dense) {
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_drec, off_tau, off_jobs, off_wmass, off_tally, total;
+    size_t off_bstats, off_drec, off_tau, off_jobs, off_wmass, off_rowreq, off_offok, off_tally, total;
     int nslot;
 };
 
@@ -1746,7 +1870,9 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 inline bool sizes_ok(const sd_params *p) {
     return p && p->batch >= 0 && p->batch <= SD_MAX_BATCH && p->num_draft >= 0 &&
            p->num_draft <= SD_MAX_DRAFT &&
-           p->vocab >= 1 && p->vocab <= SD_MAX_VOCAB;
+           p->vocab >= 1 && p->vocab <= SD_MAX_VOCAB &&
+           (!p->draft_offsets ||
+            (p->total_drafts >= 0 && p->total_drafts <= int64_t(p->batch) * p->num_draft));
 }
 
 // Slots of the counter tally: about sqrt(B), at most 256.
@@ -1758,7 +1884,7 @@ inline int tally_slots(int B) {
 
 inline Layout layout_of(const sd_params *p) {
     Layout L{};
-    L.rows = int64_t(p->batch) * (p->num_draft + 1);
+    L.rows = p->draft_offsets ? p->total_drafts + p->batch : int64_t(p->batch) * (p->num_draft + 1);
     L.C = (p->vocab + kBlock - 1) / kBlock;
     L.W = (p->vocab + 31) / 32;
     L.nchunk = (L.C + SDV_BLOCKS_PER_WAVE - 1) / SDV_BLOCKS_PER_WAVE;
@@ -1767,7 +1893,9 @@ inline Layout layout_of(const sd_params *p) {
     L.off_tau = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
     L.off_jobs = L.off_tau + align256(size_t(L.rows) * sizeof(float));
     L.off_wmass = L.off_jobs + align256(size_t(p->batch) * sizeof(DenseJob));
-    L.off_tally = L.off_wmass + align256(size_t(p->batch) * L.C * sizeof(double));
+    L.off_rowreq = L.off_wmass + align256(size_t(p->batch) * L.C * sizeof(double));
+    L.off_offok = L.off_rowreq + align256(p->draft_offsets ? size_t(L.rows) * sizeof(int32_t) : 0);
+    L.off_tally = L.off_offok + 256;
     L.nslot = tally_slots(p->batch);
     L.total = L.off_tally + align256(size_t(L.nslot + 2) * kTallyStride * sizeof(uint64_t));
     return L;
@@ -1812,16 +1940,20 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     using namespace sdv;
     if (!p || !out_counters) return SD_ERR_INVALID_ARG;
     if (p->batch < 0 || p->num_draft < 0 || p->vocab < 1) return SD_ERR_INVALID_ARG;
+    if (p->draft_offsets &&
+        (p->total_drafts < 0 || p->total_drafts > int64_t(p->batch) * p->num_draft))
+        return SD_ERR_INVALID_ARG;
     if (p->logits_dtype != SD_DTYPE_F32 && p->logits_dtype != SD_DTYPE_BF16) return SD_ERR_INVALID_ARG;
     if (!sizes_ok(p)) return SD_ERR_UNSUPPORTED;
     const int B = p->batch, k = p->num_draft, V = p->vocab;
     if (B == 0) {
         hipLaunchKernelGGL(empty_batch_kernel, dim3(1), dim3(64), 0, stream, out_counters, p->status,
-                           p->dbg_flags);
+                           p->dbg_flags, p->accept_histogram, k);
         return hipGetLastError() == hipSuccess ? SD_OK : SD_ERR_HIP;
     }
     if (!target_logits || !temperature || !out_tokens || !out_num_accepted) return SD_ERR_INVALID_ARG;
-    if (k > 0 && !draft_token_ids) return SD_ERR_INVALID_ARG;
+    const bool ragged = p->draft_offsets != nullptr;
+    if ((ragged ? p->total_drafts > 0 : k > 0) && !draft_token_ids) return SD_ERR_INVALID_ARG;
     const Layout L = layout_of(p);
     if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SD_ERR_WORKSPACE;
@@ -1841,6 +1973,11 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.q = draft_probs;
     ra.seed = seed;
     ra.tau = p->top_k ? reinterpret_cast<float *>(ws + L.off_tau) : nullptr;
+    int32_t *row_req = reinterpret_cast<int32_t *>(ws + L.off_rowreq);
+    uint32_t *off_ok = reinterpret_cast<uint32_t *>(ws + L.off_offok);
+    ra.off = p->draft_offsets;
+    ra.row_req = ragged ? row_req : nullptr;
+    ra.off_ok = ragged ? off_ok : nullptr;
     ra.bstats = reinterpret_cast<BlockStat *>(ws + L.off_bstats);
     ra.drec = reinterpret_cast<DraftRec *>(ws + L.off_drec);
     ra.tally = reinterpret_cast<unsigned long long *>(ws + L.off_tally);
@@ -1882,6 +2019,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.bstats = ra.bstats;
     fa.drec = ra.drec;
     fa.tau = ra.tau;
+    fa.off = ra.off;
+    fa.off_ok = ra.off_ok;
     fa.jobs = reinterpret_cast<DenseJob *>(ws + L.off_jobs);
     fa.wmass = reinterpret_cast<double *>(ws + L.off_wmass);
     // Long rows: the residual masses of the rejected rows are summed by a
@@ -1900,6 +2039,11 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr)
                       : pick_final<float>(aligned, draft_probs != nullptr);
 
+    if (ragged) {
+        hipLaunchKernelGGL(ragged_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, p->draft_offsets, B, k,
+                           p->total_drafts, row_req, off_ok);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    }
     if (topk) {
         TopkArgs ta;
         ta.logits = target_logits;
@@ -1907,6 +2051,9 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         ta.temperature = temperature;
         ta.top_k = p->top_k;
         ta.tau = const_cast<float *>(ra.tau);
+        ta.off = ra.off;
+        ta.row_req = ra.row_req;
+        ta.off_ok = ra.off_ok;
         ta.kp1 = k + 1;
         ta.V = V;
         ta.W = L.W;
@@ -1932,6 +2079,11 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         hipLaunchKernelGGL(k3, dim3(gx, static_cast<unsigned>(B)), dim3(kThreads), 0, stream, fa);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
         hipLaunchKernelGGL(k4, dim3(B), dim3(kFinalThreads), 0, stream, fa);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    }
+    if (p->accept_histogram) {
+        hipLaunchKernelGGL(histogram_kernel, dim3(1), dim3(1024), 0, stream, out_num_accepted, B, k,
+                           p->accept_histogram);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }
     return SD_OK;

@@ -95,3 +95,75 @@ def assert_parity(gpu, orc, requests=None, max_flagged=2):
         raise AssertionError(f"{len(mism)} mismatching requests {mism[:10]}; {detail}")
     assert len(flagged) <= max_flagged, f"too many flagged requests: {flagged}"
     return flagged
+
+
+# ------------------------------------------------------------ ragged calls
+
+def run_gpu_ragged(wl, max_draft, seed=None):
+    """wl: logits [rows, V], draft_token_ids [T], draft_offsets [B+1] (device
+    int32), draft_probs [T, V] or None, bitmask [rows, W] or None,
+    temperature [B], top_k or None, seed."""
+    import rejection_sampling_verification_amd as sdv
+    lg = wl["logits"]
+    B = wl["draft_offsets"].shape[0] - 1
+    rows, V = lg.shape
+    v = sdv.Verifier(B, max_draft, V, lg.dtype, lg.device, debug=True, histogram=True,
+                     total_drafts=rows - B)
+    r = v(lg, wl["draft_token_ids"], wl["draft_probs"], wl["bitmask"], wl["temperature"],
+          wl["seed"] if seed is None else seed, wl["top_k"], draft_offsets=wl["draft_offsets"])
+    torch.cuda.synchronize()
+    out = {name: getattr(r, name).cpu().numpy().copy() for name in r._fields if getattr(r, name) is not None}
+    out["counters"] = out["out_counters"].view(np.uint64)
+    out["status"] = int(out["status"].view(np.uint32)[0])
+    return out
+
+
+def run_oracle_ragged(wl, max_draft, seed=None):
+    def cv(t):
+        if t is None:
+            return None
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            t = t.float()
+        return t.cpu().numpy()
+    rows = wl["logits"].shape[0]
+    B = wl["draft_offsets"].shape[0] - 1
+    return oracle.sd_verify_ragged(cv(wl["logits"]), cv(wl["draft_token_ids"]), cv(wl["draft_offsets"]),
+                                   cv(wl["draft_probs"]), cv(wl["bitmask"]), cv(wl["temperature"]),
+                                   seed=wl["seed"] if seed is None else seed, top_k=cv(wl["top_k"]),
+                                   max_draft=max_draft, total_drafts=rows - B)
+
+
+def assert_parity_ragged(gpu, orc, off, max_flagged=2):
+    """Per request over its own rows and drafts; counters, status and the
+    histogram over the call (exact unless a request is flagged)."""
+    off = np.asarray(off, dtype=np.int64)
+    B = off.shape[0] - 1
+    mism, flagged = [], []
+    for b in range(B):
+        err_o = orc["request_status"][b] != 0
+        if err_o != (gpu["out_num_accepted"][b] == -1):
+            mism.append(b)
+            continue
+        if err_o:
+            continue
+        if orc["flag_accept"][b] or orc["flag_gumbel"][b]:
+            flagged.append(b)
+            continue
+        k = int(off[b + 1] - off[b])
+        r0, d0 = int(off[b]) + b, int(off[b])
+        if (orc["num_accepted"][b] != gpu["out_num_accepted"][b]
+                or not np.array_equal(orc["out_tokens"][r0:r0 + k + 1], gpu["out_tokens"][r0:r0 + k + 1])
+                or not _close(gpu["row_lse"][r0:r0 + k + 1], orc["row_lse"][r0:r0 + k + 1], LSE_RTOL)
+                or not _close(gpu["accept_prob"][d0:d0 + k], orc["accept_prob"][d0:d0 + k], ACC_RTOL)):
+            mism.append(b)
+    assert not mism, f"{len(mism)} mismatching requests {mism[:10]}"
+    assert len(flagged) <= max_flagged, f"too many flagged requests: {flagged}"
+    R, I, D, A = (int(v) for v in orc["counters"])
+    gR, gI, gD, gA = (int(v) for v in gpu["counters"])
+    assert (gR, gI, gD) == (R, I, D), ((gR, gI, gD), (R, I, D))
+    if not flagged:
+        assert gA == A
+        assert np.array_equal(gpu["accept_histogram"].astype(np.int64), orc["accept_histogram"])
+    assert gpu["status"] == orc["status"], (gpu["status"], orc["status"])
+    return flagged

@@ -32,9 +32,12 @@ def test_library_exports_every_declared_symbol():
 
 def test_params_struct_layout_matches_header():
     import rejection_sampling_verification_amd as sdv
-    # 3 x int32 + enum, then 8 pointers
-    assert ctypes.sizeof(sdv.SdParams) == 16 + 8 * 8
+    # 3 x int32 + enum, then 8 pointers, offsets, total_drafts, histogram
+    assert ctypes.sizeof(sdv.SdParams) == 16 + 11 * 8
     assert sdv.SdParams.top_k.offset == 16
+    assert sdv.SdParams.draft_offsets.offset == 16 + 8 * 8
+    assert sdv.SdParams.total_drafts.offset == 16 + 9 * 8
+    assert sdv.SdParams.accept_histogram.offset == 16 + 10 * 8
 
 
 def test_status_strings():
@@ -131,3 +134,20 @@ def test_package_refuses_to_import_without_the_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="missing"):
         spec.loader.exec_module(mod)
+
+
+def test_ragged_host_checks_and_workspace():
+    import rejection_sampling_verification_amd as sdv
+    lib = sdv.library()
+    nul = ctypes.c_void_p(0)
+    counters = (ctypes.c_uint64 * 4)()
+    p = sdv.SdParams()
+    p.batch, p.num_draft, p.vocab, p.logits_dtype = 4, 3, 100, 1
+    p.draft_offsets = 1 << 20                      # a fake device address; never read here
+    for total in (-1, 13):                         # below 0, above B * num_draft
+        p.total_drafts = total
+        assert lib.sd_verify(nul, nul, nul, nul, nul, 0, nul, nul, counters, ctypes.byref(p), nul, 0, nul) == -1
+    assert sdv.sd_verify_workspace_size(4, 3, 100, total_drafts=13) == 0
+    ws_r = sdv.sd_verify_workspace_size(4, 3, 100, total_drafts=5)
+    ws_u = sdv.sd_verify_workspace_size(4, 3, 100)
+    assert ws_r > 0 and ws_u > 0 and ws_r < ws_u + 4096
