@@ -175,6 +175,41 @@ def cpu_baseline(wl, n_requests, min_seconds=10.0):
             "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
 
 
+def cpu_baseline_ragged(wl, min_seconds=10.0):
+    """The ragged oracle on one host thread over the whole workload, repeated
+    until at least min_seconds have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    def cv(t):
+        if t is None:
+            return None
+        t = t.detach()
+        return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+    import torch
+    host = {key: cv(wl[key]) for key in ("logits", "draft_token_ids", "draft_offsets", "draft_probs",
+                                         "bitmask", "temperature", "top_k")}
+    passes = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.sd_verify_ragged(host["logits"], host["draft_token_ids"], host["draft_offsets"],
+                                    host["draft_probs"], host["bitmask"], host["temperature"],
+                                    seed=wl["seed"], top_k=host["top_k"], max_draft=wl["max_draft"])
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    T = host["draft_token_ids"].shape[0]
+    return {"value": passes * T / dt, "unit": "verified draft positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} passes over the whole workload ({T} drafts), float64 NumPy on "
+                      f"one thread, {dt:.1f} s",
+            "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,15 +247,29 @@ def main():
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     wl = make_workload(args.workload, device=dev)
     lg = wl["logits"]
-    B, kp1, V = lg.shape
-    k = kp1 - 1
+    ragged = "draft_offsets" in wl
+    if ragged:  # per-request draft counts: rows packed, positions = all drafts
+        rows, V = lg.shape
+        B = wl["draft_offsets"].shape[0] - 1
+        k = wl["max_draft"]
+        positions = rows - B
+        kw = {"draft_offsets": wl["draft_offsets"]}
+        vkw = {"total_drafts": positions}
+    else:
+        B, kp1, V = lg.shape
+        k = kp1 - 1
+        positions = B * k
+        kw, vkw = {}, {}
     copies = [lg] + [lg.clone() for _ in range(max(0, args.copies - 1))]
-    v = sdv.Verifier(B, k, V, lg.dtype, dev)
+    v = sdv.Verifier(B, k, V, lg.dtype, dev, **vkw)
     call_args = (wl["draft_token_ids"], wl["draft_probs"], wl["bitmask"], wl["temperature"],
                  wl["seed"], wl["top_k"])
 
+    def call(s, **extra):
+        return v(copies[s % len(copies)], *call_args, **kw, **extra)
+
     for s in range(args.warmup):
-        v(copies[s % len(copies)], *call_args)
+        call(s)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
@@ -230,20 +279,20 @@ def main():
     t0 = time.perf_counter()
     ev0.record()
     for s in range(args.steps):
-        v(copies[s % len(copies)], *call_args)
+        call(s)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     step_s = max(wall, gpu_ms / 1e3) / args.steps
-    value = B * k / step_s
+    value = positions / step_s
     print(f"[bench] timed {args.steps} steps: {step_s * 1e6:.1f} us/step", file=sys.stderr, flush=True)
 
     # ---- per-call distribution: HIP events between consecutive calls
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     marks[0].record()
     for s in range(args.steps):
-        v(copies[s % len(copies)], *call_args)
+        call(s)
         marks[s + 1].record()
     torch.cuda.synchronize()
     call_us = sorted(marks[s].elapsed_time(marks[s + 1]) * 1e3 for s in range(args.steps))
@@ -256,7 +305,7 @@ def main():
         b.record()
     torch.cuda.synchronize()
     for s, (a, b) in enumerate(pairs):
-        v(copies[s % len(copies)], *call_args, row_stats_events=(a.cuda_event, b.cuda_event))
+        call(s, row_stats_events=(a.cuda_event, b.cuda_event))
     torch.cuda.synchronize()
     k1_ms = sorted(a.elapsed_time(b) for a, b in pairs)
     k1_avg_s = sum(k1_ms) / len(k1_ms) / 1e3
@@ -264,13 +313,15 @@ def main():
         wl["bitmask"].numel() * 4 if wl["bitmask"] is not None else 0)
     achieved = k1_bytes / k1_avg_s / 1e9
     digest = source_digest()
-    traffic = measured_traffic(digest)
+    # the committed counter summary covers the ngram workload only
+    traffic = measured_traffic(digest) if args.workload == "ngram" and args.copies >= 4 else None
 
     # ---- one debug call for the flag counts
-    vd = sdv.Verifier(B, k, V, lg.dtype, dev, debug=True)
-    r = vd(lg, *call_args)
+    vd = sdv.Verifier(B, k, V, lg.dtype, dev, debug=True, **vkw)
+    r = vd(lg, *call_args, **kw)
     torch.cuda.synchronize()
-    n_res = int((r.out_num_accepted < k).sum().item()) if wl["draft_probs"] is not None else 0
+    kb = (wl["draft_offsets"][1:] - wl["draft_offsets"][:-1]) if ragged else k
+    n_res = int((r.out_num_accepted < kb).sum().item()) if wl["draft_probs"] is not None else 0
     algo = algorithmic_bytes(wl, n_res)
     flags = [int(f) for f in r.flags.cpu().tolist()]
 
@@ -278,7 +329,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_requests or B)
+        cpu = cpu_baseline_ragged(wl) if ragged else cpu_baseline(wl, args.cpu_requests or B)
 
     out = {
         "metric": METRIC,
@@ -293,10 +344,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: B={B} k={k} V={V} "
+        "config": {"workload": f"{args.workload}: B={B} "
+                               f"{f'k_b up to {k}, {positions} drafts' if ragged else f'k={k}'} V={V} "
                                f"{'bf16' if lg.dtype == torch.bfloat16 else 'fp32'} logits, "
                                f"{'one-hot' if wl['draft_probs'] is None else 'dense'} drafts",
-                   "batch": B, "num_draft": k, "vocab": V, "input_copies": len(copies)},
+                   "batch": B, "num_draft": k, "vocab": V, "drafts_per_call": positions,
+                   "input_copies": len(copies)},
         "call_us": {"p10": call_us[len(call_us) // 10], "p50": call_us[len(call_us) // 2],
                     "p90": call_us[(9 * len(call_us)) // 10]},
         "hbm_gbps_whole_call": algo / step_s / 1e9,

@@ -175,3 +175,14 @@ def test_uniform_histogram():
     if not flagged:
         assert np.array_equal(r.accept_histogram.cpu().numpy().astype(np.int64), orc["accept_histogram"])
     assert int(r.accept_histogram.sum().item()) == B
+
+
+def test_ngram_ragged_full():
+    """The ragged ngram workload at full size (B=256, k_b 1..7, V=151936),
+    every request against the oracle (one-hot drafts keep it quick)."""
+    announce("ngram_ragged full")
+    wl = make_workload("ngram_ragged", device=DEV)
+    off = wl["draft_offsets"].cpu().numpy()
+    gpu, orc = run_gpu_ragged(wl, wl["max_draft"]), run_oracle_ragged(wl, wl["max_draft"])
+    assert_parity_ragged(gpu, orc, off, max_flagged=2)
+    assert int(gpu["counters"][0]) == int(off[-1]) and gpu["status"] == 0

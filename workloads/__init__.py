@@ -19,6 +19,9 @@ dataset).  `batch=` shrinks a workload to fewer requests at the same k and V:
               draft positions draw x uniformly from their row's disallowed tokens, the
               rest x ~ q with q = softmax(0.8 l + N(0,1)) restricted to the allowed
               tokens; T = 0.7
+  ngram_ragged B=256, k_b uniform on 1..7 (max 7, mean 4), V=151936: the ngram recipe
+              per request with its own draft count; rows packed without padding
+              (draft_offsets [B+1]); "max_draft" = 7
   long_k      B=512, k=12, V=151936, bf16 ~ N(0, 3^2); q = softmax(0.7 l + N(0, 1.5^2));
               x ~ q (unrestricted); a quarter of the requests greedy, the rest
               T ~ U[0.6, 1.2] with top_k = 50; a random half of the requests carry
@@ -35,9 +38,11 @@ WORKLOADS = {
     "ngram": dict(B=256, k=4, V=151936, dtype=torch.bfloat16),
     "structured": dict(B=128, k=5, V=128256, dtype=torch.bfloat16),
     "long_k": dict(B=512, k=12, V=151936, dtype=torch.bfloat16),
+    "ngram_ragged": dict(B=256, k=7, V=151936, dtype=torch.bfloat16),
 }
 
-_SEED_BASE = {"tiny": 1001, "draft_model": 1002, "ngram": 1003, "structured": 1004, "long_k": 1005}
+_SEED_BASE = {"tiny": 1001, "draft_model": 1002, "ngram": 1003, "structured": 1004, "long_k": 1005,
+              "ngram_ragged": 1006}
 
 
 def pack_bitmask(allowed):
@@ -162,6 +167,28 @@ def make_workload(name, device="cpu", batch=None, seed=None):
             sel = mrows[r0:r0 + step]
             al = _exact_allowed(sel.numel() * kp1, V, n_allowed, gen, dev).reshape(-1, kp1, V)
             mask[sel] = pack_bitmask(al)
+    elif name == "ngram_ragged":
+        ks = torch.randint(1, k + 1, (B,), generator=gen, device=dev)
+        off = torch.zeros(B + 1, dtype=torch.int64, device=dev)
+        off[1:] = torch.cumsum(ks, 0)
+        total = int(off[-1].item())
+        rows = total + B
+        logits = normal((rows, V), 3.0).to(dtype)
+        bidx = torch.repeat_interleave(torch.arange(B, device=dev), ks)
+        pos = torch.arange(total, device=dev) - off[bidx]
+        drow = off[bidx] + bidx + pos                       # the row of each draft
+        amax = torch.argmax(logits[drow].float(), dim=-1)
+        uni = torch.randint(0, V, (total,), generator=gen, device=dev)
+        pick = torch.rand(total, generator=gen, device=dev) < 0.6
+        x = torch.where(pick, amax, uni)
+        T = torch.ones(B, device=dev)
+        return {
+            "name": name, "logits": logits.contiguous(),
+            "draft_token_ids": x.to(torch.int32).contiguous(),
+            "draft_offsets": off.to(torch.int32).contiguous(), "max_draft": k,
+            "draft_probs": None, "bitmask": None, "temperature": T.contiguous(),
+            "top_k": None, "seed": 0,
+        }
     else:
         raise KeyError(name)
 
@@ -194,6 +221,26 @@ def to_numpy(wl, requests=None):
 
 
 def algorithmic_bytes(wl, n_residual_rows=None):
+    if "draft_offsets" in wl:
+        return _algorithmic_bytes_ragged(wl, n_residual_rows)
+    return _algorithmic_bytes_uniform(wl, n_residual_rows)
+
+
+def _algorithmic_bytes_ragged(wl, n_residual_rows=None):
+    logits = wl["logits"]
+    rows, V = logits.shape
+    B = wl["draft_offsets"].shape[0] - 1
+    T = rows - B
+    total = logits.numel() * logits.element_size() + (B + 1) * 4
+    if wl["bitmask"] is not None:
+        total += wl["bitmask"].numel() * 4
+    if wl["draft_probs"] is not None:
+        total += T * 4 + int(n_residual_rows or 0) * V * 4
+    total += T * 4 + B * 4 + rows * 4 + B * 4
+    return total
+
+
+def _algorithmic_bytes_uniform(wl, n_residual_rows=None):
     """Bytes the method has to move for one call: every logit once, every mask
     word once, one draft-probability row per residual draw (dense q, no top-k;
     n_residual_rows = requests that rejected a draft), the q gathers at the
