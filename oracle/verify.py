@@ -51,6 +51,7 @@ from . import philox
 BLOCK = 2048            # tokens per level-1 block of the two-level Gumbel-max
 ACCEPT_FLAG_EPS = 1e-6  # |u - a| below this marks a boundary accept draw
 GUMBEL_FLAG_EPS = 1e-5  # top-2 Gumbel keys closer than this mark a near tie
+TOP_P_FLAG_EPS = 1e-6   # a cumulative mass within this of top_p marks a boundary row
 
 # status bits (a request with any bit set produces -1 outputs)
 ST_DRAFT_ID = 1         # draft id outside [0, V)
@@ -78,12 +79,36 @@ def accept_probability(p, q):
     return min(1.0, p / q)
 
 
-def target_distribution(logits_row, allowed_row, T, top_k):
+def top_p_threshold(logits_row, keep, T, top_p):
+    """The top-p cut of one row: the largest logit value v such that the
+    tokens of `keep` with logit >= v hold at least top_p of the tempered mass
+    of `keep` (pyshine, "Verification": top-p is one of the sampling
+    constraints applied before the accept test).  Tokens are taken from the
+    largest logit down and every token tied with the last one taken stays, so
+    the cut does not depend on the order of equal logits.  Returns (v, flag):
+    flag is 1 when the mass at v or at the next larger value lies within
+    TOP_P_FLAG_EPS of top_p, where another rounding could move the cut."""
+    vals = logits_row[keep].astype(np.float64)
+    s = vals / T
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    distinct = np.unique(vals)[::-1]                     # largest first
+    mass = np.array([w[vals == v].sum() for v in distinct])
+    cum = np.cumsum(mass)
+    idx = int(np.argmax(cum >= top_p)) if np.any(cum >= top_p) else len(distinct) - 1
+    flag = abs(cum[idx] - top_p) < TOP_P_FLAG_EPS or \
+        (idx > 0 and abs(top_p - cum[idx - 1]) < TOP_P_FLAG_EPS)
+    return float(distinct[idx]), int(flag)
+
+
+def target_distribution(logits_row, allowed_row, T, top_k, top_p=0.0, flags=None):
     """p over the vocabulary for one row (T > 0), and its log-normaliser.
 
     Allowed tokens with a finite logit form the support; with top_k > 0 the
-    support is cut to the tokens whose logit is >= the top_k-th largest of them.
-    Returns (p, lse) with lse = log sum exp(l/T) over the support.
+    support is cut to the tokens whose logit is >= the top_k-th largest of them,
+    and with 0 < top_p < 1 then to the tokens above the top-p cut of what is
+    left (top_p_threshold).  Returns (p, lse) with lse = log sum exp(l/T) over
+    the support.  `flags` (a list) receives the top-p boundary flag.
     """
     l = logits_row
     keep = allowed_row & np.isfinite(l)
@@ -91,6 +116,11 @@ def target_distribution(logits_row, allowed_row, T, top_k):
         vals = np.sort(l[keep])[::-1]
         if vals.size > top_k:
             keep = keep & (l >= vals[top_k - 1])
+    if 0.0 < top_p < 1.0 and np.any(keep):
+        v, flag = top_p_threshold(l, keep, T, top_p)
+        keep = keep & (l >= v)
+        if flags is not None:
+            flags.append(flag)
     s = l[keep] / T
     m = s.max()
     e = np.zeros(l.shape[0])
@@ -150,7 +180,7 @@ def gumbel_two_level(r, seed, b, a, block=BLOCK):
     return y, _near_tie(key1) + _near_tie(key2)
 
 
-def _verify_request(l, x, q, allowed, T, top_k, seed, b, block):
+def _verify_request(l, x, q, allowed, T, top_k, seed, b, block, top_p=0.0):
     """One request.  l: [k+1, V] float64; x: [k]; q: [k, V] or None;
     allowed: [k+1, V] bool.  Returns a dict of per-request results."""
     k, V = x.shape[0], l.shape[1]
@@ -163,6 +193,7 @@ def _verify_request(l, x, q, allowed, T, top_k, seed, b, block):
         "accept_prob": np.full(k, np.nan),
         "flag_accept": 0,
         "flag_gumbel": 0,
+        "flag_topp": 0,
     }
     st = 0
     if not (math.isfinite(T) and T >= 0.0):
@@ -197,8 +228,10 @@ def _verify_request(l, x, q, allowed, T, top_k, seed, b, block):
     else:
         p = np.zeros((k + 1, V))
         lse = np.zeros(k + 1)
+        tp_flags = []
         for i in range(k + 1):
-            p[i], lse[i] = target_distribution(l[i], allowed[i], T, top_k)
+            p[i], lse[i] = target_distribution(l[i], allowed[i], T, top_k, top_p, tp_flags)
+        res["flag_topp"] = int(sum(tp_flags))
         res["row_lse"] = lse
         acc = np.array([accept_probability(p[i, x[i]], 1.0 if q is None else q[i, x[i]])
                         for i in range(k)])
@@ -229,7 +262,7 @@ def _verify_request(l, x, q, allowed, T, top_k, seed, b, block):
 
 
 def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperature=None,
-              seed=0, top_k=None, block=BLOCK, request_ids=None):
+              seed=0, top_k=None, block=BLOCK, request_ids=None, top_p=None):
     """Verify a batch of drafted requests.
 
     logits:          [B, k+1, V] float (bf16 values given exactly as float32/64)
@@ -239,6 +272,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
     temperature:     [B] float; 0 selects the greedy rule
     seed:            64-bit Philox key
     top_k:           [B] integer or None; values <= 0 switch top-k off
+    top_p:           [B] float or None; values outside (0, 1) switch top-p off
     request_ids:     optional [B] global request index of each batch entry, used
                      as b in the Philox counters (for checking a sample of a
                      larger batch one request at a time); default 0 .. B-1
@@ -254,6 +288,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
     T_all = np.asarray(temperature, dtype=np.float64).reshape(B)
     tk_all = np.zeros(B, dtype=np.int64) if top_k is None else \
         np.asarray(top_k, dtype=np.int64).reshape(B)
+    tp_all = np.zeros(B) if top_p is None else np.asarray(top_p, dtype=np.float64).reshape(B)
     gid = list(range(B)) if request_ids is None else [int(r) for r in request_ids]
 
     out = {
@@ -264,6 +299,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
         "accept_prob": np.full((B, k), np.nan),
         "flag_accept": np.zeros(B, dtype=np.int64),
         "flag_gumbel": np.zeros(B, dtype=np.int64),
+        "flag_topp": np.zeros(B, dtype=np.int64),
     }
     R = I = A = 0
     status = 0
@@ -275,7 +311,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
             allowed = unpack_bitmask(np.asarray(bitmask[b]), V)
         q = None if draft_probs is None else np.asarray(draft_probs[b], dtype=np.float64)
         r = _verify_request(l, x_all[b], q, allowed, float(T_all[b]), int(tk_all[b]),
-                            seed, gid[b], block)
+                            seed, gid[b], block, float(tp_all[b]))
         out["out_tokens"][b] = r["tokens"]
         out["num_accepted"][b] = r["num_accepted"]
         out["request_status"][b] = r["status"]
@@ -283,6 +319,7 @@ def sd_verify(logits, draft_token_ids, draft_probs=None, bitmask=None, temperatu
         out["accept_prob"][b] = r["accept_prob"]
         out["flag_accept"][b] = r["flag_accept"]
         out["flag_gumbel"][b] = r["flag_gumbel"]
+        out["flag_topp"][b] = r["flag_topp"]
         status |= r["status"]
         R += r["R"]
         I += r["I"]
@@ -306,7 +343,7 @@ def accept_histogram(num_accepted, request_status, kmax):
 
 def sd_verify_ragged(logits, draft_token_ids, draft_offsets, draft_probs=None, bitmask=None,
                      temperature=None, seed=0, top_k=None, max_draft=None, total_drafts=None,
-                     block=BLOCK):
+                     block=BLOCK, top_p=None):
     """Requests with their own draft lengths (a drafter that proposes a
     variable number of tokens per request, infra-guide 5.2, dynamic draft
     length).  Request b has k_b = off[b+1] - off[b] drafts; its rows are
@@ -343,6 +380,7 @@ def sd_verify_ragged(logits, draft_token_ids, draft_offsets, draft_probs=None, b
     T_all = np.asarray(temperature, dtype=np.float64).reshape(B)
     tk_all = np.zeros(B, dtype=np.int64) if top_k is None else \
         np.asarray(top_k, dtype=np.int64).reshape(B)
+    tp_all = np.zeros(B) if top_p is None else np.asarray(top_p, dtype=np.float64).reshape(B)
     kb = off[1:] - off[:-1]
     kmax = int(max(kb.max(), 0)) if max_draft is None and B > 0 else int(max_draft or 0)
     out = {
@@ -353,6 +391,7 @@ def sd_verify_ragged(logits, draft_token_ids, draft_offsets, draft_probs=None, b
         "accept_prob": np.full(total, np.nan),
         "flag_accept": np.zeros(B, dtype=np.int64),
         "flag_gumbel": np.zeros(B, dtype=np.int64),
+        "flag_topp": np.zeros(B, dtype=np.int64),
     }
     R = I = A = 0
     status = 0
@@ -373,7 +412,7 @@ def sd_verify_ragged(logits, draft_token_ids, draft_offsets, draft_probs=None, b
             allowed = unpack_bitmask(np.asarray(bitmask[r0:r0 + k + 1]), V)
         q = None if draft_probs is None else np.asarray(draft_probs[o0:o1], dtype=np.float64)
         r = _verify_request(l, x_all[o0:o1], q, allowed, float(T_all[b]), int(tk_all[b]),
-                            seed, b, block)
+                            seed, b, block, float(tp_all[b]))
         out["out_tokens"][r0:r0 + k + 1] = r["tokens"]
         out["num_accepted"][b] = r["num_accepted"]
         out["request_status"][b] = r["status"]
@@ -381,6 +420,7 @@ def sd_verify_ragged(logits, draft_token_ids, draft_offsets, draft_probs=None, b
         out["accept_prob"][o0:o1] = r["accept_prob"]
         out["flag_accept"][b] = r["flag_accept"]
         out["flag_gumbel"][b] = r["flag_gumbel"]
+        out["flag_topp"][b] = r["flag_topp"]
         status |= r["status"]
         R += r["R"]
         I += r["I"]

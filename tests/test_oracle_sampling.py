@@ -11,6 +11,7 @@
 * two-level Gumbel-max: chi-square against r / sum(r) for several block sizes
 * one-hot drafts: the q = None run equals an explicit one-hot q run bit for bit
 """
+import math
 import numpy as np
 import pytest
 from scipy import special, stats
@@ -127,6 +128,88 @@ def test_top_k_support_brute_force():
         assert brute.sum() >= min(top_k, allowed.sum())
 
 
+def _top_p_brute(l, allowed, T, top_p):
+    """Keep set of top-p by hand: walk tokens from the largest logit down,
+    adding probabilities one token at a time, stop once the running mass
+    reaches top_p, then keep every token tied with the last one added."""
+    idx = [j for j in range(len(l)) if allowed[j] and np.isfinite(l[j])]
+    w = {j: math.exp(l[j] / T) for j in idx}
+    Z = sum(w.values())
+    order = sorted(idx, key=lambda j: -l[j])
+    run, last = 0.0, None
+    for j in order:
+        run += w[j] / Z
+        last = l[j]
+        if run >= top_p:
+            break
+    return np.array([j in w and l[j] >= last for j in range(len(l))])
+
+
+def test_top_p_support_brute_force():
+    rng = np.random.default_rng(41)
+    for trial in range(400):
+        V = int(rng.integers(1, 40))
+        l = rng.normal(scale=2.0, size=V)
+        if trial % 3 == 0:
+            l = np.round(l)                          # ties at the cut
+        allowed = rng.random(V) < 0.8
+        allowed[rng.integers(0, V)] = True
+        T = float(rng.uniform(0.3, 2.0))
+        top_p = float(rng.uniform(0.05, 0.99))
+        p, _ = ov.target_distribution(l, allowed, T, 0, top_p)
+        brute = _top_p_brute(l, allowed, T, top_p)
+        flags = []
+        ov.target_distribution(l, allowed, T, 0, top_p, flags)
+        if not flags[0]:                             # away from the boundary: exact
+            assert np.array_equal(p > 0, brute), (trial, top_p)
+        kept = p > 0
+        assert kept.any()
+        # the kept mass reaches top_p and dropping its smallest value would not
+        w = np.where(allowed, np.exp(l / T), 0.0)
+        w /= w.sum()
+        assert w[kept].sum() >= top_p - 1e-12
+        vmin = l[kept].min()
+        assert w[kept & (l > vmin)].sum() < top_p + 1e-12
+
+
+def test_top_p_special_cases():
+    l = np.array([3.0, 1.0, 1.0, -2.0, 0.5])
+    allowed = np.ones(5, bool)
+    # a tiny top_p keeps only the largest logit (and its ties)
+    p, _ = ov.target_distribution(l, allowed, 1.0, 0, 1e-9)
+    assert list(p > 0) == [True, False, False, False, False]
+    # a cut that lands on tied tokens keeps both
+    w = np.exp(l) / np.exp(l).sum()
+    p, _ = ov.target_distribution(l, allowed, 1.0, 0, w[0] + 0.5 * w[1])
+    assert list(p > 0) == [True, True, True, False, False]
+    # top_p exactly at a cumulative mass is a boundary row, and flagged
+    flags = []
+    ov.target_distribution(l, allowed, 1.0, 0, float(w[0]), flags)
+    assert flags == [1]
+    # outside (0, 1) it is off
+    for tp in (0.0, 1.0, -0.5, 2.0):
+        p, _ = ov.target_distribution(l, allowed, 1.0, 0, tp)
+        assert np.all(p > 0)
+
+
+def test_top_p_after_top_k():
+    """top-k first, then top-p over what top-k kept, renormalised."""
+    rng = np.random.default_rng(43)
+    for trial in range(200):
+        V = int(rng.integers(2, 30))
+        l = rng.normal(size=V)
+        allowed = np.ones(V, bool)
+        top_k = int(rng.integers(1, V + 1))
+        top_p = float(rng.uniform(0.1, 0.95))
+        p, _ = ov.target_distribution(l, allowed, 1.0, top_k, top_p)
+        kept_k = np.array([np.sum(l > l[j]) < top_k for j in range(V)])
+        brute = _top_p_brute(np.where(kept_k, l, -np.inf), kept_k, 1.0, top_p)
+        flags = []
+        ov.target_distribution(l, allowed, 1.0, top_k, top_p, flags)
+        if not flags[0]:
+            assert np.array_equal(p > 0, brute), trial
+
+
 # ------------------------------------------------- exact law of one position
 
 def _law_of_emitted(p, q, one_hot_x=None):
@@ -153,7 +236,7 @@ def _law_of_emitted(p, q, one_hot_x=None):
     return law
 
 
-@pytest.mark.parametrize("mode", ["dense", "dense_masked", "dense_topk", "one_hot"])
+@pytest.mark.parametrize("mode", ["dense", "dense_masked", "dense_topk", "dense_topp", "one_hot"])
 def test_exact_enumeration_v8(mode):
     rng = np.random.default_rng(5)
     V, k = 8, 2
@@ -166,8 +249,9 @@ def test_exact_enumeration_v8(mode):
             allowed[:, 0] = True
         if mode == "dense_topk":
             top_k = 3
+        top_p = 0.7 if mode == "dense_topp" else 0.0
         T = float(rng.uniform(0.5, 2.0))
-        p = np.array([ov.target_distribution(l[i], allowed[i], T, top_k)[0]
+        p = np.array([ov.target_distribution(l[i], allowed[i], T, top_k, top_p)[0]
                       for i in range(k + 1)])
         q = rng.dirichlet(np.ones(V) * 0.7, size=k)
         for i in range(k):      # each drafted position, given the earlier ones accepted
@@ -215,9 +299,9 @@ def _chi2_ok(counts, probs, alpha=1e-3):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked", "top_k"])
+@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked", "top_k", "top_p"])
 def test_chi_square_emitted_tokens(mode):
-    rng = np.random.default_rng(10 + ["dense", "one_hot", "masked", "top_k"].index(mode))
+    rng = np.random.default_rng(10 + ["dense", "one_hot", "masked", "top_k", "top_p"].index(mode))
     B, k, V = 12000, 2, 8
     l1 = rng.normal(scale=1.0, size=(k + 1, V))
     allowed1 = np.ones((k + 1, V), bool)
@@ -227,15 +311,18 @@ def test_chi_square_emitted_tokens(mode):
         allowed1[:, :2] = True
     if mode == "top_k":
         top_k = 4
+    top_p = 0.6 if mode == "top_p" else 0.0
     T = 0.9
-    p = np.array([ov.target_distribution(l1[i], allowed1[i], T, top_k)[0] for i in range(k + 1)])
+    p = np.array([ov.target_distribution(l1[i], allowed1[i], T, top_k, top_p)[0]
+                  for i in range(k + 1)])
     q1 = rng.dirichlet(np.ones(V), size=k)
     logits = np.broadcast_to(l1, (B, k + 1, V))
     x = np.stack([rng.choice(V, size=B, p=q1[i]) for i in range(k)], axis=1)
     q = None if mode == "one_hot" else np.broadcast_to(q1, (B, k, V))
     mask = None if mode != "masked" else np.broadcast_to(_pack(allowed1), (B, k + 1, 1))
     tk = None if mode != "top_k" else np.full(B, top_k)
-    out = sd_verify(logits, x, q, mask, np.full(B, T), seed=99, top_k=tk)
+    tp = None if mode != "top_p" else np.full(B, top_p)
+    out = sd_verify(logits, x, q, mask, np.full(B, T), seed=99, top_k=tk, top_p=tp)
     tok, na = out["out_tokens"], out["num_accepted"]
     for i in range(k + 1):
         sel = na >= i
