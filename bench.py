@@ -361,7 +361,7 @@ def main():
                      "p10_us": k1_ms[len(k1_ms) // 10] * 1e3, "p90_us": k1_ms[(9 * len(k1_ms)) // 10] * 1e3,
                      "bytes_per_launch": k1_bytes, "source_digest": digest},
         "cpu_baseline": cpu,
-        "flags": {"accept_boundary": flags[0], "gumbel_near_tie": flags[1]},
+        "flags": {"accept_boundary": flags[0], "gumbel_near_tie": flags[1], "top_p_boundary": flags[2]},
         "gpu_ms_timed_region": gpu_ms,
         "wall_s_timed_region": wall,
     }

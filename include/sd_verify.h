@@ -88,9 +88,11 @@ typedef struct {
      *                             (greedy rows: the largest allowed logit)
      *   dbg_accept_prob [B, k]    min(1, p/q) (greedy: 1 if x == argmax else 0)
      *   dbg_request_flags [B]     per request: boundary accept draws
-     *                             (|u - a| < 1e-6) in the low 16 bits, Gumbel
-     *                             near ties (top-2 keys closer than 1e-5) above
-     *   dbg_flags [2]             totals of the two flag kinds over the call */
+     *                             (|u - a| < 1e-6) in bits 0..11, Gumbel near
+     *                             ties (top-2 keys closer than 1e-5) in bits
+     *                             12..23, top-p boundary rows (the cut within
+     *                             1e-6 of top_p in mass) in bits 24..31
+     *   dbg_flags [3]             totals of the three flag kinds over the call */
     double *dbg_row_lse;
     double *dbg_accept_prob;
     uint32_t *dbg_request_flags;
@@ -123,6 +125,12 @@ typedef struct {
      * by every call.  Accepted drafts per position i follow as the sum of
      * the buckets above i. */
     uint32_t *accept_histogram;
+    /* device [B] or NULL: top-p per request, applied after top-k; values
+     * outside (0, 1) switch it off.  A sampling request keeps, at every row,
+     * the allowed tokens whose logit is >= the largest value v such that the
+     * tokens >= v hold top_p of the tempered mass left by top-k (ties at v
+     * kept).  Greedy ignores it. */
+    const float *top_p;
 } sd_params;
 
 /* Bytes of device workspace sd_verify needs for these sizes (0 for B = 0),

@@ -51,7 +51,7 @@ from . import philox
 BLOCK = 2048            # tokens per level-1 block of the two-level Gumbel-max
 ACCEPT_FLAG_EPS = 1e-6  # |u - a| below this marks a boundary accept draw
 GUMBEL_FLAG_EPS = 1e-5  # top-2 Gumbel keys closer than this mark a near tie
-TOP_P_FLAG_EPS = 1e-6   # a cumulative mass within this of top_p marks a boundary row
+TOP_P_FLAG_EPS = 1e-9   # a cumulative mass within this of top_p marks a boundary row
 
 # status bits (a request with any bit set produces -1 outputs)
 ST_DRAFT_ID = 1         # draft id outside [0, V)

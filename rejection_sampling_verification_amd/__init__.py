@@ -55,6 +55,7 @@ class SdParams(ctypes.Structure):
         ("draft_offsets", ctypes.c_void_p),
         ("total_drafts", ctypes.c_int64),
         ("accept_histogram", ctypes.c_void_p),
+        ("top_p", ctypes.c_void_p),
     ]
 
 
@@ -135,7 +136,7 @@ class VerifyResult(NamedTuple):
     row_lse: Optional[torch.Tensor] = None         # [B, k+1] float64
     accept_prob: Optional[torch.Tensor] = None     # [B, k] float64
     request_flags: Optional[torch.Tensor] = None   # [B] int32 (uint32 bits)
-    flags: Optional[torch.Tensor] = None           # [2] int32 (uint32 counts)
+    flags: Optional[torch.Tensor] = None           # [3] int32 (uint32 counts)
     accept_histogram: Optional[torch.Tensor] = None  # [k+1] int32 (uint32 counts)
 
 
@@ -204,7 +205,7 @@ class Verifier:
             self.row_lse = torch.empty(lse_shape, dtype=torch.float64, device=dev)
             self.accept_prob = torch.empty(acc_shape, dtype=torch.float64, device=dev)
             self.request_flags = torch.empty(self.B, dtype=torch.int32, device=dev)
-            self.flags = torch.empty(2, dtype=torch.int32, device=dev)
+            self.flags = torch.empty(3, dtype=torch.int32, device=dev)
             self.params.dbg_row_lse = self.row_lse.data_ptr()
             self.params.dbg_accept_prob = self.accept_prob.data_ptr()
             self.params.dbg_request_flags = self.request_flags.data_ptr()
@@ -212,7 +213,7 @@ class Verifier:
 
     def __call__(self, target_logits, draft_token_ids, draft_probs=None, bitmask=None,
                  temperature=None, seed=0, top_k=None, stream=None, row_stats_events=None,
-                 draft_offsets=None):
+                 draft_offsets=None, top_p=None):
         B, k, V, dev = self.B, self.k, self.V, self.device
         W = (V + 31) // 32
         if self.ragged:
@@ -238,6 +239,8 @@ class Verifier:
         _check(temperature, "temperature", torch.float32, (B,), dev)
         _check(top_k, "top_k", torch.int32, (B,), dev)
         self.params.top_k = None if top_k is None else top_k.data_ptr()
+        _check(top_p, "top_p", torch.float32, (B,), dev)
+        self.params.top_p = None if top_p is None else top_p.data_ptr()
         if row_stats_events is not None:
             self.params.row_stats_event_begin, self.params.row_stats_event_end = row_stats_events
         else:
@@ -261,23 +264,24 @@ class Verifier:
 
 
 def sd_verify(target_logits, draft_token_ids, draft_probs=None, bitmask=None, temperature=None,
-              seed=0, top_k=None, debug=False, stream=None):
+              seed=0, top_k=None, debug=False, stream=None, top_p=None):
     """Verify one batch; returns fresh output tensors (see VerifyResult).
 
     target_logits [B, k+1, V] bf16/fp32, draft_token_ids [B, k] int32,
     draft_probs [B, k, V] fp32 or None (one-hot drafts), bitmask
     [B, k+1, ceil(V/32)] int32 or None, temperature [B] fp32 (0 = greedy),
-    seed (64-bit Philox key), top_k [B] int32 or None.
+    seed (64-bit Philox key), top_k [B] int32 or None, top_p [B] fp32 or None.
     """
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, k+1, V]")
     B, kp1, V = target_logits.shape
     v = Verifier(B, kp1 - 1, V, target_logits.dtype, target_logits.device, debug=debug)
-    return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream)
+    return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream,
+             top_p=top_p)
 
 
 def sd_verify_ragged(target_logits, draft_token_ids, draft_offsets, draft_probs=None,
-                     bitmask=None, temperature=None, seed=0, top_k=None, max_draft=None,
+                     bitmask=None, temperature=None, seed=0, top_k=None, top_p=None, max_draft=None,
                      debug=False, histogram=False, stream=None):
     """Verify requests with their own draft counts; returns fresh outputs.
 
@@ -294,7 +298,7 @@ def sd_verify_ragged(target_logits, draft_token_ids, draft_offsets, draft_probs=
     v = Verifier(B, SD_MAX_DRAFT if max_draft is None else max_draft, V, target_logits.dtype,
                  target_logits.device, debug=debug, histogram=histogram, total_drafts=rows - B)
     return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream,
-             draft_offsets=draft_offsets)
+             draft_offsets=draft_offsets, top_p=top_p)
 
 
 def rates_from_counters(counters, steps):

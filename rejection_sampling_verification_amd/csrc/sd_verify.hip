@@ -351,7 +351,7 @@ __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
     if (blockIdx.x != 0) return;
     for (int w = threadIdx.x; w < a.ntally; w += blockDim.x) a.tally[w * kTallyStride] = 0ull;
     if (threadIdx.x == 0 && a.status) *a.status = 0u;
-    if (threadIdx.x < 2 && a.dbg_flags) a.dbg_flags[threadIdx.x] = 0u;
+    if (threadIdx.x < 3 && a.dbg_flags) a.dbg_flags[threadIdx.x] = 0u;
 }
 
 // Which rows a chunked wave works on, and their parameters (wave-uniform).
@@ -716,6 +716,8 @@ struct TopkArgs {
     const float *temperature;
     const int32_t *top_k;
     float *tau;  // [rows]
+    uint32_t *tau_flag;      // [rows] 1: the top-p cut of the row is a boundary case
+    const float *top_p;      // [B] or nullptr
     const int32_t *off;      // ragged: draft offsets, or nullptr
     const int32_t *row_req;  // ragged: request of each row
     const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
@@ -730,12 +732,17 @@ constexpr int kTopkUnroll = 4;
 // anchor: for top-k of a few percent of the vocabulary or less it holds the
 // K-th largest, and it draws few of the row's elements into the histogram.
 constexpr uint32_t kTopkFirstSpan = 256;
+constexpr double kTopPFlagEps = 1e-9;  // boundary threshold of a top-p cut, relative to the mass
 
 struct TopkShared {
     uint32_t hist[kTopkWindow];
     uint32_t part[kTopkThreads];  // per-thread sums of 4 bins, scanned in place
     uint32_t red[kTopkWaves];
-    uint32_t found_digit, found_rank;
+    uint32_t found_digit, found_rank, lowest;
+    double mass[kTopkWindow];     // top-p: kept mass per bin
+    double dpart[kTopkThreads];
+    double red_d[kTopkWaves];
+    double found_mass;
 };
 
 // The P values of one 16-byte group of the row at token `tok` with excluded
@@ -837,35 +844,32 @@ __device__ bool topk_pick(TopkShared &sh, int nbins, uint32_t lo, uint32_t need,
     return digit != 0xffffffffu;
 }
 
+// One row of the threshold kernel: where its logits and mask lie.
 template <typename ET, bool ALIGNED, bool MASKED>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+struct TopkRow {
+    const ET *rowp;
+    const uint8_t *mrow;
+    __amdgpu_buffer_rsrc_t rs, rm;
+    int V;
+    __device__ __forceinline__ void load(int64_t tok, float *v) const {
+        topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, V, tok, v);
+    }
+};
+
+// The K-th largest allowed finite logit of the row, or -inf when the row
+// holds at most K of them (see the comment above TopkArgs).
+template <typename ET, bool ALIGNED, bool MASKED>
+__device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, int K) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int64_t kStep = int64_t(kTopkThreads) * P;
-    __shared__ TopkShared sh;
-    const int row = blockIdx.x, tid = threadIdx.x;
-    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call
-    int b, i, kb;
-    int64_t d0;
-    row_owner(a.off, a.row_req, row, a.kp1, b, i, kb, d0);
-    const float T = uniform_load(a.temperature + b);
-    const int K = uniform_load(a.top_k + b);
-    if (!(T > 0.0f && T <= FLT_MAX) || K <= 0) {
-        if (tid == 0) a.tau[row] = -INFINITY;
-        return;
-    }
-    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;
-    const uint8_t *mrow =
-        MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
-    const int64_t V = a.V;
-    const __amdgpu_buffer_rsrc_t rs = buffer_of(rowp, uint32_t(a.V) * sizeof(ET));
-    const __amdgpu_buffer_rsrc_t rm = buffer_of(MASKED ? static_cast<const void *>(mrow) : static_cast<const void *>(rowp),
-                                                MASKED ? uint32_t(a.W) * 4u : 0u);
+    const int tid = threadIdx.x;
+    const int64_t V = r.V;
 
     // anchor: the largest top-half code among the first 16 KB of the row
     uint32_t anchor = 0;
     for (int64_t tok = int64_t(tid) * P; tok < V && tok < 4 * kStep; tok += kStep) {
         float v[P];
-        topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, a.V, tok, v);
+        r.load(tok, v);
 #pragma unroll
         for (int e = 0; e < P; ++e)
             if (v[e] == v[e]) anchor = max(anchor, ordered_code(v[e]) >> 16);
@@ -874,7 +878,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
     uint32_t hi = min(anchor + 128u, 0xffffu);
     uint32_t span = kTopkFirstSpan;  // the first window is narrow: fewer LDS atomics
-    uint32_t need = static_cast<uint32_t>(K);
+    const uint32_t need = static_cast<uint32_t>(K);
     uint32_t digit = 0, rank = 0;
     bool first = true, found = false;
     // The window only ever moves one way (up while the K-th largest lies above
@@ -889,8 +893,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
             float v[kTopkUnroll][P];
 #pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u)
-                topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, a.V, tok0 + u * kStep, v[u]);
+            for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u)
 #pragma unroll
@@ -905,10 +908,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         above = block_sum_u<kTopkWaves>(above, sh.red);
         if (first) {
             support = block_sum_u<kTopkWaves>(support, sh.red);
-            if (support <= static_cast<uint32_t>(K)) {  // every supported token stays
-                if (tid == 0) a.tau[row] = -INFINITY;
-                return;
-            }
+            if (support <= need) return -INFINITY;  // every supported token stays
             first = false;
         }
         if (above >= need) {  // the K-th largest lies above the window
@@ -924,10 +924,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         hi = lo - 1u;         // the K-th largest lies below the window
         span = kTopkWindow;
     }
-    if (!found) {
-        if (tid == 0) a.tau[row] = -INFINITY;
-        return;
-    }
+    if (!found) return -INFINITY;
 
     uint32_t code;
     if (sizeof(ET) == 2) {
@@ -941,7 +938,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             lds_barrier();
             for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
                 float v[P];
-                topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, a.V, tok, v);
+                r.load(tok, v);
 #pragma unroll
                 for (int e = 0; e < P; ++e) {
                     if (v[e] != v[e]) continue;
@@ -950,14 +947,230 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
                 }
             }
             lds_barrier();
-            uint32_t byte = 0, r = 0;
-            topk_pick(sh, 256, 0u, want, byte, r);  // holds `want` elements by construction
+            uint32_t byte = 0, rk = 0;
+            topk_pick(sh, 256, 0u, want, byte, rk);  // holds `want` elements by construction
             prefix = (prefix << 8) | byte;
-            want = r;
+            want = rk;
         }
         code = prefix;
     }
-    if (tid == 0) a.tau[row] = float_of_code(code);
+    return float_of_code(code);
+}
+
+// Suffix sums of the per-bin masses (bin i = digit lo + i, nbins of them):
+// finds the bin where the mass counted from the top first reaches `target`.
+// Returns false when the histogram holds less; `before` receives the mass
+// above the found bin.  All threads call it.
+__device__ bool topp_pick(TopkShared &sh, int nbins, uint32_t lo, double target, uint32_t &digit,
+                          double &before, bool clamp) {
+    const int tid = threadIdx.x;
+    const int per = nbins / kTopkThreads;  // 4 or 1
+    double own = 0.0;
+    for (int i = 0; i < per; ++i) own += sh.mass[tid * per + i];
+    sh.dpart[tid] = own;
+    if (tid == 0) sh.lowest = 0xffffffffu;
+    for (int d = 1; d < kTopkThreads; d <<= 1) {
+        lds_barrier();
+        const double add = (tid + d < kTopkThreads) ? sh.dpart[tid + d] : 0.0;
+        lds_barrier();
+        sh.dpart[tid] += add;
+    }
+    lds_barrier();
+    const double incl = sh.dpart[tid];
+    if (tid == 0) sh.found_digit = 0xffffffffu;
+    for (int i = 0; i < per; ++i)
+        if (sh.mass[tid * per + i] > 0.0) atomicMin(&sh.lowest, uint32_t(tid * per + i));
+    lds_barrier();
+    if (incl >= target && incl - own < target) {
+        double acc = incl - own;
+        for (int i = per - 1; i >= 0; --i) {
+            const double m = sh.mass[tid * per + i];
+            if (acc + m >= target) {
+                sh.found_digit = lo + uint32_t(tid * per + i);
+                sh.found_mass = acc;
+                break;
+            }
+            acc += m;
+        }
+    }
+    lds_barrier();
+    // A refinement pass sums the bin it refines in another order: a target
+    // at the bin's very bottom may then sit a rounding error beyond its
+    // sub-bins, and the lowest non-empty sub-bin is the cut.
+    if (clamp && sh.found_digit == 0xffffffffu && sh.lowest != 0xffffffffu) {
+        digit = lo + sh.lowest;
+        before = sh.dpart[0] - sh.mass[sh.lowest];
+        lds_barrier();
+        return true;
+    }
+    digit = sh.found_digit;
+    before = sh.found_mass;
+    lds_barrier();  // the next histogram pass may clear the shared fields
+    return digit != 0xffffffffu;
+}
+
+// The top-p cut of the row over the tokens with l >= tau_k: the largest
+// logit value v whose tokens >= v hold top_p of the tempered mass left by
+// top-k (pyshine "vLLM, part 2", "Verification": top-p among the sampling
+// constraints applied before the accept test; ties at v stay).  Masses are
+// 2^((l - M) log2(e) / T) with M the row's largest kept logit, in fp64 from
+// the argument on (a cut deep in a long tail steps by masses far below fp32
+// rounding).  *flag is set when the mass at the cut, or just above it, lies
+// within the boundary threshold of top_p.
+template <typename ET, bool ALIGNED, bool MASKED>
+__device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, float tau_k,
+                              float top_p, float T, uint32_t *flag) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int64_t kStep = int64_t(kTopkThreads) * P;
+    const int tid = threadIdx.x;
+    const int64_t V = r.V;
+    // the largest kept logit
+    uint32_t mcode = 0;
+    for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
+        float v[kTopkUnroll][P];
+#pragma unroll
+        for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
+#pragma unroll
+        for (int u = 0; u < kTopkUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if (v[u][e] == v[u][e] && !(v[u][e] < tau_k)) mcode = max(mcode, ordered_code(v[u][e]));
+    }
+    mcode = block_max_u<kTopkWaves>(mcode, sh.red);
+    *flag = 0u;
+    if (mcode == 0u) return tau_k;  // nothing kept: the row is reported empty
+    const float M = float_of_code(mcode);
+    const double cd = kLog2e / static_cast<double>(T);
+    const double mcd = static_cast<double>(M) * cd;
+
+    const uint32_t top = mcode >> 16;
+    uint32_t hi = top, span = kTopkFirstSpan;
+    double total = 0.0, target = 0.0;
+    uint32_t digit = 0;
+    double before = 0.0, above_mass = 0.0;
+    uint32_t lo_found = 0;
+    bool found = false;
+    // The first pass sums the whole kept mass; each further pass moves the
+    // window down, so at most 65536 / kTopkWindow + 1 passes run.
+    for (int pass = 0; pass < 0x10000 / kTopkWindow + 2; ++pass) {
+        const uint32_t lo = hi >= span - 1 ? hi - (span - 1) : 0u;
+        for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.mass[i] = 0.0;
+        lds_barrier();
+        double below = 0.0, in_window = 0.0;
+        for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
+            float v[kTopkUnroll][P];
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < P; ++e) {
+                    const float x = v[u][e];
+                    if (x != x || x < tau_k) continue;
+                    const uint32_t d = ordered_code(x) >> 16;
+                    if (d > hi) continue;  // counted in an earlier pass
+                    const double w = exp2(fma(static_cast<double>(x), cd, -mcd));
+                    if (d >= lo) {
+                        atomicAdd(&sh.mass[d - lo], w);
+                        in_window += w;
+                    } else {
+                        below += w;
+                    }
+                }
+        }
+        below = block_sum_d<kTopkWaves>(below, sh.red_d);
+        in_window = block_sum_d<kTopkWaves>(in_window, sh.red_d);
+        if (pass == 0) {
+            total = below + in_window;
+            target = static_cast<double>(top_p) * total;
+        }
+        if (topp_pick(sh, kTopkWindow, lo, target - above_mass, digit, before, false)) {
+            before += above_mass;
+            lo_found = lo;
+            found = true;
+            break;
+        }
+        if (lo == 0u) break;  // cannot happen: the window sums reach the total
+        above_mass += in_window;
+        hi = lo - 1u;
+        span = kTopkWindow;
+    }
+    if (!found) return tau_k;
+
+    uint32_t code;
+    double at_cut, just_above;
+    if (sizeof(ET) == 2) {
+        code = (digit << 16) | ((digit & 0x8000u) ? 0u : 0xffffu);
+        at_cut = before + sh.mass[digit - lo_found];  // a bf16 bin holds one value
+        just_above = before;
+    } else {
+        // two byte passes over the elements sharing the selected top half
+        uint32_t prefix = digit;
+        double above_bin = before;
+        for (int shift = 8; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += kTopkThreads) sh.mass[i] = 0.0;
+            lds_barrier();
+            for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
+                float v[P];
+                r.load(tok, v);
+#pragma unroll
+                for (int e = 0; e < P; ++e) {
+                    const float x = v[e];
+                    if (x != x || x < tau_k) continue;
+                    const uint32_t cc = ordered_code(x);
+                    if ((cc >> (shift + 8)) == prefix)
+                        atomicAdd(&sh.mass[(cc >> shift) & 0xffu], exp2(fma(static_cast<double>(x), cd, -mcd)));
+                }
+            }
+            lds_barrier();
+            uint32_t byte = 0;
+            double b2 = 0.0;
+            topp_pick(sh, 256, 0u, target - above_bin, byte, b2, true);
+            above_bin += b2;
+            if (shift == 0) at_cut = above_bin + sh.mass[byte];
+            prefix = (prefix << 8) | byte;
+        }
+        code = prefix;
+        just_above = above_bin;
+    }
+    const double eps = kTopPFlagEps * total;
+    *flag = (fabs(at_cut - target) < eps || fabs(target - just_above) < eps) ? 1u : 0u;
+    return float_of_code(code);
+}
+
+template <typename ET, bool ALIGNED, bool MASKED>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+    __shared__ TopkShared sh;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call
+    int b, i, kb;
+    int64_t d0;
+    row_owner(a.off, a.row_req, row, a.kp1, b, i, kb, d0);
+    const float T = uniform_load(a.temperature + b);
+    const int K = a.top_k ? uniform_load(a.top_k + b) : 0;
+    const float Pp = a.top_p ? uniform_load(a.top_p + b) : 0.0f;
+    const bool use_p = Pp > 0.0f && Pp < 1.0f;
+    if (!(T > 0.0f && T <= FLT_MAX) || (K <= 0 && !use_p)) {
+        if (tid == 0) {
+            a.tau[row] = -INFINITY;
+            a.tau_flag[row] = 0u;
+        }
+        return;
+    }
+    TopkRow<ET, ALIGNED, MASKED> r;
+    r.rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;
+    r.mrow = MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
+    r.rs = buffer_of(r.rowp, uint32_t(a.V) * sizeof(ET));
+    r.rm = buffer_of(MASKED ? static_cast<const void *>(r.mrow) : static_cast<const void *>(r.rowp),
+                     MASKED ? uint32_t(a.W) * 4u : 0u);
+    r.V = a.V;
+    float tau = K > 0 ? select_top_k(r, sh, K) : -INFINITY;
+    uint32_t flag = 0u;
+    if (use_p) tau = select_top_p(r, sh, tau, Pp, T, &flag);
+    if (tid == 0) {
+        a.tau[row] = tau;
+        a.tau_flag[row] = flag;
+    }
 }
 
 // ------------------------------------------------------------------ finalize
@@ -999,7 +1212,8 @@ struct FinalArgs {
     uint32_t *status;
     const BlockStat *bstats;
     const DraftRec *drec;
-    const float *tau;  // [rows] top-k thresholds, or nullptr
+    const float *tau;  // [rows] top-k / top-p thresholds, or nullptr
+    const uint32_t *tau_flag;  // [rows] top-p boundary rows (with tau)
     DenseJob *jobs;    // [B] dense q only
     double *wmass;     // [B, C] dense q only: residual mass per block
     int split_dense;   // dense q: 1 = residual masses by the grid-wide kernels
@@ -1613,13 +1827,20 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     if (tid < k && a.dbg_acc) a.dbg_acc[geo.draft0 + tid] = st ? NAN : sh.acc[tid];
     if (tid == 0) {
         a.out_num_accepted[b] = n;
+        // top-p boundary rows of this request (sampling requests only)
+        uint32_t ftp = 0u;
+        if (!st && a.tau && !greedy && (a.dbg_req_flags || a.dbg_flags))
+            for (int r = 0; r < kp1; ++r) ftp += a.tau_flag[geo.row0 + r];
         if (a.dbg_req_flags)
-            a.dbg_req_flags[b] = st ? 0u : (uint32_t(min(sh.flag_acc, 0xffff)) | (uint32_t(fg) << 16));
+            a.dbg_req_flags[b] = st ? 0u
+                                    : (uint32_t(min(sh.flag_acc, 0xfff)) | (uint32_t(min(fg, 0xfff)) << 12) |
+                                       (min(ftp, 0xffu) << 24));
         if (st) {
             if (a.status) atomicOr(a.status, st);
         } else if (a.dbg_flags) {
             if (sh.flag_acc) atomicAdd(&a.dbg_flags[0], static_cast<uint32_t>(sh.flag_acc));
             if (fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
+            if (ftp) atomicAdd(&a.dbg_flags[2], ftp);
         }
         tally_call(a, b, before, share);
     }
@@ -1758,7 +1979,7 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
     }
     if (tid == 0) {
         a.out_tokens[j.row] = y;
-        if (a.dbg_req_flags) a.dbg_req_flags[b] += static_cast<uint32_t>(fg) << 16;
+        if (a.dbg_req_flags) a.dbg_req_flags[b] += static_cast<uint32_t>(fg) << 12;
         if (a.dbg_flags && fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
     }
 }
@@ -1768,7 +1989,7 @@ __global__ void empty_batch_kernel(uint64_t *counters, uint32_t *status, uint32_
                                    uint32_t *hist, int kmax) {
     if (threadIdx.x < 4) counters[threadIdx.x] = 0ull;
     if (threadIdx.x == 0 && status) *status = 0u;
-    if (threadIdx.x < 2 && flags) flags[threadIdx.x] = 0u;
+    if (threadIdx.x < 3 && flags) flags[threadIdx.x] = 0u;
     if (hist)
         for (int i = threadIdx.x; i <= kmax; i += blockDim.x) hist[i] = 0u;
 }
@@ -1861,7 +2082,7 @@ FinalFn pick_final(bool aligned, bool dense) {
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_drec, off_tau, off_jobs, off_wmass, off_rowreq, off_offok, off_tally, total;
+    size_t off_bstats, off_drec, off_tau, off_tauflag, off_jobs, off_wmass, off_rowreq, off_offok, off_tally, total;
     int nslot;
 };
 
@@ -1891,7 +2112,8 @@ inline Layout layout_of(const sd_params *p) {
     L.off_bstats = 0;
     L.off_drec = align256(size_t(L.rows) * L.C * sizeof(BlockStat));
     L.off_tau = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
-    L.off_jobs = L.off_tau + align256(size_t(L.rows) * sizeof(float));
+    L.off_tauflag = L.off_tau + align256(size_t(L.rows) * sizeof(float));
+    L.off_jobs = L.off_tauflag + align256(size_t(L.rows) * sizeof(uint32_t));
     L.off_wmass = L.off_jobs + align256(size_t(p->batch) * sizeof(DenseJob));
     L.off_rowreq = L.off_wmass + align256(size_t(p->batch) * L.C * sizeof(double));
     L.off_offok = L.off_rowreq + align256(p->draft_offsets ? size_t(L.rows) * sizeof(int32_t) : 0);
@@ -1972,7 +2194,9 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.draft = draft_token_ids;
     ra.q = draft_probs;
     ra.seed = seed;
-    ra.tau = p->top_k ? reinterpret_cast<float *>(ws + L.off_tau) : nullptr;
+    const bool thresholds = p->top_k != nullptr || p->top_p != nullptr;
+    ra.tau = thresholds ? reinterpret_cast<float *>(ws + L.off_tau) : nullptr;
+    uint32_t *tau_flag = reinterpret_cast<uint32_t *>(ws + L.off_tauflag);
     int32_t *row_req = reinterpret_cast<int32_t *>(ws + L.off_rowreq);
     uint32_t *off_ok = reinterpret_cast<uint32_t *>(ws + L.off_offok);
     ra.off = p->draft_offsets;
@@ -2019,6 +2243,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.bstats = ra.bstats;
     fa.drec = ra.drec;
     fa.tau = ra.tau;
+    fa.tau_flag = tau_flag;
     fa.off = ra.off;
     fa.off_ok = ra.off_ok;
     fa.jobs = reinterpret_cast<DenseJob *>(ws + L.off_jobs);
@@ -2033,7 +2258,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.W = L.W;
     fa.C = L.C;
 
-    const bool topk = p->top_k != nullptr;
+    const bool topk = thresholds;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
                          : pick_row_stats<float>(masked, aligned, topk);
     FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr)
@@ -2051,6 +2276,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         ta.temperature = temperature;
         ta.top_k = p->top_k;
         ta.tau = const_cast<float *>(ra.tau);
+        ta.tau_flag = tau_flag;
+        ta.top_p = p->top_p;
         ta.off = ra.off;
         ta.row_req = ra.row_req;
         ta.off_ok = ra.off_ok;

@@ -25,7 +25,7 @@ def run_gpu(wl, seed=None):
     B, kp1, V = lg.shape
     v = sdv.Verifier(B, kp1 - 1, V, lg.dtype, lg.device, debug=True)
     r = v(lg, wl["draft_token_ids"], wl["draft_probs"], wl["bitmask"], wl["temperature"],
-          wl["seed"] if seed is None else seed, wl["top_k"])
+          wl["seed"] if seed is None else seed, wl["top_k"], top_p=wl.get("top_p"))
     torch.cuda.synchronize()
     out = {name: getattr(r, name).cpu().numpy().copy() for name in r._fields if getattr(r, name) is not None}
     out["counters"] = out["out_counters"].view(np.uint64)
@@ -37,7 +37,7 @@ def run_oracle(wl, requests=None, seed=None):
     n = to_numpy(wl, requests)
     return oracle.sd_verify(n["logits"], n["draft_token_ids"], n["draft_probs"], n["bitmask"],
                             n["temperature"], seed=wl["seed"] if seed is None else seed,
-                            top_k=n["top_k"], request_ids=requests)
+                            top_k=n["top_k"], request_ids=requests, top_p=n.get("top_p"))
 
 
 def _close(a, b, rtol):
@@ -59,7 +59,7 @@ def compare(gpu, orc, requests=None, check_counters=True):
         if err_o != err_g:
             mism.append(b)
             continue
-        if orc["flag_accept"][j] or orc["flag_gumbel"][j]:
+        if orc["flag_accept"][j] or orc["flag_gumbel"][j] or orc["flag_topp"][j]:
             flagged.append(b)
             continue
         if (orc["num_accepted"][j] != gpu["out_num_accepted"][b]
@@ -110,7 +110,8 @@ def run_gpu_ragged(wl, max_draft, seed=None):
     v = sdv.Verifier(B, max_draft, V, lg.dtype, lg.device, debug=True, histogram=True,
                      total_drafts=rows - B)
     r = v(lg, wl["draft_token_ids"], wl["draft_probs"], wl["bitmask"], wl["temperature"],
-          wl["seed"] if seed is None else seed, wl["top_k"], draft_offsets=wl["draft_offsets"])
+          wl["seed"] if seed is None else seed, wl["top_k"], draft_offsets=wl["draft_offsets"],
+          top_p=wl.get("top_p"))
     torch.cuda.synchronize()
     out = {name: getattr(r, name).cpu().numpy().copy() for name in r._fields if getattr(r, name) is not None}
     out["counters"] = out["out_counters"].view(np.uint64)
@@ -131,7 +132,8 @@ def run_oracle_ragged(wl, max_draft, seed=None):
     return oracle.sd_verify_ragged(cv(wl["logits"]), cv(wl["draft_token_ids"]), cv(wl["draft_offsets"]),
                                    cv(wl["draft_probs"]), cv(wl["bitmask"]), cv(wl["temperature"]),
                                    seed=wl["seed"] if seed is None else seed, top_k=cv(wl["top_k"]),
-                                   max_draft=max_draft, total_drafts=rows - B)
+                                   max_draft=max_draft, total_drafts=rows - B,
+                                   top_p=cv(wl.get("top_p")))
 
 
 def assert_parity_ragged(gpu, orc, off, max_flagged=2):
@@ -147,7 +149,7 @@ def assert_parity_ragged(gpu, orc, off, max_flagged=2):
             continue
         if err_o:
             continue
-        if orc["flag_accept"][b] or orc["flag_gumbel"][b]:
+        if orc["flag_accept"][b] or orc["flag_gumbel"][b] or orc["flag_topp"][b]:
             flagged.append(b)
             continue
         k = int(off[b + 1] - off[b])

@@ -32,8 +32,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_params_struct_layout_matches_header():
     import rejection_sampling_verification_amd as sdv
-    # 3 x int32 + enum, then 8 pointers, offsets, total_drafts, histogram
-    assert ctypes.sizeof(sdv.SdParams) == 16 + 11 * 8
+    # 3 x int32 + enum, then 8 pointers, offsets, total_drafts, histogram, top_p
+    assert ctypes.sizeof(sdv.SdParams) == 16 + 12 * 8
+    assert sdv.SdParams.top_p.offset == 16 + 11 * 8
     assert sdv.SdParams.top_k.offset == 16
     assert sdv.SdParams.draft_offsets.offset == 16 + 8 * 8
     assert sdv.SdParams.total_drafts.offset == 16 + 9 * 8

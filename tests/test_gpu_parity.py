@@ -206,6 +206,39 @@ def test_top_k_threshold_far_from_the_first_tokens():
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [7, 1001, 2049, 6150, 20000])
+def test_top_p_sizes(V, dtype):
+    announce(f"top-p custom V={V} dtype={dtype}")
+    for dense, masked, tk in [(True, False, None), (False, True, (0, 5, 50)), (True, True, (0, 20))]:
+        wl = _custom(10, 3, V, dtype=dtype, dense=dense, masked=masked, greedy_frac=0.2,
+                     seed=2 * V + 3 * dense + masked, top_k=tk)
+        g = torch.Generator(device=DEV)
+        g.manual_seed(V)
+        choice = torch.tensor([0.0, 0.3, 0.9, 0.99, 1.0], device=DEV)
+        wl["top_p"] = choice[torch.randint(0, 5, (10,), generator=g, device=DEV)].contiguous()
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_top_p_ties_and_extremes():
+    announce("top-p with integer logits and extreme values")
+    for dtype in (torch.bfloat16, torch.float32):
+        wl = _custom(24, 4, 5000, dtype=dtype, dense=True, integer_logits=True, seed=31)
+        wl["top_p"] = torch.tensor([1e-6, 0.2, 0.5, 0.8, 0.95, 0.999] * 4, device=DEV)
+        assert_parity(run_gpu(wl), run_oracle(wl))
+        # a wide spread of logits: the cut far below the largest value
+        wl = _custom(8, 2, 30000, dtype=dtype, dense=False, std=25.0, seed=32)
+        wl["top_p"] = torch.full((8,), 0.97, device=DEV)
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_long_k_with_top_p_scaled():
+    announce("long_k B=8 with top-k 50 and top-p 0.9")
+    wl = make_workload("long_k", device=DEV, batch=8)
+    wl["top_p"] = torch.full((8,), 0.9, device=DEV)
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
 # ------------------------------------------------------- shapes and variants
 
 @pytest.mark.parametrize("V", [1, 7, 8, 1001, 2047, 2048, 2049, 6144, 6150])
@@ -321,7 +354,7 @@ def test_counter_example_on_gpu():
     assert [int(v) for v in gpu["counters"]] == [1000, 200, 800, 600]
 
 
-@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked", "top_k"])
+@pytest.mark.parametrize("mode", ["dense", "one_hot", "masked", "top_k", "top_p"])
 def test_chi_square_on_gpu(mode):
     """Emitted tokens follow the target law (pyshine, "Verification": the output
     is statistically indistinguishable from undrafted decoding)."""
@@ -338,7 +371,8 @@ def test_chi_square_on_gpu(mode):
         allowed[:, :2] = True
     T = 0.9
     top_k = 4 if mode == "top_k" else 0
-    p = np.array([ov.target_distribution(l1[i].double().numpy(), allowed[i].numpy(), T, top_k)[0]
+    top_p = 0.6 if mode == "top_p" else 0.0
+    p = np.array([ov.target_distribution(l1[i].double().numpy(), allowed[i].numpy(), T, top_k, top_p)[0]
                   for i in range(k + 1)])
     q1 = torch.softmax(torch.randn((k, V), generator=g), -1)
     x = torch.stack([torch.multinomial(q1[i], B, replacement=True, generator=g) for i in range(k)], 1)
@@ -348,6 +382,7 @@ def test_chi_square_on_gpu(mode):
           "bitmask": None if mode != "masked" else pack_bitmask(allowed).expand(B, k + 1, 1).contiguous().to(DEV),
           "temperature": torch.full((B,), T, device=DEV),
           "top_k": torch.full((B,), top_k, dtype=torch.int32, device=DEV) if top_k else None,
+          "top_p": torch.full((B,), top_p, device=DEV) if top_p else None,
           "seed": 2024}
     runs = [run_gpu(wl, seed=2024 + r) for r in range(4)]
     tok = np.concatenate([g["out_tokens"] for g in runs])

@@ -74,6 +74,15 @@ def test_ragged_sizes(V, dtype):
         assert_parity_ragged(gpu, orc, off)
 
 
+def test_ragged_top_p():
+    announce("ragged with top-p")
+    ks = [0, 3, 1, 8, 5, 2, 7]
+    wl, off = _ragged(ks, 6000, dense=True, masked=True, greedy_frac=0.2, seed=77, top_k=(0, 40))
+    wl["top_p"] = torch.tensor([0.9, 0.5, 0.0, 0.95, 0.7, 0.3, 0.99], device=DEV)
+    gpu, orc = run_gpu_ragged(wl, 8), run_oracle_ragged(wl, 8)
+    assert_parity_ragged(gpu, orc, off)
+
+
 def test_ragged_largest_draft_count():
     announce("ragged k_b up to 64")
     ks = [64, 0, 17, 64, 3, 40]
