@@ -162,7 +162,7 @@ def cpu_baseline(wl, n_requests, min_seconds=10.0):
         while True:
             oracle.sd_verify(host["logits"], host["draft_token_ids"], host["draft_probs"],
                              host["bitmask"], host["temperature"], seed=wl["seed"],
-                             top_k=host["top_k"], request_ids=req)
+                             top_k=host["top_k"], request_ids=req, top_p=host.get("top_p"))
             passes += 1
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
@@ -189,15 +189,17 @@ def cpu_baseline_ragged(wl, min_seconds=10.0):
         t = t.detach()
         return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
     import torch
-    host = {key: cv(wl[key]) for key in ("logits", "draft_token_ids", "draft_offsets", "draft_probs",
-                                         "bitmask", "temperature", "top_k")}
+    host = {key: cv(wl.get(key)) for key in ("logits", "draft_token_ids", "draft_offsets",
+                                             "draft_probs", "bitmask", "temperature", "top_k",
+                                             "top_p")}
     passes = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
             oracle.sd_verify_ragged(host["logits"], host["draft_token_ids"], host["draft_offsets"],
                                     host["draft_probs"], host["bitmask"], host["temperature"],
-                                    seed=wl["seed"], top_k=host["top_k"], max_draft=wl["max_draft"])
+                                    seed=wl["seed"], top_k=host["top_k"], max_draft=wl["max_draft"],
+                                    top_p=host["top_p"])
             passes += 1
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
@@ -223,6 +225,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="CSV")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="apply this top-p to every request of the workload")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -246,6 +250,9 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     wl = make_workload(args.workload, device=dev)
+    if args.top_p is not None:
+        nreq = wl["temperature"].shape[0]
+        wl["top_p"] = torch.full((nreq,), float(args.top_p), device=dev)
     lg = wl["logits"]
     ragged = "draft_offsets" in wl
     if ragged:  # per-request draft counts: rows packed, positions = all drafts
@@ -264,6 +271,9 @@ def main():
     v = sdv.Verifier(B, k, V, lg.dtype, dev, **vkw)
     call_args = (wl["draft_token_ids"], wl["draft_probs"], wl["bitmask"], wl["temperature"],
                  wl["seed"], wl["top_k"])
+
+    if wl.get("top_p") is not None:
+        kw["top_p"] = wl["top_p"]
 
     def call(s, **extra):
         return v(copies[s % len(copies)], *call_args, **kw, **extra)
@@ -314,7 +324,8 @@ def main():
     achieved = k1_bytes / k1_avg_s / 1e9
     digest = source_digest()
     # the committed counter summary covers the ngram workload only
-    traffic = measured_traffic(digest) if args.workload == "ngram" and args.copies >= 4 else None
+    traffic = measured_traffic(digest) if (args.workload == "ngram" and args.copies >= 4
+                                           and args.top_p is None) else None
 
     # ---- one debug call for the flag counts
     vd = sdv.Verifier(B, k, V, lg.dtype, dev, debug=True, **vkw)
@@ -347,7 +358,8 @@ def main():
         "config": {"workload": f"{args.workload}: B={B} "
                                f"{f'k_b up to {k}, {positions} drafts' if ragged else f'k={k}'} V={V} "
                                f"{'bf16' if lg.dtype == torch.bfloat16 else 'fp32'} logits, "
-                               f"{'one-hot' if wl['draft_probs'] is None else 'dense'} drafts",
+                               f"{'one-hot' if wl['draft_probs'] is None else 'dense'} drafts"
+                               f"{'' if args.top_p is None else f', top-p {args.top_p}'}",
                    "batch": B, "num_draft": k, "vocab": V, "drafts_per_call": positions,
                    "input_copies": len(copies)},
         "call_us": {"p10": call_us[len(call_us) // 10], "p50": call_us[len(call_us) // 2],
