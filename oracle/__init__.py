@@ -22,6 +22,11 @@ What it computes, and where the pages define it
 * ``philox`` -- Philox4x32-10 from Salmon, Moraes, Dror and Shaw, "Parallel
   Random Numbers: As Easy as 1, 2, 3" (SC'11), which supplies every uniform
   the sampler draws.  The pages name no generator; this is a reading.
+* ``ngram.propose`` / ``ngram.propose_batch`` -- the n-gram (prompt lookup)
+  draft proposer: the history's tail looked up earlier in the same history,
+  longest window first, earliest occurrence on ties, the following tokens
+  copied (infra-guide 5.2, sections 4.1 and 6; pyshine "vLLM, part 2",
+  "Choosing a drafter").
 * ``rates`` -- survival D/R, acceptance A/D, yield A/R and mean acceptance
   length 1 + A/steps (fanout, sections "Work a denominator example" and
   "Mean acceptance length uses another denominator"; infra-guide 5.2 section 7.1).
@@ -29,9 +34,11 @@ What it computes, and where the pages define it
 Pins (tests marked ``not gpu``): the pages' worked counter examples, SciPy's
 softmax/logsumexp, NumPy argmax, brute-force top-k, rocRAND's own Philox
 compiled on the host, closed forms of the Weyl constants, exact enumeration of
-the accept/resample law at V=8, and chi-square tests of the sampled tokens.
+the accept/resample law at V=8, chi-square tests of the sampled tokens, and
+for the n-gram proposer the pages' worked lookups, brute force and the
+Z-function of the reversed history.
 """
 
-from . import philox, rates, verify  # noqa: F401
+from . import ngram, philox, rates, verify  # noqa: F401
 from .verify import sd_verify, sd_verify_ragged  # noqa: F401
 from .rates import sd_rates  # noqa: F401
