@@ -1,13 +1,15 @@
 """Python binding of the MI355X speculative-decoding verifier (libsdverify.so).
 
-Argument marshalling only: every step of verification runs in the HIP kernels
-behind the C ABI declared in include/sd_verify.h.  PyTorch supplies device
+Argument marshalling only: every step of verification and of the n-gram draft
+proposer runs in the HIP kernels behind the C ABI declared in
+include/sd_verify.h and include/sd_ngram.h.  PyTorch supplies device
 memory and the current stream.  Importing this package fails loudly when the
 library has not been built (python -m rejection_sampling_verification_amd.build).
 
 Entry points mirror the C ABI names: ``sd_verify``, ``sd_verify_workspace_size``,
-``sd_status_string``, ``sd_rates``; ``Verifier`` keeps the workspace and
-outputs of repeated same-shape calls.
+``sd_status_string``, ``sd_rates``, ``sd_ngram_propose``,
+``sd_ngram_workspace_size``; ``Verifier`` and ``NgramProposer`` keep the
+workspace and outputs of repeated same-shape calls.
 """
 import ctypes
 import math
@@ -34,8 +36,13 @@ SD_STATUS_BAD_LOGIT = 8
 SD_STATUS_BAD_DRAFT_PROB = 16
 SD_STATUS_BAD_OFFSETS = 32
 
-# every symbol include/sd_verify.h declares
-EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates")
+SD_NGRAM_MAX_N = 256
+SD_NGRAM_MAX_BATCH = 65535
+SD_NGRAM_STATUS_BAD_LENGTH = 1
+
+# every symbol include/sd_verify.h and include/sd_ngram.h declare
+EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates",
+                    "sd_ngram_propose", "sd_ngram_workspace_size")
 
 
 class SdParams(ctypes.Structure):
@@ -59,6 +66,21 @@ class SdParams(ctypes.Structure):
     ]
 
 
+class SdNgramParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("min_n", ctypes.c_int32),
+        ("max_n", ctypes.c_int32),
+        ("num_draft", ctypes.c_int32),
+        ("stride", ctypes.c_int64),
+        ("max_model_len", ctypes.c_int64),
+        ("out_match_len", ctypes.c_void_p),
+        ("out_draft_offsets", ctypes.c_void_p),
+        ("out_drafts_flat", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
 def _load():
     if not os.path.exists(LIBRARY_PATH):
         raise ImportError(
@@ -78,6 +100,13 @@ def _load():
     lib.sd_rates.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint64,
                              ctypes.POINTER(ctypes.c_double)]
     lib.sd_rates.restype = ctypes.c_int
+    lib.sd_ngram_workspace_size.argtypes = [ctypes.POINTER(SdNgramParams)]
+    lib.sd_ngram_workspace_size.restype = ctypes.c_size_t
+    lib.sd_ngram_propose.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(SdNgramParams), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    lib.sd_ngram_propose.restype = ctypes.c_int
     return lib
 
 
@@ -299,6 +328,85 @@ def sd_verify_ragged(target_logits, draft_token_ids, draft_offsets, draft_probs=
                  target_logits.device, debug=debug, histogram=histogram, total_drafts=rows - B)
     return v(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed, top_k, stream,
              draft_offsets=draft_offsets, top_p=top_p)
+
+
+class NgramResult(NamedTuple):
+    drafts: torch.Tensor             # [B, k] int32, -1 after each request's drafts
+    num_drafts: torch.Tensor         # [B] int32
+    match_len: torch.Tensor          # [B] int32, 0 = nothing proposed
+    draft_offsets: torch.Tensor      # [B+1] int32, cumulative num_drafts
+    drafts_flat: torch.Tensor        # [B*k] int32: the drafts back to back (first offsets[B])
+    status: torch.Tensor             # [1] int32 holding the uint32 status bits
+
+
+def _ngram_params(batch, min_n, max_n, num_draft, stride, max_model_len):
+    p = SdNgramParams()
+    p.batch, p.min_n, p.max_n, p.num_draft = int(batch), int(min_n), int(max_n), int(num_draft)
+    p.stride, p.max_model_len = int(stride), int(max_model_len)
+    return p
+
+
+def sd_ngram_workspace_size(batch, stride, min_n=1, max_n=1, num_draft=0, max_model_len=0):
+    """Device workspace bytes of the n-gram proposer for these sizes."""
+    p = _ngram_params(batch, min_n, max_n, num_draft, stride, max_model_len)
+    return int(_lib.sd_ngram_workspace_size(ctypes.byref(p)))
+
+
+class NgramProposer:
+    """Outputs and workspace of the n-gram proposer for a history table of
+    [batch, stride] int32 tokens; each call overwrites the tensors it returns."""
+
+    def __init__(self, batch, stride, min_n, max_n, num_draft, max_model_len=0, device=None):
+        dev = torch.device(device) if device is not None else torch.device("cuda")
+        if dev.type != "cuda":
+            raise ValueError("the proposer runs on a HIP device")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.B, self.stride, self.k = int(batch), int(stride), int(num_draft)
+        self.params = _ngram_params(batch, min_n, max_n, num_draft, stride, max_model_len)
+        probe = _ngram_params(max(self.B, 1), min_n, max_n, num_draft, stride, max_model_len)
+        if int(_lib.sd_ngram_workspace_size(ctypes.byref(probe))) == 0:
+            raise ValueError(f"unsupported n-gram proposer sizes: batch={batch} stride={stride} "
+                             f"min_n={min_n} max_n={max_n} k={num_draft}")
+        ws = int(_lib.sd_ngram_workspace_size(ctypes.byref(self.params)))
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.workspace_bytes = ws
+        self.drafts = torch.empty((self.B, self.k), dtype=torch.int32, device=dev)
+        self.num_drafts = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.match_len = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.draft_offsets = torch.empty(self.B + 1, dtype=torch.int32, device=dev)
+        self.drafts_flat = torch.empty(max(self.B * self.k, 1), dtype=torch.int32, device=dev)
+        self.status = torch.empty(1, dtype=torch.int32, device=dev)
+        self.params.out_match_len = self.match_len.data_ptr()
+        self.params.out_draft_offsets = self.draft_offsets.data_ptr()
+        self.params.out_drafts_flat = self.drafts_flat.data_ptr()
+        self.params.status = self.status.data_ptr()
+
+    def __call__(self, tokens, lengths, stream=None):
+        dev = self.device
+        _check(tokens, "tokens", torch.int32, (self.B, self.stride), dev)
+        _check(lengths, "lengths", torch.int32, (self.B,), dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = _lib.sd_ngram_propose(
+            _ptr(tokens), _ptr(lengths), _ptr(self.drafts), _ptr(self.num_drafts),
+            ctypes.byref(self.params), ctypes.c_void_p(self.workspace.data_ptr()),
+            ctypes.c_size_t(self.workspace_bytes), ctypes.c_void_p(int(stream)))
+        if rc != SD_OK:
+            raise RuntimeError(f"sd_ngram_propose failed: {sd_status_string(rc)} ({rc})")
+        return NgramResult(self.drafts, self.num_drafts, self.match_len, self.draft_offsets,
+                           self.drafts_flat, self.status)
+
+
+def sd_ngram_propose(tokens, lengths, min_n, max_n, num_draft, max_model_len=0, stream=None):
+    """n-gram drafts for a [B, stride] int32 history table whose row b holds
+    lengths[b] tokens; returns fresh outputs (see NgramResult)."""
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [B, stride]")
+    B, stride = tokens.shape
+    prop = NgramProposer(B, stride, min_n, max_n, num_draft, max_model_len, tokens.device)
+    return prop(tokens, lengths, stream)
 
 
 def rates_from_counters(counters, steps):

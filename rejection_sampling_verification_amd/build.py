@@ -2,7 +2,8 @@
 
     python -m rejection_sampling_verification_amd.build
 
-compiles csrc/sd_verify.hip into libsdverify.so next to this file.
+compiles csrc/sd_verify.hip (the verifier) and csrc/sd_ngram.hip (the n-gram
+proposer) into libsdverify.so next to this file.
 """
 import os
 import shutil
@@ -11,7 +12,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SOURCE = os.path.join(PKG_DIR, "csrc", "sd_verify.hip")
+SOURCES = [os.path.join(PKG_DIR, "csrc", name) for name in ("sd_verify.hip", "sd_ngram.hip")]
 LIBRARY = os.path.join(PKG_DIR, "libsdverify.so")
 ARCH = "gfx950"
 
@@ -29,7 +30,7 @@ def compile_command(output=LIBRARY, extra=()):
         # would wait for an atomic's return right after issuing it
         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", os.path.join(ROOT, "include"),
-        *extra, "-o", output, SOURCE,
+        *extra, "-o", output, *SOURCES,
     ]
 
 

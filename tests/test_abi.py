@@ -1,5 +1,5 @@
-"""The C ABI library loads, exports every symbol include/sd_verify.h declares,
-and its host-only logic behaves (no GPU compute here)."""
+"""The C ABI library loads, exports every symbol include/*.h declares, and its
+host-only logic behaves (no GPU compute here)."""
 import ctypes
 import math
 import os
@@ -8,18 +8,23 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sd_verify.h")
+HEADERS = [os.path.join(ROOT, "include", name) for name in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if name.endswith(".h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names |= set(re.findall(r"\b(sd_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_expected_entry_points():
+    assert [os.path.basename(h) for h in HEADERS] == ["sd_ngram.h", "sd_verify.h"]
     assert _declared_functions() == sorted(
-        ["sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates"])
+        ["sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates",
+         "sd_ngram_propose", "sd_ngram_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -152,3 +157,41 @@ def test_ragged_host_checks_and_workspace():
     ws_r = sdv.sd_verify_workspace_size(4, 3, 100, total_drafts=5)
     ws_u = sdv.sd_verify_workspace_size(4, 3, 100)
     assert ws_r > 0 and ws_u > 0 and ws_r < ws_u + 4096
+
+
+def test_ngram_params_layout_and_host_checks():
+    import rejection_sampling_verification_amd as sdv
+    # 4 x int32, stride and max_model_len, then 4 pointers
+    assert ctypes.sizeof(sdv.SdNgramParams) == 16 + 2 * 8 + 4 * 8
+    assert sdv.SdNgramParams.stride.offset == 16
+    assert sdv.SdNgramParams.out_match_len.offset == 32
+    assert sdv.SdNgramParams.status.offset == 56
+    lib = sdv.library()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(p, ws=nul, nbytes=0):
+        return lib.sd_ngram_propose(fake, fake, fake, fake, ctypes.byref(p), ws, nbytes, nul)
+
+    good = dict(batch=4, min_n=2, max_n=5, num_draft=4, stride=5000, max_model_len=0)
+    for key, bad, code in [("min_n", 0, -1), ("max_n", 1, -1), ("num_draft", -1, -1), ("stride", 0, -1),
+                           ("batch", -1, -1), ("max_model_len", -1, -1), ("max_n", 257, -2),
+                           ("num_draft", 65, -2), ("batch", 65536, -2), ("stride", 1 << 31, -2)]:
+        kw = dict(good, **{key: bad})
+        p = sdv._ngram_params(kw["batch"], kw["min_n"], kw["max_n"], kw["num_draft"], kw["stride"],
+                              kw["max_model_len"])
+        assert call(p) == code, (key, bad)
+        assert sdv.sd_ngram_workspace_size(kw["batch"], kw["stride"], kw["min_n"], kw["max_n"],
+                                           kw["num_draft"], kw["max_model_len"]) == 0
+    p = sdv._ngram_params(**{"batch": 4, "min_n": 2, "max_n": 5, "num_draft": 4, "stride": 5000,
+                             "max_model_len": 0})
+    assert lib.sd_ngram_propose(nul, fake, fake, fake, ctypes.byref(p), nul, 0, nul) == -1
+    assert lib.sd_ngram_propose(fake, fake, fake, fake, None, nul, 0, nul) == -1
+    p.out_drafts_flat = 1 << 20                    # flat drafts need the offsets
+    assert call(p) == -1
+    p.out_drafts_flat = None
+    assert call(p) == -3                           # no workspace
+    ws = sdv.sd_ngram_workspace_size(4, 5000, 2, 5, 4)
+    assert ws >= 4 * 3 * 8 and ws % 256 == 0       # one 8-byte key per (request, 2048 positions)
+    assert call(p, fake, ws - 1) == -3
+    assert sdv.sd_ngram_workspace_size(0, 5000, 2, 5, 4) == 0

@@ -27,6 +27,19 @@ dataset).  `batch=` shrinks a workload to fewer requests at the same k and V:
               T ~ U[0.6, 1.2] with top_k = 50; a random half of the requests carry
               bitmasks allowing exactly round(0.1 V) tokens per row, the others
               all-ones rows
+
+History tables for the n-gram proposer (make_histories):
+
+  ngram_propose B=256 token histories in a [256, 16384] int32 table, V=151936,
+              windows 2..5, k=4, context length 16384 (so histories longer than
+              16380 get no drafts).  Lengths uniform on [2048, 16384].  A history
+              is a prompt of uniform random tokens (the first half) followed by
+              "generated" text built segment by segment: with probability 0.5 a
+              copy of an earlier span (length uniform on 8..64, start uniform over
+              the text so far), else a fresh run of 1..16 uniform tokens -- the
+              text-reuse pattern prompt lookup serves (summaries quoting their
+              source, edited code).  Slots past a row's length hold random tokens
+              that the proposer never reads.
 """
 import math
 
@@ -257,3 +270,51 @@ def _algorithmic_bytes_uniform(wl, n_residual_rows=None):
             total += int(n_residual_rows) * V * 4
     total += B * k * 4 + B * 4 + B * kp1 * 4 + B * 4
     return total
+
+
+HISTORY_WORKLOADS = {
+    "ngram_propose": dict(B=256, stride=16384, Lmin=2048, V=151936, min_n=2, max_n=5, k=4,
+                          max_model_len=16384),
+}
+
+
+def _history(rng, L, V, copy_p=0.5, span=(8, 64), fresh=(1, 16)):
+    import numpy as np
+    h = np.empty(L, dtype=np.int64)
+    P = L // 2
+    h[:P] = rng.integers(0, V, size=P)
+    n = P
+    while n < L:
+        if n > 0 and rng.random() < copy_p:
+            m = int(rng.integers(span[0], span[1] + 1))
+            s0 = int(rng.integers(0, n))
+            m = min(m, L - n)
+            if s0 + m <= n:
+                h[n:n + m] = h[s0:s0 + m]
+            else:
+                for t in range(m):       # overlaps what it copies, like repeated text
+                    h[n + t] = h[s0 + t]
+        else:
+            m = min(int(rng.integers(fresh[0], fresh[1] + 1)), L - n)
+            h[n:n + m] = rng.integers(0, V, size=m)
+        n += m
+    return h
+
+
+def make_histories(name="ngram_propose", device="cpu", batch=None, seed=None, **overrides):
+    """Inputs of one n-gram proposer call: tokens [B, stride] int32 and
+    lengths [B] int32 on `device`, plus the call's settings (min_n, max_n, k,
+    max_model_len, V).  Built with NumPy's seeded generator on the host."""
+    import numpy as np
+    cfg = dict(HISTORY_WORKLOADS[name], **overrides)
+    B = cfg["B"] if batch is None else int(batch)
+    rng = np.random.default_rng(7 if seed is None else seed)
+    stride, V = cfg["stride"], cfg["V"]
+    lengths = rng.integers(cfg["Lmin"], stride + 1, size=B)
+    table = rng.integers(0, V, size=(B, stride))
+    for b in range(B):
+        table[b, :lengths[b]] = _history(rng, int(lengths[b]), V)
+    return {"tokens": torch.tensor(table, dtype=torch.int32, device=device),
+            "lengths": torch.tensor(lengths, dtype=torch.int32, device=device),
+            "min_n": cfg["min_n"], "max_n": cfg["max_n"], "k": cfg["k"],
+            "max_model_len": cfg["max_model_len"], "V": V}
