@@ -18,6 +18,7 @@ Printed as one JSON line, with
                 workload.
 
   python bench.py [--steps K] [--warmup W] [--workload ngram]
+  python bench.py --workload ngram_propose   # the n-gram proposer over 256 histories
   python bench.py --copy-calibration    # plain 1 GiB device copy, for PMC scaling
   python bench.py --summarize-pmc FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
       # turns four `rocprofv3 --pmc` counter files into the traffic summary
@@ -41,19 +42,25 @@ SOURCES = ["rejection_sampling_verification_amd/csrc/sd_verify.hip",
            "include/sd_verify.h"]
 
 
-def source_digest():
+PROPOSER_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ngram_match_propose_traffic.txt")
+PROPOSER_SOURCES = ["rejection_sampling_verification_amd/csrc/sd_ngram.hip",
+                    "rejection_sampling_verification_amd/csrc/wave.h",
+                    "include/sd_ngram.h", "include/sd_verify.h"]
+
+
+def source_digest(sources=None):
     h = hashlib.sha256()
-    for rel in SOURCES:
+    for rel in SOURCES if sources is None else sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest):
-    """HBM bytes per row-statistics launch from the committed PMC summary,
-    if it was taken on the current kernel sources."""
+def measured_traffic(digest, path=TRAFFIC_FILE):
+    """HBM bytes per launch of the measured kernel from a committed PMC
+    summary, if it was taken on the current kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
@@ -116,11 +123,11 @@ def _mean_kib(path, counter, match):
     return sum(vals) / len(vals), len(vals)
 
 
-def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
-    """HBM bytes per row-statistics launch: FETCH_SIZE and WRITE_SIZE (KiB
-    per dispatch), each scaled by what the same counter reads for the plain
-    copy of COPY_BYTES."""
-    is_k1 = lambda n: "row_stats" in n
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel="row_stats"):
+    """HBM bytes per launch of `kernel` (row_stats or ngram_match):
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
+    same counter reads for the plain copy of COPY_BYTES."""
+    is_k1 = lambda n: kernel in n
     is_copy = lambda n: "copy" in n.lower()  # the copy itself, not the fill before it
     f_k1, n_f = _mean_kib(fetch_csv, "FETCH_SIZE", is_k1)
     w_k1, n_w = _mean_kib(write_csv, "WRITE_SIZE", is_k1)
@@ -131,10 +138,10 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     fetch_b = f_k1 * 1024.0 * f_scale
     write_b = w_k1 * 1024.0 * w_scale
     lines = [
-        f"source_digest: {source_digest()}",
-        f"row_stats_dispatches: {n_f} (FETCH_SIZE run), {n_w} (WRITE_SIZE run)",
-        f"row_stats_fetch_kib_per_dispatch: {f_k1:.1f}",
-        f"row_stats_write_kib_per_dispatch: {w_k1:.1f}",
+        f"source_digest: {source_digest(PROPOSER_SOURCES if kernel == 'ngram_match' else None)}",
+        f"{kernel}_dispatches: {n_f} (FETCH_SIZE run), {n_w} (WRITE_SIZE run)",
+        f"{kernel}_fetch_kib_per_dispatch: {f_k1:.1f}",
+        f"{kernel}_write_kib_per_dispatch: {w_k1:.1f}",
         f"copy_fetch_kib_per_dispatch: {f_cp:.1f} (plain copy of {COPY_BYTES} bytes)",
         f"copy_write_kib_per_dispatch: {w_cp:.1f}",
         f"fetch_scale: {f_scale:.4f}",
@@ -212,6 +219,121 @@ def cpu_baseline_ragged(wl, min_seconds=10.0):
             "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
 
 
+PROPOSER_METRIC = "n-gram proposals/sec (B=256 token histories of 2048..16384, windows 2..5, k=4)"
+
+
+def cpu_baseline_proposer(wl, min_seconds=10.0):
+    """The n-gram oracle on one host thread over the whole history table,
+    repeated until at least min_seconds have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.ngram import propose_batch
+    tokens, lengths = wl["tokens"].cpu().numpy(), wl["lengths"].cpu().numpy()
+    passes = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            propose_batch(tokens, lengths, wl["min_n"], wl["max_n"], wl["k"], wl["max_model_len"])
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    B = lengths.shape[0]
+    return {"value": passes * B / dt, "unit": "requests/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over the whole table ({B} histories), NumPy on one thread, "
+                      f"{dt:.1f} s",
+            "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+
+
+def bench_proposer(args, dev):
+    """One step = one sd_ngram_propose call over the 256-history table (match
+    kernel + emit kernel).  Tables rotate over enough device copies to keep
+    the 256 MB Infinity Cache from holding them."""
+    import torch
+    import rejection_sampling_verification_amd as sdv
+    from workloads import make_histories
+
+    print("[bench] generating n-gram histories", file=sys.stderr, flush=True)
+    wl = make_histories(device=dev)
+    tokens, lengths = wl["tokens"], wl["lengths"]
+    B, stride = tokens.shape
+    ncopy = max(args.copies, 20)
+    copies = [tokens] + [tokens.clone() for _ in range(ncopy - 1)]
+    prop = sdv.NgramProposer(B, stride, wl["min_n"], wl["max_n"], wl["k"], wl["max_model_len"], dev)
+
+    def call(s, **extra):
+        return prop(copies[s % ncopy], lengths, **extra)
+
+    for s in range(args.warmup):
+        call(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(args.steps):
+        call(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    step_s = max(wall, gpu_ms / 1e3) / args.steps
+    print(f"[bench] timed {args.steps} steps: {step_s * 1e6:.1f} us/step", file=sys.stderr, flush=True)
+
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in pairs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for s, (a, b) in enumerate(pairs):
+        call(s, match_events=(a.cuda_event, b.cuda_event))
+    torch.cuda.synchronize()
+    km = sorted(a.elapsed_time(b) for a, b in pairs)
+    k_avg_s = sum(km) / len(km) / 1e3
+    # algorithmic bytes of the match kernel: every token of every searched
+    # history once, the lengths, and one 8-byte key per workgroup
+    Lh = [int(v) for v in lengths.cpu().tolist()]
+    mml, k = wl["max_model_len"], wl["k"]
+    searched = [L for L in Lh if 0 <= L <= stride and not (mml and L + k > mml)]
+    nchunk = -(-stride // 2048)
+    match_bytes = 4 * sum(searched) + 4 * B + 8 * B * nchunk
+    achieved = match_bytes / k_avg_s / 1e9
+    r = call(0)
+    torch.cuda.synchronize()
+    nd = int(r.num_drafts.sum().item())
+    cpu = None if args.no_cpu_baseline else cpu_baseline_proposer(wl)
+    out = {
+        "metric": PROPOSER_METRIC,
+        "value": B / step_s,
+        "unit": "requests/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": f"ngram_propose: B={B} token histories in a [{B}, {stride}] int32 table, "
+                               f"lengths 2048..{stride}, windows {wl['min_n']}..{wl['max_n']}, "
+                               f"k={k}, context {mml}",
+                   "batch": B, "stride": stride, "history_tokens": sum(Lh),
+                   "drafts_per_call": nd, "input_copies": ncopy},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(source_digest(PROPOSER_SOURCES), PROPOSER_TRAFFIC_FILE)
+                     if ncopy >= 20 else None, "kernel": "ngram_match",
+                     "avg_us": k_avg_s * 1e6, "p10_us": km[len(km) // 10] * 1e3,
+                     "p90_us": km[(9 * len(km)) // 10] * 1e3, "bytes_per_launch": match_bytes},
+        "cpu_baseline": cpu,
+        "gpu_ms_timed_region": gpu_ms,
+        "wall_s_timed_region": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,12 +347,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="CSV")
+    ap.add_argument("--pmc-kernel", default="row_stats", choices=["row_stats", "ngram_match"])
     ap.add_argument("--top-p", type=float, default=None,
                     help="apply this top-p to every request of the workload")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, kernel=args.pmc_kernel)
         return
 
     if args.gpus != 1:
@@ -248,6 +371,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "ngram_propose":
+        bench_proposer(args, dev)
+        return
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     wl = make_workload(args.workload, device=dev)
     if args.top_p is not None:

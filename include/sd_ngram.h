@@ -59,6 +59,10 @@ typedef struct {
                                    of out_draft_offsets (needs out_draft_offsets); slots
                                    past offsets[B] are left as they were */
     uint32_t *status;           /* device [1]: SD_NGRAM_STATUS_* bits of the call */
+    /* optional hipEvent_t handles (NULL = none) recorded on `stream` right
+     * before and right after the match kernel, to time it alone */
+    void *match_event_begin;
+    void *match_event_end;
 } sd_ngram_params;
 
 /* Device workspace bytes sd_ngram_propose needs for these sizes (0 when the

@@ -78,6 +78,8 @@ class SdNgramParams(ctypes.Structure):
         ("out_draft_offsets", ctypes.c_void_p),
         ("out_drafts_flat", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("match_event_begin", ctypes.c_void_p),
+        ("match_event_end", ctypes.c_void_p),
     ]
 
 
@@ -383,10 +385,14 @@ class NgramProposer:
         self.params.out_drafts_flat = self.drafts_flat.data_ptr()
         self.params.status = self.status.data_ptr()
 
-    def __call__(self, tokens, lengths, stream=None):
+    def __call__(self, tokens, lengths, stream=None, match_events=None):
         dev = self.device
         _check(tokens, "tokens", torch.int32, (self.B, self.stride), dev)
         _check(lengths, "lengths", torch.int32, (self.B,), dev)
+        if match_events is not None:
+            self.params.match_event_begin, self.params.match_event_end = match_events
+        else:
+            self.params.match_event_begin = self.params.match_event_end = None
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         rc = _lib.sd_ngram_propose(

@@ -161,8 +161,8 @@ def test_ragged_host_checks_and_workspace():
 
 def test_ngram_params_layout_and_host_checks():
     import rejection_sampling_verification_amd as sdv
-    # 4 x int32, stride and max_model_len, then 4 pointers
-    assert ctypes.sizeof(sdv.SdNgramParams) == 16 + 2 * 8 + 4 * 8
+    # 4 x int32, stride and max_model_len, then 4 output pointers and 2 events
+    assert ctypes.sizeof(sdv.SdNgramParams) == 16 + 2 * 8 + 6 * 8
     assert sdv.SdNgramParams.stride.offset == 16
     assert sdv.SdNgramParams.out_match_len.offset == 32
     assert sdv.SdNgramParams.status.offset == 56
