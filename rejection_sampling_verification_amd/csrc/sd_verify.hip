@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "sd_verify.h"
 #include "philox.h"
@@ -739,11 +740,55 @@ struct TopkShared {
     uint32_t part[kTopkThreads];  // per-thread sums of 4 bins, scanned in place
     uint32_t red[kTopkWaves];
     uint32_t found_digit, found_rank, lowest;
-    double mass[kTopkWindow];     // top-p: kept mass per bin
+};
+
+// The top-p selection's per-bin masses beside the top-k histogram (only the
+// kernels that apply top-p carry them).
+struct ToppShared : TopkShared {
+    double mass[kTopkWindow];     // kept mass per bin
     double dpart[kTopkThreads];
     double red_d[kTopkWaves];
     double found_mass;
 };
+
+// What the top-k selection leaves for a top-p cut after it.
+struct TopkResult {
+    float tau;         // the threshold; -inf when every supported token stays
+    uint32_t lo;       // first code (top 16 bits) of the last histogram window
+    uint32_t maxcode;  // the row's largest allowed finite code (0: none)
+    bool window;       // bf16 rows: hist holds, per code from lo, the count of
+                       // every kept element (nothing kept lies above the window)
+};
+
+// The bf16 value whose order-preserving code has top half d (a bf16 value's
+// 32-bit code has an all-zero low half when positive, all-one when negative).
+__device__ __forceinline__ float bf16_value_of_digit(uint32_t d) {
+    return float_of_code((d << 16) | ((d & 0x8000u) ? 0u : 0xffffu));
+}
+
+// 2^t for t <= 0 in fp64, within about 3e-13 relative: t = n + f with
+// n = rint(t) and |f| <= 1/2; e^(f ln 2) from its Taylor series to degree 10
+// (the first omitted term, (ln 2 / 2)^11 / 11!, is below 2.2e-13), scaled by
+// 2^n.  Arguments below -1100 give 0.  Top-p masses need far less than fp64
+// rounding but far more than fp32 gives (the boundary band is 1e-9 of the
+// mass), and this costs about half a general exp2.
+__device__ __forceinline__ double exp2_precise_nonpos(double t) {
+    t = fmax(t, -1100.0);
+    const double n = rint(t);
+    const double y = (t - n) * 0.6931471805599453;  // ln 2
+    double p = 1.0 / 3628800.0;                     // 1/10!
+    p = fma(p, y, 1.0 / 362880.0);
+    p = fma(p, y, 1.0 / 40320.0);
+    p = fma(p, y, 1.0 / 5040.0);
+    p = fma(p, y, 1.0 / 720.0);
+    p = fma(p, y, 1.0 / 120.0);
+    p = fma(p, y, 1.0 / 24.0);
+    p = fma(p, y, 1.0 / 6.0);
+    p = fma(p, y, 0.5);
+    p = fma(p, y, 1.0);
+    p = fma(p, y, 1.0);
+    return ldexp(p, static_cast<int>(n));
+}
 
 // The P values of one 16-byte group of the row at token `tok` with excluded
 // tokens (masked, past V, NaN, +-inf) as NaN.
@@ -857,9 +902,11 @@ struct TopkRow {
 };
 
 // The K-th largest allowed finite logit of the row, or -inf when the row
-// holds at most K of them (see the comment above TopkArgs).
-template <typename ET, bool ALIGNED, bool MASKED>
-__device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, int K) {
+// holds at most K of them (see the comment above TopkArgs); also the row's
+// largest code and, for bf16 rows, whether the last histogram holds every
+// kept element (the largest code only when TRACK_MAX: a top-p cut follows).
+template <typename ET, bool ALIGNED, bool MASKED, bool TRACK_MAX>
+__device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, int K) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int64_t kStep = int64_t(kTopkThreads) * P;
     const int tid = threadIdx.x;
@@ -879,7 +926,7 @@ __device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
     uint32_t hi = min(anchor + 128u, 0xffffu);
     uint32_t span = kTopkFirstSpan;  // the first window is narrow: fewer LDS atomics
     const uint32_t need = static_cast<uint32_t>(K);
-    uint32_t digit = 0, rank = 0;
+    uint32_t digit = 0, rank = 0, maxcode = 0, lo_found = 0, above_found = 0;
     bool first = true, found = false;
     // The window only ever moves one way (up while the K-th largest lies above
     // it, down while it lies below), so at most 65536 / kTopkWindow + 1 passes
@@ -888,7 +935,7 @@ __device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
         const uint32_t lo = hi >= span - 1 ? hi - (span - 1) : 0u;
         for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.hist[i] = 0u;
         lds_barrier();
-        uint32_t above = 0, support = 0;
+        uint32_t above = 0, support = 0, mx = 0;
         // kTopkUnroll groups per thread in flight per iteration
         for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
             float v[kTopkUnroll][P];
@@ -900,7 +947,9 @@ __device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
                 for (int e = 0; e < P; ++e) {
                     if (v[u][e] != v[u][e]) continue;
                     ++support;
-                    const uint32_t d = ordered_code(v[u][e]) >> 16;
+                    const uint32_t c = ordered_code(v[u][e]);
+                    if (TRACK_MAX) mx = max(mx, c);
+                    const uint32_t d = c >> 16;
                     if (d > hi) ++above;
                     else if (d >= lo) atomicAdd(&sh.hist[d - lo], 1u);
                 }
@@ -908,7 +957,8 @@ __device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
         above = block_sum_u<kTopkWaves>(above, sh.red);
         if (first) {
             support = block_sum_u<kTopkWaves>(support, sh.red);
-            if (support <= need) return -INFINITY;  // every supported token stays
+            if (TRACK_MAX) maxcode = block_max_u<kTopkWaves>(mx, sh.red);
+            if (support <= need) return TopkResult{-INFINITY, 0u, maxcode, false};  // every token stays
             first = false;
         }
         if (above >= need) {  // the K-th largest lies above the window
@@ -918,13 +968,15 @@ __device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
         }
         if (topk_pick(sh, kTopkWindow, lo, need - above, digit, rank)) {
             found = true;
+            lo_found = lo;
+            above_found = above;
             break;
         }
         if (lo == 0u) break;  // cannot happen: the row holds more than K
         hi = lo - 1u;         // the K-th largest lies below the window
         span = kTopkWindow;
     }
-    if (!found) return -INFINITY;
+    if (!found) return TopkResult{-INFINITY, 0u, maxcode, false};
 
     uint32_t code;
     if (sizeof(ET) == 2) {
@@ -954,14 +1006,14 @@ __device__ float select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
         }
         code = prefix;
     }
-    return float_of_code(code);
+    return TopkResult{float_of_code(code), lo_found, maxcode, sizeof(ET) == 2 && above_found == 0u};
 }
 
 // Suffix sums of the per-bin masses (bin i = digit lo + i, nbins of them):
 // finds the bin where the mass counted from the top first reaches `target`.
 // Returns false when the histogram holds less; `before` receives the mass
 // above the found bin.  All threads call it.
-__device__ bool topp_pick(TopkShared &sh, int nbins, uint32_t lo, double target, uint32_t &digit,
+__device__ bool topp_pick(ToppShared &sh, int nbins, uint32_t lo, double target, uint32_t &digit,
                           double &before, bool clamp) {
     const int tid = threadIdx.x;
     const int per = nbins / kTopkThreads;  // 4 or 1
@@ -1016,27 +1068,33 @@ __device__ bool topp_pick(TopkShared &sh, int nbins, uint32_t lo, double target,
 // 2^((l - M) log2(e) / T) with M the row's largest kept logit, in fp64 from
 // the argument on (a cut deep in a long tail steps by masses far below fp32
 // rounding).  *flag is set when the mass at the cut, or just above it, lies
-// within the boundary threshold of top_p.
+// within the boundary threshold of top_p.  `known_max` (with have_max) is the
+// row's largest allowed finite code when top-k already found it, which saves
+// a pass over the row.
 template <typename ET, bool ALIGNED, bool MASKED>
-__device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, float tau_k,
-                              float top_p, float T, uint32_t *flag) {
+__device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, ToppShared &sh, float tau_k,
+                              uint32_t known_max, bool have_max, float top_p, float T, uint32_t *flag) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int64_t kStep = int64_t(kTopkThreads) * P;
+    constexpr bool kBf16 = sizeof(ET) == 2;
+    constexpr int kPer = kTopkWindow / kTopkThreads;
     const int tid = threadIdx.x;
     const int64_t V = r.V;
     // the largest kept logit
-    uint32_t mcode = 0;
-    for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
-        float v[kTopkUnroll][P];
+    uint32_t mcode = known_max;
+    if (!have_max) {
+        for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
+            float v[kTopkUnroll][P];
 #pragma unroll
-        for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
+            for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
 #pragma unroll
-        for (int u = 0; u < kTopkUnroll; ++u)
+            for (int u = 0; u < kTopkUnroll; ++u)
 #pragma unroll
-            for (int e = 0; e < P; ++e)
-                if (v[u][e] == v[u][e] && !(v[u][e] < tau_k)) mcode = max(mcode, ordered_code(v[u][e]));
+                for (int e = 0; e < P; ++e)
+                    if (v[u][e] == v[u][e] && !(v[u][e] < tau_k)) mcode = max(mcode, ordered_code(v[u][e]));
+        }
+        mcode = block_max_u<kTopkWaves>(mcode, sh.red);
     }
-    mcode = block_max_u<kTopkWaves>(mcode, sh.red);
     *flag = 0u;
     if (mcode == 0u) return tau_k;  // nothing kept: the row is reported empty
     const float M = float_of_code(mcode);
@@ -1051,10 +1109,14 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
     uint32_t lo_found = 0;
     bool found = false;
     // The first pass sums the whole kept mass; each further pass moves the
-    // window down, so at most 65536 / kTopkWindow + 1 passes run.
+    // window down, so at most 65536 / kTopkWindow + 1 passes run.  bf16 bins
+    // hold one value each: they are counted and priced once per bin.
     for (int pass = 0; pass < 0x10000 / kTopkWindow + 2; ++pass) {
         const uint32_t lo = hi >= span - 1 ? hi - (span - 1) : 0u;
-        for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.mass[i] = 0.0;
+        for (int i = tid; i < kTopkWindow; i += kTopkThreads) {
+            if (kBf16) sh.hist[i] = 0u;
+            else sh.mass[i] = 0.0;
+        }
         lds_barrier();
         double below = 0.0, in_window = 0.0;
         for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
@@ -1069,16 +1131,33 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
                     if (x != x || x < tau_k) continue;
                     const uint32_t d = ordered_code(x) >> 16;
                     if (d > hi) continue;  // counted in an earlier pass
-                    const double w = exp2(fma(static_cast<double>(x), cd, -mcd));
                     if (d >= lo) {
-                        atomicAdd(&sh.mass[d - lo], w);
-                        in_window += w;
-                    } else {
-                        below += w;
+                        if (kBf16) {
+                            atomicAdd(&sh.hist[d - lo], 1u);
+                        } else {
+                            const double w = exp2_precise_nonpos(fma(static_cast<double>(x), cd, -mcd));
+                            atomicAdd(&sh.mass[d - lo], w);
+                            in_window += w;
+                        }
+                    } else if (pass == 0) {  // below the window: only the total needs it
+                        below += exp2_precise_nonpos(fma(static_cast<double>(x), cd, -mcd));
                     }
                 }
         }
-        below = block_sum_d<kTopkWaves>(below, sh.red_d);
+        if (kBf16) {
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int bin = tid * kPer + i;
+                const uint32_t n = sh.hist[bin];
+                const double m = n ? static_cast<double>(n) *
+                                         exp2_precise_nonpos(fma(static_cast<double>(bf16_value_of_digit(lo + bin)), cd, -mcd))
+                                   : 0.0;
+                sh.mass[bin] = m;
+                in_window += m;
+            }
+        }
+        if (pass == 0) below = block_sum_d<kTopkWaves>(below, sh.red_d);
         in_window = block_sum_d<kTopkWaves>(in_window, sh.red_d);
         if (pass == 0) {
             total = below + in_window;
@@ -1119,7 +1198,7 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
                     if (x != x || x < tau_k) continue;
                     const uint32_t cc = ordered_code(x);
                     if ((cc >> (shift + 8)) == prefix)
-                        atomicAdd(&sh.mass[(cc >> shift) & 0xffu], exp2(fma(static_cast<double>(x), cd, -mcd)));
+                        atomicAdd(&sh.mass[(cc >> shift) & 0xffu], exp2_precise_nonpos(fma(static_cast<double>(x), cd, -mcd)));
                 }
             }
             lds_barrier();
@@ -1138,9 +1217,43 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared 
     return float_of_code(code);
 }
 
-template <typename ET, bool ALIGNED, bool MASKED>
+// The top-p cut of a bf16 row straight from the top-k histogram, when that
+// holds every kept element (TopkResult::window): bin masses are the counts
+// times the bin value's mass, so no pass over the row is needed.
+__device__ float top_p_in_window(ToppShared &sh, const TopkResult &tk, float top_p, float T, uint32_t *flag) {
+    constexpr int kPer = kTopkWindow / kTopkThreads;
+    const int tid = threadIdx.x;
+    const uint32_t tau_digit = ordered_code(tk.tau) >> 16;
+    const double cd = kLog2e / static_cast<double>(T);
+    const double mcd = static_cast<double>(float_of_code(tk.maxcode)) * cd;
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int bin = tid * kPer + i;
+        const uint32_t d = tk.lo + uint32_t(bin);
+        const uint32_t n = sh.hist[bin];
+        const double m = (n != 0u && d >= tau_digit)
+                             ? static_cast<double>(n) *
+                                   exp2_precise_nonpos(fma(static_cast<double>(bf16_value_of_digit(d)), cd, -mcd))
+                             : 0.0;
+        sh.mass[bin] = m;
+        acc += m;
+    }
+    const double total = block_sum_d<kTopkWaves>(acc, sh.red_d);
+    const double target = static_cast<double>(top_p) * total;
+    uint32_t digit = 0;
+    double before = 0.0;
+    *flag = 0u;
+    if (!topp_pick(sh, kTopkWindow, tk.lo, target, digit, before, false)) return tk.tau;  // cannot happen
+    const double at_cut = before + sh.mass[digit - tk.lo];
+    const double eps = kTopPFlagEps * total;
+    *flag = (fabs(at_cut - target) < eps || fabs(target - before) < eps) ? 1u : 0u;
+    return bf16_value_of_digit(digit);
+}
+
+template <typename ET, bool ALIGNED, bool MASKED, bool TOPP>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-    __shared__ TopkShared sh;
+    __shared__ typename std::conditional<TOPP, ToppShared, TopkShared>::type sh;
     const int row = blockIdx.x, tid = threadIdx.x;
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call
     int b, i, kb;
@@ -1148,8 +1261,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     row_owner(a.off, a.row_req, row, a.kp1, b, i, kb, d0);
     const float T = uniform_load(a.temperature + b);
     const int K = a.top_k ? uniform_load(a.top_k + b) : 0;
-    const float Pp = a.top_p ? uniform_load(a.top_p + b) : 0.0f;
-    const bool use_p = Pp > 0.0f && Pp < 1.0f;
+    const float Pp = TOPP ? uniform_load(a.top_p + b) : 0.0f;
+    const bool use_p = TOPP && Pp > 0.0f && Pp < 1.0f;
     if (!(T > 0.0f && T <= FLT_MAX) || (K <= 0 && !use_p)) {
         if (tid == 0) {
             a.tau[row] = -INFINITY;
@@ -1164,9 +1277,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     r.rm = buffer_of(MASKED ? static_cast<const void *>(r.mrow) : static_cast<const void *>(r.rowp),
                      MASKED ? uint32_t(a.W) * 4u : 0u);
     r.V = a.V;
-    float tau = K > 0 ? select_top_k(r, sh, K) : -INFINITY;
+    TopkResult tk{-INFINITY, 0u, 0u, false};
+    if (K > 0) tk = select_top_k<ET, ALIGNED, MASKED, TOPP>(r, sh, K);
+    float tau = tk.tau;
     uint32_t flag = 0u;
-    if (use_p) tau = select_top_p(r, sh, tau, Pp, T, &flag);
+    if constexpr (TOPP) {
+        if (use_p)
+            tau = tk.window ? top_p_in_window(sh, tk, Pp, T, &flag)
+                            : select_top_p(r, sh, tk.tau, tk.maxcode, K > 0, Pp, T, &flag);
+    }
     if (tid == 0) {
         a.tau[row] = tau;
         a.tau_flag[row] = flag;
@@ -2067,10 +2186,16 @@ DenseFn pick_dense_draw(bool aligned) {
     return aligned ? dense_draw_kernel<ET, true> : dense_draw_kernel<ET, false>;
 }
 
+template <typename ET, bool TOPP>
+TopkFn pick_topk_p(bool aligned, bool masked) {
+    if (aligned) return masked ? topk_kernel<ET, true, true, TOPP> : topk_kernel<ET, true, false, TOPP>;
+    return masked ? topk_kernel<ET, false, true, TOPP> : topk_kernel<ET, false, false, TOPP>;
+}
+
+// Kernels without top-p leave its masses and fp64 registers out.
 template <typename ET>
-TopkFn pick_topk(bool aligned, bool masked) {
-    if (aligned) return masked ? topk_kernel<ET, true, true> : topk_kernel<ET, true, false>;
-    return masked ? topk_kernel<ET, false, true> : topk_kernel<ET, false, false>;
+TopkFn pick_topk(bool aligned, bool masked, bool topp) {
+    return topp ? pick_topk_p<ET, true>(aligned, masked) : pick_topk_p<ET, false>(aligned, masked);
 }
 
 template <typename ET>
@@ -2284,7 +2409,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         ta.kp1 = k + 1;
         ta.V = V;
         ta.W = L.W;
-        const TopkFn k0 = bf16 ? pick_topk<uint16_t>(aligned, masked) : pick_topk<float>(aligned, masked);
+        const bool topp = p->top_p != nullptr;
+        const TopkFn k0 = bf16 ? pick_topk<uint16_t>(aligned, masked, topp) : pick_topk<float>(aligned, masked, topp);
         hipLaunchKernelGGL(k0, dim3(static_cast<unsigned>(L.rows)), dim3(kTopkThreads), 0, stream, ta);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }

@@ -232,6 +232,26 @@ def test_top_p_ties_and_extremes():
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+def test_top_p_after_top_k_paths():
+    """bf16 rows whose top-k histogram holds every kept token (the cut comes
+    from it), rows whose largest values lie above that histogram's window
+    (the cut takes passes over the row), and rows where top-k keeps all."""
+    announce("top-p after top-k: histogram and pass paths")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8)
+    B, k, V = 9, 2, 40000
+    lg = torch.randn((B, k + 1, V), generator=g, device=DEV) * 2.0
+    lg[3:6, :, 20000:] += 60.0                       # far above the first 16 KB of the row
+    x = torch.randint(0, V, (B, k), generator=g, device=DEV).to(torch.int32)
+    for dtype in (torch.bfloat16, torch.float32):
+        wl = {"name": "custom", "logits": lg.to(dtype).contiguous(), "draft_token_ids": x,
+              "draft_probs": None, "bitmask": None, "temperature": torch.full((B,), 0.9, device=DEV),
+              "top_k": torch.tensor([50, 700, 5000] * 3, dtype=torch.int32, device=DEV),
+              "top_p": torch.tensor([0.5, 0.9, 0.99] * 3, device=DEV), "seed": 78}
+        wl["top_k"][6:] = V + 5                      # keeps every token
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
 def test_long_k_with_top_p_scaled():
     announce("long_k B=8 with top-k 50 and top-p 0.9")
     wl = make_workload("long_k", device=DEV, batch=8)
