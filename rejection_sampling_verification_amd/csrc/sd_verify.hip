@@ -1365,7 +1365,7 @@ struct FinalShared {
 };
 
 // Gumbel keys are compared in fp32 relative to a per-row constant, where
-// they stay within about 2e-6 of their exact values; packed with their index
+// they stay within 3e-6 of their exact values; packed with their index
 // (wave.h) one 64-bit maximum finds the winner, lowest index on ties, and a
 // ballot finds whether another key lies within the near-tie threshold.
 constexpr float kTieEps = static_cast<float>(kGumbelFlagEps);
