@@ -10,7 +10,8 @@ A 128-bit counter (four 32-bit words) and a 64-bit key (two words) map to four
 32-bit multipliers, keeping both halves of each 64-bit product, and mixes the
 high halves with the other two words and the round key; between rounds the key
 is advanced by two Weyl increments.  The pages do not name a generator: that it
-is Philox, and the counter layout below, are readings of this build.
+is Philox, and the counter layout below, are readings where the pages are
+silent.
 
 Counter layout (word0, word1, word2, word3) of each stream, key = (seed low
 32 bits, seed high 32 bits):
