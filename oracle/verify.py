@@ -32,8 +32,9 @@ The method (pages cited by title and section):
    randomness).
 7. Counters R, I, D = R - I, A (fanout, "Name the three counters").
 
-Readings where the pages are silent (each listed in the design notes): the RNG streams of ``oracle.philox``; sampling by two-level Gumbel-max
-over blocks of ``BLOCK`` tokens; lowest index wins every tie; a token with
+Readings where the pages are silent (each listed in the design notes): the
+RNG streams of ``oracle.philox``; sampling by two-level Gumbel-max over blocks
+of ``BLOCK`` tokens; lowest index wins every tie; a token with
 p = 0 is rejected, q = 0 with p > 0 accepts; I counts drafts whose own mask bit
 is 0; top-k keeps every allowed finite token >= the k-th largest allowed
 logit, counted with multiplicity, at every position of a sampling request;
