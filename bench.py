@@ -182,6 +182,98 @@ def cpu_baseline(wl, n_requests, min_seconds=10.0):
             "host_affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__}
 
 
+POOL_KEYS = ("logits", "draft_token_ids", "draft_probs", "bitmask", "temperature", "top_k", "top_p")
+
+
+def cpu_pool_child(folder, cores, min_seconds):
+    """Runs in a fresh interpreter that never touches the GPU: the oracle over
+    the saved workload, requests split across `cores` worker processes, whole
+    passes repeated until min_seconds have passed.  Prints one JSON line."""
+    import multiprocessing as mp
+
+    import numpy as np
+    meta = json.load(open(os.path.join(folder, "meta.json")))
+    B = meta["B"]
+    chunks = [list(range(B))[w::cores] for w in range(cores)]
+    chunks = [c for c in chunks if c]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    passes = 0
+    with ctx.Pool(len(chunks), initializer=_pool_init, initargs=(folder, meta)) as pool:
+        while True:
+            pool.map(_pool_work, chunks)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    print(json.dumps({"passes": passes, "seconds": dt, "workers": len(chunks), "requests": B,
+                      "positions_per_pass": meta["positions"], "numpy": np.__version__}), flush=True)
+
+
+_POOL = {}
+
+
+def _pool_init(folder, meta):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+    _POOL["meta"] = meta
+    _POOL["arrays"] = {key: (np.load(os.path.join(folder, key + ".npy"), mmap_mode="r")
+                             if os.path.exists(os.path.join(folder, key + ".npy")) else None)
+                       for key in POOL_KEYS}
+
+
+def _pool_work(reqs):
+    import numpy as np
+
+    import oracle
+    a, meta = _POOL["arrays"], _POOL["meta"]
+    pick = lambda v: None if v is None else np.asarray(v[reqs])
+    oracle.sd_verify(pick(a["logits"]), pick(a["draft_token_ids"]), pick(a["draft_probs"]),
+                     pick(a["bitmask"]), pick(a["temperature"]), seed=meta["seed"], top_k=pick(a["top_k"]),
+                     request_ids=reqs, top_p=pick(a["top_p"]))
+    return len(reqs)
+
+
+def cpu_baseline_all_cores(wl, min_seconds=10.0):
+    """The same oracle over the whole workload on every host core the process
+    may use (at most 16): requests split across worker processes started in a
+    child interpreter that never initialises the GPU.  Returns None when the
+    leg cannot run."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
+    from workloads import to_numpy
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    host = to_numpy(wl)
+    folder = tempfile.mkdtemp(prefix="sdv_cpu_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        for key in POOL_KEYS:
+            if host.get(key) is not None:
+                np.save(os.path.join(folder, key + ".npy"), np.ascontiguousarray(host[key]))
+        B, k = host["draft_token_ids"].shape
+        with open(os.path.join(folder, "meta.json"), "w") as f:
+            json.dump({"B": int(B), "seed": int(wl["seed"]), "positions": int(B * k)}, f)
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-pool-child", folder,
+                              str(cores), str(min_seconds)], capture_output=True, text=True, timeout=180)
+        if res.returncode != 0:
+            print(f"[bench] all-core CPU leg failed: {res.stderr[-400:]}", file=sys.stderr, flush=True)
+            return None
+        r = json.loads(res.stdout.strip().splitlines()[-1])
+    except (OSError, ValueError, subprocess.SubprocessError) as e:
+        print(f"[bench] all-core CPU leg failed: {e}", file=sys.stderr, flush=True)
+        return None
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    return {"value": r["passes"] * r["positions_per_pass"] / r["seconds"], "unit": "verified draft positions/s",
+            "cores": r["workers"], "kind": "oracle",
+            "sample": f"{r['passes']} passes over the whole workload ({r['requests']} requests), float64 "
+                      f"NumPy, one worker process per core, {r['seconds']:.1f} s",
+            "numpy": r["numpy"]}
+
+
 def cpu_baseline_ragged(wl, min_seconds=10.0):
     """The ragged oracle on one host thread over the whole workload, repeated
     until at least min_seconds have passed."""
@@ -348,10 +440,16 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="CSV")
     ap.add_argument("--pmc-kernel", default="row_stats", choices=["row_stats", "ngram_match"])
+    ap.add_argument("--cpu-pool-child", nargs=3, metavar=("DIR", "CORES", "SECONDS"),
+                    help=argparse.SUPPRESS)
     ap.add_argument("--top-p", type=float, default=None,
                     help="apply this top-p to every request of the workload")
     args = ap.parse_args()
 
+    if args.cpu_pool_child:
+        folder, cores, secs = args.cpu_pool_child
+        cpu_pool_child(folder, int(cores), float(secs))
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, kernel=args.pmc_kernel)
         return
@@ -463,10 +561,13 @@ def main():
     flags = [int(f) for f in r.flags.cpu().tolist()]
 
     ceiling = copy_ceiling_gbps()
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline_ragged(wl) if ragged else cpu_baseline(wl, args.cpu_requests or B)
+        if not ragged:
+            print("[bench] timing the CPU oracle on every core", file=sys.stderr, flush=True)
+            cpu_all = cpu_baseline_all_cores(wl)
 
     out = {
         "metric": METRIC,
@@ -499,6 +600,7 @@ def main():
                      "p10_us": k1_ms[len(k1_ms) // 10] * 1e3, "p90_us": k1_ms[(9 * len(k1_ms)) // 10] * 1e3,
                      "bytes_per_launch": k1_bytes, "source_digest": digest},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "flags": {"accept_boundary": flags[0], "gumbel_near_tie": flags[1], "top_p_boundary": flags[2]},
         "gpu_ms_timed_region": gpu_ms,
         "wall_s_timed_region": wall,
