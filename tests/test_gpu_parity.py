@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from parity import announce, assert_parity, run_gpu, run_oracle
 from workloads import make_workload, pack_bitmask
 
@@ -250,6 +251,22 @@ def test_top_p_after_top_k_paths():
               "top_p": torch.tensor([0.5, 0.9, 0.99] * 3, device=DEV), "seed": 78}
         wl["top_k"][6:] = V + 5                      # keeps every token
         assert_parity(run_gpu(wl), run_oracle(wl))
+
+
+def test_top_p_extreme_temperatures_masks_and_errors():
+    """Top-p at temperatures that push masses to underflow or make them all
+    alike, on masked rows, beside greedy requests and requests in error."""
+    announce("top-p extremes")
+    for dtype in (torch.bfloat16, torch.float32):
+        wl = _custom(12, 3, 3000, dtype=dtype, dense=False, masked=True, density=0.05, seed=41,
+                     top_k=(0, 0, 7))
+        wl["temperature"] = torch.tensor([1e-3, 0.01, 1.0, 30.0, 1e4, 0.0, 0.7, 1e-3, 5.0, 0.0, 2.0, -1.0],
+                                         device=DEV)
+        wl["top_p"] = torch.tensor([0.9, 0.5, 0.3, 0.9, 0.99, 0.9, 1e-7, 0.999, 0.6, 0.0, 0.95, 0.9],
+                                   device=DEV)
+        gpu, orc = run_gpu(wl), run_oracle(wl)
+        assert_parity(gpu, orc)
+        assert gpu["status"] & oracle.verify.ST_TEMPERATURE
 
 
 def test_long_k_with_top_p_scaled():
