@@ -1375,52 +1375,78 @@ __device__ __forceinline__ bool near_tie(float key, int idx, uint64_t best) {
 }
 
 // Residual masses W_c = sum_j max(p_j - q_j, 0) of one row for dense q, with
-// p_j = 2^(l_j c - M) / S in fp32.  One wave per block; clamped loads.
+// p_j = 2^(l_j c - M) / S in fp32.  One wave per block, two blocks of a wave
+// in flight together; clamped loads.
 template <typename ET, bool ALIGNED>
-__device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const float *qrow, int V,
-                                   int C, float c, float M, double S, float tau, double *Wout) {
-    constexpr int P = Logit<ET>::kPer16;
-    constexpr int G = kBlock / (kWave * P);
-    const int lane = threadIdx.x & (kWave - 1);
-    const float invS = static_cast<float>(1.0 / S);
-    const uint8_t *mb = reinterpret_cast<const uint8_t *>(mrow);
-    for (int blk = wave_id(); blk < C; blk += kFinalWaves) {
-        float acc = 0.0f;
+struct DenseSlab {  // one wave's share of a block: P logits and P q values per group
+    static constexpr int P = Logit<ET>::kPer16;
+    static constexpr int G = kBlock / (kWave * P);
+    float lv[G][P], qv[G][P];
+
+    __device__ __forceinline__ void load(const ET *rowp, const float *qrow, int V, int blk, int lane) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
-            float lv[P], qv[P];
             if (ALIGNED) {
                 const int64_t tc = tok < V ? tok : int64_t(V - P);
-                Logit<ET>::unpack(*reinterpret_cast<const uint4 *>(rowp + tc), lv);
+                Logit<ET>::unpack(*reinterpret_cast<const uint4 *>(rowp + tc), lv[g]);
 #pragma unroll
                 for (int h = 0; h < P / 4; ++h) {
                     const float4 f = *reinterpret_cast<const float4 *>(qrow + tc + 4 * h);
-                    qv[4 * h] = f.x;
-                    qv[4 * h + 1] = f.y;
-                    qv[4 * h + 2] = f.z;
-                    qv[4 * h + 3] = f.w;
+                    qv[g][4 * h] = f.x;
+                    qv[g][4 * h + 1] = f.y;
+                    qv[g][4 * h + 2] = f.z;
+                    qv[g][4 * h + 3] = f.w;
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < P; ++e) {
                     const int64_t tc = tok + e < V ? tok + e : int64_t(V - 1);
-                    lv[e] = Logit<ET>::to_float(rowp[tc]);
-                    qv[e] = qrow[tc];
+                    lv[g][e] = Logit<ET>::to_float(rowp[tc]);
+                    qv[g][e] = qrow[tc];
                 }
             }
+        }
+    }
+
+    __device__ __forceinline__ double mass(const uint8_t *mb, int V, int blk, int lane, float c, float M,
+                                           float invS, float tau) const {
+        float acc = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t tok = int64_t(blk) * kBlock + (g * kWave + lane) * P;
 #pragma unroll
             for (int e = 0; e < P; ++e) {
                 const int64_t j = tok + e;
                 const int64_t jc = j < V ? j : int64_t(V - 1);
-                bool live = j < V && lv[e] > -INFINITY && !(lv[e] < tau);
-                if (mrow) live = live && ((mb[jc >> 3] >> (jc & 7)) & 1u);
-                const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[e], c, -M)) * invS : 0.0f;
-                acc += live ? fmaxf(p - qv[e], 0.0f) : 0.0f;
+                bool live = j < V && lv[g][e] > -INFINITY && !(lv[g][e] < tau);
+                if (mb) live = live && ((mb[jc >> 3] >> (jc & 7)) & 1u);
+                const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[g][e], c, -M)) * invS : 0.0f;
+                acc += live ? fmaxf(p - qv[g][e], 0.0f) : 0.0f;
             }
         }
-        const double w = wave_sum_d(static_cast<double>(acc));
-        if (lane == 0) Wout[blk] = w;
+        return wave_sum_d(static_cast<double>(acc));
+    }
+};
+
+template <typename ET, bool ALIGNED>
+__device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const float *qrow, int V,
+                                   int C, float c, float M, double S, float tau, double *Wout) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float invS = static_cast<float>(1.0 / S);
+    const uint8_t *mb = reinterpret_cast<const uint8_t *>(mrow);
+    for (int blk = wave_id(); blk < C; blk += 2 * kFinalWaves) {
+        const int blk2 = blk + kFinalWaves;
+        const bool two = blk2 < C;
+        DenseSlab<ET, ALIGNED> x, y;
+        x.load(rowp, qrow, V, blk, lane);
+        y.load(rowp, qrow, V, two ? blk2 : blk, lane);  // a repeat of blk is loaded but not summed
+        const double wx = x.mass(mb, V, blk, lane, c, M, invS, tau);
+        if (lane == 0) Wout[blk] = wx;
+        if (two) {
+            const double wy = y.mass(mb, V, blk2, lane, c, M, invS, tau);
+            if (lane == 0) Wout[blk2] = wy;
+        }
     }
 }
 
@@ -1455,16 +1481,30 @@ __device__ __forceinline__ void load4_masked(const ET *row, const uint32_t *mrow
     }
 }
 
+// ln x for positive x from the hardware base-2 logarithm of its fp32
+// mantissa in [0.5, 1), where that logarithm is accurate to about 1e-7
+// absolute: within about 1e-7 of ln x plus the rounding of x to fp32.
+// Arguments below the fp32 range give -inf.
+__device__ __forceinline__ double ln_of(double x) {
+    const float xf = static_cast<float>(x);
+    if (!(xf > 0.0f)) return -INFINITY;
+    const int e = __builtin_amdgcn_frexp_expf(xf);
+    const float m = __builtin_amdgcn_frexp_mantf(xf);
+    return (static_cast<double>(e) + static_cast<double>(__builtin_amdgcn_logf(m))) * kLn2;
+}
+
 // Level 2: the token of block cb of row n drawn under the weights of `mode`
 // (4 tokens per thread; values from the staged LDS copy when `staged`).  All
 // threads call it; returns (token, near-tie flag), token -1 when the block
-// holds no positive weight.
+// holds no positive weight.  wblk: the level-1 residual mass of block cb
+// (dense mode; 1 otherwise).
 template <typename ET, bool ALIGNED>
 __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_t row, int x, int cb,
-                       int mode, float c, double invT, const float *qrow, bool staged, int attempt) {
+                       int mode, float c, double invT, const float *qrow, bool staged, int attempt,
+                       double wblk = 1.0) {
     const int V = a.V;
     const int64_t j0 = int64_t(cb) * kBlock + threadIdx.x * 4;
-    float lv[4];
+    float lv[4], qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (staged) {
         const float4 f = *reinterpret_cast<const float4 *>(&sh.blockv[threadIdx.x * 4]);
         lv[0] = f.x;
@@ -1476,10 +1516,24 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_
                                   a.mask ? a.mask + row * a.W : nullptr, j0, V, lv);
         if (a.tau) apply_tau<4>(lv, a.tau[row]);
     }
+    if (mode == kModeDense) {  // in flight with the logits; lanes past V read (and drop) the last four
+        if (ALIGNED) {
+            const int64_t jc = j0 + 4 <= V ? j0 : int64_t(V) - 4;
+            const float4 f = *reinterpret_cast<const float4 *>(qrow + jc);
+            qv[0] = f.x;
+            qv[1] = f.y;
+            qv[2] = f.z;
+            qv[3] = f.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qv[e] = qrow[j0 + e < V ? j0 + e : int64_t(V - 1)];
+        }
+    }
     float g[4];
     draw_token_gumbels4(key_of(a.seed), b, n, static_cast<uint32_t>(j0), g);
     const float M = sh.M[n];
     const double S = sh.S[n];
+    const double invS = 1.0 / S, invW = 1.0 / wblk;
     const double lref = static_cast<double>(M) / static_cast<double>(c);  // about the row's max logit
     float keys[4];
     uint64_t best = 0, second = 0;
@@ -1489,10 +1543,14 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_
         keys[e] = -INFINITY;
         if (!(lv[e] > -INFINITY)) continue;  // masked, -inf, or past V
         if (mode == kModeDense) {
-            const double p = exp2(static_cast<double>(lv[e]) * c - static_cast<double>(M)) / S;
-            const double r = p - static_cast<double>(qrow[j]);
+            const double p = exp2_precise_nonpos(static_cast<double>(lv[e]) * c - static_cast<double>(M)) * invS;
+            const double r = p - static_cast<double>(qv[e]);
             if (!(r > 0.0)) continue;
-            keys[e] = static_cast<float>(log(r) + static_cast<double>(g[e]));
+            // Keys relative to the block's residual mass (one constant for the
+            // whole draw): a token that can win has ln(r / W) >= ln(1/2048) -
+            // 2.9 - 16.7 (W is at most 2048 times the largest r; Gumbel
+            // variates lie in [-2.9, 16.7]), so its key stays small.
+            keys[e] = static_cast<float>(ln_of(r * invW) + static_cast<double>(g[e]));
         } else {
             if (mode == kModeOneHot && j == x) continue;
             keys[e] = static_cast<float>((static_cast<double>(lv[e]) - lref) * invT + static_cast<double>(g[e]));
@@ -1688,7 +1746,10 @@ __device__ __forceinline__ void tally_call(const FinalArgs &a, int b, unsigned l
     }
 }
 
-template <typename ET, bool ALIGNED, bool DENSE>
+// DENSE: dense draft probabilities; SPLIT (with DENSE): the residual masses
+// of rejected rows are left to the grid-wide kernels, so this instantiation
+// carries no in-kernel residual pass and its registers.
+template <typename ET, bool ALIGNED, bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -1861,7 +1922,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             const float *qrow = (DENSE && n < k) ? a.q + (geo.draft0 + n) * V : nullptr;
             int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
-            if (DENSE && mode == kModeDense && a.split_dense) {
+            if (DENSE && SPLIT && mode == kModeDense) {
                 // left to the residual kernels; -1 stands in until they write y
                 if (tid == 0) {
                     DenseJob j;
@@ -1878,7 +1939,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 }
                 deferred = true;
             }
-            if (DENSE && mode == kModeDense && !a.split_dense) {
+            if (DENSE && !SPLIT && mode == kModeDense) {
                 const int64_t row = geo.row0 + n;
                 dense_block_masses<ET, ALIGNED>(
                     reinterpret_cast<const ET *>(a.logits) + row * V,
@@ -1919,7 +1980,8 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 }
                 const int2 r2 =
                     level2<ET, ALIGNED>(a, sh, b, n, geo.row0 + n, n < k ? sh.X[n] : -1, l1.c, mode, c,
-                                        invT, qrow, sh.staged_c == l1.c, attempt);
+                                        invT, qrow, sh.staged_c == l1.c, attempt,
+                                        (DENSE && !SPLIT && mode == kModeDense) ? sW[l1.c] : 1.0);
                 if (r2.x >= 0) {
                     y = r2.x;
                     fg = l1.flag + r2.y;
@@ -2088,7 +2150,7 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
             l1 = j.l1p;
         }
         const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, j.row, sh.X[n], l1.c, mode, j.c, invT, qrow,
-                                            false, attempt);
+                                            false, attempt, mode == kModeDense ? W[l1.c] : 1.0);
         if (r2.x >= 0) {
             y = r2.x;
             fg = l1.flag + r2.y;
@@ -2199,9 +2261,11 @@ TopkFn pick_topk(bool aligned, bool masked, bool topp) {
 }
 
 template <typename ET>
-FinalFn pick_final(bool aligned, bool dense) {
-    if (dense) return aligned ? finalize_kernel<ET, true, true> : finalize_kernel<ET, false, true>;
-    return aligned ? finalize_kernel<ET, true, false> : finalize_kernel<ET, false, false>;
+FinalFn pick_final(bool aligned, bool dense, bool split) {
+    if (dense && split)
+        return aligned ? finalize_kernel<ET, true, true, true> : finalize_kernel<ET, false, true, true>;
+    if (dense) return aligned ? finalize_kernel<ET, true, true, false> : finalize_kernel<ET, false, true, false>;
+    return aligned ? finalize_kernel<ET, true, false, false> : finalize_kernel<ET, false, false, false>;
 }
 
 struct Layout {
@@ -2386,8 +2450,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     const bool topk = thresholds;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
                          : pick_row_stats<float>(masked, aligned, topk);
-    FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr)
-                      : pick_final<float>(aligned, draft_probs != nullptr);
+    FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr, fa.split_dense != 0)
+                      : pick_final<float>(aligned, draft_probs != nullptr, fa.split_dense != 0);
 
     if (ragged) {
         hipLaunchKernelGGL(ragged_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, p->draft_offsets, B, k,
