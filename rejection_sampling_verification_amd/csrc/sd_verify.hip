@@ -256,6 +256,7 @@ struct RowStatsArgs {
     DraftRec *drec;           // [rows]
     unsigned long long *tally;  // counter tally, zeroed here, accumulated by finalize
     int ntally;                 // words of the tally
+    uint64_t *out_counters;     // the call's R, I, D, A: zeroed here, added to by finalize
     uint32_t *status;         // zeroed here when given
     uint32_t *dbg_flags;      // zeroed here when given
     const int32_t *off;       // ragged: [B + 1] draft offsets, or nullptr
@@ -351,6 +352,7 @@ __device__ __forceinline__ double key_of_mass(float mass, float mc, float g) {
 __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
     if (blockIdx.x != 0) return;
     for (int w = threadIdx.x; w < a.ntally; w += blockDim.x) a.tally[w * kTallyStride] = 0ull;
+    if (threadIdx.x < 4) a.out_counters[threadIdx.x] = 0ull;
     if (threadIdx.x == 0 && a.status) *a.status = 0u;
     if (threadIdx.x < 3 && a.dbg_flags) a.dbg_flags[threadIdx.x] = 0u;
 }
@@ -1322,7 +1324,7 @@ struct FinalArgs {
     int32_t *out_tokens;
     int32_t *out_num_accepted;
     uint64_t *out_counters;
-    unsigned long long *tally;  // nslot slot words, then the two call words
+    unsigned long long *tally;  // nslot slot words
     int nslot;
     double *dbg_lse;
     double *dbg_acc;
@@ -1695,18 +1697,17 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
 }
 
 // Counters of the call.  Every workgroup finishes at about the same time, so
-// one word hit by all of them would serialise their atomics; instead request
-// b adds to slot word b % nslot, and the request that completes a slot adds
-// the slot's sums to the two call words.  Each level packs the arrival count
-// with the sums into one 64-bit word, so the workgroup that completes a level
-// reads that level's totals in its own atomic's return value: no fence and
-// no ordering between different words is needed, and the integer sums do not
+// words hit by all of them would serialise their atomics; instead request b
+// adds to slot word b % nslot, and the request that completes a slot adds the
+// slot's sums to the four output counters (zeroed by the row-statistics
+// kernel) with atomics whose results nobody waits for.  A slot word packs the
+// arrival count with the sums, so the workgroup that completes a slot reads
+// the slot's totals in its own atomic's return value: no fence and no
+// ordering between different words is needed, and the integer sums do not
 // depend on the order of arrival.  A request in error adds only its arrival.
-//   slot word:   arrivals [0,9)  accepted [9,24)  outside grammar [24,39)  drafts [39,54)
-//   call word 0: slots [0,9)  accepted [9,31)  drafts [31,53)          -> writes R and A
-//   call word 1: slots [0,9)  outside grammar [9,31)  drafts [31,53)   -> writes I and D
-// Field widths hold B <= 65535 requests of at most 64 drafts, with at most
-// 256 slots of at most 256 requests.
+//   slot word: arrivals [0,9)  accepted [9,24)  outside grammar [24,39)  drafts [39,54)
+// Field widths hold at most 256 slots of at most 256 requests of at most 64
+// drafts.
 __device__ __forceinline__ unsigned long long tally_share(int accepted, int invalid, int drafts) {
     return 1ull | (static_cast<unsigned long long>(accepted) << 9) |
            (static_cast<unsigned long long>(invalid) << 24) |
@@ -1730,20 +1731,11 @@ __device__ __forceinline__ void tally_call(const FinalArgs &a, int b, unsigned l
     if (static_cast<int>(slot & 0x1ffull) != members) return;
     const unsigned long long acc = (slot >> 9) & 0x7fffull, inv = (slot >> 24) & 0x7fffull,
                              drafts = (slot >> 39) & 0x7fffull;
-    unsigned long long *call = a.tally + S * kTallyStride;
-    const unsigned long long w0 = 1ull | (acc << 9) | (drafts << 31);
-    const unsigned long long w1 = 1ull | (inv << 9) | (drafts << 31);
-    const unsigned long long t0 = atomicAdd(&call[0], w0) + w0;
-    const unsigned long long t1 = atomicAdd(&call[kTallyStride], w1) + w1;
-    if (static_cast<int>(t0 & 0x1ffull) == S) {
-        a.out_counters[0] = (t0 >> 31) & 0x3fffffull;
-        a.out_counters[3] = (t0 >> 9) & 0x3fffffull;
-    }
-    if (static_cast<int>(t1 & 0x1ffull) == S) {
-        const uint64_t R = (t1 >> 31) & 0x3fffffull, I = (t1 >> 9) & 0x3fffffull;
-        a.out_counters[1] = I;
-        a.out_counters[2] = R - I;
-    }
+    unsigned long long *out = reinterpret_cast<unsigned long long *>(a.out_counters);
+    atomicAdd(&out[0], drafts);        // R
+    atomicAdd(&out[1], inv);           // I
+    atomicAdd(&out[2], drafts - inv);  // D
+    atomicAdd(&out[3], acc);           // A
 }
 
 // DENSE: dense draft probabilities; SPLIT (with DENSE): the residual masses
@@ -2308,7 +2300,7 @@ inline Layout layout_of(const sd_params *p) {
     L.off_offok = L.off_rowreq + align256(p->draft_offsets ? size_t(L.rows) * sizeof(int32_t) : 0);
     L.off_tally = L.off_offok + 256;
     L.nslot = tally_slots(p->batch);
-    L.total = L.off_tally + align256(size_t(L.nslot + 2) * kTallyStride * sizeof(uint64_t));
+    L.total = L.off_tally + align256(size_t(L.nslot) * kTallyStride * sizeof(uint64_t));
     return L;
 }
 
@@ -2394,7 +2386,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.bstats = reinterpret_cast<BlockStat *>(ws + L.off_bstats);
     ra.drec = reinterpret_cast<DraftRec *>(ws + L.off_drec);
     ra.tally = reinterpret_cast<unsigned long long *>(ws + L.off_tally);
-    ra.ntally = L.nslot + 2;
+    ra.ntally = L.nslot;
+    ra.out_counters = out_counters;
     ra.status = p->status;
     ra.dbg_flags = p->dbg_flags;
     ra.ntasks = L.rows * L.nchunk;
