@@ -90,8 +90,10 @@ typedef struct {
      *   dbg_request_flags [B]     per request: boundary accept draws
      *                             (|u - a| < 1e-6) in bits 0..11, Gumbel near
      *                             ties (top-2 keys closer than 1e-5) in bits
-     *                             12..23, top-p boundary rows (the cut within
-     *                             1e-6 of top_p in mass) in bits 24..31
+     *                             12..23, top-p boundary rows (the mass at
+     *                             the cut, or just above it, within 1e-9 of
+     *                             top_p, relative to the row's kept mass) in
+     *                             bits 24..31
      *   dbg_flags [3]             totals of the three flag kinds over the call */
     double *dbg_row_lse;
     double *dbg_accept_prob;

@@ -3,7 +3,9 @@
     python -m rejection_sampling_verification_amd.build
 
 compiles csrc/sd_verify.hip (the verifier) and csrc/sd_ngram.hip (the n-gram
-proposer) into libsdverify.so next to this file.
+proposer) into libsdverify.so next to this file, then the test suite's
+C-ABI caller tests/c_abi_check (plain C++ against include/sd_verify.h and the
+library, no Python).
 """
 import os
 import shutil
@@ -14,6 +16,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 SOURCES = [os.path.join(PKG_DIR, "csrc", name) for name in ("sd_verify.hip", "sd_ngram.hip")]
 LIBRARY = os.path.join(PKG_DIR, "libsdverify.so")
+C_CHECK_SOURCE = os.path.join(ROOT, "tests", "c_abi_check.cpp")
+C_CHECK = os.path.join(ROOT, "tests", "c_abi_check")
 ARCH = "gfx950"
 
 
@@ -34,6 +38,14 @@ def compile_command(output=LIBRARY, extra=()):
     ]
 
 
+def c_check_command(output=C_CHECK):
+    return [
+        hipcc_path(), "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), C_CHECK_SOURCE,
+        "-L", PKG_DIR, "-lsdverify", "-Wl,-rpath,$ORIGIN/../rejection_sampling_verification_amd",
+        "-o", output,
+    ]
+
+
 def build_library(verbose=False):
     tmp = LIBRARY + ".tmp"
     cmd = compile_command(tmp)
@@ -43,6 +55,14 @@ def build_library(verbose=False):
     os.replace(tmp, LIBRARY)
     if verbose:
         print("built", LIBRARY)
+    if os.path.exists(C_CHECK_SOURCE):
+        cmd = c_check_command(C_CHECK + ".tmp")
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+        os.replace(C_CHECK + ".tmp", C_CHECK)
+        if verbose:
+            print("built", C_CHECK)
     return LIBRARY
 
 
