@@ -448,15 +448,77 @@ struct SweepBlock {
     int64_t dpos; // the row's draft index (draft rows)
 };
 
-__device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, int64_t gb) {
+// Where a block of the sweep lies: its (row, block) and, for calls with k
+// drafts per request, the row's request and position.  A wave's sweep steps
+// by a fixed number of blocks, so the cursor advances by precomputed
+// quotients and remainders: dividing a 64-bit block index for every block
+// costs more scalar instructions than the block's reduction leaves room for.
+struct SweepCursor {
+    int64_t gb;
+    int row, blk, b, i;
+};
+
+struct SweepStep {
+    int64_t stride;  // blocks between a wave's consecutive blocks
+    int drow, dblk;  // stride = drow * C + dblk
+    int db, di;      // drow = db * kp1 + di
+};
+
+__device__ __forceinline__ SweepCursor cursor_at(const RowStatsArgs &a, int64_t gb) {
+    SweepCursor c;
+    c.gb = gb;
+    c.row = static_cast<int>(gb / a.C);
+    c.blk = static_cast<int>(gb - int64_t(c.row) * a.C);
+    c.b = c.row / a.kp1;  // uniform layout (ragged calls look their rows up)
+    c.i = c.row - c.b * a.kp1;
+    return c;
+}
+
+__device__ __forceinline__ SweepStep step_of(const RowStatsArgs &a, int64_t stride) {
+    SweepStep s;
+    s.stride = stride;
+    s.drow = static_cast<int>(stride / a.C);
+    s.dblk = static_cast<int>(stride - int64_t(s.drow) * a.C);
+    s.db = s.drow / a.kp1;
+    s.di = s.drow - s.db * a.kp1;
+    return s;
+}
+
+// The cursor one step on: dblk < C and di < kp1, so one carry each suffices.
+__device__ __forceinline__ SweepCursor advance(const RowStatsArgs &a, SweepCursor c, const SweepStep &s) {
+    c.gb += s.stride;
+    c.blk += s.dblk;
+    int carry = 0;
+    if (c.blk >= a.C) {
+        c.blk -= a.C;
+        carry = 1;
+    }
+    c.row += s.drow + carry;
+    c.i += s.di + carry;
+    c.b += s.db;
+    if (c.i >= a.kp1) {
+        c.i -= a.kp1;
+        c.b += 1;
+    }
+    return c;
+}
+
+__device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const SweepCursor &c) {
     SweepBlock s;
-    s.gb = gb;
-    s.row = static_cast<int>(gb / a.C);
-    s.blk = static_cast<int>(gb - int64_t(s.row) * a.C);
+    s.gb = c.gb;
+    s.row = c.row;
+    s.blk = c.blk;
     s.full = int64_t(s.blk + 1) * kBlock <= a.V;
     int kb;
     int64_t d0;
-    row_owner(a.off, a.row_req, s.row, a.kp1, s.b, s.i, kb, d0);
+    if (a.off) {
+        row_owner(a.off, a.row_req, s.row, a.kp1, s.b, s.i, kb, d0);
+    } else {
+        s.b = c.b;
+        s.i = c.i;
+        kb = a.kp1 - 1;
+        d0 = int64_t(c.b) * kb;
+    }
     s.dpos = d0 + s.i;
     const float T = uniform_load(a.temperature + s.b);
     s.greedy = (T == 0.0f);
@@ -596,12 +658,14 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
     int count = 0;
     uint4 ra[G], rb[G];
     uint32_t ma[G], mb[G];
-    SweepBlock sa = sweep_block(a, g0);
+    const SweepStep step = step_of(a, stride);
+    SweepCursor ca = cursor_at(a, g0), cb;
+    SweepBlock sa = sweep_block(a, ca);
     issue_block<ET, MASKED>(a, sa, lane, ra, ma);
     for (;;) {
-        const int64_t g1 = sa.gb + stride;
-        const bool more1 = g1 < a.nblk;
-        const SweepBlock sb = sweep_block(a, more1 ? g1 : sa.gb);
+        const bool more1 = ca.gb + stride < a.nblk;
+        cb = more1 ? advance(a, ca, step) : ca;
+        const SweepBlock sb = sweep_block(a, cb);
         issue_block<ET, MASKED>(a, sb, lane, rb, mb, more1);
         if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
         if (count == kWave) {
@@ -610,9 +674,9 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
             count = 0;
         }
         if (!more1) break;
-        const int64_t g2 = sb.gb + stride;
-        const bool more2 = g2 < a.nblk;
-        sa = sweep_block(a, more2 ? g2 : sb.gb);
+        const bool more2 = cb.gb + stride < a.nblk;
+        ca = more2 ? advance(a, cb, step) : cb;
+        sa = sweep_block(a, ca);
         issue_block<ET, MASKED>(a, sa, lane, ra, ma, more2);
         if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
         if (count == kWave) {
