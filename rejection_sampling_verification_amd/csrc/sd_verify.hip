@@ -1426,14 +1426,15 @@ struct FinalShared {
     double red_d[kFinalWaves];
     uint64_t red_u[kFinalWaves];
     uint32_t red_b[kFinalWaves];
-    uint64_t red2[2][2 * kFinalWaves];  // top-2 scratch of level-2 draws, by attempt
+    uint4 race[2][kFinalWaves];  // per-wave level-2 results (best, index, runner-up), by attempt
     float blockv[kBlock];       // that block's logits, -inf where masked or past V
 };
 
 // Gumbel keys are compared in fp32 relative to a per-row constant, where
-// they stay within 3e-6 of their exact values; packed with their index
-// (wave.h) one 64-bit maximum finds the winner, lowest index on ties, and a
-// ballot finds whether another key lies within the near-tie threshold.
+// they stay within 3e-6 of their exact values; as order-preserving codes
+// (wave.h) a maximum finds the winner, lowest index on ties, and a second
+// pass or the runner-up finds whether another key lies within the near-tie
+// threshold.
 constexpr float kTieEps = static_cast<float>(kGumbelFlagEps);
 
 __device__ __forceinline__ bool near_tie(float key, int idx, uint64_t best) {
@@ -1551,6 +1552,55 @@ __device__ __forceinline__ void load4_masked(const ET *row, const uint32_t *mrow
 // mantissa in [0.5, 1), where that logarithm is accurate to about 1e-7
 // absolute: within about 1e-7 of ln x plus the rounding of x to fp32.
 // Arguments below the fp32 range give -inf.
+// The winner of a level-2 race over a workgroup of NW waves, and whether it
+// is a near tie.  Thread t holds the codes (ordered_code of the key, 0 = no
+// candidate) of indices base + 4t .. base + 4t + 3, so indices ascend with
+// the thread and the slot.  Each wave finds its largest code (the lowest
+// index on equal codes) and the largest code among its other candidates;
+// the waves' triples meet in `scratch` after one barrier (consecutive races
+// use different scratch, so none is needed between them).  Returns (index,
+// near-tie flag), index -1 when no thread has a candidate.
+template <int NW>
+__device__ __forceinline__ int2 race_winner(const uint32_t (&code)[4], int base, uint4 *scratch) {
+    uint32_t lm = code[0];
+    int le = 0;
+#pragma unroll
+    for (int e = 1; e < 4; ++e)
+        if (code[e] > lm) {
+            lm = code[e];
+            le = e;
+        }
+    uint32_t lrest = 0u;  // the lane's largest code besides its winner
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e != le) lrest = max(lrest, code[e]);
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wm = wave_max_u(lm);
+    const uint64_t holders = __ballot(wm != 0u && lm == wm);
+    const int wl = holders ? static_cast<int>(__builtin_ctzll(holders)) : 0;  // lowest lane, lowest index
+    const uint32_t ws = wave_max_u(lane == wl ? lrest : lm);
+    const int wi = __builtin_amdgcn_readlane(base + 4 * static_cast<int>(threadIdx.x) + le, wl);
+    if (lane == 0) scratch[threadIdx.x >> 6] = make_uint4(wm, static_cast<uint32_t>(wi), ws, 0u);
+    lds_barrier();
+    uint32_t bm = 0u, sm = 0u;
+    int bi = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {  // waves hold ascending index ranges: strict > keeps the lowest
+        const uint4 r = scratch[w];
+        if (r.x > bm) {
+            sm = max(sm, bm);
+            bm = r.x;
+            bi = static_cast<int>(r.y);
+        } else {
+            sm = max(sm, r.x);
+        }
+        sm = max(sm, r.z);
+    }
+    if (bm == 0u) return make_int2(-1, 0);
+    const bool tie = sm != 0u && float_of_code(sm) >= float_of_code(bm) - kTieEps;
+    return make_int2(bi, tie ? 1 : 0);
+}
+
 __device__ __forceinline__ double ln_of(double x) {
     const float xf = static_cast<float>(x);
     if (!(xf > 0.0f)) return -INFINITY;
@@ -1601,12 +1651,11 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_
     const double S = sh.S[n];
     const double invS = 1.0 / S, invW = 1.0 / wblk;
     const double lref = static_cast<double>(M) / static_cast<double>(c);  // about the row's max logit
-    float keys[4];
-    uint64_t best = 0, second = 0;
+    uint32_t code[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t j = j0 + e;
-        keys[e] = -INFINITY;
+        code[e] = 0u;  // no candidate
         if (!(lv[e] > -INFINITY)) continue;  // masked, -inf, or past V
         if (mode == kModeDense) {
             const double p = exp2_precise_nonpos(static_cast<double>(lv[e]) * c - static_cast<double>(M)) * invS;
@@ -1616,20 +1665,15 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_
             // whole draw): a token that can win has ln(r / W) >= ln(1/2048) -
             // 2.9 - 16.7 (W is at most 2048 times the largest r; Gumbel
             // variates lie in [-2.9, 16.7]), so its key stays small.
-            keys[e] = static_cast<float>(ln_of(r * invW) + static_cast<double>(g[e]));
+            code[e] = ordered_code(static_cast<float>(ln_of(r * invW) + static_cast<double>(g[e])));
         } else {
             if (mode == kModeOneHot && j == x) continue;
-            keys[e] = static_cast<float>((static_cast<double>(lv[e]) - lref) * invT + static_cast<double>(g[e]));
+            code[e] = ordered_code(
+                static_cast<float>((static_cast<double>(lv[e]) - lref) * invT + static_cast<double>(g[e])));
         }
-        merge_top2(best, second, pack_key(keys[e], static_cast<int>(j)), 0ull);
     }
-    // one reduction finds the winner and the runner-up (a near tie when its
-    // key is within the flag threshold); consecutive attempts use different
-    // scratch, so no barrier is needed between them
-    block_top2_u64<kFinalWaves>(best, second, sh.red2[attempt & 1]);
-    if (best == 0) return make_int2(-1, 0);
-    const bool tie = second != 0 && packed_key(second) >= packed_key(best) - kTieEps;
-    return make_int2(packed_index(best), tie ? 1 : 0);
+    return race_winner<kFinalWaves>(code, static_cast<int>(j0) - 4 * static_cast<int>(threadIdx.x),
+                                    sh.race[attempt & 1]);
 }
 
 // A lane's share of one row's block statistics, blocks lane + 64 j for
@@ -1721,21 +1765,29 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
     const float m = wave_max(mx);
     const double ref = static_cast<double>(m) * kLn2;  // keys relative to the row
     double s = 0.0;
-    uint64_t bp = 0, bx = 0;
+    uint32_t cp = 0u, cxm = 0u;  // the lane's largest codes (0 = none), at its lowest block
+    int ip = INT_MAX, ix = INT_MAX;
     if (!bad && m > -INFINITY) {
         for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
             const BlockStat e = fold_entry(st, fc, j, cb);
             if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
             s += static_cast<double>(e.s) * exp2_nonpos(static_cast<double>(e.m) - static_cast<double>(m));
-            const float kp = static_cast<float>(e.key - ref);
-            bp = max_u64(bp, pack_key(kp, cb));
-            if (cb != cx) bx = max_u64(bx, pack_key(kp, cb));
-            else if (keyx > -INFINITY) bx = max_u64(bx, pack_key(static_cast<float>(keyx - ref), cb));
+            const uint32_t code = ordered_code(static_cast<float>(e.key - ref));
+            const uint32_t codex = cb != cx ? code
+                                   : (keyx > -INFINITY ? ordered_code(static_cast<float>(keyx - ref)) : 0u);
+            if (code > cp) {
+                cp = code;
+                ip = cb;
+            }
+            if (codex > cxm) {
+                cxm = codex;
+                ix = cb;
+            }
         }
     }
     s = wave_sum_d(s);
-    bp = wave_max_u64(bp);
-    bx = wave_max_u64(bx);
+    const uint64_t bp = wave_argmax_code(cp, ip);
+    const uint64_t bx = wave_argmax_code(cxm, ix);
     bool tp = false, tx = false;
     if (bp != 0) {
         for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {

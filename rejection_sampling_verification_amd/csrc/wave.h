@@ -133,6 +133,23 @@ __device__ __forceinline__ int packed_index(uint64_t p) {
     return static_cast<int>(0xffffffffu - static_cast<uint32_t>(p));
 }
 
+// A packed key built from an ordered code directly (code 0 = no candidate).
+__device__ __forceinline__ uint64_t pack_code(uint32_t code, int idx) {
+    return code ? (static_cast<uint64_t>(code) << 32) | (0xffffffffu - static_cast<uint32_t>(idx)) : 0ull;
+}
+
+// The largest of a wave's codes (0 = none) and the lowest index that holds
+// it, as the packed word pack_code makes: a 32-bit max ladder, then a min
+// ladder over the indices of the lanes holding the maximum.  Each lane
+// passes its own largest code with the lowest index it has for that code.
+// Cheaper than a 64-bit ladder, whose steps need two moves and a 64-bit
+// compare each.
+__device__ __forceinline__ uint64_t wave_argmax_code(uint32_t code, int idx) {
+    const uint32_t m = wave_max_u(code);
+    const int i = wave_min_i((m != 0u && code == m) ? idx : INT_MAX);
+    return pack_code(m, i);
+}
+
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {  // out-of-range lanes read 0
     const int lo = dpp_i<CTRL, ROW_MASK>(0, static_cast<int>(static_cast<uint32_t>(v)));
@@ -152,36 +169,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
     return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// The two largest of a wave's packed keys (0 = none): every lane gets them.
-// Packed keys carry distinct indices, so the second is a different element.
-__device__ __forceinline__ void merge_top2(uint64_t &b1, uint64_t &b2, uint64_t o1, uint64_t o2) {
-    const uint64_t lo = b1 < o1 ? b1 : o1;
-    b1 = max_u64(b1, o1);
-    b2 = max_u64(lo, max_u64(b2, o2));
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_top2_step(uint64_t &b1, uint64_t &b2) {
-    const uint64_t o1 = dpp_u64<CTRL, ROW_MASK>(b1), o2 = dpp_u64<CTRL, ROW_MASK>(b2);
-    merge_top2(b1, b2, o1, o2);
-}
-
-__device__ __forceinline__ void wave_top2_u64(uint64_t &b1, uint64_t &b2) {
-    dpp_top2_step<0x111, 0xf>(b1, b2);
-    dpp_top2_step<0x112, 0xf>(b1, b2);
-    dpp_top2_step<0x114, 0xf>(b1, b2);
-    dpp_top2_step<0x118, 0xf>(b1, b2);
-    dpp_top2_step<0x142, 0xa>(b1, b2);
-    dpp_top2_step<0x143, 0xc>(b1, b2);
-    const auto rl = [](uint64_t v) {
-        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
-        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
-        return (static_cast<uint64_t>(hi) << 32) | lo;
-    };
-    b1 = rl(b1);
-    b2 = rl(b2);
 }
 
 // Workgroup barrier that orders LDS traffic only: unlike __syncthreads it
@@ -242,23 +229,6 @@ __device__ __forceinline__ uint32_t block_max_u(uint32_t v, uint32_t *scratch) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) r = max(r, scratch[w]);
     return r;
-}
-
-// The workgroup's two largest packed keys with one barrier.  `scratch` holds
-// 2 NW elements and must not be written by another reduction before every
-// thread has returned from this one (alternate two scratch arrays).
-template <int NW>
-__device__ __forceinline__ void block_top2_u64(uint64_t &b1, uint64_t &b2, uint64_t *scratch) {
-    wave_top2_u64(b1, b2);
-    if ((threadIdx.x & 63) == 0) {
-        scratch[2 * (threadIdx.x >> 6)] = b1;
-        scratch[2 * (threadIdx.x >> 6) + 1] = b2;
-    }
-    lds_barrier();
-    b1 = scratch[0];
-    b2 = scratch[1];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) merge_top2(b1, b2, scratch[2 * w], scratch[2 * w + 1]);
 }
 
 template <int NW>
