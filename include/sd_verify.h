@@ -157,8 +157,13 @@ size_t sd_verify_workspace_size(const sd_params *p);
  *   out_counters      device [4] uint64 = R, I, D, A of this call (overwritten)
  *   p                 host pointer to the sizes and optional outputs
  *   workspace         device scratch of >= sd_verify_workspace_size(p) bytes,
- *                     256-byte aligned; contents need no initialisation and
- *                     must not be shared by calls that overlap in time
+ *                     256-byte aligned, zero-filled once before its first
+ *                     use (hipMemset): its first 16 KB hold the row sweep's
+ *                     block-claim counters, which every call that launches
+ *                     returns to zero, so a workspace stays ready for calls
+ *                     of any size; the rest is scratch.  After a call that
+ *                     returned SD_ERR_HIP, zero it again.  Must not be shared
+ *                     by calls that overlap in time
  * Returns SD_OK or a negative sd_status; nothing is launched on error. */
 int sd_verify(const void *target_logits, const int32_t *draft_token_ids,
               const float *draft_probs, const int32_t *bitmask,

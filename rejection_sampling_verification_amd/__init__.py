@@ -193,11 +193,14 @@ def _check(t, name, dtype, shape, device):
 class Verifier:
     """Outputs and workspace for repeated calls of one shape.
 
-    Each call overwrites the tensors it returns.
+    Each call overwrites the tensors it returns.  `workspace`, if given, is a
+    uint8 device tensor of at least sd_verify_workspace_size bytes, zero-filled
+    before its first use; verifiers of any shapes may share one, as long as
+    their calls do not overlap in time.
     """
 
     def __init__(self, batch, num_draft, vocab, logits_dtype=torch.bfloat16, device=None,
-                 debug=False, histogram=False, total_drafts=None):
+                 debug=False, histogram=False, total_drafts=None, workspace=None):
         dev = torch.device(device) if device is not None else torch.device("cuda")
         if dev.type != "cuda":
             raise ValueError("the verifier runs on a HIP device")
@@ -217,7 +220,15 @@ class Verifier:
         ws = int(_lib.sd_verify_workspace_size(ctypes.byref(self.params)))
         self.params.draft_offsets = None
         dev = self.device
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            if (workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous()
+                    or workspace.numel() < ws or workspace.data_ptr() % 256):
+                raise ValueError(f"workspace must be a contiguous, 256-byte aligned uint8 tensor of "
+                                 f">= {ws} bytes on {dev}")
+            self.workspace = workspace
+        else:
+            # zero-filled once: the library leaves it ready for the next call
+            self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.workspace_bytes = ws
         tok_shape = (self.rows,) if self.ragged else (self.B, self.k + 1)
         self.out_tokens = torch.empty(tok_shape, dtype=torch.int32, device=dev)

@@ -31,7 +31,10 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "sd_verify.h"
 #include "philox.h"
@@ -41,7 +44,7 @@
 #define SDV_BLOCKS_PER_WAVE 4   // element kernel: 2048-token blocks per wave task
 #endif
 #ifndef SDV_ROW_STATS_GRID
-#define SDV_ROW_STATS_GRID 2048 // vector kernel: workgroups of the block sweep
+#define SDV_ROW_STATS_GRID 768  // vector kernel: workgroups when the occupancy query fails
 #endif
 #ifndef SDV_LOGITS_CACHE_POLICY
 #define SDV_LOGITS_CACHE_POLICY 2  // logits loads: non-temporal (read once, kept out of the caches)
@@ -163,9 +166,6 @@ __device__ __forceinline__ T uniform_load(const T *p) {
 // format).  Loads at offsets >= bytes return zero instead of faulting.
 constexpr int kBufferWord3 = 0x00020000;
 
-// Byte offset beyond every buffer_of range (rows are at most 16 MiB).
-constexpr int kPastAnyBuffer = 0x40000000;
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
                                              kBufferWord3);
@@ -244,6 +244,30 @@ struct DraftRec {
     double pad;
 };
 
+// Division of 0 <= n < 2^31 by a fixed 1 <= d < 2^31 as a multiply and a
+// shift (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", the round-up method): with l = ceil(log2 d) and
+// m = ceil(2^(31 + l) / d) <= 2^31 + ... < 2^32, n / d = (n m) >> (31 + l)
+// for every such n.  Wave-uniform operands keep it on the scalar unit, and
+// it has no branch.
+struct DivMagic {
+    uint32_t m;
+    int shift;  // 31 + l
+};
+
+inline DivMagic div_magic(int d) {
+    int l = 0;
+    while ((int64_t(1) << l) < d) ++l;
+    DivMagic r;
+    r.shift = 31 + l;
+    r.m = static_cast<uint32_t>(((uint64_t(1) << r.shift) + uint64_t(d) - 1) / uint64_t(d));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t div_fixed(uint32_t n, const DivMagic &f) {
+    return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> f.shift);
+}
+
 struct RowStatsArgs {
     const void *logits;
     const uint32_t *mask;     // nullptr = no bitmask
@@ -265,6 +289,9 @@ struct RowStatsArgs {
     int64_t ntasks;           // rows * nchunk (chunked element kernel)
     int64_t nblk;             // rows * C (vector kernel sweep)
     int k, kp1, V, W, C, cpw, nchunk;
+    uint32_t *sweep;          // claim counters of the vector sweep (zero on entry)
+    int parts_log2;           // the sweep's partitions: 2^parts_log2 <= kSweepParts
+    DivMagic divC, divK;      // division by C and by kp1
 };
 
 // Per-block statistics of a sampling row from one lane's values v (masked
@@ -275,12 +302,12 @@ __device__ __forceinline__ float2 softmax_block(const float *v, float c) {
     float m = v[0];
 #pragma unroll
     for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
-    m = wave_max(m);
+    m = wave_max_coded(m);  // a NaN logit makes the sum NaN either way
     if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
     const float mc = m * c;
-    float s = 0.0f;
+    float s = __builtin_amdgcn_exp2f(fmaf(v[0], c, -mc));
 #pragma unroll
-    for (int e = 0; e < NV; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mc));
+    for (int e = 1; e < NV; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mc));
     return make_float2(mc, wave_sum(s));
 }
 
@@ -449,58 +476,106 @@ struct SweepBlock {
 };
 
 // Where a block of the sweep lies: its (row, block) and, for calls with k
-// drafts per request, the row's request and position.  A wave's sweep steps
-// by a fixed number of blocks, so the cursor advances by precomputed
-// quotients and remainders: dividing a 64-bit block index for every block
-// costs more scalar instructions than the block's reduction leaves room for.
+// drafts per request, the row's request and position.
 struct SweepCursor {
     int64_t gb;
     int row, blk, b, i;
 };
 
-struct SweepStep {
-    int64_t stride;  // blocks between a wave's consecutive blocks
-    int drow, dblk;  // stride = drow * C + dblk
-    int db, di;      // drow = db * kp1 + di
-};
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint64_t>(v)));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint64_t>(v) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 __device__ __forceinline__ SweepCursor cursor_at(const RowStatsArgs &a, int64_t gb) {
+    // uniform by construction; said explicitly because the claim's lane-0
+    // branch would otherwise let the compiler treat the index as per-lane
+    gb = uniform_i64(gb);
     SweepCursor c;
     c.gb = gb;
-    c.row = static_cast<int>(gb / a.C);
-    c.blk = static_cast<int>(gb - int64_t(c.row) * a.C);
-    c.b = c.row / a.kp1;  // uniform layout (ragged calls look their rows up)
-    c.i = c.row - c.b * a.kp1;
+    const uint32_t g = static_cast<uint32_t>(gb);  // < 2^31 (checked by the host)
+    const uint32_t row = div_fixed(g, a.divC);
+    c.row = static_cast<int>(row);
+    c.blk = static_cast<int>(g - row * static_cast<uint32_t>(a.C));
+    const uint32_t b = div_fixed(row, a.divK);  // uniform layout (ragged calls look their rows up)
+    c.b = static_cast<int>(b);
+    c.i = static_cast<int>(row - b * static_cast<uint32_t>(a.kp1));
     return c;
 }
 
-__device__ __forceinline__ SweepStep step_of(const RowStatsArgs &a, int64_t stride) {
-    SweepStep s;
-    s.stride = stride;
-    s.drow = static_cast<int>(stride / a.C);
-    s.dblk = static_cast<int>(stride - int64_t(s.drow) * a.C);
-    s.db = s.drow / a.kp1;
-    s.di = s.drow - s.db * a.kp1;
-    return s;
+// The sweep hands blocks out dynamically.  Per-wave throughput varies by
+// tens of percent (which HBM channels a wave's blocks hit, which XCD it runs
+// on), and workgroups that start late would otherwise carry a full share to
+// the end of the kernel, so a static split ends with a long tail of few busy
+// waves.  Instead the blocks form interleaved partitions (partition p:
+// blocks p, p + P, p + 2P, ...), each with a claim counter that its home
+// waves increment; P is kSweepParts, or a smaller power of two when the grid
+// has fewer wave slots per XCD, so that every partition has home waves.  The
+// grid is the resident capacity.  A wave takes its first two blocks
+// statically and claims the rest one at a time.  A claim's round trip under
+// full HBM load is longer than one block's time, so two claims are kept in
+// flight.  Home partitions mix workgroups of all eight XCDs (workgroups go to
+// XCDs round-robin), so the XCDs' speeds average out within a partition; one
+// counter serves about 1/64 of the claims, well below the rate at which one
+// address takes returning atomics.
+constexpr int kSweepParts = 64;
+constexpr int kSweepCtrStride = 64;  // 32-bit words between counters: one 256-byte line each
+
+struct SweepPlan {  // 32-bit: block indices are below 2^31, and scalar compares are 32-bit
+    int lg;     // log2 of the number of partitions
+    int p;      // home partition
+    int lim;    // blocks in the partition
+    int k0, k1; // the wave's two static blocks (partition indices)
+    int kdyn;   // the partition index the counter's first claim stands for
+    uint32_t *ctr;
+};
+
+// Needs gridDim.x to be a multiple of 8 and 2^parts_log2 <= 4 gridDim.x / 8.
+__device__ __forceinline__ SweepPlan plan_of(const RowStatsArgs &a) {
+    constexpr int WPG = kThreads / kWave;
+    const int lg = a.parts_log2, P = 1 << lg;
+    const int x = blockIdx.x & 7;
+    const int u = static_cast<int>(blockIdx.x >> 3) * WPG + wave_id();
+    const int U = static_cast<int>(gridDim.x >> 3) * WPG;
+    SweepPlan pl;
+    pl.lg = lg;
+    pl.p = u & (P - 1);
+    const int n_p = 8 * ((U - pl.p + P - 1) >> lg);  // waves at home in p
+    pl.lim = a.nblk > pl.p ? static_cast<int>((a.nblk - pl.p + P - 1) >> lg) : 0;
+    pl.k0 = x + 8 * (u >> lg);
+    pl.k1 = pl.k0 + n_p;
+    pl.kdyn = 2 * n_p;
+    pl.ctr = a.sweep + pl.p * kSweepCtrStride;
+    return pl;
 }
 
-// The cursor one step on: dblk < C and di < kp1, so one carry each suffices.
-__device__ __forceinline__ SweepCursor advance(const RowStatsArgs &a, SweepCursor c, const SweepStep &s) {
-    c.gb += s.stride;
-    c.blk += s.dblk;
-    int carry = 0;
-    if (c.blk >= a.C) {
-        c.blk -= a.C;
-        carry = 1;
-    }
-    c.row += s.drow + carry;
-    c.i += s.di + carry;
-    c.b += s.db;
-    if (c.i >= a.kp1) {
-        c.i -= a.kp1;
-        c.b += 1;
-    }
-    return c;
+__device__ __forceinline__ int64_t block_of(const SweepPlan &pl, int k) {
+    return pl.p + (static_cast<int64_t>(k) << pl.lg);
+}
+
+// Waits for the last load of a block that is not reduced (skipped, or the
+// dead look-ahead; loads complete in order), so that on every path the
+// block's registers are settled when the loop comes round again and reusing
+// them as temporaries waits for nothing.
+__device__ __forceinline__ void settle(const uint4 &last) { asm volatile("" ::"v"(last.w)); }
+
+// Issues a claim (lane 0's atomic); its result is read by `claimed`, as late
+// as possible.
+__device__ __forceinline__ uint32_t claim(const SweepPlan &pl, int lane) {
+    uint32_t r = 0u;
+    if (lane == 0) r = atomicAdd(pl.ctr, 1u);
+    return r;
+}
+
+// The claimed partition index, saturated at lim (no more blocks).  kdyn may
+// exceed lim (a partition with fewer blocks than two per home wave), and the
+// counter's value is unbounded, so the sum is formed only below lim.
+__device__ __forceinline__ int claimed(const SweepPlan &pl, uint32_t r) {
+    const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(r), 0));
+    if (pl.kdyn >= pl.lim) return pl.lim;
+    return c < static_cast<uint32_t>(pl.lim - pl.kdyn) ? pl.kdyn + static_cast<int>(c) : pl.lim;
 }
 
 __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const SweepCursor &c) {
@@ -536,32 +611,35 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const S
     return s;
 }
 
-// Issue the loads of one block through buffer resources spanning its row (and
-// its mask row): every block takes the same instructions, and the groups of a
-// partial block that lie past the row read zeros (they are replaced by -inf
-// when the block is reduced).
+// Issue the loads of block blk of a row through buffer resources that start
+// at the block and end with its row (and its mask row): every block takes
+// the same instructions with the same per-lane offsets (no per-block vector
+// arithmetic), and the groups of a partial block that lie past the row read
+// zeros (they are replaced by -inf when the block is reduced).  A dead issue
+// (the sweep's look-ahead past its last block) gets an empty range: its
+// loads return zeros and touch no memory.
 template <typename ET, bool MASKED>
-__device__ __forceinline__ void issue_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
-                                            uint4 *r, uint32_t *m, bool live = true) {
+__device__ __forceinline__ void issue_block(const RowStatsArgs &a, int row, int blk, int lane, uint4 *r,
+                                            uint32_t *m, bool live = true) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
-    const __amdgpu_buffer_rsrc_t rs = buffer_of(
-        reinterpret_cast<const ET *>(a.logits) + int64_t(s.row) * a.V, uint32_t(a.V) * sizeof(ET));
-    // A dead issue (the sweep's look-ahead past its last block) points past
-    // the end of the buffer: such loads return zeros and touch no memory.
-    const int base = live ? s.blk * kBlock * int(sizeof(ET)) + lane * 16 : kPastAnyBuffer;
+    const uint32_t boff = uint32_t(blk) * kBlock * uint32_t(sizeof(ET));
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_of(reinterpret_cast<const char *>(a.logits) + (int64_t(row) * a.V) * int64_t(sizeof(ET)) + boff,
+                  live ? uint32_t(a.V) * uint32_t(sizeof(ET)) - boff : 0u);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, SDV_LOGITS_CACHE_POLICY);
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + g * kWave * 16, 0, SDV_LOGITS_CACHE_POLICY);
         r[g] = make_uint4(w.x, w.y, w.z, w.w);
     }
     if (MASKED) {
-        const __amdgpu_buffer_rsrc_t rm = buffer_of(a.mask + int64_t(s.row) * a.W, uint32_t(a.W) * 4u);
-        const int mbase = live ? s.blk * (kBlock / 8) + ((lane * P) >> 3) : kPastAnyBuffer;
+        const uint32_t moff = uint32_t(blk) * (kBlock / 8);
+        const __amdgpu_buffer_rsrc_t rm = buffer_of(reinterpret_cast<const char *>(a.mask + int64_t(row) * a.W) + moff,
+                                                    live ? uint32_t(a.W) * 4u - moff : 0u);
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, mbase + g * kWave * P / 8, 0, 0);
+            m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, ((lane * P) >> 3) + g * kWave * P / 8, 0, 0);
     }
 }
 
@@ -597,19 +675,18 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
                                              const uint4 *r, const uint32_t *m, Stash &st, int slot) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
+    // Every block is unpacked the same way and a partial one is then cut at V
+    // in place (V is a multiple of the group width here): one set of
+    // registers for both, where two unpacking paths would end in copies.
     float v[G * P];
-    if (s.full) {
-        unpack_full_block<ET, MASKED>(r, m, lane, v);
-    } else {
+    unpack_full_block<ET, MASKED>(r, m, lane, v);
+    if (!s.full) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t tok = int64_t(s.blk) * kBlock + (g * kWave + lane) * P;
-            Logit<ET>::unpack(r[g], v + g * P);
-            uint32_t bits = tok < a.V ? 0xffu : 0u;
-            if (MASKED) bits &= (P == 8) ? m[g] : (m[g] >> (uint32_t(tok) & 4u));
 #pragma unroll
             for (int e = 0; e < P; ++e)
-                if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
+                if (tok >= a.V) v[g * P + e] = -INFINITY;
         }
     }
     if (TOPK) apply_tau<G * P>(v, s.tau);
@@ -649,43 +726,77 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
     zero_call_outputs(a);
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t stride = int64_t(gridDim.x) * (kThreads / kWave);
-    const int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
-    if (g0 >= a.nblk) return;
+    const SweepPlan pl = plan_of(a);
+    if (pl.k0 >= pl.lim) return;
     const PhiloxKey key = key_of(a.seed);
     Stash st;
     st.kind = 0;
     int count = 0;
     uint4 ra[G], rb[G];
     uint32_t ma[G], mb[G];
-    const SweepStep step = step_of(a, stride);
-    SweepCursor ca = cursor_at(a, g0), cb;
-    SweepBlock sa = sweep_block(a, ca);
-    issue_block<ET, MASKED>(a, sa, lane, ra, ma);
-    for (;;) {
-        const bool more1 = ca.gb + stride < a.nblk;
-        cb = more1 ? advance(a, ca, step) : ca;
-        const SweepBlock sb = sweep_block(a, cb);
-        issue_block<ET, MASKED>(a, sb, lane, rb, mb, more1);
+    // Blocks in flight: the current one's loads, the next one's index, and the
+    // claims of the two after (issued before the loads of the blocks ahead of
+    // them, so that waiting for a claim never waits for those loads).  A dead
+    // look-ahead issue (no next block) names the wave's first block and reads
+    // nothing.
+    // Each block's loads are issued before the rest of its description is
+    // worked out (the temperature scale is a double division): temporaries
+    // placed after the issue cannot take the registers the loads fill, and a
+    // temporary in a register with a load outstanding waits for every load.
+    const SweepCursor c0 = cursor_at(a, block_of(pl, pl.k0));
+    issue_block<ET, MASKED>(a, c0.row, c0.blk, lane, ra, ma);
+    SweepBlock sa = sweep_block(a, c0);
+    // Two claims are in flight, one for each half of the loop (claims of one
+    // lane on one address return in the order issued, so once a claim finds
+    // the partition exhausted, so does the other).  Claims are issued without
+    // a condition: one past the end only returns "exhausted", and a claim kept
+    // under a condition would have its register copied, which waits for it.
+    int kn = pl.k1;
+    uint32_t ca = claim(pl, lane);
+    uint32_t cb = claim(pl, lane);
+    // One exit, at the bottom: with breaks in both halves the compiler's
+    // loop form has paths on which the look-ahead's loads look outstanding
+    // at the top, and every temporary placed in those registers then waits
+    // for all loads.
+    bool more = true;
+    do {
+        const bool more1 = kn < pl.lim;
+        const SweepCursor c1 = cursor_at(a, block_of(pl, more1 ? kn : pl.k0));
+        issue_block<ET, MASKED>(a, c1.row, c1.blk, lane, rb, mb, more1);
+        const SweepBlock sb = sweep_block(a, c1);
         if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
+        else settle(ra[G - 1]);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
             st.kind = 0;
             count = 0;
         }
-        if (!more1) break;
-        const bool more2 = cb.gb + stride < a.nblk;
-        ca = more2 ? advance(a, cb, step) : cb;
-        sa = sweep_block(a, ca);
-        issue_block<ET, MASKED>(a, sa, lane, ra, ma, more2);
-        if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
-        if (count == kWave) {
-            flush_stash(a, st, key, lane, count);
-            st.kind = 0;
-            count = 0;
+        if (more1) {
+            kn = claimed(pl, ca);
+            const bool more2 = kn < pl.lim;
+            ca = claim(pl, lane);
+            const SweepCursor c2 = cursor_at(a, block_of(pl, more2 ? kn : pl.k0));
+            issue_block<ET, MASKED>(a, c2.row, c2.blk, lane, ra, ma, more2);
+            sa = sweep_block(a, c2);
+            if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
+            else settle(rb[G - 1]);
+            if (count == kWave) {
+                flush_stash(a, st, key, lane, count);
+                st.kind = 0;
+                count = 0;
+            }
+            if (more2) {
+                kn = claimed(pl, cb);
+                cb = claim(pl, lane);
+            } else {
+                settle(ra[G - 1]);  // the dead look-ahead (it reads nothing)
+                more = false;
+            }
+        } else {
+            settle(rb[G - 1]);
+            more = false;
         }
-        if (!more2) break;
-    }
+    } while (more);
     flush_stash(a, st, key, lane, count);
 }
 
@@ -1404,6 +1515,7 @@ struct FinalArgs {
     int split_dense;   // dense q: 1 = residual masses by the grid-wide kernels
     const int32_t *off;      // ragged: [B + 1] draft offsets, or nullptr
     const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
+    uint32_t *sweep;         // the row-statistics sweep's claim counters, reset here
     int B, k, V, W, C;       // k: the uniform draft count, or the largest k_b
 };
 
@@ -1874,6 +1986,9 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     const PhiloxKey key = key_of(a.seed);
     const float c = greedy || bad_T ? 0.0f : scale_of(T);
     constexpr bool one_hot = !DENSE;
+    // the row-statistics kernel has finished: its claim counters go back to
+    // zero for the next call
+    if (b == 0 && tid < kSweepParts) a.sweep[tid * kSweepCtrStride] = 0u;
 
     // ---- this wave's first row's block statistics, in flight with the drafts
     FoldCache fc;
@@ -1928,11 +2043,8 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                     ra.mask = a.mask;
                     ra.V = V;
                     ra.W = a.W;
-                    SweepBlock sb;
-                    sb.row = static_cast<int>(row);
-                    sb.blk = l1.c;
-                    if (a.mask) issue_block<ET, true>(ra, sb, lane, stage_r, stage_m);
-                    else issue_block<ET, false>(ra, sb, lane, stage_r, stage_m);
+                    if (a.mask) issue_block<ET, true>(ra, static_cast<int>(row), l1.c, lane, stage_r, stage_m);
+                    else issue_block<ET, false>(ra, static_cast<int>(row), l1.c, lane, stage_r, stage_m);
                     stage_row = i;
                     stage_c = l1.c;
                 }
@@ -2376,10 +2488,30 @@ FinalFn pick_final(bool aligned, bool dense, bool split) {
     return aligned ? finalize_kernel<ET, true, false, false> : finalize_kernel<ET, false, false, false>;
 }
 
+// Workgroups of kThreads threads of `kernel` that the current device holds
+// at once (0 when the runtime cannot say); cached per device and kernel.
+inline int64_t resident_workgroups(const void *kernel) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int64_t> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, kernel);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+        return 0;
+    const int64_t n = int64_t(cus) * per_cu;
+    cache[key] = n;
+    return n;
+}
+
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_bstats, off_drec, off_tau, off_tauflag, off_jobs, off_wmass, off_rowreq, off_offok, off_tally, total;
+    size_t off_sweep, off_bstats, off_drec, off_tau, off_tauflag, off_jobs, off_wmass, off_rowreq, off_offok, off_tally, total;
     int nslot;
 };
 
@@ -2406,8 +2538,10 @@ inline Layout layout_of(const sd_params *p) {
     L.C = (p->vocab + kBlock - 1) / kBlock;
     L.W = (p->vocab + 31) / 32;
     L.nchunk = (L.C + SDV_BLOCKS_PER_WAVE - 1) / SDV_BLOCKS_PER_WAVE;
-    L.off_bstats = 0;
-    L.off_drec = align256(size_t(L.rows) * L.C * sizeof(BlockStat));
+    // the sweep's claim counters first, at the same place for every size
+    L.off_sweep = 0;
+    L.off_bstats = size_t(kSweepParts) * kSweepCtrStride * sizeof(uint32_t);
+    L.off_drec = L.off_bstats + align256(size_t(L.rows) * L.C * sizeof(BlockStat));
     L.off_tau = L.off_drec + align256(size_t(L.rows) * sizeof(DraftRec));
     L.off_tauflag = L.off_tau + align256(size_t(L.rows) * sizeof(float));
     L.off_jobs = L.off_tauflag + align256(size_t(L.rows) * sizeof(uint32_t));
@@ -2515,11 +2649,9 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.C = L.C;
     ra.cpw = SDV_BLOCKS_PER_WAVE;
     ra.nchunk = L.nchunk;
-    const int64_t waves_per_wg = kThreads / kWave;
-    int64_t grid1 = aligned ? (ra.nblk + waves_per_wg - 1) / waves_per_wg
-                            : (ra.ntasks + waves_per_wg - 1) / waves_per_wg;
-    if (aligned) grid1 = std::min<int64_t>(grid1, SDV_ROW_STATS_GRID);
-    if (grid1 > INT_MAX) return SD_ERR_UNSUPPORTED;
+    ra.sweep = reinterpret_cast<uint32_t *>(ws + L.off_sweep);
+    ra.divC = div_magic(L.C);
+    ra.divK = div_magic(k + 1);
 
     FinalArgs fa;
     fa.logits = target_logits;
@@ -2550,6 +2682,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     // grid over (request, block); short rows are summed inside the finalize
     // kernel, which saves two launches.
     fa.split_dense = (draft_probs && L.C >= kDenseSplitBlocks) ? 1 : 0;
+    fa.sweep = ra.sweep;
     fa.B = B;
     fa.k = k;
     fa.V = V;
@@ -2559,6 +2692,23 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     const bool topk = thresholds;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
                          : pick_row_stats<float>(masked, aligned, topk);
+    const int64_t waves_per_wg = kThreads / kWave;
+    int64_t grid1;
+    if (aligned && ra.nblk >= (int64_t(1) << 31)) return SD_ERR_UNSUPPORTED;  // block indices are 31-bit
+    if (aligned) {
+        // the resident capacity, a multiple of 8 (the sweep's partition
+        // layout), and no more than two blocks per wave need
+        int64_t cap = resident_workgroups(reinterpret_cast<const void *>(k1));
+        if (cap < 8) cap = SDV_ROW_STATS_GRID;
+        const int64_t need = (ra.nblk + 2 * waves_per_wg - 1) / (2 * waves_per_wg);
+        grid1 = (std::min(cap, need) + 7) / 8 * 8;
+        ra.parts_log2 = 0;  // partitions: a power of two, at most the wave slots per XCD
+        while ((int64_t(2) << ra.parts_log2) <= std::min<int64_t>(kSweepParts, grid1 / 8 * waves_per_wg))
+            ++ra.parts_log2;
+    } else {
+        grid1 = (ra.ntasks + waves_per_wg - 1) / waves_per_wg;
+    }
+    if (grid1 > INT_MAX) return SD_ERR_UNSUPPORTED;
     FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr, fa.split_dense != 0)
                       : pick_final<float>(aligned, draft_probs != nullptr, fa.split_dense != 0);
 

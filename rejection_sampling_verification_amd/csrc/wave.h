@@ -121,6 +121,11 @@ __device__ __forceinline__ float float_of_code(uint32_t c) {
     return __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
 }
 
+// The largest of a wave's floats through their codes (a NaN lane wins): each
+// step of the integer ladder is one DPP instruction, where the float ladder
+// also needs moves that quiet signaling NaNs.
+__device__ __forceinline__ float wave_max_coded(float v) { return float_of_code(wave_max_u(ordered_code(v))); }
+
 // A key and its index in one word: the larger word holds the larger key, and
 // the lower index among equal keys.  0 stands for "no candidate".
 __device__ __forceinline__ uint64_t pack_key(float key, int idx) {

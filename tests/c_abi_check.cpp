@@ -108,6 +108,7 @@ int main(int argc, char **argv) {
     p.status = d_status;
     const size_t ws = sd_verify_workspace_size(&p);
     CHECK_HIP(hipMalloc(&d_ws, ws ? ws : 256));
+    CHECK_HIP(hipMemset(d_ws, 0, ws ? ws : 256));  // zero-filled before its first call
 
     // calls the host must refuse before launching anything
     int refused[4];
