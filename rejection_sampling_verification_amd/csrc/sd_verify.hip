@@ -1924,6 +1924,73 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
     }
 }
 
+// The same fold when the row has at most 64 kFoldCache blocks, so that the
+// cache holds all of them (absent blocks read as empty): straight-line code
+// over the cached entries instead of a loop whose trip count differs by lane.
+__device__ __forceinline__ void fold_sampling_row_cached(const FoldCache &fc, int i, int cx, double keyx,
+                                                         FinalShared &sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    bool bad = false;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kFoldCache; ++j) {
+        const BlockStat &e = fc.e[j];
+        bad |= (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
+        mx = fmaxf(mx, e.m);
+    }
+    bad = wave_any(bad);
+    const float m = wave_max_coded(mx);
+    const double ref = static_cast<double>(m) * kLn2;  // keys relative to the row
+    double s = 0.0;
+    uint32_t cp = 0u, cxm = 0u;  // the lane's largest codes (0 = none), at its lowest block
+    int ip = INT_MAX, ix = INT_MAX;
+    float kps[kFoldCache];
+    bool live[kFoldCache];
+#pragma unroll
+    for (int j = 0; j < kFoldCache; ++j) {
+        const BlockStat &e = fc.e[j];
+        const int cb = lane + kWave * j;
+        live[j] = !bad && m > -INFINITY && e.m > -INFINITY && e.s > 0.0f;
+        kps[j] = static_cast<float>(e.key - ref);
+        if (!live[j]) continue;
+        s += static_cast<double>(e.s) * exp2_nonpos(static_cast<double>(e.m) - static_cast<double>(m));
+        const uint32_t code = ordered_code(kps[j]);
+        const uint32_t codex = cb != cx ? code
+                               : (keyx > -INFINITY ? ordered_code(static_cast<float>(keyx - ref)) : 0u);
+        if (code > cp) {
+            cp = code;
+            ip = cb;
+        }
+        if (codex > cxm) {
+            cxm = codex;
+            ix = cb;
+        }
+    }
+    s = wave_sum_d(s);
+    const uint64_t bp = wave_argmax_code(cp, ip);
+    const uint64_t bx = wave_argmax_code(cxm, ix);
+    bool tp = false, tx = false;
+#pragma unroll
+    for (int j = 0; j < kFoldCache; ++j) {
+        const int cb = lane + kWave * j;
+        if (!live[j]) continue;
+        tp |= near_tie(kps[j], cb, bp);
+        if (cb != cx) tx |= near_tie(kps[j], cb, bx);
+        else if (keyx > -INFINITY) tx |= near_tie(static_cast<float>(keyx - ref), cb, bx);
+    }
+    tp = bp != 0 && wave_any(tp);
+    tx = bp != 0 && wave_any(tx);
+    if (lane == 0) {
+        sh.M[i] = m;
+        sh.S[i] = s;
+        sh.G[i] = -1;
+        sh.l1p[i] = bp ? Level1{packed_index(bp), tp ? 1 : 0} : Level1{-1, 0};
+        sh.l1x[i] = bx ? Level1{packed_index(bx), tx ? 1 : 0} : Level1{-1, 0};
+        if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
+        else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+    }
+}
+
 // Counters of the call.  Every workgroup finishes at about the same time, so
 // words hit by all of them would serialise their atomics; instead request b
 // adds to slot word b % nslot, and the request that completes a slot adds the
@@ -2034,7 +2101,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             }
             const int xi = (i < k) ? sh.X[i] : -1;
             const int cx = (one_hot && xi >= 0 && xi < V) ? xi / kBlock : -1;
-            fold_sampling_row(st, fc, C, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
+            if (C <= kWave * kFoldCache)
+                fold_sampling_row_cached(fc, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
+            else
+                fold_sampling_row(st, fc, C, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
             if (ALIGNED && kp1 <= kFinalWaves) {
                 const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
                 if (l1.c >= 0) {
