@@ -1531,9 +1531,9 @@ struct FinalShared {
     float lx[kMaxDraft], qx[kMaxDraft];
     double keyx[kMaxDraft];
     double acc[kMaxDraft];
-    unsigned char ok[kMaxDraft], flag[kMaxDraft], invalid[kMaxDraft];
+    double u[kMaxDraft];        // the accept draws
+    unsigned char ok[kMaxDraft], flag[kMaxDraft], invalid[kMaxDraft], badq[kMaxDraft];
     uint32_t status;
-    int nacc, flag_acc, ninvalid;
     int staged_c;               // block of the sampled row held in blockv (-1: none)
     double red_d[kFinalWaves];
     uint64_t red_u[kFinalWaves];
@@ -1927,9 +1927,20 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
 // The same fold when the row has at most 64 kFoldCache blocks, so that the
 // cache holds all of them (absent blocks read as empty): straight-line code
 // over the cached entries instead of a loop whose trip count differs by lane.
-__device__ __forceinline__ void fold_sampling_row_cached(const FoldCache &fc, int i, int cx, double keyx,
-                                                         FinalShared &sh) {
+// It runs in two parts so that the block the row would sample is known, and
+// its loads issued, before the normaliser and the tie flags are worked out.
+struct CachedFold {
+    float m;                  // the row's max (log2 units)
+    double ref;               // keys relative to m ln 2
+    bool bad;                 // a NaN or +inf logit in the row
+    uint64_t bp, bx;          // level-1 winners under p and without the draft (0: none)
+    float kps[kFoldCache];    // the entries' keys relative to ref
+    bool live[kFoldCache];    // entries with mass
+};
+
+__device__ __forceinline__ CachedFold fold_races(const FoldCache &fc, int cx, double keyx) {
     const int lane = threadIdx.x & (kWave - 1);
+    CachedFold f;
     bool bad = false;
     float mx = -INFINITY;
 #pragma unroll
@@ -1938,25 +1949,21 @@ __device__ __forceinline__ void fold_sampling_row_cached(const FoldCache &fc, in
         bad |= (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
         mx = fmaxf(mx, e.m);
     }
-    bad = wave_any(bad);
-    const float m = wave_max_coded(mx);
-    const double ref = static_cast<double>(m) * kLn2;  // keys relative to the row
-    double s = 0.0;
+    f.bad = wave_any(bad);
+    f.m = wave_max_coded(mx);
+    f.ref = static_cast<double>(f.m) * kLn2;
     uint32_t cp = 0u, cxm = 0u;  // the lane's largest codes (0 = none), at its lowest block
     int ip = INT_MAX, ix = INT_MAX;
-    float kps[kFoldCache];
-    bool live[kFoldCache];
 #pragma unroll
     for (int j = 0; j < kFoldCache; ++j) {
         const BlockStat &e = fc.e[j];
         const int cb = lane + kWave * j;
-        live[j] = !bad && m > -INFINITY && e.m > -INFINITY && e.s > 0.0f;
-        kps[j] = static_cast<float>(e.key - ref);
-        if (!live[j]) continue;
-        s += static_cast<double>(e.s) * exp2_nonpos(static_cast<double>(e.m) - static_cast<double>(m));
-        const uint32_t code = ordered_code(kps[j]);
+        f.live[j] = !f.bad && f.m > -INFINITY && e.m > -INFINITY && e.s > 0.0f;
+        f.kps[j] = static_cast<float>(e.key - f.ref);
+        if (!f.live[j]) continue;
+        const uint32_t code = ordered_code(f.kps[j]);
         const uint32_t codex = cb != cx ? code
-                               : (keyx > -INFINITY ? ordered_code(static_cast<float>(keyx - ref)) : 0u);
+                               : (keyx > -INFINITY ? ordered_code(static_cast<float>(keyx - f.ref)) : 0u);
         if (code > cp) {
             cp = code;
             ip = cb;
@@ -1966,29 +1973,69 @@ __device__ __forceinline__ void fold_sampling_row_cached(const FoldCache &fc, in
             ix = cb;
         }
     }
-    s = wave_sum_d(s);
-    const uint64_t bp = wave_argmax_code(cp, ip);
-    const uint64_t bx = wave_argmax_code(cxm, ix);
+    f.bp = wave_argmax_code(cp, ip);
+    f.bx = wave_argmax_code(cxm, ix);
+    return f;
+}
+
+__device__ __forceinline__ void fold_finish(const FoldCache &fc, const CachedFold &f, int i, int cx, double keyx,
+                                            FinalShared &sh) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double s = 0.0;
     bool tp = false, tx = false;
 #pragma unroll
     for (int j = 0; j < kFoldCache; ++j) {
+        const BlockStat &e = fc.e[j];
         const int cb = lane + kWave * j;
-        if (!live[j]) continue;
-        tp |= near_tie(kps[j], cb, bp);
-        if (cb != cx) tx |= near_tie(kps[j], cb, bx);
-        else if (keyx > -INFINITY) tx |= near_tie(static_cast<float>(keyx - ref), cb, bx);
+        if (!f.live[j]) continue;
+        s += static_cast<double>(e.s) * exp2_nonpos(static_cast<double>(e.m) - static_cast<double>(f.m));
+        tp |= near_tie(f.kps[j], cb, f.bp);
+        if (cb != cx) tx |= near_tie(f.kps[j], cb, f.bx);
+        else if (keyx > -INFINITY) tx |= near_tie(static_cast<float>(keyx - f.ref), cb, f.bx);
     }
-    tp = bp != 0 && wave_any(tp);
-    tx = bp != 0 && wave_any(tx);
+    s = wave_sum_d(s);
+    tp = f.bp != 0 && wave_any(tp);
+    tx = f.bp != 0 && wave_any(tx);
     if (lane == 0) {
-        sh.M[i] = m;
+        sh.M[i] = f.m;
         sh.S[i] = s;
         sh.G[i] = -1;
-        sh.l1p[i] = bp ? Level1{packed_index(bp), tp ? 1 : 0} : Level1{-1, 0};
-        sh.l1x[i] = bx ? Level1{packed_index(bx), tx ? 1 : 0} : Level1{-1, 0};
-        if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
-        else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+        sh.l1p[i] = f.bp ? Level1{packed_index(f.bp), tp ? 1 : 0} : Level1{-1, 0};
+        sh.l1x[i] = f.bx ? Level1{packed_index(f.bx), tx ? 1 : 0} : Level1{-1, 0};
+        if (f.bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
+        else if (f.m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
     }
+}
+
+// Position i's verdict, taken by lane 0 of the wave that folded row i: the
+// accept probability min(1, p/q) (pyshine "vLLM, part 2", "Verification"),
+// the accept draw against it, its boundary flag, and whether the draft's q is
+// unusable (reported only when nothing else is wrong).  Greedy rows accept a
+// draft equal to the row's argmax.
+__device__ __forceinline__ void judge_position(FinalShared &sh, int i, bool greedy, float c, bool one_hot) {
+    const int xi = sh.X[i];
+    bool ok, flag = false, badq = false;
+    double acc;
+    if (greedy) {
+        ok = (xi == sh.G[i]);
+        acc = ok ? 1.0 : 0.0;
+    } else {
+        const bool inv = sh.invalid[i];
+        const float lx = sh.lx[i], qx = sh.qx[i];
+        double p = 0.0;
+        if (!inv && lx > -INFINITY)
+            p = exp2(static_cast<double>(lx) * c - static_cast<double>(sh.M[i])) / sh.S[i];
+        badq = !one_hot && !(qx >= 0.0f && qx <= FLT_MAX);
+        const double q = qx;
+        acc = (p == 0.0) ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+        const double u = sh.u[i];
+        ok = u < acc;
+        flag = fabs(u - acc) < kAcceptFlagEps;
+    }
+    sh.acc[i] = acc;
+    sh.ok[i] = ok;
+    sh.flag[i] = flag;
+    sh.badq[i] = badq;
 }
 
 // Counters of the call.  Every workgroup finishes at about the same time, so
@@ -2033,6 +2080,19 @@ __device__ __forceinline__ void tally_call(const FinalArgs &a, int b, unsigned l
     atomicAdd(&out[3], acc);           // A
 }
 
+// Issue the loads of block c of a row for the staging (c < 0: none).
+template <typename ET>
+__device__ __forceinline__ void stage_block(const FinalArgs &a, int row, int c, int lane, uint4 *r, uint32_t *m) {
+    if (c < 0) return;
+    RowStatsArgs ra;  // only the fields issue_block reads
+    ra.logits = a.logits;
+    ra.mask = a.mask;
+    ra.V = a.V;
+    ra.W = a.W;
+    if (a.mask) issue_block<ET, true>(ra, row, c, lane, r, m);
+    else issue_block<ET, false>(ra, row, c, lane, r, m);
+}
+
 // DENSE: dense draft probabilities; SPLIT (with DENSE): the residual masses
 // of rejected rows are left to the grid-wide kernels, so this instantiation
 // carries no in-kernel residual pass and its registers.
@@ -2067,11 +2127,10 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     const bool xok = tid < k && x >= 0 && x < V;
     DraftRec rec;
     if (tid < k) rec = a.drec[geo.row0 + tid];  // read only when xok and T is valid
+    // the accept draws depend on nothing loaded: drawn while the loads fly
+    const double u_acc = tid < k ? draw_accept(key, b, tid) : 0.0;
     if (tid == 0) {
         sh.status = (bad_T ? SD_STATUS_TEMPERATURE : 0u) | (geo.ok ? 0u : SD_STATUS_BAD_OFFSETS);
-        sh.nacc = 0;
-        sh.flag_acc = 0;
-        sh.ninvalid = 0;
         sh.staged_c = -1;
     }
     __syncthreads();
@@ -2082,6 +2141,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
         sh.qx[tid] = rec.qx;
         sh.keyx[tid] = rec.keyx;
         sh.invalid[tid] = !(rec.allowed & 1u);
+        sh.u[tid] = u_acc;
     }
     __syncthreads();
 
@@ -2097,73 +2157,58 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             if (i != wave) load_fold_cache(st, C, lane, fc);  // rows past the first wave of rows
             if (greedy) {
                 fold_greedy_row(st, fc, C, i, sh);
+                if (i < k && lane == 0) judge_position(sh, i, true, c, one_hot);
                 continue;
             }
             const int xi = (i < k) ? sh.X[i] : -1;
             const int cx = (one_hot && xi >= 0 && xi < V) ? xi / kBlock : -1;
-            if (C <= kWave * kFoldCache)
-                fold_sampling_row_cached(fc, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
-            else
-                fold_sampling_row(st, fc, C, i, cx, cx >= 0 ? sh.keyx[i] : -INFINITY, sh);
-            if (ALIGNED && kp1 <= kFinalWaves) {
+            const double keyx = cx >= 0 ? sh.keyx[i] : -INFINITY;
+            int pre = -1;  // the block this row samples from, if it is the one emitting
+            if (C <= kWave * kFoldCache) {
+                const CachedFold f = fold_races(fc, cx, keyx);
+                const uint64_t w = (i < k) ? (one_hot ? f.bx : 0ull) : f.bp;
+                pre = w ? packed_index(w) : -1;
+                if (ALIGNED && kp1 <= kFinalWaves) stage_block<ET>(a, static_cast<int>(row), pre, lane, stage_r, stage_m);
+                fold_finish(fc, f, i, cx, keyx, sh);
+            } else {
+                fold_sampling_row(st, fc, C, i, cx, keyx, sh);
                 const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
-                if (l1.c >= 0) {
-                    RowStatsArgs ra;  // only the fields issue_block reads
-                    ra.logits = a.logits;
-                    ra.mask = a.mask;
-                    ra.V = V;
-                    ra.W = a.W;
-                    if (a.mask) issue_block<ET, true>(ra, static_cast<int>(row), l1.c, lane, stage_r, stage_m);
-                    else issue_block<ET, false>(ra, static_cast<int>(row), l1.c, lane, stage_r, stage_m);
-                    stage_row = i;
-                    stage_c = l1.c;
-                }
+                pre = l1.c;
+                if (ALIGNED && kp1 <= kFinalWaves) stage_block<ET>(a, static_cast<int>(row), pre, lane, stage_r, stage_m);
             }
+            if (ALIGNED && kp1 <= kFinalWaves && pre >= 0) {
+                stage_row = i;
+                stage_c = pre;
+            }
+            if (i < k && lane == 0) judge_position(sh, i, false, c, one_hot);
         }
     }
     lds_barrier();
 
-    // ---- per-position accept probabilities and verdicts; wave 0 holds the
-    //      k <= 64 positions and scans them with ballots
-    if (wave == 0 && sh.status == 0) {
-        bool ok = false, flag = false, inv = false;
-        double acc = 0.0;
+    // ---- every wave reads the k <= 64 verdicts and finds the first
+    //      rejection with ballots (all waves agree, so no barrier follows)
+    uint32_t st = sh.status;
+    int nacc = 0, flag_acc = 0, ninv = 0;
+    {
+        bool okv = false, flv = false, inv = false, bq = false;
         if (lane < k) {
-            const int xi = sh.X[lane];
+            okv = sh.ok[lane];
+            flv = sh.flag[lane];
             inv = sh.invalid[lane];
-            if (greedy) {
-                ok = (xi == sh.G[lane]);
-                acc = ok ? 1.0 : 0.0;
-            } else {
-                const float lx = sh.lx[lane], qx = sh.qx[lane];
-                double p = 0.0;
-                if (!inv && lx > -INFINITY)
-                    p = exp2(static_cast<double>(lx) * c - static_cast<double>(sh.M[lane])) / sh.S[lane];
-                if (!one_hot && !(qx >= 0.0f && qx <= FLT_MAX))
-                    atomicOr(&sh.status, SD_STATUS_BAD_DRAFT_PROB);
-                const double q = qx;
-                acc = (p == 0.0) ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-                const double u = draw_accept(key, b, lane);
-                ok = u < acc;
-                flag = fabs(u - acc) < kAcceptFlagEps;
-            }
-            sh.acc[lane] = acc;
+            bq = sh.badq[lane];
         }
-        const uint64_t okm = __ballot(ok), flm = __ballot(flag), invm = __ballot(inv);
+        if (st == 0 && __ballot(bq) != 0ull) st = SD_STATUS_BAD_DRAFT_PROB;
+        const uint64_t okm = __ballot(okv), flm = __ballot(flv), invm = __ballot(inv);
         const uint64_t kmask = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
         const uint64_t rejected = ~okm & kmask;
-        const int n = rejected ? __builtin_ctzll(rejected) : k;      // first rejection
-        const uint64_t scanned = n < k ? ((2ull << n) - 1ull) : kmask;  // positions tested
-        if (lane == 0) {
-            sh.nacc = n;
-            sh.flag_acc = __popcll(flm & scanned);
-            sh.ninvalid = __popcll(invm);
-        }
+        nacc = rejected ? static_cast<int>(__builtin_ctzll(rejected)) : k;  // first rejection
+        const uint64_t scanned = nacc < k ? ((2ull << nacc) - 1ull) : kmask;  // positions tested
+        flag_acc = __popcll(flm & scanned);
+        ninv = __popcll(invm);
     }
-    lds_barrier();
 
     // ---- the wave that loaded the sampled row's block puts it in LDS
-    if (sh.status == 0 && stage_row >= 0 && stage_row == sh.nacc) {
+    if (st == 0 && stage_row >= 0 && stage_row == nacc) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float v[P];
@@ -2192,19 +2237,18 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     // also wait for the atomic.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (tid == 0) {
-        const bool err = sh.status != 0;
-        share = tally_share(err ? 0 : sh.nacc, err ? 0 : sh.ninvalid, err ? 0 : k);
+        const bool err = st != 0;
+        share = tally_share(err ? 0 : nacc, err ? 0 : ninv, err ? 0 : k);
         before = tally_slot(a, b, share);
     }
     lds_barrier();
 
     // ---- the emitted token
-    const uint32_t st = sh.status;
     int y = -1, fg = 0;
     bool deferred = false;
     if (DENSE && tid == 0) a.jobs[b].row = -1;  // overwritten below for a dense draw
     if (st == 0) {
-        const int n = sh.nacc;
+        const int n = nacc;
         if (greedy) {
             y = sh.G[n];
         } else {
@@ -2283,7 +2327,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     }
 
     // ---- outputs, and this request's share of the counters
-    const int n = st ? -1 : sh.nacc;
+    const int n = st ? -1 : nacc;
     if (tid < kp1 && geo.ok) {  // a malformed ragged call has no slots to write
         int tok = -1;
         if (!st) tok = tid < n ? sh.X[tid] : (tid == n ? y : -1);
@@ -2304,12 +2348,12 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             for (int r = 0; r < kp1; ++r) ftp += a.tau_flag[geo.row0 + r];
         if (a.dbg_req_flags)
             a.dbg_req_flags[b] = st ? 0u
-                                    : (uint32_t(min(sh.flag_acc, 0xfff)) | (uint32_t(min(fg, 0xfff)) << 12) |
+                                    : (uint32_t(min(flag_acc, 0xfff)) | (uint32_t(min(fg, 0xfff)) << 12) |
                                        (min(ftp, 0xffu) << 24));
         if (st) {
             if (a.status) atomicOr(a.status, st);
         } else if (a.dbg_flags) {
-            if (sh.flag_acc) atomicAdd(&a.dbg_flags[0], static_cast<uint32_t>(sh.flag_acc));
+            if (flag_acc) atomicAdd(&a.dbg_flags[0], static_cast<uint32_t>(flag_acc));
             if (fg) atomicAdd(&a.dbg_flags[1], static_cast<uint32_t>(fg));
             if (ftp) atomicAdd(&a.dbg_flags[2], ftp);
         }
