@@ -44,7 +44,10 @@
 #define SDV_BLOCKS_PER_WAVE 4   // element kernel: 2048-token blocks per wave task
 #endif
 #ifndef SDV_ROW_STATS_GRID
-#define SDV_ROW_STATS_GRID 768  // vector kernel: workgroups when the occupancy query fails
+#define SDV_ROW_STATS_GRID 768  // claimed sweep: workgroups when the occupancy query fails
+#endif
+#ifndef SDV_ROW_STATS_GRID_STRIDED
+#define SDV_ROW_STATS_GRID_STRIDED 2048  // strided (masked) sweep: workgroups
 #endif
 #ifndef SDV_LOGITS_CACHE_POLICY
 #define SDV_LOGITS_CACHE_POLICY 2  // logits loads: non-temporal (read once, kept out of the caches)
@@ -505,7 +508,43 @@ __device__ __forceinline__ SweepCursor cursor_at(const RowStatsArgs &a, int64_t 
     return c;
 }
 
-// The sweep hands blocks out dynamically.  Per-wave throughput varies by
+// The strided sweep steps its cursor by a fixed number of blocks: by
+// precomputed quotients and remainders, one carry each.
+struct SweepStep {
+    int64_t stride;  // blocks between a wave's consecutive blocks
+    int drow, dblk;  // stride = drow * C + dblk
+    int db, di;      // drow = db * kp1 + di
+};
+
+__device__ __forceinline__ SweepStep step_of(const RowStatsArgs &a, int64_t stride) {
+    SweepStep st;
+    st.stride = stride;
+    st.drow = static_cast<int>(stride / a.C);
+    st.dblk = static_cast<int>(stride - int64_t(st.drow) * a.C);
+    st.db = st.drow / a.kp1;
+    st.di = st.drow - st.db * a.kp1;
+    return st;
+}
+
+__device__ __forceinline__ SweepCursor advance(const RowStatsArgs &a, SweepCursor c, const SweepStep &s) {
+    c.gb += s.stride;
+    c.blk += s.dblk;
+    int carry = 0;
+    if (c.blk >= a.C) {
+        c.blk -= a.C;
+        carry = 1;
+    }
+    c.row += s.drow + carry;
+    c.i += s.di + carry;
+    c.b += s.db;
+    if (c.i >= a.kp1) {
+        c.i -= a.kp1;
+        c.b += 1;
+    }
+    return c;
+}
+
+// The claimed sweep hands blocks out dynamically.  Per-wave throughput varies by
 // tens of percent (which HBM channels a wave's blocks hit, which XCD it runs
 // on), and workgroups that start late would otherwise carry a full share to
 // the end of the kernel, so a static split ends with a long tail of few busy
@@ -611,35 +650,49 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const S
     return s;
 }
 
-// Issue the loads of block blk of a row through buffer resources that start
-// at the block and end with its row (and its mask row): every block takes
-// the same instructions with the same per-lane offsets (no per-block vector
-// arithmetic), and the groups of a partial block that lie past the row read
-// zeros (they are replaced by -inf when the block is reduced).  A dead issue
-// (the sweep's look-ahead past its last block) gets an empty range: its
-// loads return zeros and touch no memory.
+// Byte offset beyond every row-based buffer range (rows are at most 16 MiB).
+constexpr int kPastAnyBuffer = 0x40000000;
+
+// Issue the loads of block blk of a row.  Without a mask the buffer resource
+// starts at the block and ends with its row: every block takes the same
+// instructions with the same per-lane offsets, and a dead issue (the sweep's
+// look-ahead past its last block) gets an empty range.  With a mask the
+// resources span the row and its mask row and the offsets carry the block (a
+// dead issue points past the end); on the masked sweep that form measured
+// faster.  Either way the groups of a partial block that lie past the row
+// read zeros (they are replaced by -inf when the block is reduced), and a
+// dead issue's loads return zeros and touch no memory.
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void issue_block(const RowStatsArgs &a, int row, int blk, int lane, uint4 *r,
                                             uint32_t *m, bool live = true) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
-    const uint32_t boff = uint32_t(blk) * kBlock * uint32_t(sizeof(ET));
-    const __amdgpu_buffer_rsrc_t rs =
-        buffer_of(reinterpret_cast<const char *>(a.logits) + (int64_t(row) * a.V) * int64_t(sizeof(ET)) + boff,
-                  live ? uint32_t(a.V) * uint32_t(sizeof(ET)) - boff : 0u);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (!MASKED) {
+        const uint32_t boff = uint32_t(blk) * kBlock * uint32_t(sizeof(ET));
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_of(reinterpret_cast<const char *>(a.logits) + (int64_t(row) * a.V) * int64_t(sizeof(ET)) + boff,
+                      live ? uint32_t(a.V) * uint32_t(sizeof(ET)) - boff : 0u);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + g * kWave * 16, 0, SDV_LOGITS_CACHE_POLICY);
-        r[g] = make_uint4(w.x, w.y, w.z, w.w);
-    }
-    if (MASKED) {
-        const uint32_t moff = uint32_t(blk) * (kBlock / 8);
-        const __amdgpu_buffer_rsrc_t rm = buffer_of(reinterpret_cast<const char *>(a.mask + int64_t(row) * a.W) + moff,
-                                                    live ? uint32_t(a.W) * 4u - moff : 0u);
+        for (int g = 0; g < G; ++g) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + g * kWave * 16, 0,
+                                                                  SDV_LOGITS_CACHE_POLICY);
+            r[g] = make_uint4(w.x, w.y, w.z, w.w);
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rs = buffer_of(
+            reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V, uint32_t(a.V) * sizeof(ET));
+        const int base = live ? blk * kBlock * int(sizeof(ET)) + lane * 16 : kPastAnyBuffer;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, SDV_LOGITS_CACHE_POLICY);
+            r[g] = make_uint4(w.x, w.y, w.z, w.w);
+        }
+        const __amdgpu_buffer_rsrc_t rm = buffer_of(a.mask + int64_t(row) * a.W, uint32_t(a.W) * 4u);
+        const int mbase = live ? blk * (kBlock / 8) + ((lane * P) >> 3) : kPastAnyBuffer;
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, ((lane * P) >> 3) + g * kWave * P / 8, 0, 0);
+            m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, mbase + g * kWave * P / 8, 0, 0);
     }
 }
 
@@ -675,18 +728,34 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
                                              const uint4 *r, const uint32_t *m, Stash &st, int slot) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
-    // Every block is unpacked the same way and a partial one is then cut at V
-    // in place (V is a multiple of the group width here): one set of
-    // registers for both, where two unpacking paths would end in copies.
+    // Without a mask every block is unpacked the same way and a partial one is
+    // then cut at V in place (V is a multiple of the group width here): one
+    // set of registers for both, where two unpacking paths end in copies.
+    // With a mask the two paths measured faster.
     float v[G * P];
-    unpack_full_block<ET, MASKED>(r, m, lane, v);
-    if (!s.full) {
+    if constexpr (!MASKED) {
+        unpack_full_block<ET, MASKED>(r, m, lane, v);
+        if (!s.full) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int64_t tok = int64_t(s.blk) * kBlock + (g * kWave + lane) * P;
+#pragma unroll
+                for (int e = 0; e < P; ++e)
+                    if (tok >= a.V) v[g * P + e] = -INFINITY;
+            }
+        }
+    } else if (s.full) {
+        unpack_full_block<ET, MASKED>(r, m, lane, v);
+    } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t tok = int64_t(s.blk) * kBlock + (g * kWave + lane) * P;
+            Logit<ET>::unpack(r[g], v + g * P);
+            uint32_t bits = tok < a.V ? 0xffu : 0u;
+            bits &= (P == 8) ? m[g] : (m[g] >> (uint32_t(tok) & 4u));
 #pragma unroll
             for (int e = 0; e < P; ++e)
-                if (tok >= a.V) v[g * P + e] = -INFINITY;
+                if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
         }
     }
     if (TOPK) apply_tau<G * P>(v, s.tau);
@@ -712,20 +781,17 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
     }
 }
 
-// Rows 16-byte aligned with V a multiple of the group width.  The grid sweeps
-// the (row, block) pairs in memory order: wave w of the grid takes blocks
-// w, w + Wt, w + 2 Wt, ... (Wt = waves in the grid), so the whole grid reads
-// one contiguous window of the logits at a time.  Each wave keeps the loads of
-// its next block in flight while it reduces the current one; the next index
-// is clamped to the current block at the end of the sweep, so every path
-// reaches a reduction with the same loads outstanding.
+// Rows 16-byte aligned with V a multiple of the group width.  Two sweeps over
+// the (row, block) pairs: without a mask the blocks are claimed dynamically
+// (sweep_claimed), with a mask they go out in a fixed grid-stride order
+// (sweep_strided), where the claims' round trips cost more than the balance
+// gains (masked rows take more work per block, so a wave holds more blocks).
+// Each wave keeps the loads of its next block in flight while it reduces the
+// current one.
 template <typename ET, bool MASKED, bool TOPK>
-__global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a) {
+__device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
-    zero_call_outputs(a);
-    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
-    const int lane = threadIdx.x & (kWave - 1);
     const SweepPlan pl = plan_of(a);
     if (pl.k0 >= pl.lim) return;
     const PhiloxKey key = key_of(a.seed);
@@ -798,6 +864,63 @@ __global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a)
         }
     } while (more);
     flush_stash(a, st, key, lane, count);
+}
+
+// Wave w of a grid of Wt waves takes blocks w, w + Wt, w + 2 Wt, ..., so the
+// whole grid reads one contiguous window of the logits at a time; the cursor
+// steps by precomputed quotients.  The look-ahead index is clamped to the
+// current block at the end of the sweep (a dead issue, reading nothing).
+template <typename ET, bool MASKED, bool TOPK>
+__device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    const int64_t stride = int64_t(gridDim.x) * (kThreads / kWave);
+    const int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
+    if (g0 >= a.nblk) return;
+    const PhiloxKey key = key_of(a.seed);
+    Stash st;
+    st.kind = 0;
+    int count = 0;
+    uint4 ra[G], rb[G];
+    uint32_t ma[G], mb[G];
+    const SweepStep step = step_of(a, stride);
+    SweepCursor ca = cursor_at(a, g0);
+    SweepBlock sa = sweep_block(a, ca);
+    issue_block<ET, MASKED>(a, ca.row, ca.blk, lane, ra, ma);
+    for (;;) {
+        const bool more1 = ca.gb + stride < a.nblk;
+        const SweepCursor cb = more1 ? advance(a, ca, step) : ca;
+        const SweepBlock sb = sweep_block(a, cb);
+        issue_block<ET, MASKED>(a, cb.row, cb.blk, lane, rb, mb, more1);
+        if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
+        if (count == kWave) {
+            flush_stash(a, st, key, lane, count);
+            st.kind = 0;
+            count = 0;
+        }
+        if (!more1) break;
+        const bool more2 = cb.gb + stride < a.nblk;
+        ca = more2 ? advance(a, cb, step) : cb;
+        sa = sweep_block(a, ca);
+        issue_block<ET, MASKED>(a, ca.row, ca.blk, lane, ra, ma, more2);
+        if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
+        if (count == kWave) {
+            flush_stash(a, st, key, lane, count);
+            st.kind = 0;
+            count = 0;
+        }
+        if (!more2) break;
+    }
+    flush_stash(a, st, key, lane, count);
+}
+
+template <typename ET, bool MASKED, bool TOPK>
+__global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a) {
+    zero_call_outputs(a);
+    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
+    const int lane = threadIdx.x & (kWave - 1);
+    if constexpr (MASKED) sweep_strided<ET, MASKED, TOPK>(a, lane);
+    else sweep_claimed<ET, MASKED, TOPK>(a, lane);
 }
 
 // Any alignment and any V: element loads clamped into the row, one chunk of
@@ -2809,7 +2932,9 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     const int64_t waves_per_wg = kThreads / kWave;
     int64_t grid1;
     if (aligned && ra.nblk >= (int64_t(1) << 31)) return SD_ERR_UNSUPPORTED;  // block indices are 31-bit
-    if (aligned) {
+    if (aligned && masked) {
+        grid1 = std::min<int64_t>((ra.nblk + waves_per_wg - 1) / waves_per_wg, SDV_ROW_STATS_GRID_STRIDED);
+    } else if (aligned) {
         // the resident capacity, a multiple of 8 (the sweep's partition
         // layout), and no more than two blocks per wave need
         int64_t cap = resident_workgroups(reinterpret_cast<const void *>(k1));
