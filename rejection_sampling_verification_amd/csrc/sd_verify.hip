@@ -46,6 +46,9 @@
 #ifndef SDV_ROW_STATS_GRID
 #define SDV_ROW_STATS_GRID 768  // claimed sweep: workgroups when the occupancy query fails
 #endif
+#ifndef SDV_SWEEP_WG_PER_CU
+#define SDV_SWEEP_WG_PER_CU 3  // claimed sweep: at most this many workgroups (waves per SIMD) per CU
+#endif
 #ifndef SDV_ROW_STATS_GRID_STRIDED
 #define SDV_ROW_STATS_GRID_STRIDED 2048  // strided (masked) sweep: workgroups
 #endif
@@ -90,6 +93,8 @@ struct Logit<uint16_t> {  // bfloat16 stored as its bit pattern
         o[6] = __uint_as_float(w.w << 16);
         o[7] = __uint_as_float(w.w & 0xffff0000u);
     }
+    // a 16-byte group whose eight tokens all unpack to -inf
+    __device__ static uint4 neg_inf_group() { return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u); }
 };
 
 template <>
@@ -102,6 +107,7 @@ struct Logit<float> {
         o[2] = __uint_as_float(w.z);
         o[3] = __uint_as_float(w.w);
     }
+    __device__ static uint4 neg_inf_group() { return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u); }
 };
 
 // One 16-byte group of a row starting at token `tok` (a multiple of the group
@@ -156,9 +162,10 @@ __device__ __forceinline__ float scale_of(float T) {
     return static_cast<float>(kLog2e / static_cast<double>(T));
 }
 
-// A wave-uniform read of memory no kernel of the call writes, through the
-// constant address space so that it becomes a scalar load (its own counter,
-// no wait on outstanding vector loads).
+// A wave-uniform read of memory that nothing writes while the kernel runs
+// (an earlier kernel of the call may have written it), through the constant
+// address space so that it becomes a scalar load (its own counter, no wait on
+// outstanding vector loads).
 template <typename T>
 __device__ __forceinline__ T uniform_load(const T *p) {
     typedef const __attribute__((address_space(4))) T ConstT;
@@ -172,6 +179,15 @@ constexpr int kBufferWord3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
                                              kBufferWord3);
+}
+
+// Wave-uniform words read with vector (buffer) loads at a uniform offset:
+// they join the in-order vector memory counter of the loads issued next to
+// them, so that one wait covers them all, where the wait for a scalar load
+// also covers every scalar load issued after it.  The caller makes them
+// uniform (`uniform_word`) where it first needs them.
+__device__ __forceinline__ uint32_t uniform_word(uint32_t w) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(w)));
 }
 
 // ------------------------------------------------------------ request geometry
@@ -734,16 +750,15 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
     // With a mask the two paths measured faster.
     float v[G * P];
     if constexpr (!MASKED) {
-        unpack_full_block<ET, MASKED>(r, m, lane, v);
+        uint4 w[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) w[g] = r[g];
         if (!s.full) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int64_t tok = int64_t(s.blk) * kBlock + (g * kWave + lane) * P;
-#pragma unroll
-                for (int e = 0; e < P; ++e)
-                    if (tok >= a.V) v[g * P + e] = -INFINITY;
-            }
+            for (int g = 0; g < G; ++g)
+                if (s.blk * kBlock + (g * kWave + lane) * P >= a.V) w[g] = Logit<ET>::neg_inf_group();
         }
+        unpack_full_block<ET, MASKED>(w, m, lane, v);
     } else if (s.full) {
         unpack_full_block<ET, MASKED>(r, m, lane, v);
     } else {
@@ -1651,12 +1666,9 @@ struct FinalShared {
     Level1 l1p[kMaxDraft + 1];  // level-1 winner under p
     Level1 l1x[kMaxDraft + 1];  // level-1 winner under p without the row's draft
     int X[kMaxDraft];
-    float lx[kMaxDraft], qx[kMaxDraft];
-    double keyx[kMaxDraft];
     double acc[kMaxDraft];
-    double u[kMaxDraft];        // the accept draws
     unsigned char ok[kMaxDraft], flag[kMaxDraft], invalid[kMaxDraft], badq[kMaxDraft];
-    uint32_t status;
+    unsigned char rowst[kMaxDraft + 1];  // per row: SD_STATUS_* bits found by its wave
     int staged_c;               // block of the sampled row held in blockv (-1: none)
     double red_d[kFinalWaves];
     uint64_t red_u[kFinalWaves];
@@ -1912,7 +1924,9 @@ __device__ int2 level2(const FinalArgs &a, FinalShared &sh, int b, int n, int64_
 }
 
 // A lane's share of one row's block statistics, blocks lane + 64 j for
-// j < kFoldCache, loaded once (absent blocks read as empty).  Rows of more
+// j < kFoldCache, loaded once (absent blocks are clamped to the last one and
+// read as empty where the cached fold uses them, so that nothing waits for
+// the loads here).  Rows of more
 // than 64 kFoldCache blocks fold the rest straight from memory.
 constexpr int kFoldCache = 2;
 
@@ -1926,11 +1940,6 @@ __device__ __forceinline__ void load_fold_cache(const BlockStat *st, int C, int 
         const int cb = lane + kWave * j;
         const int cc = cb < C ? cb : C - 1;  // clamped: every lane loads, no branch
         fc.e[j] = st[cc];
-        if (cb >= C) {
-            fc.e[j].m = -INFINITY;
-            fc.e[j].s = 0.0f;
-            fc.e[j].key = -INFINITY;
-        }
     }
 }
 
@@ -1969,8 +1978,8 @@ __device__ __forceinline__ void fold_greedy_row(const BlockStat *st, const FoldC
         sh.M[i] = m;
         sh.G[i] = gi;
         sh.S[i] = 1.0;
-        if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
-        else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+        if (bad) sh.rowst[i] |= SD_STATUS_BAD_LOGIT;
+        else if (m == -INFINITY) sh.rowst[i] |= SD_STATUS_EMPTY_ROW;
     }
 }
 
@@ -2042,8 +2051,8 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
         sh.G[i] = -1;
         sh.l1p[i] = bp ? Level1{packed_index(bp), tp ? 1 : 0} : Level1{-1, 0};
         sh.l1x[i] = bx ? Level1{packed_index(bx), tx ? 1 : 0} : Level1{-1, 0};
-        if (bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
-        else if (m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+        if (bad) sh.rowst[i] |= SD_STATUS_BAD_LOGIT;
+        else if (m == -INFINITY) sh.rowst[i] |= SD_STATUS_EMPTY_ROW;
     }
 }
 
@@ -2061,14 +2070,19 @@ struct CachedFold {
     bool live[kFoldCache];    // entries with mass
 };
 
-__device__ __forceinline__ CachedFold fold_races(const FoldCache &fc, int cx, double keyx) {
+__device__ __forceinline__ CachedFold fold_races(FoldCache &fc, int C, int cx, double keyx) {
     const int lane = threadIdx.x & (kWave - 1);
     CachedFold f;
     bool bad = false;
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kFoldCache; ++j) {
-        const BlockStat &e = fc.e[j];
+        BlockStat &e = fc.e[j];
+        if (lane + kWave * j >= C) {  // past the row: empty
+            e.m = -INFINITY;
+            e.s = 0.0f;
+            e.key = -INFINITY;
+        }
         bad |= (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
         mx = fmaxf(mx, e.m);
     }
@@ -2125,9 +2139,57 @@ __device__ __forceinline__ void fold_finish(const FoldCache &fc, const CachedFol
         sh.G[i] = -1;
         sh.l1p[i] = f.bp ? Level1{packed_index(f.bp), tp ? 1 : 0} : Level1{-1, 0};
         sh.l1x[i] = f.bx ? Level1{packed_index(f.bx), tx ? 1 : 0} : Level1{-1, 0};
-        if (f.bad) atomicOr(&sh.status, SD_STATUS_BAD_LOGIT);
-        else if (f.m == -INFINITY) atomicOr(&sh.status, SD_STATUS_EMPTY_ROW);
+        if (f.bad) sh.rowst[i] |= SD_STATUS_BAD_LOGIT;
+        else if (f.m == -INFINITY) sh.rowst[i] |= SD_STATUS_EMPTY_ROW;
     }
+}
+
+// A draft row's draft token and what the row sweep recorded about it, read
+// by the wave that folds the row, with the position's accept draw.
+struct RowDraft {
+    int x = -1;            // the draft token (unchecked)
+    float lx = -INFINITY;  // its logit
+    float qx = 1.0f;       // q_i(x)
+    bool invalid = false;  // outside the mask
+    double keyx = -INFINITY;  // level-1 key of its block without it
+    double u = 0.0;        // the accept draw
+};
+
+// Row i's draft and record as issued loads (rows past the request's drafts
+// read zeros); `settle_row_draft` takes the values once they are needed.
+struct RowDraftLoads {
+    uint32_t x;
+    uint32_t lx, qx, allowed;
+    uint32_t keyx_lo, keyx_hi;
+};
+
+__device__ __forceinline__ RowDraftLoads issue_row_draft(const FinalArgs &a, const ReqGeom &geo, int i) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t rd = buffer_of(a.draft + geo.draft0, uint32_t(geo.k) * 4u);
+    const __amdgpu_buffer_rsrc_t rr =
+        buffer_of(a.drec + geo.row0, uint32_t(geo.k + 1) * uint32_t(sizeof(DraftRec)));
+    RowDraftLoads l;
+    l.x = __builtin_amdgcn_raw_buffer_load_b32(rd, 0, i * 4, 0);
+    const int ro = i * int(sizeof(DraftRec));
+    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rr, 0, ro, 0);  // sx, lx, qx, allowed
+    const u32x2 kx = __builtin_amdgcn_raw_buffer_load_b64(rr, 0, ro + 16, 0);
+    l.lx = r.y;
+    l.qx = r.z;
+    l.allowed = r.w;
+    l.keyx_lo = kx.x;
+    l.keyx_hi = kx.y;
+    return l;
+}
+
+__device__ __forceinline__ RowDraft settle_row_draft(const RowDraftLoads &l) {
+    RowDraft d;  // the record is used only when x is valid
+    d.x = static_cast<int>(uniform_word(l.x));
+    d.lx = __uint_as_float(uniform_word(l.lx));
+    d.qx = __uint_as_float(uniform_word(l.qx));
+    d.invalid = !(uniform_word(l.allowed) & 1u);
+    d.keyx = __hiloint2double(static_cast<int>(uniform_word(l.keyx_hi)), static_cast<int>(uniform_word(l.keyx_lo)));
+    return d;
 }
 
 // Position i's verdict, taken by lane 0 of the wave that folded row i: the
@@ -2135,23 +2197,21 @@ __device__ __forceinline__ void fold_finish(const FoldCache &fc, const CachedFol
 // the accept draw against it, its boundary flag, and whether the draft's q is
 // unusable (reported only when nothing else is wrong).  Greedy rows accept a
 // draft equal to the row's argmax.
-__device__ __forceinline__ void judge_position(FinalShared &sh, int i, bool greedy, float c, bool one_hot) {
-    const int xi = sh.X[i];
+__device__ __forceinline__ void judge_position(FinalShared &sh, int i, bool greedy, float c, bool one_hot,
+                                               const RowDraft &d) {
     bool ok, flag = false, badq = false;
     double acc;
     if (greedy) {
-        ok = (xi == sh.G[i]);
+        ok = (d.x == sh.G[i]);
         acc = ok ? 1.0 : 0.0;
     } else {
-        const bool inv = sh.invalid[i];
-        const float lx = sh.lx[i], qx = sh.qx[i];
         double p = 0.0;
-        if (!inv && lx > -INFINITY)
-            p = exp2(static_cast<double>(lx) * c - static_cast<double>(sh.M[i])) / sh.S[i];
-        badq = !one_hot && !(qx >= 0.0f && qx <= FLT_MAX);
-        const double q = qx;
+        if (!d.invalid && d.lx > -INFINITY)
+            p = exp2(static_cast<double>(d.lx) * c - static_cast<double>(sh.M[i])) / sh.S[i];
+        badq = !one_hot && !(d.qx >= 0.0f && d.qx <= FLT_MAX);
+        const double q = d.qx;
         acc = (p == 0.0) ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-        const double u = sh.u[i];
+        const double u = d.u;
         ok = u < acc;
         flag = fabs(u - acc) < kAcceptFlagEps;
     }
@@ -2229,90 +2289,93 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const ReqGeom geo = req_geom(a.off, a.off_ok, b, a.k);
     const int k = geo.k, kp1 = geo.k + 1, V = a.V, C = a.C;
-    const float T = uniform_load(a.temperature + b);
-    const bool greedy = (T == 0.0f);
-    const bool bad_T = !greedy && !(T > 0.0f && T <= FLT_MAX);
-    const bool skip_rows = bad_T || !geo.ok;  // nothing of the request's rows is read
+    // ---- this wave's first row: its block statistics, draft and record are
+    //      all in flight before anything waits for memory
+    FoldCache fc;
+    if (geo.ok && wave < kp1) load_fold_cache(a.bstats + (geo.row0 + wave) * C, C, lane, fc);
+    const RowDraftLoads rl = issue_row_draft(a, geo, wave);
+    const uint32_t Tw = __builtin_amdgcn_raw_buffer_load_b32(buffer_of(a.temperature, uint32_t(a.B) * 4u), 0, b * 4, 0);
     const PhiloxKey key = key_of(a.seed);
-    const float c = greedy || bad_T ? 0.0f : scale_of(T);
-    constexpr bool one_hot = !DENSE;
+    // the accept draw depends on nothing loaded: drawn while the loads fly
+    const double u0 = wave < k ? draw_accept(key, b, wave) : 0.0;
     // the row-statistics kernel has finished: its claim counters go back to
     // zero for the next call
     if (b == 0 && tid < kSweepParts) a.sweep[tid * kSweepCtrStride] = 0u;
-
-    // ---- this wave's first row's block statistics, in flight with the drafts
-    FoldCache fc;
-    if (!skip_rows && wave < kp1) load_fold_cache(a.bstats + (geo.row0 + wave) * C, C, lane, fc);
-
-    // ---- drafts, and what the sweep recorded about them
-    int x = -1;
-    if (tid < k) x = a.draft[geo.draft0 + tid];
-    const bool xok = tid < k && x >= 0 && x < V;
-    DraftRec rec;
-    if (tid < k) rec = a.drec[geo.row0 + tid];  // read only when xok and T is valid
-    // the accept draws depend on nothing loaded: drawn while the loads fly
-    const double u_acc = tid < k ? draw_accept(key, b, tid) : 0.0;
-    if (tid == 0) {
-        sh.status = (bad_T ? SD_STATUS_TEMPERATURE : 0u) | (geo.ok ? 0u : SD_STATUS_BAD_OFFSETS);
-        sh.staged_c = -1;
-    }
-    __syncthreads();
-    if (tid < k) {
-        sh.X[tid] = x;
-        if (!xok) atomicOr(&sh.status, SD_STATUS_DRAFT_ID);
-        sh.lx[tid] = rec.lx;
-        sh.qx[tid] = rec.qx;
-        sh.keyx[tid] = rec.keyx;
-        sh.invalid[tid] = !(rec.allowed & 1u);
-        sh.u[tid] = u_acc;
-    }
-    __syncthreads();
+    if (tid == 0) sh.staged_c = -1;  // read only after the fold's barrier
+    const float T = __uint_as_float(uniform_word(Tw));
+    const bool greedy = (T == 0.0f);
+    const bool bad_T = !greedy && !(T > 0.0f && T <= FLT_MAX);
+    const bool skip_rows = bad_T || !geo.ok;  // nothing of the request's rows is used
+    const float c = greedy || bad_T ? 0.0f : scale_of(T);
+    constexpr bool one_hot = !DENSE;
+    RowDraft rd = settle_row_draft(rl);
+    rd.u = u0;
 
     // ---- one wave per row: fold the block statistics; sampling rows also run
-    //      their level-1 race and start loading the block they would sample
+    //      their level-1 race and start loading the block they would sample;
+    //      draft rows then take their position's verdict
     uint4 stage_r[G];
     uint32_t stage_m[G];
     int stage_row = -1, stage_c = -1;
-    if (!skip_rows) {
-        for (int i = wave; i < kp1; i += kFinalWaves) {
-            const int64_t row = geo.row0 + i;
-            const BlockStat *st = a.bstats + row * C;
-            if (i != wave) load_fold_cache(st, C, lane, fc);  // rows past the first wave of rows
-            if (greedy) {
-                fold_greedy_row(st, fc, C, i, sh);
-                if (i < k && lane == 0) judge_position(sh, i, true, c, one_hot);
-                continue;
+    for (int i = wave; i < kp1; i += kFinalWaves) {
+        const int64_t row = geo.row0 + i;
+        const BlockStat *st = a.bstats + row * C;
+        if (i != wave) {  // rows past the first wave of rows
+            if (geo.ok) load_fold_cache(st, C, lane, fc);
+            if (i < k) {
+                rd = settle_row_draft(issue_row_draft(a, geo, i));
+                rd.u = draw_accept(key, b, i);
             }
-            const int xi = (i < k) ? sh.X[i] : -1;
-            const int cx = (one_hot && xi >= 0 && xi < V) ? xi / kBlock : -1;
-            const double keyx = cx >= 0 ? sh.keyx[i] : -INFINITY;
-            int pre = -1;  // the block this row samples from, if it is the one emitting
-            if (C <= kWave * kFoldCache) {
-                const CachedFold f = fold_races(fc, cx, keyx);
-                const uint64_t w = (i < k) ? (one_hot ? f.bx : 0ull) : f.bp;
-                pre = w ? packed_index(w) : -1;
-                if (ALIGNED && kp1 <= kFinalWaves) stage_block<ET>(a, static_cast<int>(row), pre, lane, stage_r, stage_m);
-                fold_finish(fc, f, i, cx, keyx, sh);
-            } else {
-                fold_sampling_row(st, fc, C, i, cx, keyx, sh);
-                const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
-                pre = l1.c;
-                if (ALIGNED && kp1 <= kFinalWaves) stage_block<ET>(a, static_cast<int>(row), pre, lane, stage_r, stage_m);
-            }
-            if (ALIGNED && kp1 <= kFinalWaves && pre >= 0) {
-                stage_row = i;
-                stage_c = pre;
-            }
-            if (i < k && lane == 0) judge_position(sh, i, false, c, one_hot);
         }
+        const int xi = (i < k) ? rd.x : -1;
+        const bool xok = xi >= 0 && xi < V;
+        if (lane == 0) {
+            sh.rowst[i] = (i < k && !xok) ? SD_STATUS_DRAFT_ID : 0u;
+            if (i < k) {
+                sh.X[i] = xi;
+                sh.invalid[i] = rd.invalid;
+            }
+        }
+        if (skip_rows) continue;
+        if (greedy) {
+            fold_greedy_row(st, fc, C, i, sh);
+            if (i < k && lane == 0) judge_position(sh, i, true, c, one_hot, rd);
+            continue;
+        }
+        const int cx = (one_hot && xok) ? xi / kBlock : -1;
+        const double keyx = cx >= 0 ? rd.keyx : -INFINITY;
+        int pre = -1;  // the block this row samples from, if it is the one emitting
+        if (C <= kWave * kFoldCache) {
+            const CachedFold f = fold_races(fc, C, cx, keyx);
+            const uint64_t w = (i < k) ? (one_hot ? f.bx : 0ull) : f.bp;
+            pre = w ? packed_index(w) : -1;
+            if (ALIGNED && kp1 <= kFinalWaves) stage_block<ET>(a, static_cast<int>(row), pre, lane, stage_r, stage_m);
+            fold_finish(fc, f, i, cx, keyx, sh);
+        } else {
+            fold_sampling_row(st, fc, C, i, cx, keyx, sh);
+            const Level1 l1 = (i < k) ? (one_hot ? sh.l1x[i] : Level1{-1, 0}) : sh.l1p[i];
+            pre = l1.c;
+            if (ALIGNED && kp1 <= kFinalWaves) stage_block<ET>(a, static_cast<int>(row), pre, lane, stage_r, stage_m);
+        }
+        if (ALIGNED && kp1 <= kFinalWaves && pre >= 0) {
+            stage_row = i;
+            stage_c = pre;
+        }
+        if (i < k && lane == 0) judge_position(sh, i, false, c, one_hot, rd);
     }
     lds_barrier();
 
-    // ---- every wave reads the k <= 64 verdicts and finds the first
-    //      rejection with ballots (all waves agree, so no barrier follows)
-    uint32_t st = sh.status;
+    // ---- every wave reads the rows' status bits and the k <= 64 verdicts and
+    //      finds the first rejection with ballots (all waves agree, so no
+    //      barrier follows)
+    uint32_t st = (bad_T ? SD_STATUS_TEMPERATURE : 0u) | (geo.ok ? 0u : SD_STATUS_BAD_OFFSETS);
     int nacc = 0, flag_acc = 0, ninv = 0;
     {
+        uint32_t rs = lane < kp1 ? sh.rowst[lane] : 0u;
+        if (kp1 > kWave) rs |= sh.rowst[kWave];
+#pragma unroll
+        for (uint32_t bit : {SD_STATUS_DRAFT_ID, SD_STATUS_EMPTY_ROW, SD_STATUS_BAD_LOGIT})
+            if (__ballot((rs & bit) != 0u) != 0ull) st |= bit;
         bool okv = false, flv = false, inv = false, bq = false;
         if (lane < k) {
             okv = sh.ok[lane];
@@ -2726,23 +2789,24 @@ FinalFn pick_final(bool aligned, bool dense, bool split) {
 }
 
 // Workgroups of kThreads threads of `kernel` that the current device holds
-// at once (0 when the runtime cannot say); cached per device and kernel.
-inline int64_t resident_workgroups(const void *kernel) {
+// at once, at most per_cu_max per CU (0 when the runtime cannot say); the
+// runtime's answer is cached per device and kernel.
+inline int64_t resident_workgroups(const void *kernel, int per_cu_max) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     static std::mutex mu;
-    static std::map<std::pair<int, const void *>, int64_t> cache;
+    static std::map<std::pair<int, const void *>, std::pair<int, int>> cache;  // (CUs, per CU)
     std::lock_guard<std::mutex> lock(mu);
     const auto key = std::make_pair(dev, kernel);
-    const auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
-        return 0;
-    const int64_t n = int64_t(cus) * per_cu;
-    cache[key] = n;
-    return n;
+    auto it = cache.find(key);
+    if (it == cache.end()) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+            return 0;
+        it = cache.emplace(key, std::make_pair(cus, per_cu)).first;
+    }
+    return int64_t(it->second.first) * std::min(it->second.second, per_cu_max);
 }
 
 struct Layout {
@@ -2937,7 +3001,10 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     } else if (aligned) {
         // the resident capacity, a multiple of 8 (the sweep's partition
         // layout), and no more than two blocks per wave need
-        int64_t cap = resident_workgroups(reinterpret_cast<const void *>(k1));
+        // Three waves per SIMD, each with a block in flight while it reduces
+        // another, keep HBM busy; a fourth (where the registers allow it)
+        // measured slower.
+        int64_t cap = resident_workgroups(reinterpret_cast<const void *>(k1), SDV_SWEEP_WG_PER_CU);
         if (cap < 8) cap = SDV_ROW_STATS_GRID;
         const int64_t need = (ra.nblk + 2 * waves_per_wg - 1) / (2 * waves_per_wg);
         grid1 = (std::min(cap, need) + 7) / 8 * 8;
