@@ -43,11 +43,11 @@
 #ifndef SDV_BLOCKS_PER_WAVE
 #define SDV_BLOCKS_PER_WAVE 4   // element kernel: 2048-token blocks per wave task
 #endif
-#ifndef SDV_ROW_STATS_GRID
-#define SDV_ROW_STATS_GRID 768  // claimed sweep: workgroups when the occupancy query fails
+#ifndef SDV_SWEEP_WAVES
+#define SDV_SWEEP_WAVES 3072  // claimed sweep: waves in the grid when the occupancy query fails
 #endif
-#ifndef SDV_SWEEP_WG_PER_CU
-#define SDV_SWEEP_WG_PER_CU 3  // claimed sweep: at most this many workgroups (waves per SIMD) per CU
+#ifndef SDV_SWEEP_WAVES_PER_SIMD
+#define SDV_SWEEP_WAVES_PER_SIMD 3  // claimed sweep: at most this many waves per SIMD
 #endif
 #ifndef SDV_ROW_STATS_GRID_STRIDED
 #define SDV_ROW_STATS_GRID_STRIDED 2048  // strided (masked) sweep: workgroups
@@ -59,7 +59,15 @@
 namespace sdv {
 
 constexpr int kBlock = SD_BLOCK_TOKENS;
-constexpr int kThreads = 256;       // row statistics: 4 waves per workgroup
+constexpr int kThreads = 256;       // row statistics (strided sweep, element path): 4 waves per workgroup
+#ifndef SDV_SWEEP_THREADS
+#define SDV_SWEEP_THREADS 768
+#endif
+// Claimed sweep: 12 waves per workgroup, one workgroup per CU.  The grid
+// starts a third as many workgroups as with 4 waves each, and the
+// dispatcher's ramp at the start of the kernel is that much shorter.
+constexpr int kSweepThreads = SDV_SWEEP_THREADS;
+constexpr int kSimdsPerCu = 4;
 constexpr int kFinalThreads = 512;  // finalize: 8 waves per request
 constexpr int kFinalWaves = kFinalThreads / 64;
 // s_waitcnt operand (GFX9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
@@ -589,7 +597,7 @@ struct SweepPlan {  // 32-bit: block indices are below 2^31, and scalar compares
 
 // Needs gridDim.x to be a multiple of 8 and 2^parts_log2 <= 4 gridDim.x / 8.
 __device__ __forceinline__ SweepPlan plan_of(const RowStatsArgs &a) {
-    constexpr int WPG = kThreads / kWave;
+    constexpr int WPG = kSweepThreads / kWave;
     const int lg = a.parts_log2, P = 1 << lg;
     const int x = blockIdx.x & 7;
     const int u = static_cast<int>(blockIdx.x >> 3) * WPG + wave_id();
@@ -930,7 +938,7 @@ __device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
 }
 
 template <typename ET, bool MASKED, bool TOPK>
-__global__ __launch_bounds__(kThreads) void row_stats_vec_kernel(RowStatsArgs a) {
+__global__ __launch_bounds__(MASKED ? kThreads : kSweepThreads) void row_stats_vec_kernel(RowStatsArgs a) {
     zero_call_outputs(a);
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
@@ -2791,7 +2799,7 @@ FinalFn pick_final(bool aligned, bool dense, bool split) {
 // Workgroups of kThreads threads of `kernel` that the current device holds
 // at once, at most per_cu_max per CU (0 when the runtime cannot say); the
 // runtime's answer is cached per device and kernel.
-inline int64_t resident_workgroups(const void *kernel, int per_cu_max) {
+inline int64_t resident_workgroups(const void *kernel, int threads, int per_cu_max) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     static std::mutex mu;
@@ -2802,7 +2810,7 @@ inline int64_t resident_workgroups(const void *kernel, int per_cu_max) {
     if (it == cache.end()) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
             return 0;
         it = cache.emplace(key, std::make_pair(cus, per_cu)).first;
     }
@@ -2993,19 +3001,20 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     const bool topk = thresholds;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
                          : pick_row_stats<float>(masked, aligned, topk);
-    const int64_t waves_per_wg = kThreads / kWave;
+    const int k1_threads = (aligned && !masked) ? kSweepThreads : kThreads;
+    const int64_t waves_per_wg = k1_threads / kWave;
     int64_t grid1;
     if (aligned && ra.nblk >= (int64_t(1) << 31)) return SD_ERR_UNSUPPORTED;  // block indices are 31-bit
     if (aligned && masked) {
         grid1 = std::min<int64_t>((ra.nblk + waves_per_wg - 1) / waves_per_wg, SDV_ROW_STATS_GRID_STRIDED);
     } else if (aligned) {
-        // the resident capacity, a multiple of 8 (the sweep's partition
-        // layout), and no more than two blocks per wave need
-        // Three waves per SIMD, each with a block in flight while it reduces
-        // another, keep HBM busy; a fourth (where the registers allow it)
-        // measured slower.
-        int64_t cap = resident_workgroups(reinterpret_cast<const void *>(k1), SDV_SWEEP_WG_PER_CU);
-        if (cap < 8) cap = SDV_ROW_STATS_GRID;
+        // The resident capacity at three waves per SIMD (each with a block in
+        // flight while it reduces another, they keep HBM busy; a fourth, where
+        // the registers allow it, measured slower), a multiple of 8 (the
+        // sweep's partition layout), and no more than two blocks per wave need.
+        const int per_cu_max = std::max<int>(1, SDV_SWEEP_WAVES_PER_SIMD * kSimdsPerCu / int(waves_per_wg));
+        int64_t cap = resident_workgroups(reinterpret_cast<const void *>(k1), k1_threads, per_cu_max);
+        if (cap < 8) cap = SDV_SWEEP_WAVES / waves_per_wg;
         const int64_t need = (ra.nblk + 2 * waves_per_wg - 1) / (2 * waves_per_wg);
         grid1 = (std::min(cap, need) + 7) / 8 * 8;
         ra.parts_log2 = 0;  // partitions: a power of two, at most the wave slots per XCD
@@ -3046,7 +3055,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     if (p->row_stats_event_begin &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_begin), stream) != hipSuccess)
         return SD_ERR_HIP;
-    hipLaunchKernelGGL(k1, dim3(static_cast<unsigned>(grid1)), dim3(kThreads), 0, stream, ra);
+    hipLaunchKernelGGL(k1, dim3(static_cast<unsigned>(grid1)), dim3(k1_threads), 0, stream, ra);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     if (p->row_stats_event_end &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_end), stream) != hipSuccess)

@@ -346,6 +346,28 @@ def test_malformed_requests():
     assert gpu["status"] == 1 | 2 | 4 | 8 | 16
 
 
+@pytest.mark.parametrize("dense", [False, True])
+def test_status_bits_past_the_first_rows(dense):
+    """k = 64: errors in rows folded after the first wave of rows, in the
+    bonus row (row 64, past the 64 lanes of the status scan) and at the last
+    draft position, one-hot and dense."""
+    announce(f"status bits k=64 dense={dense}")
+    wl = _custom(6, 64, 2500, dense=dense, masked=True, seed=21)
+    wl["logits"][0, 64, 17] = float("nan")                    # NaN at an allowed token
+    wl["bitmask"][0, 64, 0] |= (1 << 17)                      # ... of the bonus row
+    wl["bitmask"][1, 40, :] = 0                               # empty row 40
+    wl["draft_token_ids"][2, 63] = 2500                       # last draft out of range
+    wl["temperature"][3] = 0.0                                # greedy, with a draft
+    wl["draft_token_ids"][3, 9] = -1                          # ... out of range at row 9
+    if dense:
+        wl["draft_probs"][4, 50, wl["draft_token_ids"][4, 50]] = float("inf")
+    gpu, orc = run_gpu(wl), run_oracle(wl)
+    want = [8, 4, 1, 1, 16 if dense else 0, 0]
+    assert list(orc["request_status"]) == want
+    assert_parity(gpu, orc)
+    assert gpu["status"] == (1 | 4 | 8 | (16 if dense else 0))
+
+
 def test_largest_batch_counters():
     """SD_MAX_BATCH requests: every workgroup's share reaches the counters,
     with requests in error among them."""
