@@ -55,6 +55,13 @@
 #ifndef SDV_LOGITS_CACHE_POLICY
 #define SDV_LOGITS_CACHE_POLICY 2  // logits loads: non-temporal (read once, kept out of the caches)
 #endif
+#ifndef SDV_CACHED_LOGITS_BYTES
+// Calls whose logits take at most this many bytes (a quarter of the 256 MB
+// Infinity Cache) read them through the caches instead, so that the
+// finalisation's second reads (the dense residual's rows, the sampled block)
+// find them there.
+#define SDV_CACHED_LOGITS_BYTES (64ll << 20)
+#endif
 
 namespace sdv {
 
@@ -686,7 +693,7 @@ constexpr int kPastAnyBuffer = 0x40000000;
 // faster.  Either way the groups of a partial block that lie past the row
 // read zeros (they are replaced by -inf when the block is reduced), and a
 // dead issue's loads return zeros and touch no memory.
-template <typename ET, bool MASKED>
+template <typename ET, bool MASKED, int POL = SDV_LOGITS_CACHE_POLICY>
 __device__ __forceinline__ void issue_block(const RowStatsArgs &a, int row, int blk, int lane, uint4 *r,
                                             uint32_t *m, bool live = true) {
     constexpr int P = Logit<ET>::kPer16;
@@ -700,7 +707,7 @@ __device__ __forceinline__ void issue_block(const RowStatsArgs &a, int row, int 
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + g * kWave * 16, 0,
-                                                                  SDV_LOGITS_CACHE_POLICY);
+                                                                  POL);
             r[g] = make_uint4(w.x, w.y, w.z, w.w);
         }
     } else {
@@ -709,7 +716,7 @@ __device__ __forceinline__ void issue_block(const RowStatsArgs &a, int row, int 
         const int base = live ? blk * kBlock * int(sizeof(ET)) + lane * 16 : kPastAnyBuffer;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, SDV_LOGITS_CACHE_POLICY);
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, POL);
             r[g] = make_uint4(w.x, w.y, w.z, w.w);
         }
         const __amdgpu_buffer_rsrc_t rm = buffer_of(a.mask + int64_t(row) * a.W, uint32_t(a.W) * 4u);
@@ -811,7 +818,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
 // gains (masked rows take more work per block, so a wave holds more blocks).
 // Each wave keeps the loads of its next block in flight while it reduces the
 // current one.
-template <typename ET, bool MASKED, bool TOPK>
+template <typename ET, bool MASKED, bool TOPK, int POL>
 __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -833,7 +840,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     // placed after the issue cannot take the registers the loads fill, and a
     // temporary in a register with a load outstanding waits for every load.
     const SweepCursor c0 = cursor_at(a, block_of(pl, pl.k0));
-    issue_block<ET, MASKED>(a, c0.row, c0.blk, lane, ra, ma);
+    issue_block<ET, MASKED, POL>(a, c0.row, c0.blk, lane, ra, ma);
     SweepBlock sa = sweep_block(a, c0);
     // Two claims are in flight, one for each half of the loop (claims of one
     // lane on one address return in the order issued, so once a claim finds
@@ -851,7 +858,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     do {
         const bool more1 = kn < pl.lim;
         const SweepCursor c1 = cursor_at(a, block_of(pl, more1 ? kn : pl.k0));
-        issue_block<ET, MASKED>(a, c1.row, c1.blk, lane, rb, mb, more1);
+        issue_block<ET, MASKED, POL>(a, c1.row, c1.blk, lane, rb, mb, more1);
         const SweepBlock sb = sweep_block(a, c1);
         if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
         else settle(ra[G - 1]);
@@ -865,7 +872,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
             const bool more2 = kn < pl.lim;
             ca = claim(pl, lane);
             const SweepCursor c2 = cursor_at(a, block_of(pl, more2 ? kn : pl.k0));
-            issue_block<ET, MASKED>(a, c2.row, c2.blk, lane, ra, ma, more2);
+            issue_block<ET, MASKED, POL>(a, c2.row, c2.blk, lane, ra, ma, more2);
             sa = sweep_block(a, c2);
             if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
             else settle(rb[G - 1]);
@@ -893,7 +900,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
 // whole grid reads one contiguous window of the logits at a time; the cursor
 // steps by precomputed quotients.  The look-ahead index is clamped to the
 // current block at the end of the sweep (a dead issue, reading nothing).
-template <typename ET, bool MASKED, bool TOPK>
+template <typename ET, bool MASKED, bool TOPK, int POL>
 __device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -909,12 +916,12 @@ __device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
     const SweepStep step = step_of(a, stride);
     SweepCursor ca = cursor_at(a, g0);
     SweepBlock sa = sweep_block(a, ca);
-    issue_block<ET, MASKED>(a, ca.row, ca.blk, lane, ra, ma);
+    issue_block<ET, MASKED, POL>(a, ca.row, ca.blk, lane, ra, ma);
     for (;;) {
         const bool more1 = ca.gb + stride < a.nblk;
         const SweepCursor cb = more1 ? advance(a, ca, step) : ca;
         const SweepBlock sb = sweep_block(a, cb);
-        issue_block<ET, MASKED>(a, cb.row, cb.blk, lane, rb, mb, more1);
+        issue_block<ET, MASKED, POL>(a, cb.row, cb.blk, lane, rb, mb, more1);
         if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
@@ -925,7 +932,7 @@ __device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
         const bool more2 = cb.gb + stride < a.nblk;
         ca = more2 ? advance(a, cb, step) : cb;
         sa = sweep_block(a, ca);
-        issue_block<ET, MASKED>(a, ca.row, ca.blk, lane, ra, ma, more2);
+        issue_block<ET, MASKED, POL>(a, ca.row, ca.blk, lane, ra, ma, more2);
         if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
@@ -937,13 +944,14 @@ __device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
     flush_stash(a, st, key, lane, count);
 }
 
-template <typename ET, bool MASKED, bool TOPK>
+// POL: the cache policy of the logits loads.
+template <typename ET, bool MASKED, bool TOPK, int POL>
 __global__ __launch_bounds__(MASKED ? kThreads : kSweepThreads) void row_stats_vec_kernel(RowStatsArgs a) {
     zero_call_outputs(a);
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
-    if constexpr (MASKED) sweep_strided<ET, MASKED, TOPK>(a, lane);
-    else sweep_claimed<ET, MASKED, TOPK>(a, lane);
+    if constexpr (MASKED) sweep_strided<ET, MASKED, TOPK, POL>(a, lane);
+    else sweep_claimed<ET, MASKED, TOPK, POL>(a, lane);
 }
 
 // Any alignment and any V: element loads clamped into the row, one chunk of
@@ -2753,11 +2761,17 @@ __global__ __launch_bounds__(1024) void histogram_kernel(const int32_t *num_acce
 using RowStatsFn = void (*)(RowStatsArgs);
 using FinalFn = void (*)(FinalArgs);
 
+template <typename ET, int POL>
+RowStatsFn pick_row_stats_vec(bool masked, bool topk) {
+    if (topk) return masked ? row_stats_vec_kernel<ET, true, true, POL> : row_stats_vec_kernel<ET, false, true, POL>;
+    return masked ? row_stats_vec_kernel<ET, true, false, POL> : row_stats_vec_kernel<ET, false, false, POL>;
+}
+
 template <typename ET>
-RowStatsFn pick_row_stats(bool masked, bool aligned, bool topk) {
+RowStatsFn pick_row_stats(bool masked, bool aligned, bool topk, bool cached) {
     if (aligned) {
-        if (topk) return masked ? row_stats_vec_kernel<ET, true, true> : row_stats_vec_kernel<ET, false, true>;
-        return masked ? row_stats_vec_kernel<ET, true, false> : row_stats_vec_kernel<ET, false, false>;
+        return cached ? pick_row_stats_vec<ET, 0>(masked, topk)
+                      : pick_row_stats_vec<ET, SDV_LOGITS_CACHE_POLICY>(masked, topk);
     }
     if (topk) return masked ? row_stats_elem_kernel<ET, true, true> : row_stats_elem_kernel<ET, false, true>;
     return masked ? row_stats_elem_kernel<ET, true, false> : row_stats_elem_kernel<ET, false, false>;
@@ -2999,8 +3013,9 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.C = L.C;
 
     const bool topk = thresholds;
-    RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk)
-                         : pick_row_stats<float>(masked, aligned, topk);
+    const bool cached = L.rows * int64_t(V) * (bf16 ? 2 : 4) <= SDV_CACHED_LOGITS_BYTES;
+    RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk, cached)
+                         : pick_row_stats<float>(masked, aligned, topk, cached);
     const int k1_threads = (aligned && !masked) ? kSweepThreads : kThreads;
     const int64_t waves_per_wg = k1_threads / kWave;
     int64_t grid1;
