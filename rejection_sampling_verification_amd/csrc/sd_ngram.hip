@@ -17,8 +17,8 @@
 // 2048 of them, stages the chunk (plus the max_n tokens before it) and the
 // tail in LDS, and reduces the packed key (c << 32 | ~e) to its maximum, which
 // orders by window length and then by earliest end.  A second one-workgroup
-// kernel combines the chunks of each request, copies the drafts and scans the
-// draft counts into the ragged offsets the verifier takes.
+// kernel combines the chunks of each request, scans the draft counts into the
+// ragged offsets the verifier takes and copies the drafts.
 //
 // Memory: each history token is read once by the chunk that holds it and at
 // most once more as the halo of the next chunk; the work is a few integer
@@ -135,50 +135,63 @@ __device__ __forceinline__ int request_result(const EmitArgs &a, int b, int L, i
     return n > 0 ? int(min(int64_t(a.k), int64_t(L) - e)) : 0;
 }
 
+// Threads own consecutive requests.  The draft counts are known from the
+// chunk keys alone, so they are scanned into the ragged offsets first (a
+// shuffle scan within each wave, then the wave totals); the history is then
+// read once per draft, into the per-request slots and the packed list.
 __global__ __launch_bounds__(kEmitThreads) void ngram_emit_kernel(EmitArgs a) {
-    __shared__ uint32_t scan[kEmitThreads];
+    __shared__ uint32_t wtot[kEmitWaves];
     __shared__ uint32_t red[kEmitWaves];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int per = (a.B + kEmitThreads - 1) / kEmitThreads;
     const int b0 = min(tid * per, a.B), b1 = min(b0 + per, a.B);
     uint32_t total = 0, bad = 0;
+    int n0 = 0, cnt0 = 0;  // the first owned request's result, kept for the copy
+    int64_t e0 = 0;
     for (int b = b0; b < b1; ++b) {
         const int L = a.lengths[b];
         if (L < 0 || int64_t(L) > a.stride) bad = SD_NGRAM_STATUS_BAD_LENGTH;
         int n;
         int64_t e;
         const int cnt = request_result(a, b, L, n, e);
-        const int32_t *h = a.tokens + int64_t(b) * a.stride;
-        int32_t *d = a.drafts + int64_t(b) * a.k;
-        for (int i = 0; i < a.k; ++i) d[i] = i < cnt ? h[e + i] : -1;
-        a.num[b] = cnt;
-        if (a.match) a.match[b] = n;
+        if (b == b0) {
+            n0 = n;
+            e0 = e;
+            cnt0 = cnt;
+        }
         total += uint32_t(cnt);
     }
+    uint32_t start = 0;
     if (a.offsets) {
-        // exclusive scan of the per-thread totals (threads own consecutive requests)
-        scan[tid] = total;
-        for (int d = 1; d < kEmitThreads; d <<= 1) {
-            lds_barrier();
-            const uint32_t add = tid >= d ? scan[tid - d] : 0u;
-            lds_barrier();
-            scan[tid] += add;
+        uint32_t incl = total;  // inclusive scan within the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t t = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), d, 64));
+            if (lane >= d) incl += t;
         }
+        if (lane == 63) wtot[wave] = incl;
         lds_barrier();
-        uint32_t start = scan[tid] - total;
-        for (int b = b0; b < b1; ++b) {
-            const int L = a.lengths[b];
-            int n;
-            int64_t e;
-            const int cnt = request_result(a, b, L, n, e);
-            a.offsets[b] = int32_t(start);
-            if (a.flat) {
-                const int32_t *h = a.tokens + int64_t(b) * a.stride;
-                for (int i = 0; i < cnt; ++i) a.flat[start + i] = h[e + i];
-            }
-            start += uint32_t(cnt);
+        uint32_t before = 0;
+        for (int w = 0; w < wave; ++w) before += wtot[w];
+        start = before + incl - total;
+        if (tid == kEmitThreads - 1) a.offsets[a.B] = int32_t(start + total);
+    }
+    for (int b = b0; b < b1; ++b) {
+        int n = n0, cnt = cnt0;
+        int64_t e = e0;
+        if (b != b0) cnt = request_result(a, b, a.lengths[b], n, e);
+        const int32_t *h = a.tokens + int64_t(b) * a.stride;
+        int32_t *d = a.drafts + int64_t(b) * a.k;
+        int32_t *f = (a.offsets && a.flat) ? a.flat + start : nullptr;
+        for (int i = 0; i < a.k; ++i) {
+            const int32_t t = i < cnt ? h[e + i] : -1;
+            d[i] = t;
+            if (f && i < cnt) f[i] = t;
         }
-        if (tid == kEmitThreads - 1) a.offsets[a.B] = int32_t(scan[kEmitThreads - 1]);
+        a.num[b] = cnt;
+        if (a.match) a.match[b] = n;
+        if (a.offsets) a.offsets[b] = int32_t(start);
+        start += uint32_t(cnt);
     }
     if (a.status) {
         bad = sdv::block_max_u<kEmitWaves>(bad, red);
