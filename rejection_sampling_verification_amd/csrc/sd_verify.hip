@@ -80,8 +80,11 @@ constexpr int kFinalWaves = kFinalThreads / 64;
 // s_waitcnt operand (GFX9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8) that waits for vmcnt = 0 only.
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kTallyStride = 32;
-constexpr int kDenseSplitBlocks = 32;  // dense q rows of at least this many blocks use the grid  // 64-bit words between tally words: one 256-byte line each
+constexpr int kTallyStride = 32;       // 64-bit words between tally words: one 256-byte line each
+#ifndef SDV_DENSE_SPLIT_BLOCKS
+#define SDV_DENSE_SPLIT_BLOCKS 32
+#endif
+constexpr int kDenseSplitBlocks = SDV_DENSE_SPLIT_BLOCKS;  // dense q rows of at least this many blocks use the grid
 constexpr int kMaxDraft = SD_MAX_DRAFT;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kLn2 = 0.6931471805599453;
