@@ -67,6 +67,9 @@ namespace sdv {
 
 constexpr int kBlock = SD_BLOCK_TOKENS;
 constexpr int kThreads = 256;       // row statistics (strided sweep, element path): 4 waves per workgroup
+#ifndef SDV_SWEEP_STATIC
+#define SDV_SWEEP_STATIC 16  // claimed sweep: static blocks per wave before it claims (even, >= 2)
+#endif
 #ifndef SDV_SWEEP_THREADS
 #define SDV_SWEEP_THREADS 768
 #endif
@@ -586,10 +589,12 @@ __device__ __forceinline__ SweepCursor advance(const RowStatsArgs &a, SweepCurso
 // blocks p, p + P, p + 2P, ...), each with a claim counter that its home
 // waves increment; P is kSweepParts, or a smaller power of two when the grid
 // has fewer wave slots per XCD, so that every partition has home waves.  The
-// grid is the resident capacity.  A wave takes its first two blocks
-// statically and claims the rest one at a time.  A claim's round trip under
-// full HBM load is longer than one block's time, so two claims are kept in
-// flight.  Home partitions mix workgroups of all eight XCDs (workgroups go to
+// grid is the resident capacity.  A wave takes its first SDV_SWEEP_STATIC
+// blocks statically and claims the rest one at a time: a claim's result
+// shares the in-order vector memory counter with the loads issued after it,
+// so every claim can delay a block, and claims are kept for the part of the
+// sweep where the imbalance builds up.  A claim's round trip under full HBM
+// load is longer than one block's time, so two claims are kept in flight.  Home partitions mix workgroups of all eight XCDs (workgroups go to
 // XCDs round-robin), so the XCDs' speeds average out within a partition; one
 // counter serves about 1/64 of the claims, well below the rate at which one
 // address takes returning atomics.
@@ -600,7 +605,8 @@ struct SweepPlan {  // 32-bit: block indices are below 2^31, and scalar compares
     int lg;     // log2 of the number of partitions
     int p;      // home partition
     int lim;    // blocks in the partition
-    int k0, k1; // the wave's two static blocks (partition indices)
+    int k0, k1; // the wave's last two static blocks (partition indices)
+    int kfirst, np;  // its first static block and the stride between its static blocks
     int kdyn;   // the partition index the counter's first claim stands for
     uint32_t *ctr;
 };
@@ -617,9 +623,11 @@ __device__ __forceinline__ SweepPlan plan_of(const RowStatsArgs &a) {
     pl.p = u & (P - 1);
     const int n_p = 8 * ((U - pl.p + P - 1) >> lg);  // waves at home in p
     pl.lim = a.nblk > pl.p ? static_cast<int>((a.nblk - pl.p + P - 1) >> lg) : 0;
-    pl.k0 = x + 8 * (u >> lg);
+    pl.kfirst = x + 8 * (u >> lg);
+    pl.np = n_p;
+    pl.k0 = pl.kfirst + (SDV_SWEEP_STATIC - 2) * n_p;
     pl.k1 = pl.k0 + n_p;
-    pl.kdyn = 2 * n_p;
+    pl.kdyn = SDV_SWEEP_STATIC * n_p;
     pl.ctr = a.sweep + pl.p * kSweepCtrStride;
     return pl;
 }
@@ -826,13 +834,50 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     const SweepPlan pl = plan_of(a);
-    if (pl.k0 >= pl.lim) return;
+    if (pl.kfirst >= pl.lim) return;
     const PhiloxKey key = key_of(a.seed);
     Stash st;
     st.kind = 0;
     int count = 0;
     uint4 ra[G], rb[G];
     uint32_t ma[G], mb[G];
+    // The static blocks before the last two, two at a time, without claims.
+    if constexpr (SDV_SWEEP_STATIC > 2) {
+        int ks = pl.kfirst;
+        const SweepCursor s0 = cursor_at(a, block_of(pl, ks));
+        issue_block<ET, MASKED, POL>(a, s0.row, s0.blk, lane, ra, ma);
+        SweepBlock xa = sweep_block(a, s0);
+        for (int j = 0; j < (SDV_SWEEP_STATIC - 2) / 2; ++j) {
+            const int kb = ks + pl.np, kc = ks + 2 * pl.np;  // kc is at most k0
+            const bool lb = kb < pl.lim, lc = kc < pl.lim;
+            const SweepCursor s1 = cursor_at(a, block_of(pl, lb ? kb : pl.kfirst));
+            issue_block<ET, MASKED, POL>(a, s1.row, s1.blk, lane, rb, mb, lb);
+            const SweepBlock xb = sweep_block(a, s1);
+            if (!xa.skip) reduce_block<ET, MASKED, TOPK>(a, xa, lane, ra, ma, st, count++);
+            else settle(ra[G - 1]);
+            if (count == kWave) {
+                flush_stash(a, st, key, lane, count);
+                st.kind = 0;
+                count = 0;
+            }
+            const SweepCursor s2 = cursor_at(a, block_of(pl, lc ? kc : pl.kfirst));
+            issue_block<ET, MASKED, POL>(a, s2.row, s2.blk, lane, ra, ma, lc);
+            xa = sweep_block(a, s2);
+            if (lb && !xb.skip) reduce_block<ET, MASKED, TOPK>(a, xb, lane, rb, mb, st, count++);
+            else settle(rb[G - 1]);
+            if (count == kWave) {
+                flush_stash(a, st, key, lane, count);
+                st.kind = 0;
+                count = 0;
+            }
+            if (!lc) {  // the partition ends within the static blocks
+                settle(ra[G - 1]);
+                flush_stash(a, st, key, lane, count);
+                return;
+            }
+            ks = kc;
+        }
+    }
     // Blocks in flight: the current one's loads, the next one's index, and the
     // claims of the two after (issued before the loads of the blocks ahead of
     // them, so that waiting for a claim never waits for those loads).  A dead
@@ -842,9 +887,14 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     // worked out (the temperature scale is a double division): temporaries
     // placed after the issue cannot take the registers the loads fill, and a
     // temporary in a register with a load outstanding waits for every load.
-    const SweepCursor c0 = cursor_at(a, block_of(pl, pl.k0));
-    issue_block<ET, MASKED, POL>(a, c0.row, c0.blk, lane, ra, ma);
-    SweepBlock sa = sweep_block(a, c0);
+    SweepBlock sa;
+    if constexpr (SDV_SWEEP_STATIC > 2) {
+        sa = sweep_block(a, cursor_at(a, block_of(pl, pl.k0)));  // its loads are in flight
+    } else {
+        const SweepCursor c0 = cursor_at(a, block_of(pl, pl.k0));
+        issue_block<ET, MASKED, POL>(a, c0.row, c0.blk, lane, ra, ma);
+        sa = sweep_block(a, c0);
+    }
     // Two claims are in flight, one for each half of the loop (claims of one
     // lane on one address return in the order issued, so once a claim finds
     // the partition exhausted, so does the other).  Claims are issued without
