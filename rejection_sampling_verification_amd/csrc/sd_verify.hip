@@ -49,9 +49,6 @@
 #ifndef SDV_SWEEP_WAVES_PER_SIMD
 #define SDV_SWEEP_WAVES_PER_SIMD 3  // claimed sweep: at most this many waves per SIMD
 #endif
-#ifndef SDV_ROW_STATS_GRID_STRIDED
-#define SDV_ROW_STATS_GRID_STRIDED 2048  // strided (masked) sweep: workgroups
-#endif
 #ifndef SDV_LOGITS_CACHE_POLICY
 #define SDV_LOGITS_CACHE_POLICY 2  // logits loads: non-temporal (read once, kept out of the caches)
 #endif
@@ -66,9 +63,12 @@
 namespace sdv {
 
 constexpr int kBlock = SD_BLOCK_TOKENS;
-constexpr int kThreads = 256;       // row statistics (strided sweep, element path): 4 waves per workgroup
+constexpr int kThreads = 256;       // element path, dense residual grid: 4 waves per workgroup
 #ifndef SDV_SWEEP_STATIC
-#define SDV_SWEEP_STATIC 16  // claimed sweep: static blocks per wave before it claims (even, >= 2)
+#define SDV_SWEEP_STATIC 16  // claimed sweep without a mask: static blocks per wave before it claims
+#endif
+#ifndef SDV_MASKED_STATIC_PCT
+#define SDV_MASKED_STATIC_PCT 75  // with a mask: percent of a wave's share taken statically
 #endif
 #ifndef SDV_SWEEP_THREADS
 #define SDV_SWEEP_THREADS 768
@@ -331,6 +331,7 @@ struct RowStatsArgs {
     int k, kp1, V, W, C, cpw, nchunk;
     uint32_t *sweep;          // claim counters of the vector sweep (zero on entry)
     int parts_log2;           // the sweep's partitions: 2^parts_log2 <= kSweepParts
+    int sweep_static;         // claimed sweep with a mask: static blocks per wave (even, >= 2)
     DivMagic divC, divK;      // division by C and by kp1
 };
 
@@ -545,42 +546,6 @@ __device__ __forceinline__ SweepCursor cursor_at(const RowStatsArgs &a, int64_t 
     return c;
 }
 
-// The strided sweep steps its cursor by a fixed number of blocks: by
-// precomputed quotients and remainders, one carry each.
-struct SweepStep {
-    int64_t stride;  // blocks between a wave's consecutive blocks
-    int drow, dblk;  // stride = drow * C + dblk
-    int db, di;      // drow = db * kp1 + di
-};
-
-__device__ __forceinline__ SweepStep step_of(const RowStatsArgs &a, int64_t stride) {
-    SweepStep st;
-    st.stride = stride;
-    st.drow = static_cast<int>(stride / a.C);
-    st.dblk = static_cast<int>(stride - int64_t(st.drow) * a.C);
-    st.db = st.drow / a.kp1;
-    st.di = st.drow - st.db * a.kp1;
-    return st;
-}
-
-__device__ __forceinline__ SweepCursor advance(const RowStatsArgs &a, SweepCursor c, const SweepStep &s) {
-    c.gb += s.stride;
-    c.blk += s.dblk;
-    int carry = 0;
-    if (c.blk >= a.C) {
-        c.blk -= a.C;
-        carry = 1;
-    }
-    c.row += s.drow + carry;
-    c.i += s.di + carry;
-    c.b += s.db;
-    if (c.i >= a.kp1) {
-        c.i -= a.kp1;
-        c.b += 1;
-    }
-    return c;
-}
-
 // The claimed sweep hands blocks out dynamically.  Per-wave throughput varies by
 // tens of percent (which HBM channels a wave's blocks hit, which XCD it runs
 // on), and workgroups that start late would otherwise carry a full share to
@@ -612,7 +577,7 @@ struct SweepPlan {  // 32-bit: block indices are below 2^31, and scalar compares
 };
 
 // Needs gridDim.x to be a multiple of 8 and 2^parts_log2 <= 4 gridDim.x / 8.
-__device__ __forceinline__ SweepPlan plan_of(const RowStatsArgs &a) {
+__device__ __forceinline__ SweepPlan plan_of(const RowStatsArgs &a, int S) {
     constexpr int WPG = kSweepThreads / kWave;
     const int lg = a.parts_log2, P = 1 << lg;
     const int x = blockIdx.x & 7;
@@ -625,9 +590,9 @@ __device__ __forceinline__ SweepPlan plan_of(const RowStatsArgs &a) {
     pl.lim = a.nblk > pl.p ? static_cast<int>((a.nblk - pl.p + P - 1) >> lg) : 0;
     pl.kfirst = x + 8 * (u >> lg);
     pl.np = n_p;
-    pl.k0 = pl.kfirst + (SDV_SWEEP_STATIC - 2) * n_p;
+    pl.k0 = pl.kfirst + (S - 2) * n_p;
     pl.k1 = pl.k0 + n_p;
-    pl.kdyn = SDV_SWEEP_STATIC * n_p;
+    pl.kdyn = S * n_p;
     pl.ctr = a.sweep + pl.p * kSweepCtrStride;
     return pl;
 }
@@ -700,8 +665,8 @@ constexpr int kPastAnyBuffer = 0x40000000;
 // instructions with the same per-lane offsets, and a dead issue (the sweep's
 // look-ahead past its last block) gets an empty range.  With a mask the
 // resources span the row and its mask row and the offsets carry the block (a
-// dead issue points past the end); on the masked sweep that form measured
-// faster.  Either way the groups of a partial block that lie past the row
+// dead issue points past the end); with masks that form measured faster (on
+// the grid-stride sweep masked calls took before).  Either way the groups of a partial block that lie past the row
 // read zeros (they are replaced by -inf when the block is reduced), and a
 // dead issue's loads return zeros and touch no memory.
 template <typename ET, bool MASKED, int POL = SDV_LOGITS_CACHE_POLICY>
@@ -822,18 +787,18 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
     }
 }
 
-// Rows 16-byte aligned with V a multiple of the group width.  Two sweeps over
-// the (row, block) pairs: without a mask the blocks are claimed dynamically
-// (sweep_claimed), with a mask they go out in a fixed grid-stride order
-// (sweep_strided), where the claims' round trips cost more than the balance
-// gains (masked rows take more work per block, so a wave holds more blocks).
-// Each wave keeps the loads of its next block in flight while it reduces the
-// current one.
+// Rows 16-byte aligned with V a multiple of the group width.  Each wave takes
+// a static prefix of its blocks (16 without a mask; three quarters of its
+// share with one, where blocks take longer and claims would delay more of
+// them) and claims the rest.  Each wave keeps the loads of its next block in
+// flight while it reduces the current one.
 template <typename ET, bool MASKED, bool TOPK, int POL>
 __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
-    const SweepPlan pl = plan_of(a);
+    // static blocks per wave: a build-time constant without a mask
+    const int S = MASKED ? a.sweep_static : SDV_SWEEP_STATIC;
+    const SweepPlan pl = plan_of(a, S);
     if (pl.kfirst >= pl.lim) return;
     const PhiloxKey key = key_of(a.seed);
     Stash st;
@@ -842,12 +807,12 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     uint4 ra[G], rb[G];
     uint32_t ma[G], mb[G];
     // The static blocks before the last two, two at a time, without claims.
-    if constexpr (SDV_SWEEP_STATIC > 2) {
+    if (S > 2) {
         int ks = pl.kfirst;
         const SweepCursor s0 = cursor_at(a, block_of(pl, ks));
         issue_block<ET, MASKED, POL>(a, s0.row, s0.blk, lane, ra, ma);
         SweepBlock xa = sweep_block(a, s0);
-        for (int j = 0; j < (SDV_SWEEP_STATIC - 2) / 2; ++j) {
+        for (int j = 0; j < (S - 2) / 2; ++j) {
             const int kb = ks + pl.np, kc = ks + 2 * pl.np;  // kc is at most k0
             const bool lb = kb < pl.lim, lc = kc < pl.lim;
             const SweepCursor s1 = cursor_at(a, block_of(pl, lb ? kb : pl.kfirst));
@@ -888,7 +853,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     // placed after the issue cannot take the registers the loads fill, and a
     // temporary in a register with a load outstanding waits for every load.
     SweepBlock sa;
-    if constexpr (SDV_SWEEP_STATIC > 2) {
+    if (S > 2) {
         sa = sweep_block(a, cursor_at(a, block_of(pl, pl.k0)));  // its loads are in flight
     } else {
         const SweepCursor c0 = cursor_at(a, block_of(pl, pl.k0));
@@ -949,62 +914,13 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     flush_stash(a, st, key, lane, count);
 }
 
-// Wave w of a grid of Wt waves takes blocks w, w + Wt, w + 2 Wt, ..., so the
-// whole grid reads one contiguous window of the logits at a time; the cursor
-// steps by precomputed quotients.  The look-ahead index is clamped to the
-// current block at the end of the sweep (a dead issue, reading nothing).
-template <typename ET, bool MASKED, bool TOPK, int POL>
-__device__ __forceinline__ void sweep_strided(const RowStatsArgs &a, int lane) {
-    constexpr int P = Logit<ET>::kPer16;
-    constexpr int G = kBlock / (kWave * P);
-    const int64_t stride = int64_t(gridDim.x) * (kThreads / kWave);
-    const int64_t g0 = int64_t(blockIdx.x) * (kThreads / kWave) + wave_id();
-    if (g0 >= a.nblk) return;
-    const PhiloxKey key = key_of(a.seed);
-    Stash st;
-    st.kind = 0;
-    int count = 0;
-    uint4 ra[G], rb[G];
-    uint32_t ma[G], mb[G];
-    const SweepStep step = step_of(a, stride);
-    SweepCursor ca = cursor_at(a, g0);
-    SweepBlock sa = sweep_block(a, ca);
-    issue_block<ET, MASKED, POL>(a, ca.row, ca.blk, lane, ra, ma);
-    for (;;) {
-        const bool more1 = ca.gb + stride < a.nblk;
-        const SweepCursor cb = more1 ? advance(a, ca, step) : ca;
-        const SweepBlock sb = sweep_block(a, cb);
-        issue_block<ET, MASKED, POL>(a, cb.row, cb.blk, lane, rb, mb, more1);
-        if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
-        if (count == kWave) {
-            flush_stash(a, st, key, lane, count);
-            st.kind = 0;
-            count = 0;
-        }
-        if (!more1) break;
-        const bool more2 = cb.gb + stride < a.nblk;
-        ca = more2 ? advance(a, cb, step) : cb;
-        sa = sweep_block(a, ca);
-        issue_block<ET, MASKED, POL>(a, ca.row, ca.blk, lane, ra, ma, more2);
-        if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
-        if (count == kWave) {
-            flush_stash(a, st, key, lane, count);
-            st.kind = 0;
-            count = 0;
-        }
-        if (!more2) break;
-    }
-    flush_stash(a, st, key, lane, count);
-}
-
 // POL: the cache policy of the logits loads.
 template <typename ET, bool MASKED, bool TOPK, int POL>
-__global__ __launch_bounds__(MASKED ? kThreads : kSweepThreads) void row_stats_vec_kernel(RowStatsArgs a) {
+__global__ __launch_bounds__(kSweepThreads) void row_stats_vec_kernel(RowStatsArgs a) {
     zero_call_outputs(a);
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
-    if constexpr (MASKED) sweep_strided<ET, MASKED, TOPK, POL>(a, lane);
-    else sweep_claimed<ET, MASKED, TOPK, POL>(a, lane);
+    sweep_claimed<ET, MASKED, TOPK, POL>(a, lane);
 }
 
 // Any alignment and any V: element loads clamped into the row, one chunk of
@@ -3069,13 +2985,11 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     const bool cached = L.rows * int64_t(V) * (bf16 ? 2 : 4) <= SDV_CACHED_LOGITS_BYTES;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk, cached)
                          : pick_row_stats<float>(masked, aligned, topk, cached);
-    const int k1_threads = (aligned && !masked) ? kSweepThreads : kThreads;
+    const int k1_threads = aligned ? kSweepThreads : kThreads;
     const int64_t waves_per_wg = k1_threads / kWave;
     int64_t grid1;
     if (aligned && ra.nblk >= (int64_t(1) << 31)) return SD_ERR_UNSUPPORTED;  // block indices are 31-bit
-    if (aligned && masked) {
-        grid1 = std::min<int64_t>((ra.nblk + waves_per_wg - 1) / waves_per_wg, SDV_ROW_STATS_GRID_STRIDED);
-    } else if (aligned) {
+    if (aligned) {
         // The resident capacity at three waves per SIMD (each with a block in
         // flight while it reduces another, they keep HBM busy; a fourth, where
         // the registers allow it, measured slower), a multiple of 8 (the
@@ -3088,6 +3002,10 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         ra.parts_log2 = 0;  // partitions: a power of two, at most the wave slots per XCD
         while ((int64_t(2) << ra.parts_log2) <= std::min<int64_t>(kSweepParts, grid1 / 8 * waves_per_wg))
             ++ra.parts_log2;
+        const int64_t per_wave = ra.nblk / (grid1 * waves_per_wg);
+        int64_t S = masked ? per_wave * SDV_MASKED_STATIC_PCT / 100 : SDV_SWEEP_STATIC;
+        S = std::max<int64_t>(2, std::min<int64_t>(S, 1 << 20)) & ~int64_t(1);
+        ra.sweep_static = int(S);
     } else {
         grid1 = (ra.ntasks + waves_per_wg - 1) / waves_per_wg;
     }
