@@ -22,7 +22,7 @@ What it computes, and where the pages define it
 * ``philox`` -- Philox4x32-10 from Salmon, Moraes, Dror and Shaw, "Parallel
   Random Numbers: As Easy as 1, 2, 3" (SC'11), which supplies every uniform
   the sampler draws.  The pages name no generator; this is a reading.
-* ``ngram.propose`` / ``ngram.propose_batch`` -- the n-gram (prompt lookup)
+* ``ngram.propose_batch`` / ``ngram.propose_one`` -- the n-gram (prompt lookup)
   draft proposer: the history's tail looked up earlier in the same history,
   longest window first, earliest occurrence on ties, the following tokens
   copied (infra-guide 5.2, sections 4.1 and 6; pyshine "vLLM, part 2",

@@ -37,32 +37,37 @@ import numpy as np
 NG_BAD_LENGTH = 1  # status bit: a history length outside [0, stride]
 
 
-def propose(history, min_n, max_n, k, max_model_len=0):
-    """One request.  Returns (n, proposal): the winning window length and the
-    copied tokens, or (None, []) when nothing is proposed."""
-    h = [int(t) for t in history]
-    L = len(h)
-    if max_model_len and L + k > max_model_len:
-        return None, []
-    for n in range(min(max_n, L - 1), min_n - 1, -1):
-        tail = h[L - n:]
-        for start in range(L - n):          # earliest first; never the tail itself
-            if h[start:start + n] == tail:
-                return n, h[start + n:start + n + k]
-    return None, []
+def _search(h, min_n, max_n):
+    """The winning (window, start) for one history h (int64 array), or
+    (0, -1) when nothing matches.
 
-
-def _propose_np(h, min_n, max_n, k):
-    """The same search over a NumPy history, one window length at a time (the
-    sliding-window comparison is the loop over starts, vectorised)."""
+    The rule, restated over occurrence ends: the n-gram the tail forms with n
+    tokens occurs ending at position e exactly when the n tokens up to e equal
+    the last n tokens of the history, i.e. when h[e - t] == h[L - 1 - t] for
+    t = 0 .. n - 1.  agree[e] counts how many such t hold in a row from t = 0,
+    capped at the longest allowed window.  An occurrence may overlap the tail
+    but may not be it, so e stops at L - 2.  The longest window is then the
+    largest agree[e] (if it reaches min_n), and its earliest occurrence is the
+    one with the smallest end.
+    """
     L = h.shape[0]
-    for n in range(min(max_n, L - 1), min_n - 1, -1):
-        windows = np.lib.stride_tricks.sliding_window_view(h[:L - 1], n)  # starts 0 .. L-1-n
-        hit = np.flatnonzero(np.all(windows == h[L - n:], axis=1))
-        if hit.size:
-            s = int(hit[0])
-            return n, h[s + n:s + n + k]
-    return None, h[:0]
+    cap = min(max_n, L - 1)
+    if cap < min_n:
+        return 0, -1
+    ends = np.arange(L - 1)
+    agree = np.zeros(L - 1, dtype=np.int64)
+    still = np.ones(L - 1, dtype=bool)     # every step so far agreed
+    for t in range(cap):
+        pos = ends - t
+        ok = still & (pos >= 0)
+        ok[ok] = h[pos[ok]] == h[L - 1 - t]
+        agree += ok
+        still = ok
+    n = int(agree.max()) if agree.size else 0
+    if n < min_n:
+        return 0, -1
+    e = int(np.flatnonzero(agree >= n)[0])
+    return n, e - n + 1
 
 
 def propose_batch(tokens, lengths, min_n, max_n, k, max_model_len=0):
@@ -91,9 +96,11 @@ def propose_batch(tokens, lengths, min_n, max_n, k, max_model_len=0):
             continue
         if max_model_len and L + k > max_model_len:
             continue
-        n, p = _propose_np(tokens[b, :L].astype(np.int64), min_n, max_n, k)
-        if n is None:
+        h = tokens[b, :L].astype(np.int64)
+        n, start = _search(h, min_n, max_n)
+        if n == 0:
             continue
+        p = h[start + n:start + n + k]
         match[b] = n
         num[b] = len(p)
         drafts[b, :len(p)] = p
@@ -102,3 +109,13 @@ def propose_batch(tokens, lengths, min_n, max_n, k, max_model_len=0):
     return {"drafts": drafts, "num_drafts": num, "match_len": match, "draft_offsets": offsets,
             "flat": flat, "request_status": rstat,
             "status": int(np.bitwise_or.reduce(rstat)) if B else 0}
+
+
+def propose_one(history, min_n, max_n, k, max_model_len=0):
+    """One history given as a sequence: (n, proposal as a list), or (None, [])
+    when nothing is proposed (propose_batch on a one-row table)."""
+    h = np.asarray(list(history), dtype=np.int64)
+    table = h.reshape(1, -1) if h.size else np.zeros((1, 1), dtype=np.int64)
+    r = propose_batch(table, [h.size], min_n, max_n, k, max_model_len)
+    n = int(r["match_len"][0])
+    return (n if n else None), [int(v) for v in r["drafts"][0, :r["num_drafts"][0]]]

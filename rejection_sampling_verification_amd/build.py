@@ -1,6 +1,6 @@
 """Build the HIP verifier library in-tree for gfx950.
 
-    python -m rejection_sampling_verification_amd.build
+    python rejection_sampling_verification_amd/build.py
 
 compiles csrc/sd_verify.hip (the verifier) and csrc/sd_ngram.hip (the n-gram
 proposer) into libsdverify.so next to this file, then the test suite's

@@ -2,17 +2,26 @@
 
 Parity rule: every request the oracle does not flag (no accept draw with
 |u - a| < 1e-6, no Gumbel level whose top-2 keys are closer than 1e-5) must
-match exactly -- accepted count, every output token, error status.  Row
-log-normalisers and accept probabilities must agree to 1e-5 relative.
+match exactly -- accepted count, every output token, error status.
+Probabilities must agree to 1e-5 relative: each accept probability
+min(1, p/q) within 1e-5 of the oracle's value times that value (an exact zero
+stays an exact zero), and each row's log-normaliser within 1e-5 absolute,
+which is 1e-5 relative on every probability of the row.  Flagged draws must
+stay below 1e-4 of the positions compared (so none at all in a call of fewer
+than 10^4 positions).
 """
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
 import oracle
 from workloads import to_numpy
 
-LSE_RTOL = 1e-5
+LSE_ATOL = 1e-5
 ACC_RTOL = 1e-5
+FLAG_FRACTION = 1e-4
 
 
 def announce(msg):
@@ -40,12 +49,61 @@ def run_oracle(wl, requests=None, seed=None):
                             top_k=n["top_k"], request_ids=requests, top_p=n.get("top_p"))
 
 
-def _close(a, b, rtol):
+_PER_REQUEST = ("out_tokens", "num_accepted", "request_status", "row_lse", "accept_prob",
+                "flag_accept", "flag_gumbel", "flag_topp")
+
+
+def run_oracle_parallel(wl, chunk=8, workers=None, seed=None):
+    """The oracle over every request of a (large) workload, chunks of
+    requests on a thread pool (the oracle's work is NumPy on large arrays,
+    which runs outside the interpreter lock); the same result as run_oracle
+    on the whole batch."""
+    B = wl["logits"].shape[0]
+    if workers is None:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = [list(range(s, min(B, s + chunk))) for s in range(0, B, chunk)]
+    hosts = [to_numpy(wl, c) for c in chunks]
+    sd = wl["seed"] if seed is None else seed
+
+    def work(job):
+        req, n = job
+        return oracle.sd_verify(n["logits"], n["draft_token_ids"], n["draft_probs"], n["bitmask"],
+                                n["temperature"], seed=sd, top_k=n["top_k"], request_ids=req,
+                                top_p=n.get("top_p"))
+
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(work, zip(chunks, hosts)))
+    out = {key: np.concatenate([r[key] for r in parts]) for key in _PER_REQUEST}
+    out["counters"] = np.sum([r["counters"] for r in parts], axis=0, dtype=np.uint64)
+    out["status"] = int(np.bitwise_or.reduce([int(r["status"]) for r in parts]))
+    out["accept_histogram"] = np.sum([r["accept_histogram"] for r in parts], axis=0)
+    return out
+
+
+def close_rel(a, b, rtol=ACC_RTOL):
+    """|a - b| <= rtol |b| elementwise (so b = 0 needs a = 0); NaN matches NaN."""
     a = np.asarray(a, float)
     b = np.asarray(b, float)
     both_nan = np.isnan(a) & np.isnan(b)
-    ok = np.abs(a - b) <= rtol * np.maximum(1.0, np.abs(b))
-    return np.all(both_nan | ok)
+    with np.errstate(invalid="ignore"):
+        ok = np.abs(a - b) <= rtol * np.abs(b)
+    return bool(np.all(both_nan | ok))
+
+
+def close_abs(a, b, atol=LSE_ATOL):
+    """|a - b| <= atol elementwise; NaN matches NaN and an infinity itself."""
+    a = np.asarray(a, float)
+    b = np.asarray(b, float)
+    both_nan = np.isnan(a) & np.isnan(b)
+    with np.errstate(invalid="ignore"):
+        ok = (a == b) | (np.abs(a - b) <= atol)
+    return bool(np.all(both_nan | ok))
+
+
+def flag_limit(positions):
+    """Flagged draws allowed among `positions` verified positions: strictly
+    fewer than FLAG_FRACTION of them."""
+    return max(0, int(np.ceil(FLAG_FRACTION * positions)) - 1)
 
 
 def compare(gpu, orc, requests=None, check_counters=True):
@@ -66,10 +124,10 @@ def compare(gpu, orc, requests=None, check_counters=True):
                 or not np.array_equal(orc["out_tokens"][j], gpu["out_tokens"][b])):
             mism.append(b)
             continue
-        if not _close(gpu["row_lse"][b], orc["row_lse"][j], LSE_RTOL):
+        if not close_abs(gpu["row_lse"][b], orc["row_lse"][j]):
             mism.append(b)
             continue
-        if not _close(gpu["accept_prob"][b], orc["accept_prob"][j], ACC_RTOL):
+        if not close_rel(gpu["accept_prob"][b], orc["accept_prob"][j]):
             mism.append(b)
     if check_counters and requests is None:
         R, I, D, A = (int(v) for v in orc["counters"])
@@ -83,7 +141,18 @@ def compare(gpu, orc, requests=None, check_counters=True):
     return mism, flagged
 
 
-def assert_parity(gpu, orc, requests=None, max_flagged=2):
+def flagged_draws(orc, idx=None):
+    """Near-boundary draws the oracle flagged (accept, Gumbel, top-p)."""
+    sel = slice(None) if idx is None else list(idx)
+    return int(np.sum(orc["flag_accept"][sel]) + np.sum(orc["flag_gumbel"][sel])
+               + np.sum(orc["flag_topp"][sel]))
+
+
+def assert_parity(gpu, orc, requests=None, allow_flags=None):
+    """Exact parity on every unflagged request, the probability tolerances,
+    and fewer flagged draws than FLAG_FRACTION of the positions compared
+    (allow_flags overrides that limit for inputs built to sit on a
+    boundary)."""
     mism, flagged = compare(gpu, orc, requests)
     if mism:
         b = mism[0]
@@ -93,7 +162,13 @@ def assert_parity(gpu, orc, requests=None, max_flagged=2):
                   f" | lse gpu {gpu['row_lse'][b]} oracle {orc['row_lse'][j]}"
                   f" | acc gpu {gpu['accept_prob'][b]} oracle {orc['accept_prob'][j]}")
         raise AssertionError(f"{len(mism)} mismatching requests {mism[:10]}; {detail}")
-    assert len(flagged) <= max_flagged, f"too many flagged requests: {flagged}"
+    positions = int(np.prod(orc["accept_prob"].shape))
+    limit = flag_limit(positions) if allow_flags is None else allow_flags
+    nflag = flagged_draws(orc)
+    assert nflag <= limit, f"{nflag} flagged draws in {positions} positions (limit {limit}): {flagged}"
+    if requests is None and "flags" in gpu:
+        g = int(gpu["flags"][0]) + int(gpu["flags"][1])
+        assert g <= limit + nflag, f"the GPU reports {g} near-boundary draws (limit {limit})"
     return flagged
 
 
@@ -136,7 +211,7 @@ def run_oracle_ragged(wl, max_draft, seed=None):
                                    top_p=cv(wl.get("top_p")))
 
 
-def assert_parity_ragged(gpu, orc, off, max_flagged=2):
+def assert_parity_ragged(gpu, orc, off, allow_flags=None):
     """Per request over its own rows and drafts; counters, status and the
     histogram over the call (exact unless a request is flagged)."""
     off = np.asarray(off, dtype=np.int64)
@@ -156,11 +231,14 @@ def assert_parity_ragged(gpu, orc, off, max_flagged=2):
         r0, d0 = int(off[b]) + b, int(off[b])
         if (orc["num_accepted"][b] != gpu["out_num_accepted"][b]
                 or not np.array_equal(orc["out_tokens"][r0:r0 + k + 1], gpu["out_tokens"][r0:r0 + k + 1])
-                or not _close(gpu["row_lse"][r0:r0 + k + 1], orc["row_lse"][r0:r0 + k + 1], LSE_RTOL)
-                or not _close(gpu["accept_prob"][d0:d0 + k], orc["accept_prob"][d0:d0 + k], ACC_RTOL)):
+                or not close_abs(gpu["row_lse"][r0:r0 + k + 1], orc["row_lse"][r0:r0 + k + 1])
+                or not close_rel(gpu["accept_prob"][d0:d0 + k], orc["accept_prob"][d0:d0 + k])):
             mism.append(b)
     assert not mism, f"{len(mism)} mismatching requests {mism[:10]}"
-    assert len(flagged) <= max_flagged, f"too many flagged requests: {flagged}"
+    positions = int(orc["accept_prob"].shape[0])
+    limit = flag_limit(positions) if allow_flags is None else allow_flags
+    nflag = flagged_draws(orc)
+    assert nflag <= limit, f"{nflag} flagged draws in {positions} positions (limit {limit}): {flagged}"
     R, I, D, A = (int(v) for v in orc["counters"])
     gR, gI, gD, gA = (int(v) for v in gpu["counters"])
     assert (gR, gI, gD) == (R, I, D), ((gR, gI, gD), (R, I, D))

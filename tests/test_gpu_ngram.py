@@ -119,7 +119,7 @@ def test_edge_cases():
         o = propose_batch(tokens, [len(h)], mn, mx, k)
         _assert_same(g, o)
         assert (int(g["match_len"][0]) or None, list(g["drafts"][0, :g["num_drafts"][0]])) == \
-            oracle.ngram.propose(h, mn, mx, k)
+            oracle.ngram.propose_one(h, mn, mx, k)
     # bad lengths set the status bit and leave the request without drafts
     tokens = np.tile(np.array([1, 2, 1, 2, 1, 2, 1, 2]), (3, 1))
     g = _gpu(tokens, [-3, 8, 9], 1, 3, 2)

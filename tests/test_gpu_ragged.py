@@ -193,5 +193,5 @@ def test_ngram_ragged_full():
     wl = make_workload("ngram_ragged", device=DEV)
     off = wl["draft_offsets"].cpu().numpy()
     gpu, orc = run_gpu_ragged(wl, wl["max_draft"]), run_oracle_ragged(wl, wl["max_draft"])
-    assert_parity_ragged(gpu, orc, off, max_flagged=2)
+    assert_parity_ragged(gpu, orc, off)
     assert int(gpu["counters"][0]) == int(off[-1]) and gpu["status"] == 0

@@ -17,7 +17,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle.ngram import NG_BAD_LENGTH, propose, propose_batch
+from oracle.ngram import NG_BAD_LENGTH, propose_batch, propose_one
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "ngram_toy.json")
 
@@ -32,7 +32,7 @@ def _batch1(h, min_n, max_n, k, max_model_len=0):
 @pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
 def test_pages_worked_lookups(case):
     want = (case["n"], case["proposal"])
-    assert propose(case["history"], case["min_n"], case["max_n"], case["k"]) == want
+    assert propose_one(case["history"], case["min_n"], case["max_n"], case["k"]) == want
     assert _batch1(case["history"], case["min_n"], case["max_n"], case["k"]) == want
 
 
@@ -87,7 +87,7 @@ def test_brute_force_and_z_function(alphabet):
         max_n = int(rng.integers(min_n, 8))
         k = int(rng.integers(0, 6))
         want = _brute(h, min_n, max_n, k)
-        assert propose(h, min_n, max_n, k) == want, (h, min_n, max_n, k)
+        assert propose_one(h, min_n, max_n, k) == want, (h, min_n, max_n, k)
         assert _by_zfunction(h, min_n, max_n, k) == want, (h, min_n, max_n, k)
         assert _batch1(h, min_n, max_n, k) == want, (h, min_n, max_n, k)
 
@@ -97,7 +97,7 @@ def test_proposal_properties_on_long_histories():
     for trial in range(30):
         L = int(rng.integers(50, 400))
         h = [int(v) for v in rng.integers(0, 4, size=L)]
-        n, p = propose(h, 2, 6, 4)
+        n, p = propose_one(h, 2, 6, 4)
         assert n is not None                       # 4 symbols: some 2-gram repeats
         s = next(s for s in range(L - n) if h[s:s + n] == h[L - n:])
         assert p == h[s + n:s + n + 4] and 1 <= len(p) <= 4
@@ -108,20 +108,20 @@ def test_proposal_properties_on_long_histories():
 
 
 def test_special_cases():
-    assert propose([1, 2, 3, 4, 5], 2, 4, 3) == (None, [])          # no token repeats
-    assert propose([1, 2, 3, 4, 5], 1, 4, 3) == (None, [])
-    assert propose([], 1, 4, 3) == (None, []) and propose([7], 1, 4, 3) == (None, [])
-    assert propose([7, 7], 1, 4, 3) == (1, [7])                     # the tail's own token follows
-    assert propose([7, 7], 2, 4, 3) == (None, [])                   # a window needs len - 1 >= n
-    assert propose([5, 5, 5, 5, 5], 2, 3, 4) == (3, [5, 5])         # overlap with the tail is allowed
-    assert propose([1, 2, 9, 1, 2], 2, 4, 0) == (2, [])             # k = 0: a match, nothing copied
-    assert propose([1, 2, 3, 1, 2, 3], 3, 3, 5) == (3, [1, 2, 3])   # cut short by the history's end
+    assert propose_one([1, 2, 3, 4, 5], 2, 4, 3) == (None, [])          # no token repeats
+    assert propose_one([1, 2, 3, 4, 5], 1, 4, 3) == (None, [])
+    assert propose_one([], 1, 4, 3) == (None, []) and propose_one([7], 1, 4, 3) == (None, [])
+    assert propose_one([7, 7], 1, 4, 3) == (1, [7])                     # the tail's own token follows
+    assert propose_one([7, 7], 2, 4, 3) == (None, [])                   # a window needs len - 1 >= n
+    assert propose_one([5, 5, 5, 5, 5], 2, 3, 4) == (3, [5, 5])         # overlap with the tail is allowed
+    assert propose_one([1, 2, 9, 1, 2], 2, 4, 0) == (2, [])             # k = 0: a match, nothing copied
+    assert propose_one([1, 2, 3, 1, 2, 3], 3, 3, 5) == (3, [1, 2, 3])   # cut short by the history's end
 
 
 def test_context_length_limit():
     h = [1, 2, 9, 1, 2]
-    assert propose(h, 2, 4, 3, max_model_len=8) == (2, [9, 1, 2])   # 5 + 3 fits
-    assert propose(h, 2, 4, 3, max_model_len=7) == (None, [])       # 5 + 3 would overflow
+    assert propose_one(h, 2, 4, 3, max_model_len=8) == (2, [9, 1, 2])   # 5 + 3 fits
+    assert propose_one(h, 2, 4, 3, max_model_len=7) == (None, [])       # 5 + 3 would overflow
     assert _batch1(h, 2, 4, 3, max_model_len=7) == (None, [])
     assert _batch1(h, 2, 4, 3, max_model_len=8) == (2, [9, 1, 2])
 
@@ -137,7 +137,7 @@ def test_batch_layout_and_bad_lengths():
         if L < 0 or L > stride:
             assert r["request_status"][b] == NG_BAD_LENGTH and r["num_drafts"][b] == 0
             continue
-        n, p = propose(list(tokens[b, :L]), 2, 5, 4)
+        n, p = propose_one(list(tokens[b, :L]), 2, 5, 4)
         assert r["match_len"][b] == (n or 0) and list(r["drafts"][b, :len(p)]) == p
         assert np.all(r["drafts"][b, len(p):] == -1)
     assert r["status"] == NG_BAD_LENGTH
@@ -147,30 +147,23 @@ def test_batch_layout_and_bad_lengths():
 
 
 def test_planted_mistakes_fail_the_pins():
-    """Each plausible slip in the search is caught by the pins above."""
-    def latest(h, min_n, max_n, k):                  # latest occurrence instead of earliest
-        L = len(h)
-        for n in range(min(max_n, L - 1), min_n - 1, -1):
-            for s in reversed(range(L - n)):
-                if h[s:s + n] == h[L - n:]:
-                    return n, h[s + n:s + n + k]
-        return None, []
+    """Each plausible slip in the search is caught by the pins above: a wrong
+    choice among the matching (window, start) pairs, or a copy taken one
+    token early."""
+    def pick(order, shift=0):
+        def wrong(h, min_n, max_n, k):
+            L = len(h)
+            hits = [(n, s) for n in range(1, L) for s in range(0, L - n)
+                    if min_n <= n <= max_n and h[s:s + n] == h[L - n:]]
+            if not hits:
+                return None, []
+            n, s = min(hits, key=order)
+            return n, h[s + n + shift:s + n + shift + k]
+        return wrong
 
-    def short_first(h, min_n, max_n, k):             # short windows before long ones
-        L = len(h)
-        for n in range(min_n, min(max_n, L - 1) + 1):
-            for s in range(L - n):
-                if h[s:s + n] == h[L - n:]:
-                    return n, h[s + n:s + n + k]
-        return None, []
-
-    def off_by_one(h, min_n, max_n, k):              # copies from the last token of the match
-        L = len(h)
-        for n in range(min(max_n, L - 1), min_n - 1, -1):
-            for s in range(L - n):
-                if h[s:s + n] == h[L - n:]:
-                    return n, h[s + n - 1:s + n - 1 + k]
-        return None, []
+    latest = pick(lambda ns: (-ns[0], -ns[1]))        # latest occurrence instead of earliest
+    short_first = pick(lambda ns: (ns[0], ns[1]))      # short windows before long ones
+    off_by_one = pick(lambda ns: (-ns[0], ns[1]), -1)  # copies from the last token of the match
 
     cases = json.load(open(GOLDEN))["cases"]
     for wrong in (latest, short_first, off_by_one):
