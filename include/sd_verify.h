@@ -52,7 +52,9 @@ typedef enum {
     SD_ERR_INVALID_ARG = -1, /* null required pointer, negative size, bad dtype */
     SD_ERR_UNSUPPORTED = -2, /* B > SD_MAX_BATCH, k > SD_MAX_DRAFT or V > SD_MAX_VOCAB */
     SD_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-    SD_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+    SD_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+    SD_ERR_SCRATCH_LIMIT = -5 /* sd_verify_noalloc: the call needs more than
+                                 SD_NOALLOC_SCRATCH_BYTES of workspace */
 } sd_status;
 
 typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
@@ -171,6 +173,37 @@ int sd_verify(const void *target_logits, const int32_t *draft_token_ids,
               int32_t *out_num_accepted, uint64_t *out_counters,
               const sd_params *p, void *workspace, size_t workspace_bytes,
               hipStream_t stream);
+
+/* Bytes of the static device scratch behind sd_verify_noalloc: every call
+ * whose sd_verify_workspace_size is at most this fits (the B=512, k=12,
+ * V=151936 long-draft shape needs about 9 MB). */
+#define SD_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* sd_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same operation, arguments and outputs as sd_verify, without the workspace
+ * arguments: the workspace is a static device array of
+ * SD_NOALLOC_SCRATCH_BYTES, one per device, held from the first call on that
+ * device until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); the caller still owns every input and
+ * output buffer.
+ *   - The first call on a device looks the array up with
+ *     hipGetSymbolAddress and clears its block-claim counters with a fill
+ *     kernel on `stream`; every later call finds them at zero, since every
+ *     call that launches leaves them so (after an SD_ERR_HIP the next call
+ *     clears them again).
+ *   - Every call on one device shares that device's array: calls that
+ *     overlap in time on one device (different streams or threads) race and
+ *     produce garbage.  Serialise them.
+ * Returns what sd_verify returns, SD_ERR_SCRATCH_LIMIT when
+ * sd_verify_workspace_size(p) exceeds SD_NOALLOC_SCRATCH_BYTES, and
+ * SD_ERR_HIP when the array cannot be looked up; nothing is launched on
+ * error. */
+int sd_verify_noalloc(const void *target_logits, const int32_t *draft_token_ids,
+                      const float *draft_probs, const int32_t *bitmask,
+                      const float *temperature, uint64_t seed, int32_t *out_tokens,
+                      int32_t *out_num_accepted, uint64_t *out_counters,
+                      const sd_params *p, hipStream_t stream);
 
 /* Static description of a return code.  Host-only. */
 const char *sd_status_string(int code);

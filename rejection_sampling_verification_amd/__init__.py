@@ -4,10 +4,11 @@ Argument marshalling only: every step of verification and of the n-gram draft
 proposer runs in the HIP kernels behind the C ABI declared in
 include/sd_verify.h and include/sd_ngram.h.  PyTorch supplies device
 memory and the current stream.  Importing this package fails loudly when the
-library has not been built (python -m rejection_sampling_verification_amd.build).
+library has not been built (python rejection_sampling_verification_amd/build.py).
 
 Entry points mirror the C ABI names: ``sd_verify``, ``sd_verify_workspace_size``,
-``sd_status_string``, ``sd_rates``, ``sd_ngram_propose``,
+``sd_status_string``, ``sd_rates``, ``sd_verify_noalloc`` (through
+``Verifier(..., noalloc=True)``), ``sd_ngram_propose``,
 ``sd_ngram_workspace_size``; ``Verifier`` and ``NgramProposer`` keep the
 workspace and outputs of repeated same-shape calls.
 """
@@ -42,7 +43,8 @@ SD_NGRAM_STATUS_BAD_LENGTH = 1
 
 # every symbol include/sd_verify.h and include/sd_ngram.h declare
 EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates",
-                    "sd_ngram_propose", "sd_ngram_workspace_size")
+                    "sd_verify_noalloc", "sd_ngram_propose", "sd_ngram_workspace_size")
+SD_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class SdParams(ctypes.Structure):
@@ -87,7 +89,7 @@ def _load():
     if not os.path.exists(LIBRARY_PATH):
         raise ImportError(
             f"{LIBRARY_PATH} is missing: build it with "
-            "`python -m rejection_sampling_verification_amd.build` (hipcc, gfx950)")
+            "`python rejection_sampling_verification_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIBRARY_PATH)
     lib.sd_verify_workspace_size.argtypes = [ctypes.POINTER(SdParams)]
     lib.sd_verify_workspace_size.restype = ctypes.c_size_t
@@ -97,6 +99,12 @@ def _load():
         ctypes.POINTER(SdParams), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
     ]
     lib.sd_verify.restype = ctypes.c_int
+    lib.sd_verify_noalloc.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(SdParams), ctypes.c_void_p,
+    ]
+    lib.sd_verify_noalloc.restype = ctypes.c_int
     lib.sd_status_string.argtypes = [ctypes.c_int]
     lib.sd_status_string.restype = ctypes.c_char_p
     lib.sd_rates.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint64,
@@ -196,11 +204,14 @@ class Verifier:
     Each call overwrites the tensors it returns.  `workspace`, if given, is a
     uint8 device tensor of at least sd_verify_workspace_size bytes, zero-filled
     before its first use; verifiers of any shapes may share one, as long as
-    their calls do not overlap in time.
+    their calls do not overlap in time.  With noalloc=True the calls go to
+    sd_verify_noalloc instead: no workspace tensor exists, the library's
+    static per-device scratch serves every such verifier, and their calls on
+    one device must not overlap in time.
     """
 
     def __init__(self, batch, num_draft, vocab, logits_dtype=torch.bfloat16, device=None,
-                 debug=False, histogram=False, total_drafts=None, workspace=None):
+                 debug=False, histogram=False, total_drafts=None, workspace=None, noalloc=False):
         dev = torch.device(device) if device is not None else torch.device("cuda")
         if dev.type != "cuda":
             raise ValueError("the verifier runs on a HIP device")
@@ -220,7 +231,15 @@ class Verifier:
         ws = int(_lib.sd_verify_workspace_size(ctypes.byref(self.params)))
         self.params.draft_offsets = None
         dev = self.device
-        if workspace is not None:
+        self.noalloc = bool(noalloc)
+        if self.noalloc:
+            if workspace is not None:
+                raise ValueError("noalloc verifiers take no workspace")
+            if ws > SD_NOALLOC_SCRATCH_BYTES:
+                raise ValueError(f"{ws} bytes of workspace exceed the static scratch "
+                                 f"({SD_NOALLOC_SCRATCH_BYTES})")
+            self.workspace = None
+        elif workspace is not None:
             if (workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous()
                     or workspace.numel() < ws or workspace.data_ptr() % 256):
                 raise ValueError(f"workspace must be a contiguous, 256-byte aligned uint8 tensor of "
@@ -289,14 +308,18 @@ class Verifier:
             self.params.row_stats_event_begin = self.params.row_stats_event_end = None
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = _lib.sd_verify(
-            _ptr(target_logits), _ptr(draft_token_ids), _ptr(draft_probs), _ptr(bitmask),
-            _ptr(temperature), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
-            _ptr(self.out_tokens), _ptr(self.out_num_accepted), _ptr(self.out_counters),
-            ctypes.byref(self.params), ctypes.c_void_p(self.workspace.data_ptr()),
-            ctypes.c_size_t(self.workspace_bytes), ctypes.c_void_p(int(stream)))
+        ptrs = (_ptr(target_logits), _ptr(draft_token_ids), _ptr(draft_probs), _ptr(bitmask),
+                _ptr(temperature), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                _ptr(self.out_tokens), _ptr(self.out_num_accepted), _ptr(self.out_counters),
+                ctypes.byref(self.params))
+        if self.noalloc:
+            rc = _lib.sd_verify_noalloc(*ptrs, ctypes.c_void_p(int(stream)))
+        else:
+            rc = _lib.sd_verify(*ptrs, ctypes.c_void_p(self.workspace.data_ptr()),
+                                ctypes.c_size_t(self.workspace_bytes), ctypes.c_void_p(int(stream)))
         if rc != SD_OK:
-            raise RuntimeError(f"sd_verify failed: {sd_status_string(rc)} ({rc})")
+            name = "sd_verify_noalloc" if self.noalloc else "sd_verify"
+            raise RuntimeError(f"{name} failed: {sd_status_string(rc)} ({rc})")
         if self.debug:
             return VerifyResult(self.out_tokens, self.out_num_accepted, self.out_counters,
                                 self.status, self.row_lse, self.accept_prob,

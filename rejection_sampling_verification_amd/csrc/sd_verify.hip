@@ -2862,6 +2862,7 @@ extern "C" const char *sd_status_string(int code) {
         case SD_ERR_UNSUPPORTED: return "unsupported size";
         case SD_ERR_WORKSPACE: return "workspace missing or too small";
         case SD_ERR_HIP: return "HIP runtime error";
+        case SD_ERR_SCRATCH_LIMIT: return "call needs more workspace than the static scratch holds";
         default: return "unknown status";
     }
 }
@@ -3064,4 +3065,72 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }
     return SD_OK;
+}
+
+// ------------------------------------------------------ allocation-free entry
+
+namespace sdv {
+
+// The workspace of sd_verify_noalloc, one copy on every device the library
+// runs on.  In host code this name stands for a host-side shadow, not for a
+// device address: the address of the copy on the current device comes from
+// hipGetSymbolAddress, and only that address reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[SD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+constexpr int kClaimWords = kSweepParts * kSweepCtrStride;  // the workspace's first 16 KB
+
+struct ScratchSlot {
+    void *ptr = nullptr;  // device address of `scratch` on this device
+    bool clear = false;   // its block-claim counters are known to be zero
+};
+
+std::mutex scratch_mu;
+ScratchSlot scratch_slots[kMaxScratchDevices];
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+}  // namespace sdv
+
+extern "C" int sd_verify_noalloc(const void *target_logits, const int32_t *draft_token_ids,
+                                 const float *draft_probs, const int32_t *bitmask,
+                                 const float *temperature, uint64_t seed, int32_t *out_tokens,
+                                 int32_t *out_num_accepted, uint64_t *out_counters, const sd_params *p,
+                                 hipStream_t stream) {
+    using namespace sdv;
+    if (!p || !out_counters) return SD_ERR_INVALID_ARG;
+    // 0 for B = 0 and for sizes sd_verify refuses itself
+    if (sd_verify_workspace_size(p) > size_t(SD_NOALLOC_SCRATCH_BYTES)) return SD_ERR_SCRATCH_LIMIT;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return SD_ERR_HIP;
+    void *ws = nullptr;
+    bool clear = false;
+    {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        ScratchSlot &slot = scratch_slots[dev];
+        if (!slot.ptr) {  // set-up, once per device, with that device current
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SD_ERR_HIP;
+            slot.ptr = ptr;
+        }
+        ws = slot.ptr;
+        clear = slot.clear;
+    }
+    if (!clear) {  // a fill kernel, not a memset, so that a captured graph replays it correctly
+        hipLaunchKernelGGL(clear_words_kernel, dim3(kClaimWords / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(ws), kClaimWords);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    }
+    const int rc = sd_verify(target_logits, draft_token_ids, draft_probs, bitmask, temperature, seed,
+                             out_tokens, out_num_accepted, out_counters, p, ws,
+                             size_t(SD_NOALLOC_SCRATCH_BYTES), stream);
+    {
+        // every call that launched leaves the counters at zero; after a
+        // launch failure the next call clears them again
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        scratch_slots[dev].clear = (rc != SD_ERR_HIP);
+    }
+    return rc;
 }

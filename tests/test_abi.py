@@ -24,7 +24,7 @@ def test_header_declares_the_expected_entry_points():
     assert [os.path.basename(h) for h in HEADERS] == ["sd_ngram.h", "sd_verify.h"]
     assert _declared_functions() == sorted(
         ["sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates",
-         "sd_ngram_propose", "sd_ngram_workspace_size"])
+         "sd_verify_noalloc", "sd_ngram_propose", "sd_ngram_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -195,3 +195,18 @@ def test_ngram_params_layout_and_host_checks():
     assert ws >= 4 * 3 * 8 and ws % 256 == 0       # one 8-byte key per (request, 2048 positions)
     assert call(p, fake, ws - 1) == -3
     assert sdv.sd_ngram_workspace_size(0, 5000, 2, 5, 4) == 0
+
+
+def test_noalloc_refuses_before_launching():
+    """sd_verify_noalloc: a null parameter block, and sizes whose workspace
+    exceeds the static scratch, are refused on the host (no HIP call)."""
+    import rejection_sampling_verification_amd as sdv
+    lib = sdv.library()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.sd_verify_noalloc(fake, fake, nul, nul, fake, 0, fake, fake, fake, None, nul) == -1
+    p = sdv.SdParams()
+    p.batch, p.num_draft, p.vocab, p.logits_dtype = 4096, 12, 151936, 1   # about 77 MB of workspace
+    assert lib.sd_verify_workspace_size(ctypes.byref(p)) > sdv.SD_NOALLOC_SCRATCH_BYTES
+    assert lib.sd_verify_noalloc(fake, fake, nul, nul, fake, 0, fake, fake, fake, ctypes.byref(p), nul) == -5
+    assert "scratch" in sdv.sd_status_string(-5)
