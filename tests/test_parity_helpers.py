@@ -8,7 +8,7 @@ import copy
 import numpy as np
 import pytest
 
-from parity import assert_parity, close_rel, flag_limit, run_oracle
+from parity import assert_parity, close_lse, close_rel, flag_limit, run_oracle
 from workloads import make_workload
 
 
@@ -91,3 +91,9 @@ def test_flag_limit_is_below_1e4_of_positions(ngram_case):
     o["flag_gumbel"][0] = 1                # one flagged draw in 12 positions
     with pytest.raises(AssertionError):
         assert_parity(gpu, o)
+
+
+def test_normaliser_bound():
+    assert close_lse([14.0 + 9e-6], [14.0]) and not close_lse([14.0 + 1.5e-5], [14.0])
+    assert close_lse([3.2e8 + 2.0], [3.2e8]) and not close_lse([3.2e8 + 200.0], [3.2e8])
+    assert close_lse([np.inf], [np.inf]) and close_lse([np.nan], [np.nan])
