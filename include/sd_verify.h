@@ -138,8 +138,9 @@ typedef struct {
 } sd_params;
 
 /* Bytes of device workspace sd_verify needs for these sizes (0 for B = 0),
- * including total_drafts for a ragged call.  Host-only; never fails (returns
- * 0 for invalid sizes). */
+ * including total_drafts for a ragged call, and a table of line maxima when
+ * top_k is not NULL (any non-NULL value: calls that pass top_k need this
+ * larger size).  Host-only; never fails (returns 0 for invalid sizes). */
 size_t sd_verify_workspace_size(const sd_params *p);
 
 /* Verify one batch (shapes below for k drafts per request; see
@@ -176,8 +177,8 @@ int sd_verify(const void *target_logits, const int32_t *draft_token_ids,
 
 /* Bytes of the static device scratch behind sd_verify_noalloc: every call
  * whose sd_verify_workspace_size is at most this fits (the B=512, k=12,
- * V=151936 long-draft shape needs about 9 MB). */
-#define SD_NOALLOC_SCRATCH_BYTES (16u << 20)
+ * V=151936 long-draft shape with top-k needs about 41 MB). */
+#define SD_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* sd_verify for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The

@@ -44,7 +44,7 @@ SD_NGRAM_STATUS_BAD_LENGTH = 1
 # every symbol include/sd_verify.h and include/sd_ngram.h declare
 EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string", "sd_rates",
                     "sd_verify_noalloc", "sd_ngram_propose", "sd_ngram_workspace_size")
-SD_NOALLOC_SCRATCH_BYTES = 16 << 20
+SD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SdParams(ctypes.Structure):
@@ -143,12 +143,15 @@ def _params(batch, num_draft, vocab, dtype_code):
 
 
 def sd_verify_workspace_size(batch, num_draft, vocab, logits_dtype=torch.bfloat16,
-                             total_drafts=None):
-    """Device workspace bytes for these sizes (total_drafts: a ragged call)."""
+                             total_drafts=None, top_k=False):
+    """Device workspace bytes for these sizes (total_drafts: a ragged call;
+    top_k: calls that pass a top-k array, which need a larger workspace)."""
     p = _params(batch, num_draft, vocab, _dtype_code(logits_dtype))
     if total_drafts is not None:
         p.draft_offsets = 1  # any non-null value: the size only depends on the mode
         p.total_drafts = int(total_drafts)
+    if top_k:
+        p.top_k = 1
     return int(_lib.sd_verify_workspace_size(ctypes.byref(p)))
 
 
@@ -228,8 +231,13 @@ class Verifier:
         if self.ragged:
             self.params.draft_offsets = 1  # placeholder until a call supplies the offsets
             self.params.total_drafts = self.T
+        # calls with top-k need more (any non-null value: the size only
+        # depends on whether a top-k array is given)
         ws = int(_lib.sd_verify_workspace_size(ctypes.byref(self.params)))
+        self.params.top_k = 1
+        self.workspace_bytes_top_k = int(_lib.sd_verify_workspace_size(ctypes.byref(self.params)))
         self.params.draft_offsets = None
+        self.params.top_k = None
         dev = self.device
         self.noalloc = bool(noalloc)
         if self.noalloc:
@@ -239,6 +247,7 @@ class Verifier:
                 raise ValueError(f"{ws} bytes of workspace exceed the static scratch "
                                  f"({SD_NOALLOC_SCRATCH_BYTES})")
             self.workspace = None
+            ws = SD_NOALLOC_SCRATCH_BYTES
         elif workspace is not None:
             if (workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous()
                     or workspace.numel() < ws or workspace.data_ptr() % 256):
@@ -247,8 +256,9 @@ class Verifier:
             self.workspace = workspace
         else:
             # zero-filled once: the library leaves it ready for the next call
+            ws = self.workspace_bytes_top_k
             self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
-        self.workspace_bytes = ws
+        self.workspace_bytes = ws if workspace is None else int(workspace.numel())
         tok_shape = (self.rows,) if self.ragged else (self.B, self.k + 1)
         self.out_tokens = torch.empty(tok_shape, dtype=torch.int32, device=dev)
         self.out_num_accepted = torch.empty(self.B, dtype=torch.int32, device=dev)
@@ -299,6 +309,9 @@ class Verifier:
             raise ValueError("temperature is required ([B] float32, 0 = greedy)")
         _check(temperature, "temperature", torch.float32, (B,), dev)
         _check(top_k, "top_k", torch.int32, (B,), dev)
+        if top_k is not None and self.workspace_bytes < self.workspace_bytes_top_k:
+            raise ValueError(f"calls with top_k need {self.workspace_bytes_top_k} bytes of workspace, "
+                             f"this verifier has {self.workspace_bytes}")
         self.params.top_k = None if top_k is None else top_k.data_ptr()
         _check(top_p, "top_p", torch.float32, (B,), dev)
         self.params.top_p = None if top_p is None else top_p.data_ptr()

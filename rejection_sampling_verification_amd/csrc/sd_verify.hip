@@ -316,6 +316,8 @@ struct RowStatsArgs {
     const float *q;           // [B, k, V] or nullptr
     uint64_t seed;
     const float *tau;         // [rows] top-k thresholds, or nullptr (no top-k)
+    const int32_t *top_k;     // [B]: with linemax, the requests whose rows record line maxima
+    void *linemax;            // [rows, C * lines per block] line maxima of top-k rows, or nullptr
     BlockStat *bstats;        // [rows, C]
     DraftRec *drec;           // [rows]
     unsigned long long *tally;  // counter tally, zeroed here, accumulated by finalize
@@ -511,6 +513,7 @@ struct SweepBlock {
     int64_t gb;   // row * C + block
     int row, blk, b, i;
     bool full, greedy, skip;
+    bool lines;   // the block's line maxima are recorded (single-pass top-k)
     float c, tau;
     int x, xrel;  // the draft and its offset in this block (-1: elsewhere)
     int64_t dpos; // the row's draft index (draft rows)
@@ -646,6 +649,7 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const S
     s.skip = !s.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     s.c = s.greedy ? 0.0f : scale_of(T);
     s.tau = a.tau ? uniform_load(a.tau + s.row) : -INFINITY;
+    s.lines = a.linemax != nullptr && !s.greedy && uniform_load(a.top_k + s.b) > 0;
     s.x = s.xrel = -1;
     if (s.i < kb) {
         const int x = uniform_load(a.draft + s.dpos);
@@ -730,7 +734,55 @@ __device__ __forceinline__ void flush_stash(const RowStatsArgs &a, const Stash &
     a.bstats[st.gb] = out;
 }
 
-template <typename ET, bool MASKED, bool TOPK>
+// Sampling rows of a top-k call: the line maxima of the block, for the
+// single-pass top-k, which then computes the row's block statistics over the
+// kept tokens; the sweep only marks a block holding an allowed NaN or +inf
+// (statistics NaN, which report the row) and otherwise leaves (-inf, 0), the
+// statistics of a row without an allowed finite value.  A line is a 128-byte
+// line of the block (8 lanes of one group of loads); its code is the
+// order-preserving code of its largest allowed finite value, 0 for none.
+// 16-bit codes for bf16 rows (a bf16 value's code has an all-zero or all-one
+// low half, so its top half orders the same), 32-bit codes for fp32 rows.
+// Entry q * G + g of the block's codes is group g's line of lanes
+// 8q .. 8q + 7, so that lane 8q + 7 stores its G codes with one write.
+template <typename ET>
+__device__ __forceinline__ float2 lines_block(const RowStatsArgs &a, int row, int blk, const float *v, int lane) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    constexpr int LPB = G * 8;  // lines per block
+    bool bad = false;
+    uint32_t code[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float m = v[g * P];
+        bad |= !(v[g * P] <= FLT_MAX);
+#pragma unroll
+        for (int e = 1; e < P; ++e) {
+            m = fmaxf(m, v[g * P + e]);
+            bad |= !(v[g * P + e] <= FLT_MAX);
+        }
+        m = fmaxf(m, dpp_f<0x111, 0xf>(-INFINITY, m));  // row_shr:1
+        m = fmaxf(m, dpp_f<0x112, 0xf>(-INFINITY, m));  // row_shr:2
+        m = fmaxf(m, dpp_f<0x114, 0xf>(-INFINITY, m));  // row_shr:4: lane 8q + 7 holds line q
+        code[g] = (m > -INFINITY && m <= FLT_MAX) ? ordered_code(m) : 0u;
+    }
+    if ((lane & 7) == 7) {
+        const int64_t idx = (int64_t(row) * a.C + blk) * LPB + (lane >> 3) * G;
+        if constexpr (sizeof(ET) == 2) {
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.linemax) + idx) =
+                make_uint2((code[0] >> 16) | (code[1] & 0xffff0000u), (code[2] >> 16) | (code[3] & 0xffff0000u));
+        } else {
+            uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<uint32_t *>(a.linemax) + idx);
+            dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
+            dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
+        }
+    }
+    return wave_any(bad) ? make_float2(NAN, NAN) : make_float2(-INFINITY, 0.0f);
+}
+
+// TOPK: 0 no top-k, 1 cut at the row's threshold tau (found before the
+// sweep), 2 record line maxima of top-k rows (tau is found after it).
+template <typename ET, bool MASKED, int TOPK>
 __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
                                              const uint4 *r, const uint32_t *m, Stash &st, int slot) {
     constexpr int P = Logit<ET>::kPer16;
@@ -764,11 +816,13 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
                 if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
         }
     }
-    if (TOPK) apply_tau<G * P>(v, s.tau);
+    if (TOPK == 1) apply_tau<G * P>(v, s.tau);
     float2 res;
     float sx = 0.0f;
     if (s.greedy) {
         res = greedy_block<G, P>(v, int64_t(s.blk) * kBlock, lane);
+    } else if (TOPK == 2 && s.lines) {
+        res = lines_block<ET>(a, s.row, s.blk, v, lane);
     } else {
         res = softmax_block<G * P>(v, s.c);
         if (s.xrel >= 0) sx = excluded_sum<G, P>(v, s.c, res.x, s.xrel, lane);
@@ -792,7 +846,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
 // share with one, where blocks take longer and claims would delay more of
 // them) and claims the rest.  Each wave keeps the loads of its next block in
 // flight while it reduces the current one.
-template <typename ET, bool MASKED, bool TOPK, int POL>
+template <typename ET, bool MASKED, int TOPK, int POL>
 __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -915,7 +969,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
 }
 
 // POL: the cache policy of the logits loads.
-template <typename ET, bool MASKED, bool TOPK, int POL>
+template <typename ET, bool MASKED, int TOPK, int POL>
 __global__ __launch_bounds__(kSweepThreads) void row_stats_vec_kernel(RowStatsArgs a) {
     zero_call_outputs(a);
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
@@ -949,7 +1003,7 @@ __device__ __forceinline__ void load_block_elem(const ET *rowp, const uint8_t *m
     }
 }
 
-template <typename ET, bool MASKED, bool TOPK>
+template <typename ET, bool MASKED, int TOPK>
 __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -968,7 +1022,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
     uint32_t m[G];
     for (int blk = t.c0; blk < t.c1; ++blk) {
         load_block_elem<ET, MASKED>(rowp, mrow, blk, a.V, lane, v, m);
-        if (TOPK) apply_tau<G * P>(v, t.tau);
+        if (TOPK == 1) apply_tau<G * P>(v, t.tau);
         BlockStat out;
         out.key = -INFINITY;
         float sx = 0.0f;
@@ -1589,6 +1643,679 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     if (tid == 0) {
         a.tau[row] = tau;
         a.tau_flag[row] = flag;
+    }
+}
+
+// ------------------------------------------------------- single-pass top-k
+
+// Calls with top-k and no top-p find each row's threshold after the sweep,
+// without a second pass over the row (pyshine "vLLM, part 2",
+// "Verification": top-k is applied before the accept test).  The sweep
+// records the code of every 128-byte line's largest allowed value (line
+// maxima).  L, the K-th largest line maximum, is at most tau, the K-th
+// largest allowed finite logit: K distinct lines each hold a value >= L.  So
+// every kept token (l >= tau) lies in a line whose maximum is >= L, and tau
+// is the K-th largest of the tokens >= L in those lines, of which there are
+// at least K.  Only the candidate lines are read again, about K of the row's
+// lines (a few KB of a 300 KB row).  One workgroup per row:
+//   1. the row's line codes into LDS (and registers), their largest;
+//   2. L from a histogram of the 1024 keys at and below the largest (a key is
+//      a bf16 code, or the top half of an fp32 code, refined by two 8-bit
+//      digit passes); rows whose K-th key lies further down search the codes
+//      in LDS instead;
+//   3. the candidate lines numbered through an LDS counter, their codes
+//      replaced by their numbers, their tokens' codes loaded into LDS and
+//      counted in the same window;
+//   4. tau the same way;
+//   5. the row's block statistics over the kept tokens with the sweep's
+//      arithmetic: each candidate line's mass by a wave over its tokens, then
+//      each block's sum over its lines in stored order.
+// The sweep computes no statistics for these rows (only marks for an allowed
+// NaN or +inf): rows with at most K allowed finite tokens keep every one
+// (tau = -inf) and get their statistics here too; rows with a NaN or +inf,
+// or without an allowed finite token, keep the sweep's marks, which report
+// them.  Rows with more than kCandLines candidate lines (K > 128, or ties)
+// take tau from radix passes over global memory.
+struct LinesArgs {
+    const void *logits;
+    const uint32_t *mask;
+    const float *temperature;
+    const int32_t *top_k;
+    const int32_t *draft;
+    const void *linemax;     // [rows, C * lines per block], per block in the sweep's lane order
+    BlockStat *bstats;       // [rows, C]
+    DraftRec *drec;          // [rows]
+    float *tau;              // [rows], written for every row
+    uint32_t *tau_flag;      // [rows], written for every row (0: no top-p here)
+    const int32_t *off;      // ragged: draft offsets, or nullptr
+    const int32_t *row_req;  // ragged: request of each row
+    const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
+    uint64_t seed;
+    int kp1, V, W, C;
+};
+
+constexpr int kLinesThreads = 256;
+constexpr int kLinesMax = 4096;   // lines of a row, 16 per thread (bf16 V <= 262144, fp32 V <= 131072)
+constexpr int kCandLines = 128;   // candidate lines whose tokens are staged in LDS
+constexpr int kWin = 1024;        // keys in the window histogram
+
+struct LinesShared {
+    uint32_t hist[2][256];  // 8-bit digit histograms, alternating
+    uint32_t digit, above, total;
+    uint32_t ncand;         // candidate lines numbered so far
+};
+
+// The digit holding the K-th largest of the codes counted in hist (the
+// caller's pass, already complete behind a barrier), given `above` codes known
+// to lie above the prefix they share: the largest digit d with
+// above + #(digits >= d) >= K, the codes above it, and the histogram's total.
+// Wave 0 scans (four bins per lane, a shuffle suffix-sum over the lanes); one
+// barrier publishes the result, and the histogram is then cleared for the
+// pass after next.
+__device__ __forceinline__ uint3 pick_digit(LinesShared &sh, int hb, uint32_t K, uint32_t above) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    if (wave_id() == 0) {
+        uint32_t c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = sh.hist[hb][4 * lane + j];
+        const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+        uint32_t suf = tot;  // bins >= 4 lane
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t t = __shfl_down(suf, d);
+            if (lane + d < kWave) suf += t;
+        }
+        const uint64_t hits = __ballot(above + suf >= K);
+        const int hl = hits ? 63 - static_cast<int>(__builtin_clzll(hits)) : 0;
+        if (lane == hl) {
+            int j = 3;
+            uint32_t sj = suf - c[0] - c[1] - c[2];  // bins >= 4 lane + 3
+            while (j > 0 && above + sj < K) {
+                --j;
+                sj += c[j];
+            }
+            sh.digit = static_cast<uint32_t>(4 * lane + j);
+            sh.above = above + sj - c[j];
+        }
+        if (lane == 0) sh.total = suf;
+    }
+    __syncthreads();
+    const uint3 r = make_uint3(sh.digit, sh.above, sh.total);
+    sh.hist[hb][tid] = 0u;  // read by wave 0 before the barrier; used again two passes on
+    return r;
+}
+
+// The K-th largest of the codes counted in a window histogram, whose bin d
+// holds the codes with key top - d: the first d at which the count from the
+// top reaches K, and the count above it; d = kWin when the window holds fewer
+// than K.  Wave 0 scans 16 bins per lane with a shuffle prefix over the
+// lanes; one barrier publishes the result, after which the bins are cleared
+// (the next use comes after another barrier).
+__device__ __forceinline__ uint2 window_pick(LinesShared &sh, uint32_t *hist, uint32_t K) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    if (wave_id() == 0) {
+        uint32_t c[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 q = reinterpret_cast<const uint4 *>(hist)[4 * lane + j];
+            c[4 * j] = q.x;
+            c[4 * j + 1] = q.y;
+            c[4 * j + 2] = q.z;
+            c[4 * j + 3] = q.w;
+        }
+        uint32_t tot = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tot += c[j];
+        uint32_t pre = tot;  // bins < 16 (lane + 1)
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t t = __shfl_up(pre, d);
+            if (lane >= d) pre += t;
+        }
+        const uint64_t hits = __ballot(pre >= K);
+        if (hits == 0ull) {
+            if (lane == 0) sh.digit = kWin;
+        } else if (lane == static_cast<int>(__builtin_ctzll(hits))) {
+            uint32_t acc = pre - tot;
+            int hit = 16;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (hit == 16) {
+                    if (acc + c[j] >= K) hit = j;
+                    else acc += c[j];
+                }
+            }
+            sh.digit = static_cast<uint32_t>(16 * lane + hit);
+            sh.above = acc;
+        }
+    }
+    __syncthreads();
+    const uint2 r = make_uint2(sh.digit, sh.above);
+    reinterpret_cast<uint4 *>(hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    return r;
+}
+
+// The K-th largest of the codes whose top half is hi16 (fp32 rows), given
+// `above` codes above them: two 8-bit digit passes over the codes that
+// `visit(f)` hands to f.
+template <typename VISIT>
+__device__ __forceinline__ uint32_t refine_low16(LinesShared &sh, uint32_t hi16, uint32_t K, uint32_t above,
+                                                 VISIT visit) {
+    uint32_t prefix = hi16 << 16;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = 8 - 8 * pass;
+        const uint32_t match = 0xffffffffu << (shift + 8);
+        visit([&](uint32_t c) {
+            if ((c & match) == prefix) atomicAdd(&sh.hist[pass][(c >> shift) & 0xffu], 1u);
+        });
+        __syncthreads();
+        const uint3 r = pick_digit(sh, pass, K, above);
+        prefix |= r.x << shift;
+        above = r.y;
+    }
+    return prefix;
+}
+
+// Sums over the workgroup of 16 per-thread counters: wave DPP ladders on
+// pairs packed in 16-bit halves (a wave counts at most 64 * 64 codes here),
+// then the waves' rows in LDS behind one barrier (red alternates by `round`).
+__device__ __forceinline__ void block_count16(const uint32_t (&cnt)[16], uint32_t (*red)[kLinesThreads / 64][16],
+                                              int round, uint32_t (&tot)[16]) {
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t s = wave_sum_u(cnt[2 * j] | (cnt[2 * j + 1] << 16));
+        if (lane == 0) {
+            red[round & 1][wave][2 * j] = s & 0xffffu;
+            red[round & 1][wave][2 * j + 1] = s >> 16;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int w = 0; w < kLinesThreads / 64; ++w) t += red[round & 1][w][j];
+        tot[j] = t;
+    }
+}
+
+// The K-th largest (with multiplicity) of the codes that `visit(f)` hands
+// to f over the workgroup (at most 64 per thread), known to lie in [lo, hi]
+// with at least K codes >= lo: a 16-way search of the code interval, each
+// round counting the codes at or above 15 pivots.  For rows whose K-th key
+// lies below the window.
+template <typename VISIT>
+__device__ __forceinline__ uint32_t kth_largest(VISIT visit, uint32_t K, uint32_t lo, uint32_t hi,
+                                                uint32_t (*red)[kLinesThreads / 64][16], int &round) {
+    while (lo < hi) {
+        const uint32_t step = (hi - lo) / 16u + 1u;  // 16 parts cover [lo, hi]
+        uint32_t cnt[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cnt[j] = 0u;
+        visit([&](uint32_t c) {
+#pragma unroll
+            for (int j = 1; j < 16; ++j) cnt[j] += (c >= lo + uint32_t(j) * step) ? 1u : 0u;
+        });
+        uint32_t tot[16];
+        block_count16(cnt, red, round++, tot);
+        // the part holding the K-th largest: the last pivot with K codes at or above it
+        uint32_t nlo = lo, nhi = hi;
+#pragma unroll
+        for (int j = 1; j < 16; ++j) {
+            const uint64_t pj = uint64_t(lo) + uint64_t(j) * step;
+            if (pj > hi) break;
+            if (tot[j] >= K) nlo = static_cast<uint32_t>(pj);
+            else {
+                nhi = static_cast<uint32_t>(pj - 1);
+                break;
+            }
+        }
+        lo = nlo;
+        hi = nhi;
+    }
+    return lo;
+}
+
+// Line `line` of a row (entry q * G + g of block c in the stored order) is
+// group g's line of lanes 8q .. 8q + 7: its first token.
+template <typename ET>
+__device__ __forceinline__ int64_t line_token(int line) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    constexpr int LPB = G * 8;
+    const int c = line / LPB, j = line % LPB;
+    return int64_t(c) * kBlock + ((j % G) * kWave + (j / G) * 8) * P;
+}
+
+template <typename ET>
+__device__ __forceinline__ uint32_t line_code(const LinesArgs &a, int64_t row, int line) {
+    constexpr int LPB = (kBlock / (kWave * Logit<ET>::kPer16)) * 8;
+    const int64_t idx = row * int64_t(a.C) * LPB + line;
+    return sizeof(ET) == 2 ? uint32_t(reinterpret_cast<const uint16_t *>(a.linemax)[idx])
+                           : reinterpret_cast<const uint32_t *>(a.linemax)[idx];
+}
+
+// The codes of line `line` of a row as 16-byte groups: group h (of 8) holds
+// the line's tokens h * P .. h * P + P - 1; 0 for masked tokens and tokens
+// past V (bf16: the top half of the code).
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void line_group_codes(const LinesArgs &a, int64_t row, int line, int h,
+                                                 uint32_t *code) {
+    constexpr int P = Logit<ET>::kPer16;
+    const int64_t tok = line_token<ET>(line) + h * P;
+    float v[P];
+    if (tok < a.V) {
+        Logit<ET>::unpack(*reinterpret_cast<const uint4 *>(reinterpret_cast<const ET *>(a.logits) + row * a.V + tok), v);
+        uint32_t bits = 0xffu;
+        if (MASKED) {
+            const uint32_t byte = reinterpret_cast<const uint8_t *>(a.mask + row * a.W)[tok >> 3];
+            bits = (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
+        }
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const bool live = ((bits >> e) & 1u) && v[e] > -INFINITY && v[e] < INFINITY;
+            const uint32_t c = ordered_code(v[e]);
+            code[e] = live ? (sizeof(ET) == 2 ? (c >> 16) : c) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < P; ++e) code[e] = 0u;
+    }
+}
+
+template <typename ET>
+__device__ __forceinline__ float value_of_code(uint32_t c) {
+    return sizeof(ET) == 2 ? bf16_value_of_digit(c) : float_of_code(c);
+}
+
+// Element e of a 16-byte vector of codes (8 x 16 bits or 4 x 32 bits).
+template <typename CT>
+__device__ __forceinline__ uint32_t code_in(const uint4 &q, int e) {
+    const uint32_t w = e * int(sizeof(CT)) < 4 ? q.x : (e * int(sizeof(CT)) < 8 ? q.y : (e * int(sizeof(CT)) < 12 ? q.z : q.w));
+    return sizeof(CT) == 2 ? ((w >> (16 * (e & 1))) & 0xffffu) : w;
+}
+
+// What the block statistics need beside the codes: the row's coordinates.
+struct LinesRow {
+    int64_t row;
+    int b, i, x;   // request, position, valid draft of a draft row (-1: none)
+    float cT;      // log2(e) / T
+};
+
+// tau from global memory by radix selection, for rows with more candidate
+// lines than LDS holds: passes over the line codes and the candidate lines.
+// Returns 0 when at most K allowed finite tokens exist.
+template <typename ET, bool MASKED>
+__device__ __forceinline__ uint32_t tau_code_global(const LinesArgs &a, LinesShared &sh, int64_t row, uint32_t L, uint32_t Ku) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int LPB = (kBlock / (kWave * P)) * 8;
+    constexpr int BITS = sizeof(ET) == 2 ? 16 : 32;
+    const int tid = threadIdx.x;
+    const int nlines = a.C * LPB;
+    uint32_t prefix = 0u, above = 0u;
+    int hb = 0;
+    for (int shift = BITS - 8; shift >= 0; shift -= 8, hb ^= 1) {
+        const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (0xffffffffu << (shift + 8));
+        for (int l = tid >> 3; l < nlines; l += kLinesThreads / 8) {  // 8 threads per line
+            if (line_code<ET>(a, row, l) < L) continue;
+            uint32_t code[P];
+            line_group_codes<ET, MASKED>(a, row, l, tid & 7, code);
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+                if (code[e] >= L && (code[e] & hi_mask) == (prefix & hi_mask))
+                    atomicAdd(&sh.hist[hb][(code[e] >> shift) & 0xffu], 1u);
+        }
+        __syncthreads();
+        const uint3 r = pick_digit(sh, hb, Ku, above);
+        if (shift == BITS - 8 && r.z < Ku) return 0u;
+        prefix |= r.x << shift;
+        above = r.y;
+    }
+    return prefix;
+}
+
+// Block statistics over the kept tokens read from global memory (rows with
+// more candidate lines than LDS holds): one wave per block, lane t on token t
+// of each candidate line.
+template <typename ET, bool MASKED>
+__device__ __forceinline__ void block_stats_global(const LinesArgs &a, const LinesRow &r, uint32_t L, uint32_t tcode) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    constexpr int LPB = G * 8;
+    constexpr int TPL = 8 * P;
+    constexpr int NW = kLinesThreads / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+    const PhiloxKey key = key_of(a.seed);
+    for (int c = wave; c < a.C; c += NW) {
+        const uint64_t cl = __ballot(lane < LPB && line_code<ET>(a, r.row, c * LPB + lane) >= L);
+        const bool has_x = r.x >= 0 && r.x / kBlock == c;
+        BlockStat out{-INFINITY, 0.0f, -INFINITY};
+        float sx = 0.0f;
+        uint32_t mcode = 0u;
+        for (uint64_t ll = cl; ll; ll &= ll - 1) {
+            uint32_t code[P];
+            const int l = static_cast<int>(__builtin_ctzll(ll));
+            line_group_codes<ET, MASKED>(a, r.row, c * LPB + l, (lane & (TPL - 1)) / P, code);
+            uint32_t cd = 0u;
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                if (lane < TPL && lane % P == q) cd = code[q];
+            if (cd >= tcode) mcode = max(mcode, cd);
+        }
+        mcode = wave_max_u(mcode);
+        if (mcode != 0u) {
+            const float mc = value_of_code<ET>(mcode) * r.cT;
+            float sl = 0.0f, sxl = 0.0f;
+            for (uint64_t ll = cl; ll; ll &= ll - 1) {
+                uint32_t code[P];
+                const int l = static_cast<int>(__builtin_ctzll(ll));
+                line_group_codes<ET, MASKED>(a, r.row, c * LPB + l, (lane & (TPL - 1)) / P, code);
+                uint32_t cd = 0u;
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                if (lane < TPL && lane % P == q) cd = code[q];
+                if (cd >= tcode) {
+                    const float term = __builtin_amdgcn_exp2f(fmaf(value_of_code<ET>(cd), r.cT, -mc));
+                    sl += term;
+                    if (line_token<ET>(c * LPB + l) + lane != r.x) sxl += term;
+                }
+            }
+            const float sum = wave_sum(sl);
+            sx = wave_sum(sxl);
+            out.m = mc;
+            out.s = sum;
+            if (lane == 0) {
+                const float g = block_gumbel(key, r.b, r.i, c);
+                out.key = key_of_mass(sum, mc, g);
+                if (has_x) a.drec[r.row].keyx = key_of_mass(sx, mc, g);
+            }
+        } else if (has_x && lane == 0) {
+            a.drec[r.row].keyx = -INFINITY;
+        }
+        if (lane == 0) {
+            a.bstats[r.row * a.C + c] = out;
+            if (has_x) a.drec[r.row].sx = sx;
+        }
+    }
+}
+
+template <typename ET, bool MASKED>
+__global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) {
+    constexpr int P = Logit<ET>::kPer16;
+    constexpr int G = kBlock / (kWave * P);
+    constexpr int LPB = G * 8;            // lines per block
+    constexpr int TPL = 8 * P;            // tokens per line
+    constexpr int NW = kLinesThreads / kWave;
+    constexpr bool BF = sizeof(ET) == 2;
+    constexpr int KS = BF ? 0 : 16;       // key = code >> KS
+    typedef typename std::conditional<BF, uint16_t, uint32_t>::type CT;
+    constexpr int PER4 = 16 / int(sizeof(CT));                 // codes per 16-byte vector
+    constexpr int NV4 = kLinesMax / kLinesThreads / PER4;      // vectors of line codes per thread
+    constexpr int CPT = NV4 * PER4;                            // lines per thread, contiguous
+    constexpr int NB = kLinesMax / 32;                         // blocks at most
+    __shared__ LinesShared sh;
+    __shared__ uint32_t red[2][NW][16];
+    __shared__ __align__(16) uint32_t hist[kWin];
+    __shared__ __align__(16) CT tcodes[kCandLines * TPL];     // the candidate lines' token codes
+    __shared__ uint16_t cand[kCandLines];                      // the candidate lines, ascending
+    __shared__ uint32_t cmax[kCandLines];                      // each candidate's largest code
+    __shared__ float lsum[kCandLines];                         // each candidate's kept mass
+    __shared__ uint32_t bmax[NB];                              // each block's largest kept code
+    __shared__ uint8_t brun[NB][2];                            // each block's run of candidates
+    __shared__ float xmass;                                    // the draft line's kept mass without it
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call
+    int b, i, kb;
+    int64_t d0;
+    row_owner(a.off, a.row_req, static_cast<int>(row), a.kp1, b, i, kb, d0);
+    const int nlines = a.C * LPB;  // at most kLinesMax (the host checks)
+    const int nv = nlines / PER4;
+    // ---- 1. the row's line codes, lines tid * CPT .. + CPT - 1 per thread,
+    // issued before the request's settings are known
+    uint4 w[NV4];
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const CT *>(a.linemax) + row * nlines);
+#pragma unroll
+        for (int j = 0; j < NV4; ++j) {
+            const int q = tid * NV4 + j;
+            w[j] = q < nv ? src[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    const float T = uniform_load(a.temperature + b);
+    const int K = uniform_load(a.top_k + b);
+    // the row is not cut unless a cut is found below
+    if (tid == 0) {
+        a.tau[row] = -INFINITY;
+        a.tau_flag[row] = 0u;
+    }
+    if (!(T > 0.0f && T <= FLT_MAX) || K <= 0) return;
+    const BlockStat *st = a.bstats + row * a.C;
+    bool bad = false;
+    for (int c = tid; c < a.C; c += kLinesThreads) {
+        const BlockStat e = st[c];
+        bad |= (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
+    }
+    uint32_t mx = 0u, nz = 0u;
+#pragma unroll
+    for (int j = 0; j < NV4; ++j)
+#pragma unroll
+        for (int e = 0; e < PER4; ++e) {
+            const uint32_t c = code_in<CT>(w[j], e);
+            mx = max(mx, c);
+            nz += c != 0u ? 1u : 0u;
+        }
+    reinterpret_cast<uint4 *>(hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    sh.hist[0][tid] = 0u;
+    sh.hist[1][tid] = 0u;
+    if (tid < NB) {
+        bmax[tid] = 0u;
+        brun[tid][0] = brun[tid][1] = 0;
+    }
+    mx = wave_max_u(mx);
+    nz = wave_sum_u(nz);
+    const bool wbad = wave_any(bad);
+    if (lane == 0) {
+        red[0][wave][0] = mx;
+        red[0][wave][1] = nz;
+        red[0][wave][2] = wbad ? 1u : 0u;
+    }
+    __syncthreads();
+    uint32_t lmax = 0u, lnz = 0u, anybad = 0u;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+        lmax = max(lmax, red[0][q][0]);
+        lnz += red[0][q][1];
+        anybad |= red[0][q][2];
+    }
+    // bad rows keep the sweep's marks, which report them; rows without an
+    // allowed finite token keep its (-inf, 0), which report them too
+    if (anybad || lnz == 0u) return;
+    const uint32_t Ku = static_cast<uint32_t>(K);
+    const uint32_t top = lmax >> KS;  // the window's first key
+    int round = 1;
+    auto visit_lines = [&](auto f) {
+#pragma unroll
+        for (int j = 0; j < NV4; ++j)
+#pragma unroll
+            for (int e = 0; e < PER4; ++e) f(code_in<CT>(w[j], e));
+    };
+    // ---- 2. L: the K-th largest line code (every nonempty line when fewer)
+    uint32_t L = 1u;
+    if (lnz >= Ku) {
+        visit_lines([&](uint32_t c) {
+            const uint32_t d = top - (c >> KS);
+            if (c != 0u && d < uint32_t(kWin)) atomicAdd(&hist[d], 1u);
+        });
+        __syncthreads();
+        const uint2 pk = window_pick(sh, hist, Ku);
+        if (pk.x < uint32_t(kWin)) {
+            if constexpr (BF) L = top - pk.x;
+            else L = refine_low16(sh, top - pk.x, Ku, pk.y, visit_lines);
+        } else {
+            L = kth_largest(visit_lines, Ku, 1u, lmax, red, round);
+        }
+    }
+    // ---- 3. the candidate lines (code >= L), listed in ascending order
+    uint32_t mine = 0u;
+    visit_lines([&](uint32_t c) { mine += c >= L ? 1u : 0u; });
+    const uint32_t incl = wave_prefix_u(mine);
+    if (lane == kWave - 1) red[round & 1][wave][0] = incl;
+    __syncthreads();
+    uint32_t pos = incl - mine, ncand = 0u;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+        const uint32_t t = red[round & 1][q][0];
+        pos += q < wave ? t : 0u;
+        ncand += t;
+    }
+    ++round;
+#pragma unroll
+    for (int j = 0; j < NV4; ++j)
+#pragma unroll
+        for (int e = 0; e < PER4; ++e) {
+            const uint32_t c = code_in<CT>(w[j], e);
+            if (c >= L) {
+                if (pos < uint32_t(kCandLines)) {
+                    cand[pos] = static_cast<uint16_t>(tid * CPT + j * PER4 + e);
+                    cmax[pos] = c;
+                }
+                ++pos;
+            }
+        }
+    __syncthreads();
+    LinesRow r;
+    r.row = row;
+    r.b = b;
+    r.i = i;
+    r.x = -1;
+    if (i < kb) {
+        const int xv = uniform_load(a.draft + d0 + i);
+        if (xv >= 0 && xv < a.V) r.x = xv;
+    }
+    r.cT = scale_of(T);
+    uint32_t tcode;
+    bool cut;
+    if (ncand <= uint32_t(kCandLines)) {
+        // ---- 4. the candidates' tokens into LDS, counted in the window
+        uint32_t tn = 0u;
+        for (uint32_t e = tid; e < ncand * 8u; e += kLinesThreads) {
+            uint32_t code[P];
+            line_group_codes<ET, MASKED>(a, row, cand[e >> 3], e & 7u, code);
+            uint4 ov;
+            if constexpr (BF) {
+                ov = make_uint4(code[0] | (code[1 % P] << 16), code[2 % P] | (code[3 % P] << 16),
+                                code[4 % P] | (code[5 % P] << 16), code[6 % P] | (code[7 % P] << 16));
+            } else {
+                ov = make_uint4(code[0], code[1 % P], code[2 % P], code[3 % P]);
+            }
+            reinterpret_cast<uint4 *>(tcodes)[e] = ov;
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (code[q] >= L) {
+                    ++tn;
+                    const uint32_t d = top - (code[q] >> KS);
+                    if (d < uint32_t(kWin)) atomicAdd(&hist[d], 1u);
+                }
+            }
+        }
+        tn = wave_sum_u(tn);
+        if (lane == 0) red[round & 1][wave][0] = tn;
+        __syncthreads();
+        uint32_t ttot = 0u;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) ttot += red[round & 1][q][0];
+        ++round;
+        cut = ttot >= Ku;
+        // ---- tau: the K-th largest candidate token at or above L.  With at
+        // most K allowed finite tokens there is no cut: every candidate line
+        // was taken (L = 1) and every allowed finite token is kept.
+        const int ntok = static_cast<int>(ncand) * TPL;
+        auto visit_tokens = [&](auto f) {
+            for (int t = tid; t < ntok; t += kLinesThreads) {
+                const uint32_t c = tcodes[t];
+                if (c >= L) f(c);
+            }
+        };
+        if (!cut) {
+            tcode = 1u;
+        } else {
+            const uint2 pk = window_pick(sh, hist, Ku);
+            if (pk.x < uint32_t(kWin)) {
+                if constexpr (BF) tcode = top - pk.x;
+                else tcode = refine_low16(sh, top - pk.x, Ku, pk.y, visit_tokens);
+            } else {
+                tcode = kth_largest(visit_tokens, Ku, L, lmax, red, round);
+            }
+        }
+        // ---- 5. the row's block statistics over the kept tokens: each
+        // block's run of candidates and largest kept code, each candidate's
+        // kept mass with a wave on its tokens, each block's sum over its run
+        for (uint32_t s = tid; s < ncand; s += kLinesThreads) {
+            const int c = cand[s] / LPB;
+            if (s == 0u || cand[s - 1] / LPB != c) brun[c][0] = static_cast<uint8_t>(s);
+            if (s + 1u == ncand || cand[s + 1] / LPB != c) brun[c][1] = static_cast<uint8_t>(s + 1u);
+            if (cmax[s] >= tcode) atomicMax(&bmax[c], cmax[s]);
+        }
+        int xline = -1;  // the draft's line
+        if (r.x >= 0) {
+            const int o = r.x % kBlock;
+            xline = (r.x / kBlock) * LPB + ((o % (kWave * P)) / P / 8) * G + o / (kWave * P);
+        }
+        __syncthreads();
+        for (uint32_t s = wave; s < ncand; s += NW) {
+            const int line = cand[s];
+            const uint32_t mk = bmax[line / LPB];
+            if (mk == 0u) continue;
+            const float mc = value_of_code<ET>(mk) * r.cT;
+            const uint32_t cd = lane < TPL ? uint32_t(tcodes[s * TPL + lane]) : 0u;
+            float term = 0.0f;
+            if (cd >= tcode) term = __builtin_amdgcn_exp2f(fmaf(value_of_code<ET>(cd), r.cT, -mc));
+            const float ls = wave_sum(term);
+            if (lane == 0) lsum[s] = ls;
+            if (line == xline) {
+                const float lx = wave_sum(line_token<ET>(line) + lane != r.x ? term : 0.0f);
+                if (lane == 0) xmass = lx;
+            }
+        }
+        __syncthreads();
+        const PhiloxKey key = key_of(a.seed);
+        for (int c = tid; c < a.C; c += kLinesThreads) {
+            const uint32_t mk = bmax[c];
+            const bool has_x = r.x >= 0 && r.x / kBlock == c;
+            BlockStat out{-INFINITY, 0.0f, -INFINITY};
+            float sx = 0.0f;
+            if (mk != 0u) {
+                const float mc = value_of_code<ET>(mk) * r.cT;
+                float sum = 0.0f;
+                for (int s = brun[c][0]; s < brun[c][1]; ++s) {
+                    const float ls = lsum[s];
+                    sum += ls;
+                    sx += cand[s] == xline ? xmass : ls;
+                }
+                out.m = mc;
+                out.s = sum;
+                const float g = block_gumbel(key, r.b, r.i, c);
+                out.key = key_of_mass(sum, mc, g);
+                if (has_x) a.drec[r.row].keyx = key_of_mass(sx, mc, g);
+            } else if (has_x) {
+                a.drec[r.row].keyx = -INFINITY;
+            }
+            a.bstats[r.row * a.C + c] = out;
+            if (has_x) a.drec[r.row].sx = sx;
+        }
+    } else {
+        tcode = tau_code_global<ET, MASKED>(a, sh, row, L, Ku);
+        cut = tcode != 0u;
+        if (!cut) tcode = 1u;  // no cut: every allowed finite token (then L = 1)
+        block_stats_global<ET, MASKED>(a, r, L, tcode);
+    }
+    if (tid == 0 && cut) {
+        const float tau = value_of_code<ET>(tcode);
+        a.tau[row] = tau;
+        if (r.x >= 0 && !(a.drec[row].lx >= tau)) a.drec[row].lx = -INFINITY;
     }
 }
 
@@ -2730,23 +3457,31 @@ __global__ __launch_bounds__(1024) void histogram_kernel(const int32_t *num_acce
 using RowStatsFn = void (*)(RowStatsArgs);
 using FinalFn = void (*)(FinalArgs);
 
+// topk: 0 none, 1 cut at tau, 2 line maxima (aligned rows only)
 template <typename ET, int POL>
-RowStatsFn pick_row_stats_vec(bool masked, bool topk) {
-    if (topk) return masked ? row_stats_vec_kernel<ET, true, true, POL> : row_stats_vec_kernel<ET, false, true, POL>;
-    return masked ? row_stats_vec_kernel<ET, true, false, POL> : row_stats_vec_kernel<ET, false, false, POL>;
+RowStatsFn pick_row_stats_vec(bool masked, int topk) {
+    if (topk == 2) return masked ? row_stats_vec_kernel<ET, true, 2, POL> : row_stats_vec_kernel<ET, false, 2, POL>;
+    if (topk == 1) return masked ? row_stats_vec_kernel<ET, true, 1, POL> : row_stats_vec_kernel<ET, false, 1, POL>;
+    return masked ? row_stats_vec_kernel<ET, true, 0, POL> : row_stats_vec_kernel<ET, false, 0, POL>;
 }
 
 template <typename ET>
-RowStatsFn pick_row_stats(bool masked, bool aligned, bool topk, bool cached) {
+RowStatsFn pick_row_stats(bool masked, bool aligned, int topk, bool cached) {
     if (aligned) {
         return cached ? pick_row_stats_vec<ET, 0>(masked, topk)
                       : pick_row_stats_vec<ET, SDV_LOGITS_CACHE_POLICY>(masked, topk);
     }
-    if (topk) return masked ? row_stats_elem_kernel<ET, true, true> : row_stats_elem_kernel<ET, false, true>;
-    return masked ? row_stats_elem_kernel<ET, true, false> : row_stats_elem_kernel<ET, false, false>;
+    if (topk) return masked ? row_stats_elem_kernel<ET, true, 1> : row_stats_elem_kernel<ET, false, 1>;
+    return masked ? row_stats_elem_kernel<ET, true, 0> : row_stats_elem_kernel<ET, false, 0>;
 }
 
 using TopkFn = void (*)(TopkArgs);
+using LinesFn = void (*)(LinesArgs);
+
+template <typename ET>
+LinesFn pick_topk_lines(bool masked) {
+    return masked ? topk_lines_kernel<ET, true> : topk_lines_kernel<ET, false>;
+}
 using DenseFn = void (*)(FinalArgs);
 
 template <typename ET>
@@ -2800,10 +3535,19 @@ inline int64_t resident_workgroups(const void *kernel, int threads, int per_cu_m
     return int64_t(it->second.first) * std::min(it->second.second, per_cu_max);
 }
 
+// The single-pass top-k holds a row's line maxima in its threads' registers:
+// top-k calls whose rows have at most kLinesMax lines (bf16 V <= 262144, fp32
+// V <= 131072) take it, others the two-pass selection.
+inline bool lines_fit(const sd_params *p) {
+    const int64_t C = (int64_t(p->vocab) + kBlock - 1) / kBlock;
+    return p->top_k != nullptr && C * (p->logits_dtype == SD_DTYPE_BF16 ? 32 : 64) <= kLinesMax;
+}
+
 struct Layout {
     int64_t rows;
     int C, W, nchunk;
-    size_t off_sweep, off_bstats, off_drec, off_tau, off_tauflag, off_jobs, off_wmass, off_rowreq, off_offok, off_tally, total;
+    size_t off_sweep, off_bstats, off_drec, off_tau, off_tauflag, off_jobs, off_wmass, off_rowreq, off_offok, off_tally,
+        off_linemax, total;
     int nslot;
 };
 
@@ -2842,7 +3586,13 @@ inline Layout layout_of(const sd_params *p) {
     L.off_offok = L.off_rowreq + align256(p->draft_offsets ? size_t(L.rows) * sizeof(int32_t) : 0);
     L.off_tally = L.off_offok + 256;
     L.nslot = tally_slots(p->batch);
-    L.total = L.off_tally + align256(size_t(L.nslot) * kTallyStride * sizeof(uint64_t));
+    L.off_linemax = L.off_tally + align256(size_t(L.nslot) * kTallyStride * sizeof(uint64_t));
+    // line maxima of the single-pass top-k: one code per 128-byte line of
+    // every row (2 bytes per 64 bf16 tokens, 4 per 32 fp32 tokens)
+    const size_t line_bytes = lines_fit(p) ? size_t(L.rows) * L.C *
+                                                 (p->logits_dtype == SD_DTYPE_BF16 ? kBlock / 64 * 2 : kBlock / 32 * 4)
+                                           : 0;
+    L.total = L.off_linemax + align256(line_bytes);
     return L;
 }
 
@@ -2919,7 +3669,13 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.q = draft_probs;
     ra.seed = seed;
     const bool thresholds = p->top_k != nullptr || p->top_p != nullptr;
-    ra.tau = thresholds ? reinterpret_cast<float *>(ws + L.off_tau) : nullptr;
+    // top-k without top-p on aligned rows: the threshold is found after the
+    // sweep from its line maxima, with no second pass over the rows
+    const bool single_pass = p->top_k != nullptr && p->top_p == nullptr && aligned && lines_fit(p);
+    float *tau_arr = reinterpret_cast<float *>(ws + L.off_tau);
+    ra.tau = (thresholds && !single_pass) ? tau_arr : nullptr;
+    ra.top_k = p->top_k;
+    ra.linemax = single_pass ? static_cast<void *>(ws + L.off_linemax) : nullptr;
     uint32_t *tau_flag = reinterpret_cast<uint32_t *>(ws + L.off_tauflag);
     int32_t *row_req = reinterpret_cast<int32_t *>(ws + L.off_rowreq);
     uint32_t *off_ok = reinterpret_cast<uint32_t *>(ws + L.off_offok);
@@ -2965,7 +3721,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.status = p->status;
     fa.bstats = ra.bstats;
     fa.drec = ra.drec;
-    fa.tau = ra.tau;
+    fa.tau = thresholds ? tau_arr : nullptr;
     fa.tau_flag = tau_flag;
     fa.off = ra.off;
     fa.off_ok = ra.off_ok;
@@ -2982,7 +3738,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.W = L.W;
     fa.C = L.C;
 
-    const bool topk = thresholds;
+    const int topk = single_pass ? 2 : (thresholds ? 1 : 0);
     const bool cached = L.rows * int64_t(V) * (bf16 ? 2 : 4) <= SDV_CACHED_LOGITS_BYTES;
     RowStatsFn k1 = bf16 ? pick_row_stats<uint16_t>(masked, aligned, topk, cached)
                          : pick_row_stats<float>(masked, aligned, topk, cached);
@@ -3019,13 +3775,13 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
                            p->total_drafts, row_req, off_ok);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }
-    if (topk) {
+    if (thresholds && !single_pass) {
         TopkArgs ta;
         ta.logits = target_logits;
         ta.mask = ra.mask;
         ta.temperature = temperature;
         ta.top_k = p->top_k;
-        ta.tau = const_cast<float *>(ra.tau);
+        ta.tau = tau_arr;
         ta.tau_flag = tau_flag;
         ta.top_p = p->top_p;
         ta.off = ra.off;
@@ -3047,6 +3803,30 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     if (p->row_stats_event_end &&
         hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_end), stream) != hipSuccess)
         return SD_ERR_HIP;
+    if (single_pass) {
+        LinesArgs la;
+        la.logits = target_logits;
+        la.mask = ra.mask;
+        la.temperature = temperature;
+        la.top_k = p->top_k;
+        la.draft = draft_token_ids;
+        la.linemax = ra.linemax;
+        la.bstats = ra.bstats;
+        la.drec = ra.drec;
+        la.tau = tau_arr;
+        la.tau_flag = tau_flag;
+        la.off = ra.off;
+        la.row_req = ra.row_req;
+        la.off_ok = ra.off_ok;
+        la.seed = seed;
+        la.kp1 = k + 1;
+        la.V = V;
+        la.W = L.W;
+        la.C = L.C;
+        const LinesFn k5 = bf16 ? pick_topk_lines<uint16_t>(masked) : pick_topk_lines<float>(masked);
+        hipLaunchKernelGGL(k5, dim3(static_cast<unsigned>(L.rows)), dim3(kLinesThreads), 0, stream, la);
+        if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
+    }
     const size_t dyn_lds = (draft_probs && !fa.split_dense) ? size_t(L.C) * sizeof(double) : 0;
     hipLaunchKernelGGL(k2, dim3(B), dim3(kFinalThreads), dyn_lds, stream, fa);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;

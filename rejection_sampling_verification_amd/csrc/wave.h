@@ -73,6 +73,19 @@ __device__ __forceinline__ uint32_t wave_sum_u(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
 }
 
+// Inclusive prefix sum over the lanes: the same ladder leaves lane i holding
+// the sum of lanes 0 .. i.
+__device__ __forceinline__ uint32_t wave_prefix_u(uint32_t v) {
+    int x = static_cast<int>(v);
+    x += dpp_i<0x111, 0xf>(0, x);
+    x += dpp_i<0x112, 0xf>(0, x);
+    x += dpp_i<0x114, 0xf>(0, x);
+    x += dpp_i<0x118, 0xf>(0, x);
+    x += dpp_i<0x142, 0xa>(0, x);
+    x += dpp_i<0x143, 0xc>(0, x);
+    return static_cast<uint32_t>(x);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
     v = max(v, static_cast<uint32_t>(dpp_i<0x111, 0xf>(0, static_cast<int>(v))));
     v = max(v, static_cast<uint32_t>(dpp_i<0x112, 0xf>(0, static_cast<int>(v))));

@@ -206,7 +206,7 @@ def test_noalloc_refuses_before_launching():
     fake = ctypes.c_void_p(0x1000)
     assert lib.sd_verify_noalloc(fake, fake, nul, nul, fake, 0, fake, fake, fake, None, nul) == -1
     p = sdv.SdParams()
-    p.batch, p.num_draft, p.vocab, p.logits_dtype = 4096, 12, 151936, 1   # about 77 MB of workspace
+    p.batch, p.num_draft, p.vocab, p.logits_dtype = 8192, 12, 151936, 1   # about 128 MB of workspace
     assert lib.sd_verify_workspace_size(ctypes.byref(p)) > sdv.SD_NOALLOC_SCRATCH_BYTES
     assert lib.sd_verify_noalloc(fake, fake, nul, nul, fake, 0, fake, fake, fake, ctypes.byref(p), nul) == -5
     assert "scratch" in sdv.sd_status_string(-5)
