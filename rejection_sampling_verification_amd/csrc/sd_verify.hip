@@ -699,11 +699,22 @@ __device__ __forceinline__ void issue_block(const RowStatsArgs &a, int row, int 
             const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, base + g * kWave * 16, 0, POL);
             r[g] = make_uint4(w.x, w.y, w.z, w.w);
         }
+        // the block's 256 mask bytes, one word per lane (spread to the lanes
+        // that use them when the block is reduced)
         const __amdgpu_buffer_rsrc_t rm = buffer_of(a.mask + int64_t(row) * a.W, uint32_t(a.W) * 4u);
-        const int mbase = live ? blk * (kBlock / 8) + ((lane * P) >> 3) : kPastAnyBuffer;
+        m[0] = __builtin_amdgcn_raw_buffer_load_b32(rm, live ? blk * (kBlock / 8) + lane * 4 : kPastAnyBuffer, 0, 0);
+    }
+}
+
+// The mask byte of each group of a lane, from the block's mask words held one
+// per lane (lane l holds bytes 4l .. 4l + 3): group g's byte of the lane is
+// byte (g * 64 + lane) * P / 8 of the block.
+template <int G, int P>
+__device__ __forceinline__ void spread_mask(uint32_t word, int lane, uint32_t *mm) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-            m[g] = __builtin_amdgcn_raw_buffer_load_b8(rm, mbase + g * kWave * P / 8, 0, 0);
+    for (int g = 0; g < G; ++g) {
+        const int byte = (g * kWave + lane) * P / 8;
+        mm[g] = (static_cast<uint32_t>(__shfl(static_cast<int>(word), byte >> 2)) >> (8 * (byte & 3))) & 0xffu;
     }
 }
 
@@ -792,6 +803,8 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
     // set of registers for both, where two unpacking paths end in copies.
     // With a mask the two paths measured faster.
     float v[G * P];
+    uint32_t mm[G];
+    if constexpr (MASKED) spread_mask<G, P>(m[0], lane, mm);
     if constexpr (!MASKED) {
         uint4 w[G];
 #pragma unroll
@@ -801,16 +814,16 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
             for (int g = 0; g < G; ++g)
                 if (s.blk * kBlock + (g * kWave + lane) * P >= a.V) w[g] = Logit<ET>::neg_inf_group();
         }
-        unpack_full_block<ET, MASKED>(w, m, lane, v);
+        unpack_full_block<ET, MASKED>(w, mm, lane, v);
     } else if (s.full) {
-        unpack_full_block<ET, MASKED>(r, m, lane, v);
+        unpack_full_block<ET, MASKED>(r, mm, lane, v);
     } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t tok = int64_t(s.blk) * kBlock + (g * kWave + lane) * P;
             Logit<ET>::unpack(r[g], v + g * P);
             uint32_t bits = tok < a.V ? 0xffu : 0u;
-            bits &= (P == 8) ? m[g] : (m[g] >> (uint32_t(tok) & 4u));
+            bits &= (P == 8) ? mm[g] : (mm[g] >> (uint32_t(tok) & 4u));
 #pragma unroll
             for (int e = 0; e < P; ++e)
                 if (!((bits >> e) & 1u)) v[g * P + e] = -INFINITY;
@@ -827,7 +840,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
         res = softmax_block<G * P>(v, s.c);
         if (s.xrel >= 0) sx = excluded_sum<G, P>(v, s.c, res.x, s.xrel, lane);
     }
-    if (s.xrel >= 0) record_draft<G, P, MASKED>(a, s.row, s.dpos, s.x, s.xrel, v, m, lane, sx);
+    if (s.xrel >= 0) record_draft<G, P, MASKED>(a, s.row, s.dpos, s.x, s.xrel, v, mm, lane, sx);
     if (lane == slot) {
         st.gb = s.gb;
         st.row = s.row;
@@ -1897,32 +1910,52 @@ __device__ __forceinline__ uint32_t line_code(const LinesArgs &a, int64_t row, i
                            : reinterpret_cast<const uint32_t *>(a.linemax)[idx];
 }
 
-// The codes of line `line` of a row as 16-byte groups: group h (of 8) holds
-// the line's tokens h * P .. h * P + P - 1; 0 for masked tokens and tokens
-// past V (bf16: the top half of the code).
+// Group h (of 8) of line `line` of a row: its 16 bytes of logits and its
+// mask byte (all ones without a mask), zeros past V.  Group h holds the
+// line's tokens h * P .. h * P + P - 1.
+struct LineGroup {
+    uint4 w;
+    uint32_t bits;
+    int64_t tok;
+};
+
+template <typename ET, bool MASKED>
+__device__ __forceinline__ LineGroup load_line_group(const LinesArgs &a, int64_t row, int line, int h) {
+    constexpr int P = Logit<ET>::kPer16;
+    LineGroup g;
+    g.tok = line_token<ET>(line) + h * P;
+    g.w = make_uint4(0u, 0u, 0u, 0u);
+    g.bits = 0u;
+    if (g.tok < a.V) {
+        g.w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const ET *>(a.logits) + row * a.V + g.tok);
+        g.bits = 0xffu;
+        if (MASKED) {
+            const uint32_t byte = reinterpret_cast<const uint8_t *>(a.mask + row * a.W)[g.tok >> 3];
+            g.bits = (P == 8) ? byte : (byte >> (uint32_t(g.tok) & 4u));
+        }
+    }
+    return g;
+}
+
+// The group's codes: 0 for masked, infinite and past-V tokens (bf16: the top
+// half of the code).
+template <typename ET>
+__device__ __forceinline__ void group_codes(const LineGroup &g, uint32_t *code) {
+    constexpr int P = Logit<ET>::kPer16;
+    float v[P];
+    Logit<ET>::unpack(g.w, v);
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        const bool live = ((g.bits >> e) & 1u) && v[e] > -INFINITY && v[e] < INFINITY;
+        const uint32_t c = ordered_code(v[e]);
+        code[e] = live ? (sizeof(ET) == 2 ? (c >> 16) : c) : 0u;
+    }
+}
+
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void line_group_codes(const LinesArgs &a, int64_t row, int line, int h,
                                                  uint32_t *code) {
-    constexpr int P = Logit<ET>::kPer16;
-    const int64_t tok = line_token<ET>(line) + h * P;
-    float v[P];
-    if (tok < a.V) {
-        Logit<ET>::unpack(*reinterpret_cast<const uint4 *>(reinterpret_cast<const ET *>(a.logits) + row * a.V + tok), v);
-        uint32_t bits = 0xffu;
-        if (MASKED) {
-            const uint32_t byte = reinterpret_cast<const uint8_t *>(a.mask + row * a.W)[tok >> 3];
-            bits = (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
-        }
-#pragma unroll
-        for (int e = 0; e < P; ++e) {
-            const bool live = ((bits >> e) & 1u) && v[e] > -INFINITY && v[e] < INFINITY;
-            const uint32_t c = ordered_code(v[e]);
-            code[e] = live ? (sizeof(ET) == 2 ? (c >> 16) : c) : 0u;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < P; ++e) code[e] = 0u;
-    }
+    group_codes<ET>(load_line_group<ET, MASKED>(a, row, line, h), code);
 }
 
 template <typename ET>
@@ -2094,10 +2127,12 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
     if (!(T > 0.0f && T <= FLT_MAX) || K <= 0) return;
     const BlockStat *st = a.bstats + row * a.C;
     bool bad = false;
-    for (int c = tid; c < a.C; c += kLinesThreads) {
-        const BlockStat e = st[c];
-        bad |= (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
+    if (tid < a.C) {  // C <= NB < kLinesThreads: thread c takes block c
+        const BlockStat e = st[tid];
+        bad = (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
     }
+    // block tid's level-1 Gumbel variate, drawn while the loads are in flight
+    const float gum = tid < a.C ? block_gumbel(key_of(a.seed), b, i, tid) : 0.0f;
     uint32_t mx = 0u, nz = 0u;
 #pragma unroll
     for (int j = 0; j < NV4; ++j)
@@ -2201,9 +2236,9 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
     if (ncand <= uint32_t(kCandLines)) {
         // ---- 4. the candidates' tokens into LDS, counted in the window
         uint32_t tn = 0u;
-        for (uint32_t e = tid; e < ncand * 8u; e += kLinesThreads) {
+        auto take = [&](const LineGroup &lg, uint32_t e) {
             uint32_t code[P];
-            line_group_codes<ET, MASKED>(a, row, cand[e >> 3], e & 7u, code);
+            group_codes<ET>(lg, code);
             uint4 ov;
             if constexpr (BF) {
                 ov = make_uint4(code[0] | (code[1 % P] << 16), code[2 % P] | (code[3 % P] << 16),
@@ -2220,6 +2255,16 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
                     if (d < uint32_t(kWin)) atomicAdd(&hist[d], 1u);
                 }
             }
+        };
+        // two groups in flight per thread
+        const uint32_t ng = ncand * 8u;
+        for (uint32_t e = tid; e < ng; e += 2 * kLinesThreads) {
+            const uint32_t e2 = e + kLinesThreads;
+            const LineGroup g1 = load_line_group<ET, MASKED>(a, row, cand[e >> 3], e & 7u);
+            LineGroup g2;
+            if (e2 < ng) g2 = load_line_group<ET, MASKED>(a, row, cand[e2 >> 3], e2 & 7u);
+            take(g1, e);
+            if (e2 < ng) take(g2, e2);
         }
         tn = wave_sum_u(tn);
         if (lane == 0) red[round & 1][wave][0] = tn;
@@ -2265,23 +2310,32 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
             xline = (r.x / kBlock) * LPB + ((o % (kWave * P)) / P / 8) * G + o / (kWave * P);
         }
         __syncthreads();
-        for (uint32_t s = wave; s < ncand; s += NW) {
-            const int line = cand[s];
-            const uint32_t mk = bmax[line / LPB];
-            if (mk == 0u) continue;
-            const float mc = value_of_code<ET>(mk) * r.cT;
-            const uint32_t cd = lane < TPL ? uint32_t(tcodes[s * TPL + lane]) : 0u;
-            float term = 0.0f;
-            if (cd >= tcode) term = __builtin_amdgcn_exp2f(fmaf(value_of_code<ET>(cd), r.cT, -mc));
-            const float ls = wave_sum(term);
-            if (lane == 0) lsum[s] = ls;
-            if (line == xline) {
-                const float lx = wave_sum(line_token<ET>(line) + lane != r.x ? term : 0.0f);
-                if (lane == 0) xmass = lx;
+        // four candidates per wave at a time (independent reductions)
+        for (uint32_t s0 = wave; s0 < ncand; s0 += 4 * NW) {
+            float term[4], ls[4];
+            int line[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t s = s0 + u * NW;
+                line[u] = s < ncand ? int(cand[s]) : -1;
+                const uint32_t mk = line[u] >= 0 ? bmax[line[u] / LPB] : 0u;
+                const float mc = value_of_code<ET>(mk) * r.cT;
+                const uint32_t cd = (mk != 0u && lane < TPL) ? uint32_t(tcodes[s * TPL + lane]) : 0u;
+                term[u] = cd >= tcode ? __builtin_amdgcn_exp2f(fmaf(value_of_code<ET>(cd), r.cT, -mc)) : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ls[u] = wave_sum(term[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (line[u] < 0) continue;
+                if (lane == 0) lsum[s0 + u * NW] = ls[u];
+                if (line[u] == xline) {
+                    const float lx = wave_sum(line_token<ET>(line[u]) + lane != r.x ? term[u] : 0.0f);
+                    if (lane == 0) xmass = lx;
+                }
             }
         }
         __syncthreads();
-        const PhiloxKey key = key_of(a.seed);
         for (int c = tid; c < a.C; c += kLinesThreads) {
             const uint32_t mk = bmax[c];
             const bool has_x = r.x >= 0 && r.x / kBlock == c;
@@ -2297,9 +2351,8 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
                 }
                 out.m = mc;
                 out.s = sum;
-                const float g = block_gumbel(key, r.b, r.i, c);
-                out.key = key_of_mass(sum, mc, g);
-                if (has_x) a.drec[r.row].keyx = key_of_mass(sx, mc, g);
+                out.key = key_of_mass(sum, mc, gum);  // c == tid
+                if (has_x) a.drec[r.row].keyx = key_of_mass(sx, mc, gum);
             } else if (has_x) {
                 a.drec[r.row].keyx = -INFINITY;
             }
@@ -2975,7 +3028,8 @@ __device__ __forceinline__ void tally_call(const FinalArgs &a, int b, unsigned l
     atomicAdd(&out[3], acc);           // A
 }
 
-// Issue the loads of block c of a row for the staging (c < 0: none).
+// Issue the loads of block c of a row for the staging (c < 0: none); with a
+// mask, m[0] receives the lane's word of the block's mask (spread_mask).
 template <typename ET>
 __device__ __forceinline__ void stage_block(const FinalArgs &a, int row, int c, int lane, uint4 *r, uint32_t *m) {
     if (c < 0) return;
@@ -3107,6 +3161,8 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
 
     // ---- the wave that loaded the sampled row's block puts it in LDS
     if (st == 0 && stage_row >= 0 && stage_row == nacc) {
+        uint32_t smm[G];
+        if (a.mask) spread_mask<G, P>(stage_m[0], lane, smm);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float v[P];
@@ -3114,7 +3170,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             const int off = (g * kWave + lane) * P;  // token offset inside the block
             const int64_t tok = int64_t(stage_c) * kBlock + off;
             uint32_t bits = tok < V ? 0xffu : 0u;
-            if (a.mask) bits &= (P == 8) ? stage_m[g] : (stage_m[g] >> (uint32_t(tok) & 4u));
+            if (a.mask) bits &= (P == 8) ? smm[g] : (smm[g] >> (uint32_t(tok) & 4u));
 #pragma unroll
             for (int e = 0; e < P; ++e)
                 if (!((bits >> e) & 1u)) v[e] = -INFINITY;

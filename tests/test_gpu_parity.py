@@ -175,6 +175,38 @@ def test_top_k_threshold_far_from_the_first_tokens():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_top_k_single_pass_edge_rows(dtype):
+    """Rows of a top-k call (aligned rows, threshold found after the sweep)
+    that leave the usual path: an allowed NaN or +inf (reported), a NaN at a
+    masked token (ignored), an empty row, fewer allowed tokens than K (no
+    cut), exactly K, K = 1, and K = 2000 (more candidate lines than LDS
+    holds)."""
+    announce(f"top-k single-pass edge rows dtype={dtype}")
+    B, k, V = 10, 3, 8192
+    wl = _custom(B, k, V, dtype=dtype, dense=True, masked=False, seed=91, top_k=(50,))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(92)
+    allowed = torch.rand((B, k + 1, V), generator=g, device=DEV) < 0.3
+    for b, n in ((4, 20), (5, 50), (8, 1)):          # rows with exactly n allowed tokens
+        allowed[b] = False
+        for i in range(k + 1):
+            allowed[b, i, torch.randperm(V, generator=g, device=DEV)[:n]] = True
+    allowed[0, 1, 100] = True
+    allowed[1, 2, 5000] = True
+    allowed[2, 0, 300] = False
+    allowed[3, 1] = False                             # empty row
+    wl["bitmask"] = pack_bitmask(allowed)
+    wl["logits"][0, 1, 100] = float("nan")
+    wl["logits"][1, 2, 5000] = float("inf")
+    wl["logits"][2, 0, 300] = float("nan")
+    wl["top_k"] = torch.tensor([50, 50, 50, 50, 50, 50, 1, 2000, 50, 7], dtype=torch.int32, device=DEV)
+    wl["temperature"][9] = 0.0                        # greedy beside them
+    gpu, orc = run_gpu(wl), run_oracle(wl)
+    assert list(orc["request_status"]) == [8, 8, 0, 4, 0, 0, 0, 0, 0, 0]
+    assert_parity(gpu, orc)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("V", [7, 1001, 2049, 6150, 20000])
 def test_top_p_sizes(V, dtype):
     announce(f"top-p custom V={V} dtype={dtype}")
