@@ -59,10 +59,8 @@ typedef struct {
                                    of out_draft_offsets (needs out_draft_offsets); slots
                                    past offsets[B] are left as they were */
     uint32_t *status;           /* device [1]: SD_NGRAM_STATUS_* bits of the call */
-    /* optional hipEvent_t handles (NULL = none) recorded on `stream` right
-     * before and right after the match kernel, to time it alone */
-    void *match_event_begin;
-    void *match_event_end;
+    /* debug only, NULL in production: timing hooks (sd_debug_timing, sd_verify.h) */
+    const sd_debug_timing *debug_timing;
 } sd_ngram_params;
 
 /* Device workspace bytes sd_ngram_propose needs for these sizes (0 when the

@@ -75,6 +75,16 @@ typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
 #define SD_STATUS_BAD_OFFSETS 32u   /* ragged call whose draft offsets are inconsistent:
                                        set on every request (see draft_offsets) */
 
+/* Debug-only timing hooks, not part of the verification contract (callers
+ * that only verify leave the pointer to them NULL): hipEvent_t handles that a
+ * call records on its stream immediately before and after its main kernel
+ * (the sweep for sd_verify, the match kernel for sd_ngram_propose), so that a
+ * benchmark can time that kernel alone.  A NULL handle is skipped. */
+typedef struct {
+    void *kernel_begin;
+    void *kernel_end;
+} sd_debug_timing;
+
 typedef struct {
     int32_t batch;      /* B, 0 <= B <= SD_MAX_BATCH requests */
     int32_t num_draft;  /* k, 0 <= k <= SD_MAX_DRAFT, the same for every request */
@@ -104,10 +114,8 @@ typedef struct {
     /* device [1] or NULL: OR of the SD_STATUS_* bits of all requests
      * (overwritten by every call). */
     uint32_t *status;
-    /* Optional hipEvent_t handles recorded on `stream` immediately before and
-     * after the row-statistics kernel (NULL = none); for timing only. */
-    void *row_stats_event_begin;
-    void *row_stats_event_end;
+    /* Debug only, NULL in production: timing hooks (sd_debug_timing). */
+    const sd_debug_timing *debug_timing;
     /* Ragged draft lengths (infra-guide 5.2, drafters that propose a variable
      * number of tokens), or NULL for k drafts per request.  device [B + 1]
      * int32 cumulative offsets: request b verifies k_b = off[b+1] - off[b]

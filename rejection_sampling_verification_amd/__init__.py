@@ -47,6 +47,12 @@ EXPORTED_SYMBOLS = ("sd_verify", "sd_verify_workspace_size", "sd_status_string",
 SD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
+class SdDebugTiming(ctypes.Structure):
+    """Debug-only timing hooks: hipEvent_t handles recorded around a call's
+    main kernel (benchmarks only)."""
+    _fields_ = [("kernel_begin", ctypes.c_void_p), ("kernel_end", ctypes.c_void_p)]
+
+
 class SdParams(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -59,8 +65,7 @@ class SdParams(ctypes.Structure):
         ("dbg_request_flags", ctypes.c_void_p),
         ("dbg_flags", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
-        ("row_stats_event_begin", ctypes.c_void_p),
-        ("row_stats_event_end", ctypes.c_void_p),
+        ("debug_timing", ctypes.POINTER(SdDebugTiming)),
         ("draft_offsets", ctypes.c_void_p),
         ("total_drafts", ctypes.c_int64),
         ("accept_histogram", ctypes.c_void_p),
@@ -80,8 +85,7 @@ class SdNgramParams(ctypes.Structure):
         ("out_draft_offsets", ctypes.c_void_p),
         ("out_drafts_flat", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
-        ("match_event_begin", ctypes.c_void_p),
-        ("match_event_end", ctypes.c_void_p),
+        ("debug_timing", ctypes.POINTER(SdDebugTiming)),
     ]
 
 
@@ -316,9 +320,10 @@ class Verifier:
         _check(top_p, "top_p", torch.float32, (B,), dev)
         self.params.top_p = None if top_p is None else top_p.data_ptr()
         if row_stats_events is not None:
-            self.params.row_stats_event_begin, self.params.row_stats_event_end = row_stats_events
+            self._timing = SdDebugTiming(*row_stats_events)
+            self.params.debug_timing = ctypes.pointer(self._timing)
         else:
-            self.params.row_stats_event_begin = self.params.row_stats_event_end = None
+            self.params.debug_timing = None
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         ptrs = (_ptr(target_logits), _ptr(draft_token_ids), _ptr(draft_probs), _ptr(bitmask),
@@ -437,9 +442,10 @@ class NgramProposer:
         _check(tokens, "tokens", torch.int32, (self.B, self.stride), dev)
         _check(lengths, "lengths", torch.int32, (self.B,), dev)
         if match_events is not None:
-            self.params.match_event_begin, self.params.match_event_end = match_events
+            self._timing = SdDebugTiming(*match_events)
+            self.params.debug_timing = ctypes.pointer(self._timing)
         else:
-            self.params.match_event_begin = self.params.match_event_end = None
+            self.params.debug_timing = None
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         rc = _lib.sd_ngram_propose(

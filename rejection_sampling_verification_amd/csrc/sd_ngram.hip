@@ -249,14 +249,14 @@ extern "C" int sd_ngram_propose(const int32_t *tokens, const int32_t *lengths, i
         m.min_n = p->min_n;
         m.max_n = p->max_n;
         m.k = p->num_draft;
-        if (p->match_event_begin &&
-            hipEventRecord(static_cast<hipEvent_t>(p->match_event_begin), stream) != hipSuccess)
+        const sd_debug_timing *dt = p->debug_timing;
+        if (dt && dt->kernel_begin &&
+            hipEventRecord(static_cast<hipEvent_t>(dt->kernel_begin), stream) != hipSuccess)
             return SD_ERR_HIP;
         hipLaunchKernelGGL(ngram_match_kernel, dim3(unsigned(B) * unsigned(nchunk)), dim3(kMatchThreads), 0,
                            stream, m);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
-        if (p->match_event_end &&
-            hipEventRecord(static_cast<hipEvent_t>(p->match_event_end), stream) != hipSuccess)
+        if (dt && dt->kernel_end && hipEventRecord(static_cast<hipEvent_t>(dt->kernel_end), stream) != hipSuccess)
             return SD_ERR_HIP;
     }
     if (B == 0 && !p->out_draft_offsets && !p->status) return SD_OK;

@@ -1,29 +1,46 @@
 // MI355X (gfx950) speculative-decoding verifier: kernels and C ABI.
 //
-// Two kernels per call, both on the caller's stream:
+// One call runs these kernels in order on the caller's stream (those in
+// brackets only when the call needs them):
 //
-//   row_stats  One wave64 per (row, chunk of blocks).  It streams the row's
-//              logits from HBM in 16-byte loads, applies the grammar bitmask,
-//              and for every block of 2048 tokens writes 8 bytes:
-//                sampling rows: (Mc, Sc) with Mc = fp32(max_j l_j * c),
-//                  Sc = sum_j 2^(l_j * c - Mc), c = log2(e) / T
-//                greedy rows:   (max_j l_j, lowest index of that max)
-//              This is the only pass over the full logits and moves > 99% of
-//              the bytes (pyshine "vLLM, part 2", "Verification": logits in
-//              fp32, temperature applied before normalising; "Grammar gates":
-//              one mask row per request and position).
-//   finalize   One 256-thread workgroup per request.  It folds the block
-//              statistics into each row's max and normaliser, gathers p(x)
-//              and q(x) at the drafts, draws the accept uniforms from Philox,
-//              scans for the first rejection (vllm-learning code walkthrough,
-//              RejectionSampler), then samples the emitted token from the
-//              residual max(p - q, 0), from p with the draft removed (one-hot
-//              drafts, infra-guide 5.2 section 4.3) or from p at the bonus
-//              position, by two-level Gumbel-max: level 1 over block masses,
-//              level 2 over the winning block's 2048 tokens (re-read, 4 KB).
-//              It writes the outputs and a per-request record; the last
-//              workgroup to finish sums the records into R, I, D, A (fanout,
-//              "Name the three counters").
+//   [ragged_prep]  ragged calls: checks the draft offsets and maps every
+//                  packed row to its request.
+//   [topk]         calls with top-p, and top-k calls whose rows the
+//                  single-pass selection cannot take (unaligned rows, very
+//                  large V): each top-k / top-p row's threshold tau, from a
+//                  pass over the row before the sweep.
+//   row_stats      the sweep, the only full pass over the logits: waves claim
+//                  2048-token blocks of all rows, stream them from HBM in
+//                  16-byte loads, apply the grammar bitmask and temperature
+//                  (pyshine "vLLM, part 2", "Verification": logits in fp32,
+//                  temperature before normalising; "Grammar gates": one mask
+//                  row per request and position), and write per block
+//                    sampling rows: (Mc, Sc) with Mc = fp32(max_j l_j * c),
+//                      Sc = sum_j 2^(l_j * c - Mc), c = log2(e) / T, and the
+//                      block's level-1 Gumbel key;
+//                    greedy rows:   (max_j l_j, lowest index of that max);
+//                    sampling rows of a single-pass top-k call: the code of
+//                      every 128-byte line's largest allowed logit instead;
+//                  plus each draft row's record: l(x), the mask bit, q(x) and
+//                  the draft block's mass without the draft.
+//   [topk_lines]   single-pass top-k: each row's tau from the line maxima and
+//                  the few lines that can hold kept tokens, then the row's
+//                  block statistics over the kept tokens.
+//   finalize       one 512-thread workgroup per request: folds the block
+//                  statistics into each row's max and normaliser, forms p(x)
+//                  and q(x), draws the accept uniforms from Philox, finds the
+//                  first rejection (vllm-learning code walkthrough,
+//                  RejectionSampler), then samples the emitted token from the
+//                  residual max(p - q, 0), from p without the draft (one-hot
+//                  drafts, infra-guide 5.2 section 4.3) or from p at the bonus
+//                  position by two-level Gumbel-max: level 1 over block
+//                  masses, level 2 over the chosen block's 2048 tokens.  It
+//                  writes the outputs and adds R, I, D, A (fanout, "Name the
+//                  three counters") through a slot tally.
+//   [dense_mass,   dense drafts over long rows: the residual's block masses
+//    dense_draw]   of every rejected row on a grid of (block, request)
+//                  workgroups, then its draw.
+//   [histogram]    requests per accepted length, when asked for.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <limits.h>
@@ -3851,13 +3868,12 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         hipLaunchKernelGGL(k0, dim3(static_cast<unsigned>(L.rows)), dim3(kTopkThreads), 0, stream, ta);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }
-    if (p->row_stats_event_begin &&
-        hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_begin), stream) != hipSuccess)
+    const sd_debug_timing *dt = p->debug_timing;
+    if (dt && dt->kernel_begin && hipEventRecord(static_cast<hipEvent_t>(dt->kernel_begin), stream) != hipSuccess)
         return SD_ERR_HIP;
     hipLaunchKernelGGL(k1, dim3(static_cast<unsigned>(grid1)), dim3(k1_threads), 0, stream, ra);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
-    if (p->row_stats_event_end &&
-        hipEventRecord(static_cast<hipEvent_t>(p->row_stats_event_end), stream) != hipSuccess)
+    if (dt && dt->kernel_end && hipEventRecord(static_cast<hipEvent_t>(dt->kernel_end), stream) != hipSuccess)
         return SD_ERR_HIP;
     if (single_pass) {
         LinesArgs la;

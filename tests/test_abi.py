@@ -37,13 +37,16 @@ def test_library_exports_every_declared_symbol():
 
 def test_params_struct_layout_matches_header():
     import rejection_sampling_verification_amd as sdv
-    # 3 x int32 + enum, then 8 pointers, offsets, total_drafts, histogram, top_p
-    assert ctypes.sizeof(sdv.SdParams) == 16 + 12 * 8
-    assert sdv.SdParams.top_p.offset == 16 + 11 * 8
+    # 3 x int32 + enum, then 7 pointers (the last the debug-only timing
+    # hooks), offsets, total_drafts, histogram, top_p
+    assert ctypes.sizeof(sdv.SdParams) == 16 + 11 * 8
+    assert sdv.SdParams.top_p.offset == 16 + 10 * 8
     assert sdv.SdParams.top_k.offset == 16
-    assert sdv.SdParams.draft_offsets.offset == 16 + 8 * 8
-    assert sdv.SdParams.total_drafts.offset == 16 + 9 * 8
-    assert sdv.SdParams.accept_histogram.offset == 16 + 10 * 8
+    assert sdv.SdParams.debug_timing.offset == 16 + 6 * 8
+    assert sdv.SdParams.draft_offsets.offset == 16 + 7 * 8
+    assert sdv.SdParams.total_drafts.offset == 16 + 8 * 8
+    assert sdv.SdParams.accept_histogram.offset == 16 + 9 * 8
+    assert ctypes.sizeof(sdv.SdDebugTiming) == 16
 
 
 def test_status_strings():
@@ -161,8 +164,9 @@ def test_ragged_host_checks_and_workspace():
 
 def test_ngram_params_layout_and_host_checks():
     import rejection_sampling_verification_amd as sdv
-    # 4 x int32, stride and max_model_len, then 4 output pointers and 2 events
-    assert ctypes.sizeof(sdv.SdNgramParams) == 16 + 2 * 8 + 6 * 8
+    # 4 x int32, stride and max_model_len, then 4 output pointers and the
+    # debug-only timing hooks
+    assert ctypes.sizeof(sdv.SdNgramParams) == 16 + 2 * 8 + 5 * 8
     assert sdv.SdNgramParams.stride.offset == 16
     assert sdv.SdNgramParams.out_match_len.offset == 32
     assert sdv.SdNgramParams.status.offset == 56
