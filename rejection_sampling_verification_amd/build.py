@@ -5,7 +5,8 @@
 compiles csrc/sd_verify.hip (the verifier) and csrc/sd_ngram.hip (the n-gram
 proposer) into libsdverify.so next to this file, then the test suite's
 C-ABI caller tests/c_abi_check (plain C++ against include/sd_verify.h and the
-library, no Python).
+library, no Python) and tests/gumbel_probe (the device Gumbel variates for
+every possible uniform).
 """
 import os
 import shutil
@@ -18,6 +19,8 @@ SOURCES = [os.path.join(PKG_DIR, "csrc", name) for name in ("sd_verify.hip", "sd
 LIBRARY = os.path.join(PKG_DIR, "libsdverify.so")
 C_CHECK_SOURCE = os.path.join(ROOT, "tests", "c_abi_check.cpp")
 C_CHECK = os.path.join(ROOT, "tests", "c_abi_check")
+GUMBEL_PROBE_SOURCE = os.path.join(ROOT, "tests", "gumbel_probe.hip")
+GUMBEL_PROBE = os.path.join(ROOT, "tests", "gumbel_probe")
 ARCH = "gfx950"
 
 
@@ -63,6 +66,16 @@ def build_library(verbose=False):
         os.replace(C_CHECK + ".tmp", C_CHECK)
         if verbose:
             print("built", C_CHECK)
+    if os.path.exists(GUMBEL_PROBE_SOURCE):
+        cmd = [hipcc_path(), "-O3", f"--offload-arch={ARCH}", "-std=c++17",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               GUMBEL_PROBE_SOURCE, "-o", GUMBEL_PROBE + ".tmp"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+        os.replace(GUMBEL_PROBE + ".tmp", GUMBEL_PROBE)
+        if verbose:
+            print("built", GUMBEL_PROBE)
     return LIBRARY
 
 

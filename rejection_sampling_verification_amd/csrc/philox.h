@@ -61,18 +61,48 @@ __device__ __forceinline__ float gumbel_of(uint32_t w) {
     return -kLn2f * __builtin_amdgcn_logf(kLn2f * -__builtin_amdgcn_logf(u));
 }
 
+// The same variate as a double, within 1.6e-7 of exact over all 2^23
+// possible u on gfx950 (the fp32 form above loses up to 1.6e-6 where u is near
+// 1, which is where the largest variates, the ones that win races, come
+// from).  L = -ln u in fp32 to a few units of its last place: for u > 3/4
+// from 1 - u = d (exact) as the series -ln(1 - d) = sum d^k / k to k = 13
+// (truncation below 5e-9 relative); else from the exponent of u plus the
+// hardware log2 of its mantissa.  Then G = -ln L = -ln 2 (e + log2 m) for
+// L = m 2^e, with the sum formed in fp64, so that no log2 result larger than
+// 1 in magnitude is rounded to fp32.
+__device__ __forceinline__ double gumbel_wide(uint32_t w) {
+    constexpr double kLn2d = 0.693147180559945309417;
+    const uint32_t m = (w >> 9) * 2u + 1u;  // u = m 2^-24
+    const uint32_t dm = (1u << 24) - m;      // 1 - u = dm 2^-24
+    float L;
+    if (dm < (1u << 22)) {
+        const float d = static_cast<float>(dm) * 0x1p-24f;
+        float s = 1.0f / 13.0f;
+#pragma unroll
+        for (int k = 12; k >= 1; --k) s = fmaf(s, d, 1.0f / static_cast<float>(k));
+        L = d * s;
+    } else {
+        const float u = static_cast<float>(m) * 0x1p-24f;
+        L = -kLn2f * (static_cast<float>(__builtin_amdgcn_frexp_expf(u)) +
+                      __builtin_amdgcn_logf(__builtin_amdgcn_frexp_mantf(u)));
+    }
+    return -kLn2d * (static_cast<double>(__builtin_amdgcn_frexp_expf(L)) +
+                     static_cast<double>(__builtin_amdgcn_logf(__builtin_amdgcn_frexp_mantf(L))));
+}
+
 __device__ __forceinline__ double draw_accept(PhiloxKey key, uint32_t b, uint32_t i) {
     return uniform_accept(philox4x32_10(make_uint4(0u, i, b, 0u), key.k0, key.k1).x);
 }
 
-// Level-1 Gumbel variates of blocks 4 g4 .. 4 g4 + 3 of row a of request b.
+// Level-1 Gumbel variates (fp64) of blocks 4 g4 .. 4 g4 + 3 of row a of
+// request b.
 __device__ __forceinline__ void draw_block_gumbels4(PhiloxKey key, uint32_t b, uint32_t a,
-                                                    uint32_t g4, float g[4]) {
+                                                    uint32_t g4, double g[4]) {
     const uint4 w = philox4x32_10(make_uint4(g4, a, b, 1u), key.k0, key.k1);
-    g[0] = gumbel_of(w.x);
-    g[1] = gumbel_of(w.y);
-    g[2] = gumbel_of(w.z);
-    g[3] = gumbel_of(w.w);
+    g[0] = gumbel_wide(w.x);
+    g[1] = gumbel_wide(w.y);
+    g[2] = gumbel_wide(w.z);
+    g[3] = gumbel_wide(w.w);
 }
 
 // Level-2 Gumbel variates of tokens j0 .. j0 + 3 (j0 a multiple of 4).

@@ -365,10 +365,18 @@ __device__ __forceinline__ float2 softmax_block(const float *v, float c) {
     m = wave_max_coded(m);  // a NaN logit makes the sum NaN either way
     if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
     const float mc = m * c;
-    float s = __builtin_amdgcn_exp2f(fmaf(v[0], c, -mc));
+    // four running sums of 8 terms each, combined pairwise: with the wave's
+    // tree the fp32 sum of these positive terms is 15 additions deep, within
+    // 15 units of 2^-24 of exact (relative)
+    static_assert(NV == 32, "32 values per lane");
+    float r[4];
 #pragma unroll
-    for (int e = 1; e < NV; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mc));
-    return make_float2(mc, wave_sum(s));
+    for (int q = 0; q < 4; ++q) {
+        r[q] = __builtin_amdgcn_exp2f(fmaf(v[8 * q], c, -mc));
+#pragma unroll
+        for (int e = 1; e < 8; ++e) r[q] += __builtin_amdgcn_exp2f(fmaf(v[8 * q + e], c, -mc));
+    }
+    return make_float2(mc, wave_sum((r[0] + r[1]) + (r[2] + r[3])));
 }
 
 // The same sum without the token at offset xrel of the block (the one-hot
@@ -377,12 +385,15 @@ template <int G, int P>
 __device__ __forceinline__ float excluded_sum(const float *v, float c, float mc, int xrel, int lane) {
     float s = 0.0f;
     if (mc > -INFINITY) {
+        static_assert(G * P == 32, "32 values per lane");
+        float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // as in softmax_block
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < P; ++e)
                 if ((g * kWave + lane) * P + e != xrel)
-                    s += __builtin_amdgcn_exp2f(fmaf(v[g * P + e], c, -mc));
+                    r[(g * P + e) / 8] += __builtin_amdgcn_exp2f(fmaf(v[g * P + e], c, -mc));
+        s = (r[0] + r[1]) + (r[2] + r[3]);
     }
     return wave_sum(s);
 }
@@ -421,19 +432,19 @@ __device__ __forceinline__ void apply_tau(float *v, float tau) {
         if (v[e] < tau) v[e] = -INFINITY;
 }
 
-// The level-1 Gumbel variate of block blk of row i of request b.
-__device__ __forceinline__ float block_gumbel(PhiloxKey key, int b, int i, int blk) {
+// The level-1 Gumbel variate (fp64) of block blk of row i of request b.
+__device__ __forceinline__ double block_gumbel(PhiloxKey key, int b, int i, int blk) {
     const uint4 w = philox4x32_10(make_uint4(uint32_t(blk) >> 2, uint32_t(i), uint32_t(b), 1u),
                                   key.k0, key.k1);
     const int q = blk & 3;
-    return gumbel_of(q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w)));
+    return gumbel_wide(q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w)));
 }
 
-// ln(mass) + Mc ln 2 + G: a level-1 key up to the row's constant (-inf when
-// the mass is zero).
-__device__ __forceinline__ double key_of_mass(float mass, float mc, float g) {
+// ln(mass) + Mc ln 2 + G (ln in fp32, within an ulp; the sum in fp64): a
+// level-1 key up to the row's constant (-inf when the mass is zero).
+__device__ __forceinline__ double key_of_mass(float mass, float mc, double g) {
     if (!(mass > 0.0f) || !(mc > -INFINITY)) return -INFINITY;
-    return static_cast<double>(logf(mass)) + static_cast<double>(mc) * kLn2 + static_cast<double>(g);
+    return static_cast<double>(logf(mass)) + static_cast<double>(mc) * kLn2 + g;
 }
 
 __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
@@ -753,7 +764,7 @@ __device__ __forceinline__ void flush_stash(const RowStatsArgs &a, const Stash &
     out.s = st.s;
     out.key = -INFINITY;
     if (st.kind >= 2 && st.m > -INFINITY) {
-        const float g = block_gumbel(key, st.b, st.i, st.blk);
+        const double g = block_gumbel(key, st.b, st.i, st.blk);
         out.key = key_of_mass(st.s, st.m, g);
         if (st.kind == 3) a.drec[st.row].keyx = key_of_mass(st.sx, st.m, g);
     } else if (st.kind == 3) {
@@ -1064,7 +1075,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_elem_kernel(RowStatsArgs a
             const float2 r = softmax_block<G * P>(v, t.c);
             out.m = r.x;
             out.s = r.y;
-            const float g = block_gumbel(key, t.b, t.i, blk);
+            const double g = block_gumbel(key, t.b, t.i, blk);
             out.key = key_of_mass(r.y, r.x, g);
             if (blk == t.xblk) {
                 sx = excluded_sum<G, P>(v, t.c, r.x, t.xrel, lane);
@@ -2077,7 +2088,7 @@ __device__ __forceinline__ void block_stats_global(const LinesArgs &a, const Lin
             out.m = mc;
             out.s = sum;
             if (lane == 0) {
-                const float g = block_gumbel(key, r.b, r.i, c);
+                const double g = block_gumbel(key, r.b, r.i, c);
                 out.key = key_of_mass(sum, mc, g);
                 if (has_x) a.drec[r.row].keyx = key_of_mass(sx, mc, g);
             }
@@ -2149,7 +2160,7 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
         bad = (e.m != e.m) | (e.s != e.s) | (e.m == INFINITY);
     }
     // block tid's level-1 Gumbel variate, drawn while the loads are in flight
-    const float gum = tid < a.C ? block_gumbel(key_of(a.seed), b, i, tid) : 0.0f;
+    const double gum = tid < a.C ? block_gumbel(key_of(a.seed), b, i, tid) : 0.0;
     uint32_t mx = 0u, nz = 0u;
 #pragma unroll
     for (int j = 0; j < NV4; ++j)
@@ -3257,13 +3268,13 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 const int g4 = tid;  // one group of four blocks per thread
                 uint64_t best = 0;
                 if (g4 < ngroups) {
-                    float gum[4];
+                    double gum[4];
                     draw_block_gumbels4(key, b, n, g4, gum);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int cb = 4 * g4 + q;
                         if (cb < C && sW[cb] > 0.0) {
-                            kq[q] = static_cast<float>(log(sW[cb]) + static_cast<double>(gum[q]));
+                            kq[q] = static_cast<float>(log(sW[cb]) + gum[q]);
                             best = max_u64(best, pack_key(kq[q], cb));
                         }
                     }
@@ -3429,13 +3440,13 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
     const int g4 = tid;  // one group of four blocks per thread
     uint64_t best = 0;
     if (g4 < ngroups) {
-        float gum[4];
+        double gum[4];
         draw_block_gumbels4(key, b, n, g4, gum);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cb = 4 * g4 + q;
             if (cb < C && W[cb] > 0.0) {
-                kq[q] = static_cast<float>(log(W[cb]) + static_cast<double>(gum[q]));
+                kq[q] = static_cast<float>(log(W[cb]) + gum[q]);
                 best = max_u64(best, pack_key(kq[q], cb));
             }
         }
