@@ -440,11 +440,21 @@ __device__ __forceinline__ double block_gumbel(PhiloxKey key, int b, int i, int 
     return gumbel_wide(q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w)));
 }
 
-// ln(mass) + Mc ln 2 + G (ln in fp32, within an ulp; the sum in fp64): a
-// level-1 key up to the row's constant (-inf when the mass is zero).
+// ln x of a positive fp32 value as (e + log2 m) ln 2 for x = m 2^e: the
+// exponent exact and the hardware log2 of the mantissa (|log2 m| <= 1), the
+// sum in fp64, so that the result is within about 5e-8 of ln x whatever its
+// size.  -inf for x <= 0.
+__device__ __forceinline__ double ln_f32(float x) {
+    if (!(x > 0.0f)) return -INFINITY;
+    return (static_cast<double>(__builtin_amdgcn_frexp_expf(x)) +
+            static_cast<double>(__builtin_amdgcn_logf(__builtin_amdgcn_frexp_mantf(x)))) * kLn2;
+}
+
+// ln(mass) + Mc ln 2 + G in fp64: a level-1 key up to the row's constant
+// (-inf when the mass is zero).
 __device__ __forceinline__ double key_of_mass(float mass, float mc, double g) {
     if (!(mass > 0.0f) || !(mc > -INFINITY)) return -INFINITY;
-    return static_cast<double>(logf(mass)) + static_cast<double>(mc) * kLn2 + g;
+    return ln_f32(mass) + static_cast<double>(mc) * kLn2 + g;
 }
 
 __device__ __forceinline__ void zero_call_outputs(const RowStatsArgs &a) {
@@ -2481,6 +2491,37 @@ __device__ __forceinline__ bool near_tie(float key, int idx, uint64_t best) {
     return idx != packed_index(best) && key >= packed_key(best) - kTieEps;
 }
 
+// The level-1 winner in fp64.  The race runs on keys rounded to fp32
+// (relative keys below 32 in magnitude round to within 2^-20), so its winner
+// w is the fp64 winner unless another key lies within the two roundings of
+// w's.  Lanes count their keys within kRaceSlack of w's fp32 key; when any
+// key but w's is that close (rare), the race is run again on the fp64 keys
+// kd (lowest block on ties), lane + 64 j for entry j, -inf where absent.
+constexpr float kRaceSlack = 0x1p-18f;
+
+template <int NJ>
+__device__ __forceinline__ uint64_t race_in_fp64(uint64_t w, const double (&kd)[NJ]) {
+    if (w == 0) return w;
+    const int lane = threadIdx.x & (kWave - 1);
+    const float wk = packed_key(w);
+    int close = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        close += (kd[j] > -INFINITY && static_cast<float>(kd[j]) >= wk - kRaceSlack) ? 1 : 0;
+    if (!wave_any(close > 1) && __popcll(__ballot(close > 0)) <= 1) return w;
+    double best = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        if (kd[j] > best) {  // j ascending: the lane's lowest block among equal keys
+            best = kd[j];
+            bi = lane + kWave * j;
+        }
+    const double m = wave_max_d(best);
+    const int i = wave_min_i((m > -INFINITY && best == m) ? bi : INT_MAX);
+    return pack_code(ordered_code(static_cast<float>(m)), i);
+}
+
 // Residual masses W_c = sum_j max(p_j - q_j, 0) of one row for dense q, with
 // p_j = 2^(l_j c - M) / S in fp32.  One wave per block, two blocks of a wave
 // in flight together; clamped loads.
@@ -2641,13 +2682,7 @@ __device__ __forceinline__ int2 race_winner(const uint32_t (&code)[4], int base,
     return make_int2(bi, tie ? 1 : 0);
 }
 
-__device__ __forceinline__ double ln_of(double x) {
-    const float xf = static_cast<float>(x);
-    if (!(xf > 0.0f)) return -INFINITY;
-    const int e = __builtin_amdgcn_frexp_expf(xf);
-    const float m = __builtin_amdgcn_frexp_mantf(xf);
-    return (static_cast<double>(e) + static_cast<double>(__builtin_amdgcn_logf(m))) * kLn2;
-}
+__device__ __forceinline__ double ln_of(double x) { return ln_f32(static_cast<float>(x)); }
 
 // Level 2: the token of block cb of row n drawn under the weights of `mode`
 // (4 tokens per thread; values from the staged LDS copy when `staged`).  All
@@ -2823,8 +2858,36 @@ __device__ __forceinline__ void fold_sampling_row(const BlockStat *st, const Fol
         }
     }
     s = wave_sum_d(s);
-    const uint64_t bp = wave_argmax_code(cp, ip);
-    const uint64_t bx = wave_argmax_code(cxm, ix);
+    uint64_t bp = wave_argmax_code(cp, ip);
+    uint64_t bx = wave_argmax_code(cxm, ix);
+    // the winners in fp64 (race_in_fp64 for rows of any length)
+    for (int r = 0; r < 2; ++r) {
+        uint64_t &w = r == 0 ? bp : bx;
+        if (w == 0) continue;
+        const float wk = packed_key(w);
+        int close = 0;
+        for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
+            const BlockStat e = fold_entry(st, fc, j, cb);
+            if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
+            const double kd = (r == 1 && cb == cx) ? keyx - ref : e.key - ref;
+            close += (kd > -INFINITY && static_cast<float>(kd) >= wk - kRaceSlack) ? 1 : 0;
+        }
+        if (!wave_any(close > 1) && __popcll(__ballot(close > 0)) <= 1) continue;
+        double best = -INFINITY;
+        int bi = INT_MAX;
+        for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
+            const BlockStat e = fold_entry(st, fc, j, cb);
+            if (!(e.m > -INFINITY) || !(e.s > 0.0f)) continue;
+            const double kd = (r == 1 && cb == cx) ? keyx - ref : e.key - ref;
+            if (kd > best) {
+                best = kd;
+                bi = cb;
+            }
+        }
+        const double m2 = wave_max_d(best);
+        const int i2 = wave_min_i((m2 > -INFINITY && best == m2) ? bi : INT_MAX);
+        w = pack_code(ordered_code(static_cast<float>(m2)), i2);
+    }
     bool tp = false, tx = false;
     if (bp != 0) {
         for (int j = 0, cb = lane; cb < C; ++j, cb += kWave) {
@@ -2905,6 +2968,15 @@ __device__ __forceinline__ CachedFold fold_races(FoldCache &fc, int C, int cx, d
     }
     f.bp = wave_argmax_code(cp, ip);
     f.bx = wave_argmax_code(cxm, ix);
+    double kd[kFoldCache], kdx[kFoldCache];
+#pragma unroll
+    for (int j = 0; j < kFoldCache; ++j) {
+        const int cb = lane + kWave * j;
+        kd[j] = f.live[j] ? fc.e[j].key - f.ref : -INFINITY;
+        kdx[j] = cb != cx ? kd[j] : (f.live[j] && keyx > -INFINITY ? keyx - f.ref : -INFINITY);
+    }
+    f.bp = race_in_fp64(f.bp, kd);
+    f.bx = race_in_fp64(f.bx, kdx);
     return f;
 }
 

@@ -113,6 +113,17 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
     return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
 }
 
+__device__ __forceinline__ double wave_max_d(double v) {
+    const double id = -INFINITY;
+    v = fmax(v, dpp_d<0x111, 0xf>(id, v));
+    v = fmax(v, dpp_d<0x112, 0xf>(id, v));
+    v = fmax(v, dpp_d<0x114, 0xf>(id, v));
+    v = fmax(v, dpp_d<0x118, 0xf>(id, v));
+    v = fmax(v, dpp_d<0x142, 0xa>(id, v));
+    v = fmax(v, dpp_d<0x143, 0xc>(id, v));
+    return readlane_d(v, 63);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
     v += dpp_d<0x111, 0xf>(0.0, v);
     v += dpp_d<0x112, 0xf>(0.0, v);
