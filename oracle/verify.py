@@ -51,6 +51,12 @@ from . import philox
 BLOCK = 2048            # tokens per level-1 block of the two-level Gumbel-max
 ACCEPT_FLAG_EPS = 1e-6  # |u - a| below this marks a boundary accept draw
 GUMBEL_FLAG_EPS = 1e-5  # top-2 Gumbel keys closer than this mark a near tie
+# Dense residuals: the kernels sum max(p - q, 0) over a block from fp32 p, whose
+# relative error (a few units of 2^-24) becomes a relative error of about
+# DENSE_W_REL_ERR * P_c / W_c in the block's residual mass W_c, where P_c is the
+# p-mass of the block's tokens with p > q.  Level-1 near ties of a dense
+# residual widen the band by that much for each of the two blocks.
+DENSE_W_REL_ERR = 6e-7
 TOP_P_FLAG_EPS = 1e-9   # a cumulative mass within this of top_p marks a boundary row
 
 # status bits (a request with any bit set produces -1 outputs)
@@ -146,12 +152,38 @@ def residual_weights(p_row, q_row, x, one_hot):
     return np.maximum(p_row - q_row, 0.0)
 
 
-def _near_tie(keys):
-    fin = np.sort(keys[np.isfinite(keys)])
-    return int(fin.size >= 2 and fin[-1] - fin[-2] < GUMBEL_FLAG_EPS)
+def _near_tie(keys, slack=None):
+    """1 when the two largest finite keys are closer than the band:
+    GUMBEL_FLAG_EPS, plus slack[i] + slack[j] for those two keys' entries
+    when a per-entry slack is given."""
+    idx = np.nonzero(np.isfinite(keys))[0]
+    if idx.size < 2:
+        return 0
+    order = idx[np.argsort(keys[idx], kind="stable")]
+    top1, top2 = order[-1], order[-2]
+    band = GUMBEL_FLAG_EPS + (0.0 if slack is None else slack[top1] + slack[top2])
+    return int(keys[top1] - keys[top2] < band)
 
 
-def gumbel_two_level(r, seed, b, a, block=BLOCK):
+def dense_level1_slack(r, p, block=BLOCK):
+    """Per block c of a dense residual r = max(p - q, 0): DENSE_W_REL_ERR *
+    P_c / W_c, with W_c the residual mass of the block and P_c the p-mass of
+    its tokens with r > 0 (0 for blocks without residual mass)."""
+    V = r.shape[0]
+    C = -(-V // block)
+    W = np.zeros(C * block)
+    W[:V] = r
+    P = np.zeros(C * block)
+    P[:V] = np.where(r > 0, p, 0.0)
+    W = W.reshape(C, block).sum(axis=1)
+    P = P.reshape(C, block).sum(axis=1)
+    out = np.zeros(C)
+    live = W > 0
+    out[live] = DENSE_W_REL_ERR * P[live] / W[live]
+    return out
+
+
+def gumbel_two_level(r, seed, b, a, block=BLOCK, p=None):
     """Draw a token with probability r_j / sum(r) by two-level Gumbel-max.
 
     Level 1 picks block c (tokens [c*block, (c+1)*block)) with key
@@ -160,6 +192,8 @@ def gumbel_two_level(r, seed, b, a, block=BLOCK):
     ln r_j + G(U_tok(b, a, j)) over r_j > 0.  The maximum of Gumbel-perturbed
     log-weights over a block is Gumbel-distributed around ln W_c, so the
     composition is exact; block = len(r) gives the flat Gumbel-max.
+    p: the target row when r is a dense residual max(p - q, 0) (the level-1
+    near-tie band then widens by DENSE_W_REL_ERR * P_c / W_c per block).
     Returns (token, number of near-tie flags).
     """
     V = r.shape[0]
@@ -170,6 +204,7 @@ def gumbel_two_level(r, seed, b, a, block=BLOCK):
     key1 = np.full(C, -np.inf)
     live = np.nonzero(W > 0)[0]
     key1[live] = np.log(W[live]) + philox.gumbel(philox.u_block(seed, b, a, live))
+    slack = None if p is None else dense_level1_slack(r, p, block)
     c_star = int(np.argmax(key1))
     lo, hi = c_star * block, min((c_star + 1) * block, V)
     rr = r[lo:hi]
@@ -177,7 +212,7 @@ def gumbel_two_level(r, seed, b, a, block=BLOCK):
     live2 = np.nonzero(rr > 0)[0]
     key2[live2] = np.log(rr[live2]) + philox.gumbel(philox.u_token(seed, b, a, lo + live2))
     y = lo + int(np.argmax(key2))
-    return y, _near_tie(key1) + _near_tie(key2)
+    return y, _near_tie(key1, slack) + _near_tie(key2)
 
 
 def _verify_request(l, x, q, allowed, T, top_k, seed, b, block, top_p=0.0):
@@ -245,13 +280,15 @@ def _verify_request(l, x, q, allowed, T, top_k, seed, b, block, top_p=0.0):
                 n_acc += 1
             else:
                 break
+        dense = n_acc < k and q is not None
         if n_acc == k:
             r = p[k]
         else:
             r = residual_weights(p[n_acc], None if q is None else q[n_acc], x[n_acc], q is None)
         if not r.sum() > 0.0:
             r = p[n_acc]
-        y, nflag = gumbel_two_level(r, seed, b, n_acc, block)
+            dense = False
+        y, nflag = gumbel_two_level(r, seed, b, n_acc, block, p[n_acc] if dense else None)
         res["flag_gumbel"] = nflag
 
     res["tokens"][:n_acc] = x[:n_acc]

@@ -359,3 +359,25 @@ def test_one_hot_equals_explicit_one_hot_q():
                 "flag_accept", "flag_gumbel"):
         assert np.array_equal(a[key], b_[key]), key
     assert a["num_accepted"].max() > 0
+
+
+def test_near_tie_band_and_its_dense_slack():
+    """Reading 13: the near-tie band is GUMBEL_FLAG_EPS, widened for a dense
+    residual by DENSE_W_REL_ERR * P_c / W_c for each of the two leading
+    blocks; only the top two keys matter."""
+    eps = ov.GUMBEL_FLAG_EPS
+    keys = np.array([-np.inf, 1.0, 1.0 + 0.9 * eps, 0.5])
+    assert ov._near_tie(keys) == 1
+    keys[2] = 1.0 + 1.1 * eps
+    assert ov._near_tie(keys) == 0
+    slack = np.array([0.0, 0.1 * eps, 0.1 * eps, 5.0])  # the third key's slack is irrelevant
+    assert ov._near_tie(keys, slack) == 1
+    assert ov._near_tie(np.array([2.0, -np.inf])) == 0
+    # the slack: block 0 holds p-mass 0.5 on tokens where p > q and residual 0.05
+    p = np.array([0.3, 0.2, 0.1, 0.4])
+    q = np.array([0.27, 0.18, 0.3, 0.25])
+    r = np.maximum(p - q, 0.0)
+    s = ov.dense_level1_slack(r, p, block=2)
+    assert s[0] == pytest.approx(ov.DENSE_W_REL_ERR * 0.5 / 0.05, rel=1e-12)
+    assert s[1] == pytest.approx(ov.DENSE_W_REL_ERR * 0.4 / 0.15, rel=1e-12)
+    assert ov.dense_level1_slack(np.zeros(4), p, block=2).tolist() == [0.0, 0.0]
