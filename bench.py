@@ -404,6 +404,7 @@ def bench_proposer(args, dev):
 
     for s in range(args.warmup):
         call(s)
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
