@@ -94,17 +94,6 @@ __device__ __forceinline__ double draw_accept(PhiloxKey key, uint32_t b, uint32_
     return uniform_accept(philox4x32_10(make_uint4(0u, i, b, 0u), key.k0, key.k1).x);
 }
 
-// Level-1 Gumbel variates (fp64) of blocks 4 g4 .. 4 g4 + 3 of row a of
-// request b.
-__device__ __forceinline__ void draw_block_gumbels4(PhiloxKey key, uint32_t b, uint32_t a,
-                                                    uint32_t g4, double g[4]) {
-    const uint4 w = philox4x32_10(make_uint4(g4, a, b, 1u), key.k0, key.k1);
-    g[0] = gumbel_wide(w.x);
-    g[1] = gumbel_wide(w.y);
-    g[2] = gumbel_wide(w.z);
-    g[3] = gumbel_wide(w.w);
-}
-
 // Level-2 Gumbel variates of tokens j0 .. j0 + 3 (j0 a multiple of 4).
 __device__ __forceinline__ void draw_token_gumbels4(PhiloxKey key, uint32_t b, uint32_t a,
                                                     uint32_t j0, float g[4]) {

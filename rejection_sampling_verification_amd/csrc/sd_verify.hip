@@ -2473,9 +2473,6 @@ struct FinalShared {
     unsigned char ok[kMaxDraft], flag[kMaxDraft], invalid[kMaxDraft], badq[kMaxDraft];
     unsigned char rowst[kMaxDraft + 1];  // per row: SD_STATUS_* bits found by its wave
     int staged_c;               // block of the sampled row held in blockv (-1: none)
-    double red_d[kFinalWaves];
-    uint64_t red_u[kFinalWaves];
-    uint32_t red_b[kFinalWaves];
     uint4 race[2][kFinalWaves];  // per-wave level-2 results (best, index, runner-up), by attempt
     float blockv[kBlock];       // that block's logits, -inf where masked or past V
 };
@@ -2683,6 +2680,36 @@ __device__ __forceinline__ int2 race_winner(const uint32_t (&code)[4], int base,
 }
 
 __device__ __forceinline__ double ln_of(double x) { return ln_f32(static_cast<float>(x)); }
+
+// Level 1 of a residual draw: block c's key is ln W_c + G_c (G_c the level-1
+// Gumbel variate of block c of position n of request b) rounded to fp32; the
+// largest key wins, the lowest block on equal keys, flagged when another key
+// lies within kTieEps.  W: the residual masses (LDS or device memory).  Each
+// wave runs the whole race, one block per lane and round, so all waves agree
+// without a barrier.
+__device__ __forceinline__ Level1 residual_level1(const double *W, int C, PhiloxKey key, int b, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t lb = 0u, ls = 0u;  // the lane's largest code (at its lowest block) and the next
+    int li = INT_MAX;
+    for (int cb = lane; cb < C; cb += kWave) {
+        const double w = W[cb];
+        if (!(w > 0.0)) continue;
+        const uint32_t code = ordered_code(static_cast<float>(ln_of(w) + block_gumbel(key, b, n, cb)));
+        if (code > lb) {
+            ls = lb;
+            lb = code;
+            li = cb;
+        } else {
+            ls = max(ls, code);
+        }
+    }
+    const uint32_t wm = wave_max_u(lb);
+    if (wm == 0u) return Level1{-1, 0};
+    const int wi = wave_min_i(lb == wm ? li : INT_MAX);
+    const uint32_t ws = wave_max_u(li == wi ? ls : lb);
+    const bool tie = ws != 0u && float_of_code(ws) >= float_of_code(wm) - kTieEps;
+    return Level1{wi, tie ? 1 : 0};
+}
 
 // Level 2: the token of block cb of row n drawn under the weights of `mode`
 // (4 tokens per thread; values from the staged LDS copy when `staged`).  All
@@ -3335,29 +3362,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                     a.tau ? a.tau[row] : -INFINITY, sW);
                 lds_barrier();
                 // residual masses are <= 1, so their keys need no reference
-                const int ngroups = (C + 3) >> 2;
-                float kq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                const int g4 = tid;  // one group of four blocks per thread
-                uint64_t best = 0;
-                if (g4 < ngroups) {
-                    double gum[4];
-                    draw_block_gumbels4(key, b, n, g4, gum);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int cb = 4 * g4 + q;
-                        if (cb < C && sW[cb] > 0.0) {
-                            kq[q] = static_cast<float>(log(sW[cb]) + gum[q]);
-                            best = max_u64(best, pack_key(kq[q], cb));
-                        }
-                    }
-                }
-                best = block_max_u64<kFinalWaves>(best, sh.red_u);
-                bool tie = false;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (kq[q] > -INFINITY) tie |= near_tie(kq[q], 4 * g4 + q, best);
-                tie = block_any<kFinalWaves>(tie, sh.red_b);
-                l1 = best ? Level1{packed_index(best), tie ? 1 : 0} : Level1{-1, 0};
+                l1 = residual_level1(sW, C, key, b, n);
             }
             // A zero residual mass, or a block that lost its mass in double
             // precision, falls back to drawing from p.
@@ -3507,29 +3512,7 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
     const double *W = a.wmass + int64_t(b) * C;
     const float *qrow = a.q + j.dpos * a.V;
     // residual masses are <= 1, so their keys need no reference
-    const int ngroups = (C + 3) >> 2;
-    float kq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    const int g4 = tid;  // one group of four blocks per thread
-    uint64_t best = 0;
-    if (g4 < ngroups) {
-        double gum[4];
-        draw_block_gumbels4(key, b, n, g4, gum);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int cb = 4 * g4 + q;
-            if (cb < C && W[cb] > 0.0) {
-                kq[q] = static_cast<float>(log(W[cb]) + gum[q]);
-                best = max_u64(best, pack_key(kq[q], cb));
-            }
-        }
-    }
-    best = block_max_u64<kFinalWaves>(best, sh.red_u);
-    bool tie = false;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (kq[q] > -INFINITY) tie |= near_tie(kq[q], 4 * g4 + q, best);
-    tie = block_any<kFinalWaves>(tie, sh.red_b);
-    Level1 l1 = best ? Level1{packed_index(best), tie ? 1 : 0} : Level1{-1, 0};
+    Level1 l1 = residual_level1(W, C, key, b, n);
     int mode = kModeDense, y = -1, fg = 0;
     const double invT = j.invT;
     for (int attempt = 0; attempt < 2; ++attempt) {

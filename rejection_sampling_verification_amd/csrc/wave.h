@@ -260,16 +260,4 @@ __device__ __forceinline__ uint32_t block_max_u(uint32_t v, uint32_t *scratch) {
     return r;
 }
 
-template <int NW>
-__device__ __forceinline__ bool block_any(bool p, uint32_t *scratch) {
-    const bool w = wave_any(p);
-    lds_barrier();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = w ? 1u : 0u;
-    lds_barrier();
-    uint32_t r = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) r |= scratch[i];
-    return r != 0;
-}
-
 }  // namespace sdv
