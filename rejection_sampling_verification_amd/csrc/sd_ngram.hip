@@ -127,9 +127,24 @@ struct EmitArgs {
 
 // The winning window and the end of its earliest occurrence for request b,
 // and how many drafts follow it.
-__device__ __forceinline__ int request_result(const EmitArgs &a, int b, int L, int &n, int64_t &e) {
+// The chunk keys are loaded eight at a time, all in flight together.
+__device__ __forceinline__ uint64_t request_key(const EmitArgs &a, int b) {
+    const unsigned long long *p = a.best + int64_t(b) * a.nchunk;
     uint64_t key = 0;
-    for (int c = 0; c < a.nchunk; ++c) key = max_u64(key, a.best[int64_t(b) * a.nchunk + c]);
+    int c = 0;
+    for (; c + 8 <= a.nchunk; c += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p[c + j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) key = max_u64(key, v[j]);
+    }
+    for (; c < a.nchunk; ++c) key = max_u64(key, p[c]);
+    return key;
+}
+
+__device__ __forceinline__ int request_result(const EmitArgs &a, int b, int L, int &n, int64_t &e) {
+    const uint64_t key = request_key(a, b);
     n = int(key >> 32);
     e = int64_t(0xffffffffu - uint32_t(key));
     return n > 0 ? int(min(int64_t(a.k), int64_t(L) - e)) : 0;
