@@ -2684,21 +2684,24 @@ __device__ __forceinline__ double ln_of(double x) { return ln_f32(static_cast<fl
 // Level 1 of a residual draw: block c's key is ln W_c + G_c (G_c the level-1
 // Gumbel variate of block c of position n of request b) rounded to fp32; the
 // largest key wins, the lowest block on equal keys, flagged when another key
-// lies within kTieEps.  W: the residual masses (LDS or device memory).  Each
-// wave runs the whole race, one block per lane and round, so all waves agree
-// without a barrier.
-__device__ __forceinline__ Level1 residual_level1(const double *W, int C, PhiloxKey key, int b, int n) {
+// lies within kTieEps.  w_of(r, c): the residual mass of block c = lane +
+// 64 r.  Each wave runs the whole race, one block per lane and round, so all
+// waves agree without a barrier.  *wwin receives the winner's mass.
+template <typename GET>
+__device__ __forceinline__ Level1 residual_level1(GET w_of, int C, PhiloxKey key, int b, int n, double *wwin) {
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t lb = 0u, ls = 0u;  // the lane's largest code (at its lowest block) and the next
     int li = INT_MAX;
-    for (int cb = lane; cb < C; cb += kWave) {
-        const double w = W[cb];
+    double lw = 0.0;            // the mass of the lane's block li
+    for (int r = 0, cb = lane; cb < C; ++r, cb += kWave) {
+        const double w = w_of(r, cb);
         if (!(w > 0.0)) continue;
         const uint32_t code = ordered_code(static_cast<float>(ln_of(w) + block_gumbel(key, b, n, cb)));
         if (code > lb) {
             ls = lb;
             lb = code;
             li = cb;
+            lw = w;
         } else {
             ls = max(ls, code);
         }
@@ -2708,6 +2711,7 @@ __device__ __forceinline__ Level1 residual_level1(const double *W, int C, Philox
     const int wi = wave_min_i(lb == wm ? li : INT_MAX);
     const uint32_t ws = wave_max_u(li == wi ? ls : lb);
     const bool tie = ws != 0u && float_of_code(ws) >= float_of_code(wm) - kTieEps;
+    *wwin = __shfl(lw, wi & (kWave - 1));  // block wi sits in lane wi mod 64
     return Level1{wi, tie ? 1 : 0};
 }
 
@@ -3336,6 +3340,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             const double invT = 1.0 / static_cast<double>(T);
             const float *qrow = (DENSE && n < k) ? a.q + (geo.draft0 + n) * V : nullptr;
             int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
+            double wdense = 1.0;  // the winning block's residual mass
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
             if (DENSE && SPLIT && mode == kModeDense) {
                 // left to the residual kernels; -1 stands in until they write y
@@ -3362,7 +3367,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                     a.tau ? a.tau[row] : -INFINITY, sW);
                 lds_barrier();
                 // residual masses are <= 1, so their keys need no reference
-                l1 = residual_level1(sW, C, key, b, n);
+                l1 = residual_level1([&](int, int cb) { return sW[cb]; }, C, key, b, n, &wdense);
             }
             // A zero residual mass, or a block that lost its mass in double
             // precision, falls back to drawing from p.
@@ -3374,7 +3379,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 const int2 r2 =
                     level2<ET, ALIGNED>(a, sh, b, n, geo.row0 + n, n < k ? sh.X[n] : -1, l1.c, mode, c,
                                         invT, qrow, sh.staged_c == l1.c, attempt,
-                                        (DENSE && !SPLIT && mode == kModeDense) ? sW[l1.c] : 1.0);
+                                        (DENSE && !SPLIT && mode == kModeDense) ? wdense : 1.0);
                 if (r2.x >= 0) {
                     y = r2.x;
                     fg = l1.flag + r2.y;
@@ -3498,21 +3503,29 @@ __global__ __launch_bounds__(kThreads) void dense_mass_kernel(FinalArgs a) {
 template <typename ET, bool ALIGNED>
 __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) {
     __shared__ FinalShared sh;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int C = a.C;
+    // the residual masses of the first four rounds of blocks are read
+    // together with the job (their place does not depend on it)
+    const double *W = a.wmass + int64_t(b) * C;
+    double w4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w4[r] = lane + kWave * r < C ? W[lane + kWave * r] : 0.0;
     const DenseJob j = a.jobs[b];
     if (j.row < 0) return;
-    const int C = a.C, n = j.n;
+    const int n = j.n;
     const PhiloxKey key = key_of(a.seed);
     if (tid == 0) {
         sh.M[n] = j.M;
         sh.S[n] = j.S;
-        sh.X[n] = a.draft[j.dpos];
     }
     lds_barrier();
-    const double *W = a.wmass + int64_t(b) * C;
     const float *qrow = a.q + j.dpos * a.V;
     // residual masses are <= 1, so their keys need no reference
-    Level1 l1 = residual_level1(W, C, key, b, n);
+    double wwin = 1.0;
+    Level1 l1 = residual_level1(
+        [&](int r, int cb) { return r == 0 ? w4[0] : r == 1 ? w4[1] : r == 2 ? w4[2] : r == 3 ? w4[3] : W[cb]; },
+        C, key, b, n, &wwin);
     int mode = kModeDense, y = -1, fg = 0;
     const double invT = j.invT;
     for (int attempt = 0; attempt < 2; ++attempt) {
@@ -3520,8 +3533,9 @@ __global__ __launch_bounds__(kFinalThreads) void dense_draw_kernel(FinalArgs a) 
             mode = kModeP;
             l1 = j.l1p;
         }
-        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, j.row, sh.X[n], l1.c, mode, j.c, invT, qrow,
-                                            false, attempt, mode == kModeDense ? W[l1.c] : 1.0);
+        // (no draft to exclude: dense q and its fallback to p keep every token)
+        const int2 r2 = level2<ET, ALIGNED>(a, sh, b, n, j.row, -1, l1.c, mode, j.c, invT, qrow, false, attempt,
+                                            mode == kModeDense ? wwin : 1.0);
         if (r2.x >= 0) {
             y = r2.x;
             fg = l1.flag + r2.y;
