@@ -2999,15 +2999,32 @@ __device__ __forceinline__ CachedFold fold_races(FoldCache &fc, int C, int cx, d
     }
     f.bp = wave_argmax_code(cp, ip);
     f.bx = wave_argmax_code(cxm, ix);
-    double kd[kFoldCache], kdx[kFoldCache];
+    // The fp32 races stand unless another key lies within kRaceSlack of the
+    // winner's (counted on the fp32 keys already at hand); only then are the
+    // fp64 keys formed and raced (race_in_fp64).
+    const float wkp = f.bp ? packed_key(f.bp) : INFINITY, wkx = f.bx ? packed_key(f.bx) : INFINITY;
+    const float kpx = keyx > -INFINITY ? static_cast<float>(keyx - f.ref) : -INFINITY;
+    int closep = 0, closex = 0;
 #pragma unroll
     for (int j = 0; j < kFoldCache; ++j) {
-        const int cb = lane + kWave * j;
-        kd[j] = f.live[j] ? fc.e[j].key - f.ref : -INFINITY;
-        kdx[j] = cb != cx ? kd[j] : (f.live[j] && keyx > -INFINITY ? keyx - f.ref : -INFINITY);
+        if (!f.live[j]) continue;
+        const float kx = lane + kWave * j != cx ? f.kps[j] : kpx;
+        closep += f.kps[j] >= wkp - kRaceSlack ? 1 : 0;
+        closex += kx > -INFINITY && kx >= wkx - kRaceSlack ? 1 : 0;
     }
-    f.bp = race_in_fp64(f.bp, kd);
-    f.bx = race_in_fp64(f.bx, kdx);
+    const bool refine_p = __popcll(__ballot(closep > 0)) + __popcll(__ballot(closep > 1)) > 1;
+    const bool refine_x = __popcll(__ballot(closex > 0)) + __popcll(__ballot(closex > 1)) > 1;
+    if (refine_p || refine_x) {
+        double kd[kFoldCache], kdx[kFoldCache];
+#pragma unroll
+        for (int j = 0; j < kFoldCache; ++j) {
+            const int cb = lane + kWave * j;
+            kd[j] = f.live[j] ? fc.e[j].key - f.ref : -INFINITY;
+            kdx[j] = cb != cx ? kd[j] : (f.live[j] && keyx > -INFINITY ? keyx - f.ref : -INFINITY);
+        }
+        if (refine_p) f.bp = race_in_fp64(f.bp, kd);
+        if (refine_x) f.bx = race_in_fp64(f.bx, kdx);
+    }
     return f;
 }
 
