@@ -125,9 +125,8 @@ struct EmitArgs {
     int B, nchunk, k;
 };
 
-// The winning window and the end of its earliest occurrence for request b,
-// and how many drafts follow it.
-// The chunk keys are loaded eight at a time, all in flight together.
+// Request b's best chunk key; the keys are loaded eight at a time, all in
+// flight together.
 __device__ __forceinline__ uint64_t request_key(const EmitArgs &a, int b) {
     const unsigned long long *p = a.best + int64_t(b) * a.nchunk;
     uint64_t key = 0;
@@ -143,6 +142,8 @@ __device__ __forceinline__ uint64_t request_key(const EmitArgs &a, int b) {
     return key;
 }
 
+// The winning window and the end of its earliest occurrence for request b,
+// and how many drafts follow it.
 __device__ __forceinline__ int request_result(const EmitArgs &a, int b, int L, int &n, int64_t &e) {
     const uint64_t key = request_key(a, b);
     n = int(key >> 32);
