@@ -601,9 +601,10 @@ __device__ __forceinline__ SweepCursor cursor_at(const RowStatsArgs &a, int64_t 
 // so every claim can delay a block, and claims are kept for the part of the
 // sweep where the imbalance builds up.  A claim's round trip under full HBM
 // load is longer than one block's time, so two claims are kept in flight.  Home partitions mix workgroups of all eight XCDs (workgroups go to
-// XCDs round-robin), so the XCDs' speeds average out within a partition; one
-// counter serves about 1/64 of the claims, well below the rate at which one
-// address takes returning atomics.
+// XCDs round-robin), so the XCDs' speeds average out within a partition.
+// Each counter serves about 1/64 of the claims; the counters still contend
+// (32 partitions measured 2.9 us slower per call, 16 partitions 16 us), and
+// 128 measured 0.6 us slower.
 constexpr int kSweepParts = 64;
 constexpr int kSweepCtrStride = 64;  // 32-bit words between counters: one 256-byte line each
 
