@@ -2998,8 +2998,11 @@ __device__ __forceinline__ CachedFold fold_races(FoldCache &fc, int C, int cx, d
             ix = cb;
         }
     }
+    // Without a draft block to leave out (the bonus row, dense q, an invalid
+    // draft) the second race is the first: it is not run.
+    const bool xrace = cx >= 0;
     f.bp = wave_argmax_code(cp, ip);
-    f.bx = wave_argmax_code(cxm, ix);
+    f.bx = xrace ? wave_argmax_code(cxm, ix) : f.bp;
     // The fp32 races stand unless another key lies within kRaceSlack of the
     // winner's (counted on the fp32 keys already at hand); only then are the
     // fp64 keys formed and raced (race_in_fp64).
@@ -3014,7 +3017,7 @@ __device__ __forceinline__ CachedFold fold_races(FoldCache &fc, int C, int cx, d
         closex += kx > -INFINITY && kx >= wkx - kRaceSlack ? 1 : 0;
     }
     const bool refine_p = __popcll(__ballot(closep > 0)) + __popcll(__ballot(closep > 1)) > 1;
-    const bool refine_x = __popcll(__ballot(closex > 0)) + __popcll(__ballot(closex > 1)) > 1;
+    const bool refine_x = xrace && __popcll(__ballot(closex > 0)) + __popcll(__ballot(closex > 1)) > 1;
     if (refine_p || refine_x) {
         double kd[kFoldCache], kdx[kFoldCache];
 #pragma unroll
@@ -3025,6 +3028,7 @@ __device__ __forceinline__ CachedFold fold_races(FoldCache &fc, int C, int cx, d
         }
         if (refine_p) f.bp = race_in_fp64(f.bp, kd);
         if (refine_x) f.bx = race_in_fp64(f.bx, kdx);
+        if (!xrace) f.bx = f.bp;
     }
     return f;
 }
