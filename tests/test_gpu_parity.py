@@ -298,6 +298,17 @@ def test_dense_long_rows(V, dtype):
     assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+def test_dense_rows_past_256_blocks():
+    """Dense q on rows of 293 blocks (V = 600000): the residual draw's level-1
+    race takes its first four rounds of 64 block masses from the loads issued
+    with the job and reads the fifth from memory as it goes."""
+    announce("dense rows V=600000 (293 blocks)")
+    wl = _custom(4, 2, 600000, dense=True, masked=True, density=0.5, seed=11)
+    gpu = run_gpu(wl)
+    assert_parity(gpu, run_oracle(wl))
+    assert (gpu["out_num_accepted"] < 2).any()  # some token comes from the residual
+
+
 def test_masked_dense_one_hot_and_greedy_mix():
     announce("custom B=24 k=6 V=40000 masked dense greedy mix")
     wl = _custom(24, 6, 40000, dense=True, masked=True, greedy_frac=0.4, density=0.1, seed=3)
