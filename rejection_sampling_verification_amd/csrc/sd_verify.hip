@@ -1342,11 +1342,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
         for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.hist[i] = 0u;
         lds_barrier();
         uint32_t above = 0, support = 0, mx = 0;
-        // kTopkUnroll groups per thread in flight per iteration
-        for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kTopkUnroll * kStep) {
-            float v[kTopkUnroll][P];
-#pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
+        auto count = [&](const float (&v)[kTopkUnroll][P]) {
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u)
 #pragma unroll
@@ -1359,6 +1355,32 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
                     if (d > hi) ++above;
                     else if (d >= lo) atomicAdd(&sh.hist[d - lo], 1u);
                 }
+        };
+        constexpr int64_t kBatch = kTopkUnroll * kStep;
+        if constexpr (ALIGNED) {
+            // kTopkUnroll groups per thread per batch, two batches in flight:
+            // the next batch loads while this one is counted (groups past V
+            // read as NaN and count nothing)
+            float va[kTopkUnroll][P], vb[kTopkUnroll][P];
+            int64_t tok0 = int64_t(tid) * P;
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, va[u]);
+            for (; tok0 < V; tok0 += 2 * kBatch) {
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + kBatch + u * kStep, vb[u]);
+                count(va);
+                if (tok0 + kBatch >= V) break;
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + 2 * kBatch + u * kStep, va[u]);
+                count(vb);
+            }
+        } else {  // element loads: one batch at a time
+            for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kBatch) {
+                float v[kTopkUnroll][P];
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, v[u]);
+                count(v);
+            }
         }
         above = block_sum_u<kTopkWaves>(above, sh.red);
         if (first) {

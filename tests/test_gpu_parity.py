@@ -145,6 +145,14 @@ def test_top_k_sizes(V, dtype):
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+def test_top_k_rows_longer_than_the_single_pass_takes():
+    """Aligned bf16 rows of 300000 tokens (147 blocks: more line maxima than
+    the single-pass top-k holds), so the two-pass selection runs them."""
+    announce("top-k aligned V=300000 (two-pass selection)")
+    wl = _custom(3, 2, 300000, dense=False, masked=True, density=0.3, seed=17, top_k=(1, 50, 4000))
+    assert_parity(run_gpu(wl), run_oracle(wl))
+
+
 def test_top_k_ties():
     announce("top-k with integer logits: many ties at the threshold")
     for dtype in (torch.bfloat16, torch.float32):
