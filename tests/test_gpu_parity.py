@@ -317,9 +317,12 @@ def test_dense_rows_past_256_blocks():
     assert (gpu["out_num_accepted"] < 2).any()  # some token comes from the residual
 
 
-def test_masked_dense_one_hot_and_greedy_mix():
-    announce("custom B=24 k=6 V=40000 masked dense greedy mix")
-    wl = _custom(24, 6, 40000, dense=True, masked=True, greedy_frac=0.4, density=0.1, seed=3)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_masked_dense_one_hot_and_greedy_mix(dtype):
+    """Rows of 20 blocks: the dense residual is summed inside the finalize
+    kernel, each wave taking two rounds of blocks."""
+    announce(f"custom B=24 k=6 V=40000 masked dense greedy mix dtype={dtype}")
+    wl = _custom(24, 6, 40000, dtype=dtype, dense=True, masked=True, greedy_frac=0.4, density=0.1, seed=3)
     assert_parity(run_gpu(wl), run_oracle(wl))
     wl["draft_probs"] = None
     assert_parity(run_gpu(wl), run_oracle(wl))
