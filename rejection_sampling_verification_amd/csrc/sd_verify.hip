@@ -527,13 +527,45 @@ __device__ __forceinline__ void record_draft(const RowStatsArgs &a, int row, int
     r.qx = a.q ? uniform_load(a.q + dpos * a.V + x) : 1.0f;
 }
 
+// The keep masks of a bf16 group for each of the 256 values of its mask
+// byte: word i keeps its low half when bit 2i is set and its high half when
+// bit 2i + 1 is, so a group masks in four bit-field inserts (forbidden tokens
+// become the bf16 pattern of -inf) instead of a test and a select per token.
+// Filled in LDS by every workgroup of a masked bf16 sweep.
+__device__ __forceinline__ void fill_keep_table(uint4 *keep) {
+    for (int t = threadIdx.x; t < 256 * 4; t += blockDim.x) {
+        const uint32_t byte = uint32_t(t) >> 2, i = uint32_t(t) & 3u;
+        const uint32_t lo = (byte >> (2 * i)) & 1u, hi = (byte >> (2 * i + 1)) & 1u;
+        reinterpret_cast<uint32_t *>(keep)[t] = (lo ? 0x0000ffffu : 0u) | (hi ? 0xffff0000u : 0u);
+    }
+}
+
+__device__ __forceinline__ uint32_t keep_or_neg_inf(uint32_t w, uint32_t k) {
+    uint32_t r = (w & k) | (0xff80ff80u & ~k);
+    asm("" : "+v"(r));  // one insert per word; the unpack then shifts and masks the result
+    return r;
+}
+
 // Raw 16-byte groups and mask bytes of one block wholly inside the row: lane
 // l reads groups l, l + 64, ... (consecutive lanes, consecutive 16 bytes).
+// keep: the keep-mask table (masked bf16 rows).
 template <typename ET, bool MASKED>
 __device__ __forceinline__ void unpack_full_block(const uint4 *r, const uint32_t *m, int lane,
-                                                  float *v) {
+                                                  float *v, const uint4 *keep = nullptr) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
+    if constexpr (MASKED && P == 8) {
+        uint4 k[G];  // all table reads in flight before the first is used
+#pragma unroll
+        for (int g = 0; g < G; ++g) k[g] = keep[m[g]];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint4 w = make_uint4(keep_or_neg_inf(r[g].x, k[g].x), keep_or_neg_inf(r[g].y, k[g].y),
+                                       keep_or_neg_inf(r[g].z, k[g].z), keep_or_neg_inf(r[g].w, k[g].w));
+            Logit<ET>::unpack(w, v + g * P);
+        }
+        return;
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         Logit<ET>::unpack(r[g], v + g * P);
@@ -834,7 +866,8 @@ __device__ __forceinline__ float2 lines_block(const RowStatsArgs &a, int row, in
 // sweep), 2 record line maxima of top-k rows (tau is found after it).
 template <typename ET, bool MASKED, int TOPK>
 __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepBlock &s, int lane,
-                                             const uint4 *r, const uint32_t *m, Stash &st, int slot) {
+                                             const uint4 *r, const uint32_t *m, Stash &st, int slot,
+                                             const uint4 *keep) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     // Without a mask every block is unpacked the same way and a partial one is
@@ -855,7 +888,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
         }
         unpack_full_block<ET, MASKED>(w, mm, lane, v);
     } else if (s.full) {
-        unpack_full_block<ET, MASKED>(r, mm, lane, v);
+        unpack_full_block<ET, MASKED>(r, mm, lane, v, keep);
     } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -899,7 +932,7 @@ __device__ __forceinline__ void reduce_block(const RowStatsArgs &a, const SweepB
 // them) and claims the rest.  Each wave keeps the loads of its next block in
 // flight while it reduces the current one.
 template <typename ET, bool MASKED, int TOPK, int POL>
-__device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
+__device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane, const uint4 *keep) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     // static blocks per wave: a build-time constant without a mask
@@ -924,7 +957,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
             const SweepCursor s1 = cursor_at(a, block_of(pl, lb ? kb : pl.kfirst));
             issue_block<ET, MASKED, POL>(a, s1.row, s1.blk, lane, rb, mb, lb);
             const SweepBlock xb = sweep_block(a, s1);
-            if (!xa.skip) reduce_block<ET, MASKED, TOPK>(a, xa, lane, ra, ma, st, count++);
+            if (!xa.skip) reduce_block<ET, MASKED, TOPK>(a, xa, lane, ra, ma, st, count++, keep);
             else settle(ra[G - 1]);
             if (count == kWave) {
                 flush_stash(a, st, key, lane, count);
@@ -934,7 +967,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
             const SweepCursor s2 = cursor_at(a, block_of(pl, lc ? kc : pl.kfirst));
             issue_block<ET, MASKED, POL>(a, s2.row, s2.blk, lane, ra, ma, lc);
             xa = sweep_block(a, s2);
-            if (lb && !xb.skip) reduce_block<ET, MASKED, TOPK>(a, xb, lane, rb, mb, st, count++);
+            if (lb && !xb.skip) reduce_block<ET, MASKED, TOPK>(a, xb, lane, rb, mb, st, count++, keep);
             else settle(rb[G - 1]);
             if (count == kWave) {
                 flush_stash(a, st, key, lane, count);
@@ -984,7 +1017,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
         const SweepCursor c1 = cursor_at(a, block_of(pl, more1 ? kn : pl.k0));
         issue_block<ET, MASKED, POL>(a, c1.row, c1.blk, lane, rb, mb, more1);
         const SweepBlock sb = sweep_block(a, c1);
-        if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++);
+        if (!sa.skip) reduce_block<ET, MASKED, TOPK>(a, sa, lane, ra, ma, st, count++, keep);
         else settle(ra[G - 1]);
         if (count == kWave) {
             flush_stash(a, st, key, lane, count);
@@ -998,7 +1031,7 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane) {
             const SweepCursor c2 = cursor_at(a, block_of(pl, more2 ? kn : pl.k0));
             issue_block<ET, MASKED, POL>(a, c2.row, c2.blk, lane, ra, ma, more2);
             sa = sweep_block(a, c2);
-            if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++);
+            if (!sb.skip) reduce_block<ET, MASKED, TOPK>(a, sb, lane, rb, mb, st, count++, keep);
             else settle(rb[G - 1]);
             if (count == kWave) {
                 flush_stash(a, st, key, lane, count);
@@ -1026,7 +1059,14 @@ __global__ __launch_bounds__(kSweepThreads) void row_stats_vec_kernel(RowStatsAr
     zero_call_outputs(a);
     if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
     const int lane = threadIdx.x & (kWave - 1);
-    sweep_claimed<ET, MASKED, TOPK, POL>(a, lane);
+    if constexpr (MASKED && sizeof(ET) == 2) {
+        __shared__ uint4 keep[256];
+        fill_keep_table(keep);
+        __syncthreads();
+        sweep_claimed<ET, MASKED, TOPK, POL>(a, lane, keep);
+    } else {
+        sweep_claimed<ET, MASKED, TOPK, POL>(a, lane, nullptr);
+    }
 }
 
 // Any alignment and any V: element loads clamped into the row, one chunk of
