@@ -363,7 +363,14 @@ __device__ __forceinline__ float2 softmax_block(const float *v, float c) {
 #pragma unroll
     for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
     m = wave_max_coded(m);  // a NaN logit makes the sum NaN either way
-    if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+    if (m == -INFINITY) {
+        // every value but a NaN is -inf here, so a NaN (of either sign) is a
+        // nonzero mantissa among the values: the statistics then carry it
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) bits |= __float_as_uint(v[e]);
+        return make_float2(-INFINITY, wave_any((bits & 0x7fffffu) != 0u) ? NAN : 0.0f);
+    }
     const float mc = m * c;
     // four running sums of 8 terms each, combined pairwise: with the wave's
     // tree the fp32 sum of these positive terms is 15 additions deep, within
@@ -1181,11 +1188,19 @@ constexpr int kTopkUnroll = 4;
 constexpr uint32_t kTopkFirstSpan = 256;
 constexpr double kTopPFlagEps = 1e-9;  // boundary threshold of a top-p cut, relative to the mass
 
+// Bins ahead of the window, one per lane: the window pass over raw bf16 codes
+// adds every element to some bin, those below the window to their lane's.
+constexpr int kTopkLead = kWave;
+
 struct TopkShared {
-    uint32_t hist[kTopkWindow];
+    // the lanes' bins, the window's bins, and one more: the raw bf16 pass
+    // counts the elements above a window of n bins in bin n
+    uint32_t bins[kTopkLead + kTopkWindow + 1];
     uint32_t part[kTopkThreads];  // per-thread sums of 4 bins, scanned in place
     uint32_t red[kTopkWaves];
     uint32_t found_digit, found_rank, lowest;
+    uint4 keep[256];              // masked bf16 rows: the keep-mask table
+    __device__ __forceinline__ uint32_t *hist() { return bins + kTopkLead; }
 };
 
 // The top-p selection's per-bin masses beside the top-k histogram (only the
@@ -1304,7 +1319,7 @@ __device__ bool topk_pick(TopkShared &sh, int nbins, uint32_t lo, uint32_t need,
     const int tid = threadIdx.x;
     const int per = nbins / kTopkThreads;  // 4 or 1
     uint32_t own = 0;
-    for (int i = 0; i < per; ++i) own += sh.hist[tid * per + i];
+    for (int i = 0; i < per; ++i) own += sh.hist()[tid * per + i];
     sh.part[tid] = own;
     // inclusive suffix sums: part[t] = sum of part[t'] for t' >= t
     for (int d = 1; d < kTopkThreads; d <<= 1) {
@@ -1320,7 +1335,7 @@ __device__ bool topk_pick(TopkShared &sh, int nbins, uint32_t lo, uint32_t need,
     if (incl >= need && incl - own < need) {
         uint32_t acc = incl - own;
         for (int i = per - 1; i >= 0; --i) {
-            const uint32_t h = sh.hist[tid * per + i];
+            const uint32_t h = sh.hist()[tid * per + i];
             if (acc + h >= need) {
                 sh.found_digit = lo + uint32_t(tid * per + i);
                 sh.found_rank = need - acc;
@@ -1342,10 +1357,74 @@ struct TopkRow {
     const uint8_t *mrow;
     __amdgpu_buffer_rsrc_t rs, rm;
     int V;
+    static constexpr int64_t kStep = int64_t(kTopkThreads) * Logit<ET>::kPer16;
     __device__ __forceinline__ void load(int64_t tok, float *v) const {
         topk_load<ET, ALIGNED, MASKED>(rowp, mrow, rs, rm, V, tok, v);
     }
+    // Aligned rows: the raw 16-byte groups tok0 + u * kStep (u < kTopkUnroll)
+    // and their mask bytes, with one offset register for all of them (the
+    // groups' distance rides in the scalar offset).  Past V: zeros.
+    __device__ __forceinline__ void raw(int64_t tok0, uint4 *w, uint32_t *m) const {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const int off = static_cast<int>(tok0 * int64_t(sizeof(ET)));
+#pragma unroll
+        for (int u = 0; u < kTopkUnroll; ++u) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, u * int(kStep * sizeof(ET)), 0);
+            w[u] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+        if (MASKED) {
+            const int moff = static_cast<int>(tok0 >> 3);
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u)
+                m[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, moff, u * int(kStep / 8), 0);
+        }
+    }
+    // The values of such a batch, excluded tokens (masked, past V, NaN,
+    // +-inf) as NaN, as load() gives them.
+    __device__ __forceinline__ void values(int64_t tok0, const uint4 *w, const uint32_t *m,
+                                           float (*v)[Logit<ET>::kPer16]) const {
+        constexpr int P = Logit<ET>::kPer16;
+#pragma unroll
+        for (int u = 0; u < kTopkUnroll; ++u) {
+            const int64_t tok = tok0 + u * kStep;
+            Logit<ET>::unpack(w[u], v[u]);
+            uint32_t bits = tok < V ? 0xffu : 0u;
+            if (MASKED) bits &= (P == 8) ? m[u] : (m[u] >> (uint32_t(tok) & 4u));
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                const bool live = ((bits >> e) & 1u) && fabsf(v[u][e]) <= FLT_MAX;
+                v[u][e] = live ? v[u][e] : NAN;
+            }
+        }
+    }
 };
+
+// Per 16-bit half of a word of bf16 values: the half's order-preserving code
+// (the top half of the 32-bit code of the value), and the larger of two codes.
+__device__ __forceinline__ uint32_t bf16_codes(uint32_t x) {
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t sgn = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, x) >> (s16x2){15, 15});
+    // per bit, (x ^ sgn) | (0x80008000 & ~x): a negative half has every bit
+    // flipped, a positive one its sign bit set; one three-input bit op (the
+    // compiler splits this form into three)
+    uint32_t c;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x3e" : "=v"(c) : "v"(x), "v"(sgn), "s"(0x80008000u));
+    return c;
+}
+
+// The middle of three signed integers (one instruction; the compiler's
+// min-of-max form takes two).
+__device__ __forceinline__ int med3_i32(int a, int lo, int hi) {
+    int r;
+    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(lo), "v"(hi));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
 
 // The K-th largest allowed finite logit of the row, or -inf when the row
 // holds at most K of them (see the comment above TopkArgs); also the row's
@@ -1379,7 +1458,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
     // run; the bound below is never reached.
     for (int pass = 0; pass < 0x10000 / kTopkWindow + 2; ++pass) {
         const uint32_t lo = hi >= span - 1 ? hi - (span - 1) : 0u;
-        for (int i = tid; i < kTopkWindow; i += kTopkThreads) sh.hist[i] = 0u;
+        for (int i = tid; i < kTopkLead + kTopkWindow + 1; i += kTopkThreads) sh.bins[i] = 0u;
         lds_barrier();
         uint32_t above = 0, support = 0, mx = 0;
         auto count = [&](const float (&v)[kTopkUnroll][P]) {
@@ -1393,26 +1472,83 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
                     if (TRACK_MAX) mx = max(mx, c);
                     const uint32_t d = c >> 16;
                     if (d > hi) ++above;
-                    else if (d >= lo) atomicAdd(&sh.hist[d - lo], 1u);
+                    else if (d >= lo) atomicAdd(&sh.hist()[d - lo], 1u);
                 }
         };
         constexpr int64_t kBatch = kTopkUnroll * kStep;
         if constexpr (ALIGNED) {
+            // bf16: each element's 16-bit code straight from the raw words,
+            // and its bin without a branch: the offset from lo, clamped below
+            // to a bin of the lane ahead of the window and above to the bin
+            // past it, whose count is then the count above the window.  Valid
+            // codes are 0x0080 .. 0xff7f (-inf and negative NaNs code below,
+            // +inf and positive NaNs above); masked tokens get code 0.  A
+            // batch that reaches past V, holds an allowed +inf or NaN, or
+            // meets a window starting below 0x0080 is counted element by
+            // element instead.  The wave's support count rides in a scalar.
+            uint32_t support_w = 0, mx16 = 0;
+            const int lane_bin = -1 - (tid & (kWave - 1));
+            auto count_codes = [&](int64_t t0, const uint4 (&w)[kTopkUnroll], const uint32_t (&m)[kTopkUnroll]) {
+                if (lo < 0x80u || __ballot(t0 + (kTopkUnroll - 1) * kStep >= V) != 0ull) return false;
+                uint32_t c[kTopkUnroll][4];
+                uint32_t bm = 0;
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u) {
+                    const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                    uint4 k = make_uint4(~0u, ~0u, ~0u, ~0u);
+                    if (MASKED) k = sh.keep[m[u]];
+                    const uint32_t kk[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        c[u][j] = MASKED ? bf16_codes(x[j]) & kk[j] : bf16_codes(x[j]);
+                        bm = max_u16x2(bm, c[u][j]);
+                    }
+                }
+                const uint32_t top = max(bm & 0xffffu, bm >> 16);
+                if (__ballot(top >= 0xff80u) != 0ull) return false;
+                if (TRACK_MAX) mx16 = max(mx16, top);
+                if (first) {
+#pragma unroll
+                    for (int u = 0; u < kTopkUnroll; ++u)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const uint32_t d = (j & 1) ? (c[u][j >> 1] >> 16) : (c[u][j >> 1] & 0xffffu);
+                            support_w += __popcll(__ballot(d >= 0x80u));
+                        }
+                }
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t d = (j & 1) ? (c[u][j >> 1] >> 16) : (c[u][j >> 1] & 0xffffu);
+                        const int t = int(d) - int(lo);
+                        atomicAdd(&sh.hist()[med3_i32(t, lane_bin, int(span))], 1u);
+                    }
+                return true;
+            };
             // kTopkUnroll groups per thread per batch, two batches in flight:
-            // the next batch loads while this one is counted (groups past V
-            // read as NaN and count nothing)
-            float va[kTopkUnroll][P], vb[kTopkUnroll][P];
+            // the next batch loads while this one is counted
+            auto count_raw = [&](int64_t t0, const uint4 (&w)[kTopkUnroll], const uint32_t (&m)[kTopkUnroll]) {
+                if constexpr (sizeof(ET) == 2)
+                    if (count_codes(t0, w, m)) return;
+                float v[kTopkUnroll][P];
+                r.values(t0, w, m, v);
+                count(v);
+            };
+            uint4 wa[kTopkUnroll], wb[kTopkUnroll];
+            uint32_t ma[kTopkUnroll] = {}, mb[kTopkUnroll] = {};
             int64_t tok0 = int64_t(tid) * P;
-#pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + u * kStep, va[u]);
+            r.raw(tok0, wa, ma);
             for (; tok0 < V; tok0 += 2 * kBatch) {
-#pragma unroll
-                for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + kBatch + u * kStep, vb[u]);
-                count(va);
+                r.raw(tok0 + kBatch, wb, mb);
+                count_raw(tok0, wa, ma);
                 if (tok0 + kBatch >= V) break;
-#pragma unroll
-                for (int u = 0; u < kTopkUnroll; ++u) r.load(tok0 + 2 * kBatch + u * kStep, va[u]);
-                count(vb);
+                r.raw(tok0 + 2 * kBatch, wa, ma);
+                count_raw(tok0 + kBatch, wb, mb);
+            }
+            if (sizeof(ET) == 2) {
+                if (TRACK_MAX && mx16 >= 0x80u) mx = max(mx, (mx16 << 16) | ((mx16 & 0x8000u) ? 0u : 0xffffu));
+                if ((tid & (kWave - 1)) == 0) support += support_w;
             }
         } else {  // element loads: one batch at a time
             for (int64_t tok0 = int64_t(tid) * P; tok0 < V; tok0 += kBatch) {
@@ -1423,6 +1559,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
             }
         }
         above = block_sum_u<kTopkWaves>(above, sh.red);
+        if (ALIGNED && sizeof(ET) == 2) above += sh.hist()[span];  // the raw pass's count above the window
         if (first) {
             support = block_sum_u<kTopkWaves>(support, sh.red);
             if (TRACK_MAX) maxcode = block_max_u<kTopkWaves>(mx, sh.red);
@@ -1434,7 +1571,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
             span = kTopkWindow;
             continue;
         }
-        if (topk_pick(sh, kTopkWindow, lo, need - above, digit, rank)) {
+        if (topk_pick(sh, int(span), lo, need - above, digit, rank)) {  // bins from span on: not the window's
             found = true;
             lo_found = lo;
             above_found = above;
@@ -1454,7 +1591,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
         uint32_t prefix = digit;  // selected high bits so far
         uint32_t want = rank;
         for (int shift = 8; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0u;
+            for (int i = tid; i < 256; i += kTopkThreads) sh.hist()[i] = 0u;
             lds_barrier();
             for (int64_t tok = int64_t(tid) * P; tok < V; tok += kStep) {
                 float v[P];
@@ -1463,7 +1600,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
                 for (int e = 0; e < P; ++e) {
                     if (v[e] != v[e]) continue;
                     const uint32_t c = ordered_code(v[e]);
-                    if ((c >> (shift + 8)) == prefix) atomicAdd(&sh.hist[(c >> shift) & 0xffu], 1u);
+                    if ((c >> (shift + 8)) == prefix) atomicAdd(&sh.hist()[(c >> shift) & 0xffu], 1u);
                 }
             }
             lds_barrier();
@@ -1582,7 +1719,7 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, ToppShared 
     for (int pass = 0; pass < 0x10000 / kTopkWindow + 2; ++pass) {
         const uint32_t lo = hi >= span - 1 ? hi - (span - 1) : 0u;
         for (int i = tid; i < kTopkWindow; i += kTopkThreads) {
-            if (kBf16) sh.hist[i] = 0u;
+            if (kBf16) sh.hist()[i] = 0u;
             else sh.mass[i] = 0.0;
         }
         lds_barrier();
@@ -1601,7 +1738,7 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, ToppShared 
                     if (d > hi) continue;  // counted in an earlier pass
                     if (d >= lo) {
                         if (kBf16) {
-                            atomicAdd(&sh.hist[d - lo], 1u);
+                            atomicAdd(&sh.hist()[d - lo], 1u);
                         } else {
                             const double w = exp2_precise_nonpos(fma(static_cast<double>(x), cd, -mcd));
                             atomicAdd(&sh.mass[d - lo], w);
@@ -1617,7 +1754,7 @@ __device__ float select_top_p(const TopkRow<ET, ALIGNED, MASKED> &r, ToppShared 
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int bin = tid * kPer + i;
-                const uint32_t n = sh.hist[bin];
+                const uint32_t n = sh.hist()[bin];
                 const double m = n ? static_cast<double>(n) *
                                          exp2_precise_nonpos(fma(static_cast<double>(bf16_value_of_digit(lo + bin)), cd, -mcd))
                                    : 0.0;
@@ -1699,7 +1836,7 @@ __device__ float top_p_in_window(ToppShared &sh, const TopkResult &tk, float top
     for (int i = 0; i < kPer; ++i) {
         const int bin = tid * kPer + i;
         const uint32_t d = tk.lo + uint32_t(bin);
-        const uint32_t n = sh.hist[bin];
+        const uint32_t n = sh.hist()[bin];
         const double m = (n != 0u && d >= tau_digit)
                              ? static_cast<double>(n) *
                                    exp2_precise_nonpos(fma(static_cast<double>(bf16_value_of_digit(d)), cd, -mcd))
@@ -1737,6 +1874,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
             a.tau_flag[row] = 0u;
         }
         return;
+    }
+    if constexpr (MASKED && ALIGNED && sizeof(ET) == 2) {
+        fill_keep_table(sh.keep);
+        lds_barrier();
     }
     TopkRow<ET, ALIGNED, MASKED> r;
     r.rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;

@@ -276,6 +276,52 @@ def test_top_p_extreme_temperatures_masks_and_errors():
         assert gpu["status"] & oracle.verify.ST_TEMPERATURE
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_two_pass_selection_on_raw_codes(masked):
+    """bf16 rows, 16-byte aligned, of a call with top-p: the two-pass
+    selection counts them on raw 16-bit codes and takes element by element
+    the batches with an allowed NaN or +inf and the windows that start at the
+    bottom of the code range.  Rows with -inf among the values, an allowed
+    NaN of either sign or +inf (reported), a NaN at a forbidden token, the
+    threshold among the most negative finite values, no allowed finite value,
+    and exactly K allowed finite values."""
+    announce(f"two-pass selection on raw bf16 codes masked={masked}")
+    B, k, V = 8, 2, 40960
+    wl = _custom(B, k, V, dense=False, seed=131 + masked)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(132 + masked)
+    lg = wl["logits"].float()
+    if masked:
+        allowed = torch.rand((B, k + 1, V), generator=g, device=DEV) < 0.5
+    else:
+        allowed = torch.ones((B, k + 1, V), dtype=torch.bool, device=DEV)
+    lg[0, :, ::97] = float("-inf")
+    lg[1, 0, 30001] = float("nan")
+    allowed[1, 0, 30001] = True
+    lg[1, 1, 777] = float("nan")                      # forbidden when masked, else reported
+    allowed[1, 1, 777] = not masked
+    lg[2, 2, 12345] = float("inf")
+    allowed[2, 2, 12345] = True
+    lg[3] = -2.0e38 * (1.0 + 0.5 * torch.rand((k + 1, V), generator=g, device=DEV))
+    lg[4] = float("-inf")
+    lg[5] = float("-inf")
+    for i in range(k + 1):
+        idx = torch.randperm(V, generator=g, device=DEV)[:50]
+        lg[5, i, idx] = torch.randn(50, generator=g, device=DEV) * 3.0
+        allowed[5, i, idx] = True
+    lgb = lg.to(torch.bfloat16).contiguous()
+    lgb.view(torch.int16)[6, 0, 5000] = -64           # 0xffc0: a NaN with the sign bit set
+    allowed[6, 0, 5000] = True
+    wl["logits"] = lgb
+    wl["bitmask"] = pack_bitmask(allowed) if masked else None
+    wl["temperature"][3] = 1e34                       # l / T of row 3 within the fp32 exponent range
+    wl["top_k"] = torch.full((B,), 50, dtype=torch.int32, device=DEV)
+    wl["top_p"] = torch.tensor([0.9, 0.9, 0.9, 0.9, 0.9, 0.95, 0.5, 0.99], device=DEV)
+    gpu, orc = run_gpu(wl), run_oracle(wl)
+    assert orc["request_status"][1] and orc["request_status"][2] and orc["request_status"][6]
+    assert_parity(gpu, orc)
+
+
 def test_long_k_with_top_p_scaled():
     announce("long_k B=8 with top-k 50 and top-p 0.9")
     wl = make_workload("long_k", device=DEV, batch=8)
