@@ -322,6 +322,34 @@ def test_two_pass_selection_on_raw_codes(masked):
     assert_parity(gpu, orc)
 
 
+@pytest.mark.parametrize("V", [8192, 8190])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_nan_alone_in_a_block(dtype, V):
+    """A NaN that is the only allowed token of its 2048-token block (the
+    block's other tokens masked or -inf), on sampling and greedy rows, with
+    and without top-k, on aligned rows and on rows of element loads: the
+    request is reported."""
+    announce(f"NaN alone in a block dtype={dtype} V={V}")
+    B, k = 8, 2
+    wl = _custom(B, k, V, dtype=dtype, dense=False, seed=141)
+    lg = wl["logits"].float()
+    allowed = torch.ones((B, k + 1, V), dtype=torch.bool, device=DEV)
+    allowed[0:2, 1, 2048:4096] = False                # block 1 of row 1 forbidden but for one token
+    allowed[0:2, 1, 3000] = True
+    lg[0:2, 1, 3000] = float("nan")
+    lg[2:4, 0, 4096:6144] = float("-inf")              # block 2 of row 0 all -inf but one NaN
+    lg[2:4, 0, 5000] = float("nan")
+    lg[4:6, 2, 2048:4096] = float("-inf")              # the same on the last row
+    lg[4:6, 2, 2049] = float("nan")
+    wl["logits"] = lg.to(dtype).contiguous()
+    wl["bitmask"] = pack_bitmask(allowed)
+    wl["temperature"][1::2] = 0.0                     # odd requests greedy
+    wl["top_k"] = torch.tensor([0, 0, 0, 0, 50, 50, 0, 50], dtype=torch.int32, device=DEV)
+    gpu, orc = run_gpu(wl), run_oracle(wl)
+    assert all(int(orc["request_status"][b]) != 0 for b in range(6))
+    assert_parity(gpu, orc)
+
+
 def test_long_k_with_top_p_scaled():
     announce("long_k B=8 with top-k 50 and top-p 0.9")
     wl = make_workload("long_k", device=DEV, batch=8)
