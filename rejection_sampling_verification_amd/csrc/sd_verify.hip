@@ -345,6 +345,12 @@ struct RowStatsArgs {
     const int32_t *off;       // ragged: [B + 1] draft offsets, or nullptr
     const int32_t *row_req;   // ragged: [rows] request of each row
     const uint32_t *off_ok;   // ragged: 1 when the offsets are consistent
+    // ragged calls the vector sweep maps itself (no prep launch): the check
+    // and the row table it writes for the kernels after it
+    int fold, B;
+    int64_t total;            // the call's total drafts
+    int32_t *row_req_out;
+    uint32_t *off_ok_out;
     int64_t ntasks;           // rows * nchunk (chunked element kernel)
     int64_t nblk;             // rows * C (vector kernel sweep)
     int k, kp1, V, W, C, cpw, nchunk;
@@ -705,6 +711,51 @@ __device__ __forceinline__ int claimed(const SweepPlan &pl, uint32_t r) {
     return c < static_cast<uint32_t>(pl.lim - pl.kdyn) ? pl.kdyn + static_cast<int>(c) : pl.lim;
 }
 
+// Ragged calls whose offsets and rows fit in LDS: the vector sweep's
+// workgroups check the draft offsets themselves, as the prep kernel does, and
+// map rows to requests in LDS.
+constexpr int kFoldRows = 8192;   // rows (total drafts + B) at most
+constexpr int kFoldReqs = 2048;   // requests at most
+struct FoldMap {
+    int32_t off[kFoldReqs + 1];
+    uint16_t req[kFoldRows];
+};
+
+__device__ __forceinline__ FoldMap &fold_map() {
+    __shared__ FoldMap m;
+    return m;
+}
+
+// Every workgroup: the offsets into LDS, the prep kernel's check, and the
+// request of every row; workgroup 0 also writes the check and the row table
+// for the kernels after the sweep.  Returns false in every thread when the
+// offsets fail (the finalize kernel reports the call).
+__device__ bool fold_ragged(const RowStatsArgs &a) {
+    FoldMap &fm = fold_map();
+    const int B = a.B;
+    for (int j = threadIdx.x; j <= B; j += blockDim.x) fm.off[j] = a.off[j];
+    __syncthreads();
+    bool bad = threadIdx.x == 0 && (fm.off[0] != 0 || int64_t(fm.off[B]) != a.total);
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int64_t d = int64_t(fm.off[b + 1]) - int64_t(fm.off[b]);
+        bad |= d < 0 || d > a.k;
+    }
+    const bool any_bad = __syncthreads_or(bad) != 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.off_ok_out = any_bad ? 0u : 1u;
+    if (any_bad) return false;
+    // the offsets now partition rows [0, total + B): request b owns k_b + 1
+    // rows from off[b] + b
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int r0 = fm.off[b] + b, kb = fm.off[b + 1] - fm.off[b];
+        for (int i = 0; i <= kb; ++i) {
+            fm.req[r0 + i] = static_cast<uint16_t>(b);
+            if (blockIdx.x == 0) a.row_req_out[r0 + i] = b;
+        }
+    }
+    __syncthreads();
+    return true;
+}
+
 __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const SweepCursor &c) {
     SweepBlock s;
     s.gb = c.gb;
@@ -713,7 +764,14 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const S
     s.full = int64_t(s.blk + 1) * kBlock <= a.V;
     int kb;
     int64_t d0;
-    if (a.off) {
+    if (a.fold) {
+        const FoldMap &fm = fold_map();
+        s.b = __builtin_amdgcn_readfirstlane(int(fm.req[s.row]));
+        const int o0 = __builtin_amdgcn_readfirstlane(fm.off[s.b]);
+        kb = __builtin_amdgcn_readfirstlane(fm.off[s.b + 1]) - o0;
+        s.i = s.row - o0 - s.b;
+        d0 = o0;
+    } else if (a.off) {
         row_owner(a.off, a.row_req, s.row, a.kp1, s.b, s.i, kb, d0);
     } else {
         s.b = c.b;
@@ -1064,7 +1122,11 @@ __device__ __forceinline__ void sweep_claimed(const RowStatsArgs &a, int lane, c
 template <typename ET, bool MASKED, int TOPK, int POL>
 __global__ __launch_bounds__(kSweepThreads) void row_stats_vec_kernel(RowStatsArgs a) {
     zero_call_outputs(a);
-    if (a.off && uniform_load(a.off_ok) == 0u) return;  // malformed ragged call: finalize reports it
+    if (a.fold) {
+        if (!fold_ragged(a)) return;  // malformed ragged call: finalize reports it
+    } else if (a.off && uniform_load(a.off_ok) == 0u) {
+        return;
+    }
     const int lane = threadIdx.x & (kWave - 1);
     if constexpr (MASKED && sizeof(ET) == 2) {
         __shared__ uint4 keep[256];
@@ -4060,6 +4122,13 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.off = p->draft_offsets;
     ra.row_req = ragged ? row_req : nullptr;
     ra.off_ok = ragged ? off_ok : nullptr;
+    // the vector sweep checks and maps a ragged call itself when nothing
+    // before it needs the row table and the call fits its LDS
+    ra.fold = ragged && aligned && !(thresholds && !single_pass) && L.rows <= kFoldRows && B <= kFoldReqs;
+    ra.B = B;
+    ra.total = ragged ? p->total_drafts : 0;
+    ra.row_req_out = row_req;
+    ra.off_ok_out = off_ok;
     ra.bstats = reinterpret_cast<BlockStat *>(ws + L.off_bstats);
     ra.drec = reinterpret_cast<DraftRec *>(ws + L.off_drec);
     ra.tally = reinterpret_cast<unsigned long long *>(ws + L.off_tally);
@@ -4148,7 +4217,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     FinalFn k2 = bf16 ? pick_final<uint16_t>(aligned, draft_probs != nullptr, fa.split_dense != 0)
                       : pick_final<float>(aligned, draft_probs != nullptr, fa.split_dense != 0);
 
-    if (ragged) {
+    if (ragged && !ra.fold) {
         hipLaunchKernelGGL(ragged_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, p->draft_offsets, B, k,
                            p->total_drafts, row_req, off_ok);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
