@@ -3,12 +3,15 @@
 // One call runs these kernels in order on the caller's stream (those in
 // brackets only when the call needs them):
 //
-//   [ragged_prep]  ragged calls: checks the draft offsets and maps every
-//                  packed row to its request.
+//   [ragged_prep]  ragged calls with a pass before the sweep, or too large
+//                  for its LDS: checks the draft offsets and maps every
+//                  packed row to its request (otherwise the sweep's
+//                  workgroups do both themselves).
 //   [topk]         calls with top-p, and top-k calls whose rows the
 //                  single-pass selection cannot take (unaligned rows, very
 //                  large V): each top-k / top-p row's threshold tau, from a
-//                  pass over the row before the sweep.
+//                  pass over the row before the sweep (bf16 rows counted on
+//                  their raw 16-bit codes).
 //   row_stats      the sweep, the only full pass over the logits: waves claim
 //                  2048-token blocks of all rows, stream them from HBM in
 //                  16-byte loads, apply the grammar bitmask and temperature

@@ -195,3 +195,27 @@ def test_ngram_ragged_full():
     gpu, orc = run_gpu_ragged(wl, wl["max_draft"]), run_oracle_ragged(wl, wl["max_draft"])
     assert_parity_ragged(gpu, orc, off)
     assert int(gpu["counters"][0]) == int(off[-1]) and gpu["status"] == 0
+
+
+@pytest.mark.parametrize("case", ["requests", "rows"])
+def test_ragged_beyond_the_sweeps_own_mapping(case):
+    """Ragged calls with more requests (2100) or more rows (8229) than the
+    sweep maps in LDS take the prep kernel's row table; one just inside both
+    limits maps itself.  Aligned bf16 rows, no threshold pass."""
+    announce(f"ragged beyond the sweep's own mapping: {case}")
+    g = np.random.default_rng(7 if case == "requests" else 8)
+    if case == "requests":
+        ks = list(g.integers(0, 3, size=2100))
+    else:
+        ks = list(g.integers(1, 9, size=1500))    # 8229 rows with this seed
+    wl, off = _ragged(ks, 1024, dense=False, greedy_frac=0.25, seed=11 if case == "requests" else 12)
+    kmax = max(int(x) for x in ks)
+    gpu, orc = run_gpu_ragged(wl, kmax), run_oracle_ragged(wl, kmax)
+    assert_parity_ragged(gpu, orc, off)
+    rows = int(off[-1]) + len(ks)
+    assert (len(ks) > 2048) if case == "requests" else (rows > 8192)
+    # just inside both limits: 2048 requests, at most 8192 rows
+    ks2 = [3] * 2048
+    wl2, off2 = _ragged(ks2, 1024, dense=False, greedy_frac=0.25, seed=13)
+    gpu2, orc2 = run_gpu_ragged(wl2, 3), run_oracle_ragged(wl2, 3)
+    assert_parity_ragged(gpu2, orc2, off2)
