@@ -337,6 +337,7 @@ struct RowStatsArgs {
     uint64_t seed;
     const float *tau;         // [rows] top-k thresholds, or nullptr (no top-k)
     const int32_t *top_k;     // [B]: with linemax, the requests whose rows record line maxima
+    const float *top_p;       // [B] or nullptr: with linemax, requests with top-p record them too
     void *linemax;            // [rows, C * lines per block] line maxima of top-k rows, or nullptr
     BlockStat *bstats;        // [rows, C]
     DraftRec *drec;           // [rows]
@@ -788,7 +789,12 @@ __device__ __forceinline__ SweepBlock sweep_block(const RowStatsArgs &a, const S
     s.skip = !s.greedy && !(T > 0.0f && T <= FLT_MAX);  // reported by finalize
     s.c = s.greedy ? 0.0f : scale_of(T);
     s.tau = a.tau ? uniform_load(a.tau + s.row) : -INFINITY;
-    s.lines = a.linemax != nullptr && !s.greedy && uniform_load(a.top_k + s.b) > 0;
+    if (a.linemax != nullptr && !s.greedy) {
+        const float pp = a.top_p ? uniform_load(a.top_p + s.b) : 0.0f;
+        s.lines = uniform_load(a.top_k + s.b) > 0 || (pp > 0.0f && pp < 1.0f);
+    } else {
+        s.lines = false;
+    }
     s.x = s.xrel = -1;
     if (s.i < kb) {
         const int x = uniform_load(a.draft + s.dpos);
@@ -1264,7 +1270,6 @@ struct TopkShared {
     uint32_t part[kTopkThreads];  // per-thread sums of 4 bins, scanned in place
     uint32_t red[kTopkWaves];
     uint32_t found_digit, found_rank, lowest;
-    uint4 keep[256];              // masked bf16 rows: the keep-mask table
     __device__ __forceinline__ uint32_t *hist() { return bins + kTopkLead; }
 };
 
@@ -1491,12 +1496,27 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
                                                                   __builtin_bit_cast(u16x2, b)));
 }
 
+// The row's access for the selection passes.
+template <typename ET, bool ALIGNED, bool MASKED>
+__device__ __forceinline__ TopkRow<ET, ALIGNED, MASKED> topk_row(const void *logits, const uint32_t *mask,
+                                                                 int64_t row, int V, int W) {
+    TopkRow<ET, ALIGNED, MASKED> r;
+    r.rowp = reinterpret_cast<const ET *>(logits) + row * V;
+    r.mrow = MASKED ? reinterpret_cast<const uint8_t *>(mask + row * W) : nullptr;
+    r.rs = buffer_of(r.rowp, uint32_t(V) * sizeof(ET));
+    r.rm = buffer_of(MASKED ? static_cast<const void *>(r.mrow) : static_cast<const void *>(r.rowp),
+                     MASKED ? uint32_t(W) * 4u : 0u);
+    r.V = V;
+    return r;
+}
+
 // The K-th largest allowed finite logit of the row, or -inf when the row
 // holds at most K of them (see the comment above TopkArgs); also the row's
 // largest code and, for bf16 rows, whether the last histogram holds every
 // kept element (the largest code only when TRACK_MAX: a top-p cut follows).
 template <typename ET, bool ALIGNED, bool MASKED, bool TRACK_MAX>
-__device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, int K) {
+__device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkShared &sh, int K,
+                                   const uint4 *keep) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int64_t kStep = int64_t(kTopkThreads) * P;
     const int tid = threadIdx.x;
@@ -1561,7 +1581,7 @@ __device__ TopkResult select_top_k(const TopkRow<ET, ALIGNED, MASKED> &r, TopkSh
                 for (int u = 0; u < kTopkUnroll; ++u) {
                     const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
                     uint4 k = make_uint4(~0u, ~0u, ~0u, ~0u);
-                    if (MASKED) k = sh.keep[m[u]];
+                    if (MASKED) k = keep[m[u]];
                     const uint32_t kk[4] = {k.x, k.y, k.z, k.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -1940,19 +1960,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         }
         return;
     }
+    // masked bf16 rows: the keep-mask table of the raw-code pass
+    __shared__ uint4 keep[(MASKED && ALIGNED && sizeof(ET) == 2) ? 256 : 1];
     if constexpr (MASKED && ALIGNED && sizeof(ET) == 2) {
-        fill_keep_table(sh.keep);
+        fill_keep_table(keep);
         lds_barrier();
     }
-    TopkRow<ET, ALIGNED, MASKED> r;
-    r.rowp = reinterpret_cast<const ET *>(a.logits) + int64_t(row) * a.V;
-    r.mrow = MASKED ? reinterpret_cast<const uint8_t *>(a.mask + int64_t(row) * a.W) : nullptr;
-    r.rs = buffer_of(r.rowp, uint32_t(a.V) * sizeof(ET));
-    r.rm = buffer_of(MASKED ? static_cast<const void *>(r.mrow) : static_cast<const void *>(r.rowp),
-                     MASKED ? uint32_t(a.W) * 4u : 0u);
-    r.V = a.V;
+    const TopkRow<ET, ALIGNED, MASKED> r = topk_row<ET, ALIGNED, MASKED>(a.logits, a.mask, row, a.V, a.W);
     TopkResult tk{-INFINITY, 0u, 0u, false};
-    if (K > 0) tk = select_top_k<ET, ALIGNED, MASKED, TOPP>(r, sh, K);
+    if (K > 0) tk = select_top_k<ET, ALIGNED, MASKED, TOPP>(r, sh, K, keep);
     float tau = tk.tau;
     uint32_t flag = 0u;
     if constexpr (TOPP) {
@@ -2001,6 +2017,7 @@ struct LinesArgs {
     const uint32_t *mask;
     const float *temperature;
     const int32_t *top_k;
+    const float *top_p;      // [B] (the kernels that apply top-p)
     const int32_t *draft;
     const void *linemax;     // [rows, C * lines per block], per block in the sweep's lane order
     BlockStat *bstats;       // [rows, C]
@@ -2381,7 +2398,134 @@ __device__ __forceinline__ void block_stats_global(const LinesArgs &a, const Lin
     }
 }
 
-template <typename ET, bool MASKED>
+// The candidate lines' staged tokens of the single-pass selection.
+template <typename CT, int TPL>
+struct LinesStage {
+    __align__(16) CT tcodes[kCandLines * TPL];  // the candidate lines' token codes
+    uint16_t cand[kCandLines];                  // the candidate lines, ascending
+    uint32_t cmax[kCandLines];                  // each candidate's largest code
+    float lsum[kCandLines];                     // each candidate's kept mass
+};
+
+// Top-p over the staged tokens at or above tcode (what top-k keeps), with the
+// selection passes' definition and arithmetic: the largest code c whose tokens
+// at or above it hold top_p of their tempered mass, masses 2^((l - M)
+// log2(e) / T) in fp64 with M the row's largest logit (code lmax); ties at c
+// stay.  Radix passes of 8 bits over the codes sum the masses per digit into
+// `bins` (256 doubles); wave 0 picks the digit where the mass from the top
+// reaches the target (a rounding shortfall takes the lowest nonempty digit).
+// Returns the cut value and sets *flag as the passes do.  All threads call it.
+template <typename ET, typename CT>
+__device__ float topp_staged(const CT *tcodes, int ntok, uint32_t tcode, uint32_t lmax, float T, float top_p,
+                             double *bins, double *red, uint32_t *flag) {
+    constexpr int W = sizeof(ET) == 2 ? 16 : 32;
+    constexpr int NW = kLinesThreads / kWave;
+    static_assert(kLinesThreads == 256, "one bin per thread");
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+    const double cd = kLog2e / static_cast<double>(T);
+    const double mcd = static_cast<double>(value_of_code<ET>(lmax)) * cd;
+    auto mass = [&](uint32_t c) {
+        return exp2_precise_nonpos(fma(static_cast<double>(value_of_code<ET>(c)), cd, -mcd));
+    };
+    double own = 0.0;
+    for (int t = tid; t < ntok; t += kLinesThreads) {
+        const uint32_t c = tcodes[t];
+        if (c >= tcode) own += mass(c);
+    }
+    own = wave_sum_d(own);
+    if (lane == 0) red[wave] = own;
+    __syncthreads();
+    double total = 0.0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) total += red[q];
+    const double target = static_cast<double>(top_p) * total;
+    uint32_t prefix = 0u;
+    double above = 0.0, at = 0.0;
+    for (int shift = W - 8; shift >= 0; shift -= 8) {
+        bins[tid] = 0.0;
+        __syncthreads();
+        for (int t = tid; t < ntok; t += kLinesThreads) {
+            const uint32_t c = tcodes[t];
+            if (c >= tcode && (shift == W - 8 || (c >> (shift + 8)) == prefix))
+                atomicAdd(&bins[(c >> shift) & 0xffu], mass(c));
+        }
+        __syncthreads();
+        if (wave == 0) {
+            double b4[4], sl = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b4[j] = bins[4 * lane + j];
+                sl += b4[j];
+            }
+            double suf = sl;  // mass of digits 4 * lane and up
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const double o = __shfl_down(suf, d);
+                if (lane + d < kWave) suf += o;
+            }
+            const uint64_t hit = __ballot(above + suf >= target);
+            const uint64_t nonempty = __ballot(sl > 0.0);
+            // the lane of the crossing (suf falls with the lane), else the
+            // lowest nonempty lane
+            const int pick = hit ? 63 - __builtin_clzll(hit) : __builtin_ctzll(nonempty);
+            if (lane == pick) {
+                double acc = above + (suf - sl);  // mass of the digits above this lane's
+                int d = -1;
+                if (hit) {
+                    for (int j = 3; j >= 0; --j) {
+                        if (acc + b4[j] >= target) {
+                            d = j;
+                            break;
+                        }
+                        acc += b4[j];
+                    }
+                }
+                if (d < 0) {  // a rounding shortfall: the lowest nonempty digit of the lane
+                    acc = above + (suf - sl);
+                    int lowest = 3;
+                    for (int j = 0; j < 4; ++j)
+                        if (b4[j] > 0.0) {
+                            lowest = j;
+                            break;
+                        }
+                    for (int j = 3; j > lowest; --j) acc += b4[j];
+                    d = lowest;
+                }
+                red[NW] = acc;
+                red[NW + 1] = static_cast<double>(4 * lane + d);
+                red[NW + 2] = b4[d];
+            }
+        }
+        __syncthreads();
+        above = red[NW];
+        prefix = (prefix << 8) | static_cast<uint32_t>(red[NW + 1]);
+        at = red[NW + 2];
+        __syncthreads();  // red and bins are reused by the next pass
+    }
+    const double eps = kTopPFlagEps * total;
+    const double at_cut = above + at;
+    *flag = (fabs(at_cut - target) < eps || fabs(target - above) < eps) ? 1u : 0u;
+    return value_of_code<ET>(prefix);
+}
+
+// A bf16 or fp32 value's code as the line maxima hold it, and the 32-bit
+// order-preserving code of a line maximum.
+template <typename ET>
+__device__ __forceinline__ uint32_t line_code_of(float v) {
+    return sizeof(ET) == 2 ? ordered_code(v) >> 16 : ordered_code(v);
+}
+
+template <typename ET>
+__device__ __forceinline__ uint32_t code32_of_line(uint32_t c) {
+    return sizeof(ET) == 2 ? ((c << 16) | ((c & 0x8000u) ? 0u : 0xffffu)) : c;
+}
+
+// TOPP: requests with top-p too (pyshine "vLLM, part 2", "Verification": the
+// sampling constraints before the accept test): the cut over what top-k keeps,
+// from the staged candidate tokens when every candidate line is staged, else
+// by passes over the row; rows of requests with top-p alone (top-k 0) take the
+// passes and their block statistics from global memory.
+template <typename ET, bool MASKED, bool TOPP>
 __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
@@ -2398,10 +2542,19 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
     __shared__ LinesShared sh;
     __shared__ uint32_t red[2][NW][16];
     __shared__ __align__(16) uint32_t hist[kWin];
-    __shared__ __align__(16) CT tcodes[kCandLines * TPL];     // the candidate lines' token codes
-    __shared__ uint16_t cand[kCandLines];                      // the candidate lines, ascending
-    __shared__ uint32_t cmax[kCandLines];                      // each candidate's largest code
-    __shared__ float lsum[kCandLines];                         // each candidate's kept mass
+    // the staged candidates; calls with top-p lay the passes' bins over them
+    // (the passes run only where nothing is staged)
+    typedef LinesStage<CT, TPL> Stage;
+    union StageOrPasses {
+        Stage st;
+        ToppShared tp;
+    };
+    __shared__ typename std::conditional<TOPP, StageOrPasses, Stage>::type staged;
+    __shared__ double pred[NW + 3];                           // top-p's reductions
+    CT *tcodes = reinterpret_cast<Stage &>(staged).tcodes;
+    uint16_t *cand = reinterpret_cast<Stage &>(staged).cand;
+    uint32_t *cmax = reinterpret_cast<Stage &>(staged).cmax;
+    float *lsum = reinterpret_cast<Stage &>(staged).lsum;
     __shared__ uint32_t bmax[NB];                              // each block's largest kept code
     __shared__ uint8_t brun[NB][2];                            // each block's run of candidates
     __shared__ float xmass;                                    // the draft line's kept mass without it
@@ -2426,12 +2579,14 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
     }
     const float T = uniform_load(a.temperature + b);
     const int K = uniform_load(a.top_k + b);
+    const float Pp = TOPP ? uniform_load(a.top_p + b) : 0.0f;
+    const bool use_p = TOPP && Pp > 0.0f && Pp < 1.0f;
     // the row is not cut unless a cut is found below
     if (tid == 0) {
         a.tau[row] = -INFINITY;
         a.tau_flag[row] = 0u;
     }
-    if (!(T > 0.0f && T <= FLT_MAX) || K <= 0) return;
+    if (!(T > 0.0f && T <= FLT_MAX) || (K <= 0 && !use_p)) return;
     const BlockStat *st = a.bstats + row * a.C;
     bool bad = false;
     if (tid < a.C) {  // C <= NB < kLinesThreads: thread c takes block c
@@ -2475,6 +2630,42 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
     // bad rows keep the sweep's marks, which report them; rows without an
     // allowed finite token keep its (-inf, 0), which report them too
     if (anybad || lnz == 0u) return;
+    LinesRow r;
+    r.row = row;
+    r.b = b;
+    r.i = i;
+    r.x = -1;
+    if (i < kb) {
+        const int xv = uniform_load(a.draft + d0 + i);
+        if (xv >= 0 && xv < a.V) r.x = xv;
+    }
+    r.cT = scale_of(T);
+    // the top-p cut over the tokens at or above tau_k (passes over the row)
+    auto topp_passes = [&](float tauk, uint32_t *flag) -> float {
+        if constexpr (TOPP) {
+            const TopkRow<ET, true, MASKED> tr = topk_row<ET, true, MASKED>(a.logits, a.mask, row, a.V, a.W);
+            return select_top_p<ET, true, MASKED>(tr, reinterpret_cast<ToppShared &>(staged), tauk,
+                                                  code32_of_line<ET>(lmax), true, Pp, T, flag);
+        } else {
+            return tauk;
+        }
+    };
+    if (TOPP && K <= 0) {
+        // top-p alone: the cut from passes over the row, then the row's block
+        // statistics over the tokens it keeps (the sweep recorded line maxima)
+        uint32_t flag = 0u;
+        const float tp = topp_passes(-INFINITY, &flag);
+        const bool cutp = tp > -INFINITY;
+        block_stats_global<ET, MASKED>(a, r, 1u, cutp ? line_code_of<ET>(tp) : 1u);
+        if (tid == 0) {
+            a.tau_flag[row] = flag;
+            if (cutp) {
+                a.tau[row] = tp;
+                if (r.x >= 0 && !(a.drec[row].lx >= tp)) a.drec[row].lx = -INFINITY;
+            }
+        }
+        return;
+    }
     const uint32_t Ku = static_cast<uint32_t>(K);
     const uint32_t top = lmax >> KS;  // the window's first key
     int round = 1;
@@ -2528,16 +2719,6 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
             }
         }
     __syncthreads();
-    LinesRow r;
-    r.row = row;
-    r.b = b;
-    r.i = i;
-    r.x = -1;
-    if (i < kb) {
-        const int xv = uniform_load(a.draft + d0 + i);
-        if (xv >= 0 && xv < a.V) r.x = xv;
-    }
-    r.cT = scale_of(T);
     uint32_t tcode;
     bool cut;
     if (ncand <= uint32_t(kCandLines)) {
@@ -2600,6 +2781,19 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
                 else tcode = refine_low16(sh, top - pk.x, Ku, pk.y, visit_tokens);
             } else {
                 tcode = kth_largest(visit_tokens, Ku, L, lmax, red, round);
+            }
+        }
+        if (use_p) {
+            // ---- top-p over what top-k keeps, all of it staged (the window
+            // histogram is free again: its bins hold the masses)
+            const float tauk = cut ? value_of_code<ET>(tcode) : -INFINITY;
+            uint32_t flag = 0u;
+            const float tp = topp_staged<ET, CT>(tcodes, ntok, tcode, lmax, T, Pp,
+                                                 reinterpret_cast<double *>(hist), pred, &flag);
+            if (tid == 0) a.tau_flag[row] = flag;
+            if (tp > tauk) {
+                tcode = line_code_of<ET>(tp);
+                cut = true;
             }
         }
         // ---- 5. the row's block statistics over the kept tokens: each
@@ -2670,6 +2864,16 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
         tcode = tau_code_global<ET, MASKED>(a, sh, row, L, Ku);
         cut = tcode != 0u;
         if (!cut) tcode = 1u;  // no cut: every allowed finite token (then L = 1)
+        if (use_p) {
+            const float tauk = cut ? value_of_code<ET>(tcode) : -INFINITY;
+            uint32_t flag = 0u;
+            const float tp = topp_passes(tauk, &flag);
+            if (tid == 0) a.tau_flag[row] = flag;
+            if (tp > tauk) {
+                tcode = line_code_of<ET>(tp);
+                cut = true;
+            }
+        }
         block_stats_global<ET, MASKED>(a, r, L, tcode);
     }
     if (tid == 0 && cut) {
@@ -3922,8 +4126,9 @@ using TopkFn = void (*)(TopkArgs);
 using LinesFn = void (*)(LinesArgs);
 
 template <typename ET>
-LinesFn pick_topk_lines(bool masked) {
-    return masked ? topk_lines_kernel<ET, true> : topk_lines_kernel<ET, false>;
+LinesFn pick_topk_lines(bool masked, bool topp) {
+    if (topp) return masked ? topk_lines_kernel<ET, true, true> : topk_lines_kernel<ET, false, true>;
+    return masked ? topk_lines_kernel<ET, true, false> : topk_lines_kernel<ET, false, false>;
 }
 using DenseFn = void (*)(FinalArgs);
 
@@ -4112,12 +4317,14 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     ra.q = draft_probs;
     ra.seed = seed;
     const bool thresholds = p->top_k != nullptr || p->top_p != nullptr;
-    // top-k without top-p on aligned rows: the threshold is found after the
-    // sweep from its line maxima, with no second pass over the rows
-    const bool single_pass = p->top_k != nullptr && p->top_p == nullptr && aligned && lines_fit(p);
+    // top-k (with or without top-p) on aligned rows: the thresholds are found
+    // after the sweep from its line maxima, with no second pass over the rows
+    // that top-k cuts
+    const bool single_pass = p->top_k != nullptr && aligned && lines_fit(p);
     float *tau_arr = reinterpret_cast<float *>(ws + L.off_tau);
     ra.tau = (thresholds && !single_pass) ? tau_arr : nullptr;
     ra.top_k = p->top_k;
+    ra.top_p = single_pass ? p->top_p : nullptr;
     ra.linemax = single_pass ? static_cast<void *>(ws + L.off_linemax) : nullptr;
     uint32_t *tau_flag = reinterpret_cast<uint32_t *>(ws + L.off_tauflag);
     int32_t *row_req = reinterpret_cast<int32_t *>(ws + L.off_rowreq);
@@ -4258,6 +4465,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         la.mask = ra.mask;
         la.temperature = temperature;
         la.top_k = p->top_k;
+        la.top_p = p->top_p;
         la.draft = draft_token_ids;
         la.linemax = ra.linemax;
         la.bstats = ra.bstats;
@@ -4272,7 +4480,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         la.V = V;
         la.W = L.W;
         la.C = L.C;
-        const LinesFn k5 = bf16 ? pick_topk_lines<uint16_t>(masked) : pick_topk_lines<float>(masked);
+        const bool topp = p->top_p != nullptr;
+        const LinesFn k5 = bf16 ? pick_topk_lines<uint16_t>(masked, topp) : pick_topk_lines<float>(masked, topp);
         hipLaunchKernelGGL(k5, dim3(static_cast<unsigned>(L.rows)), dim3(kLinesThreads), 0, stream, la);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }

@@ -260,6 +260,25 @@ def test_top_p_after_top_k_paths():
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+def test_top_p_after_top_k_over_spread_magnitudes():
+    """Top-p after top-k where what top-k keeps spans many binades (the cut
+    then comes from passes over the row, not the staged candidates' window),
+    with more candidate lines than LDS stages, beside top-p alone (top-k 0)."""
+    announce("top-p after top-k over widely spread magnitudes")
+    B, k, V = 8, 2, 20000
+    g = torch.Generator(device=DEV)
+    g.manual_seed(15)
+    for dtype in (torch.bfloat16, torch.float32):
+        mag = torch.exp(torch.rand((B, k + 1, V), generator=g, device=DEV) * 40 - 20)
+        lg = (mag * torch.sign(torch.randn((B, k + 1, V), generator=g, device=DEV))).to(dtype).contiguous()
+        x = torch.randint(0, V, (B, k), generator=g, device=DEV).to(torch.int32)
+        wl = {"name": "custom", "logits": lg, "draft_token_ids": x, "draft_probs": None,
+              "bitmask": None, "temperature": torch.full((B,), 20.0, device=DEV),
+              "top_k": torch.tensor([40, 3000, 15000, 0, 40, 3000, 15000, 0], dtype=torch.int32, device=DEV),
+              "top_p": torch.tensor([0.9, 0.9, 0.99, 0.9, 0.5, 0.3, 0.999, 0.7], device=DEV), "seed": 79}
+        assert_parity(run_gpu(wl), run_oracle(wl))
+
+
 def test_top_p_extreme_temperatures_masks_and_errors():
     """Top-p at temperatures that push masses to underflow or make them all
     alike, on masked rows, beside greedy requests and requests in error."""
@@ -276,17 +295,20 @@ def test_top_p_extreme_temperatures_masks_and_errors():
         assert gpu["status"] & oracle.verify.ST_TEMPERATURE
 
 
+@pytest.mark.parametrize("V", [40960, 270336])
 @pytest.mark.parametrize("masked", [False, True])
-def test_two_pass_selection_on_raw_codes(masked):
-    """bf16 rows, 16-byte aligned, of a call with top-p: the two-pass
-    selection counts them on raw 16-bit codes and takes element by element
-    the batches with an allowed NaN or +inf and the windows that start at the
-    bottom of the code range.  Rows with -inf among the values, an allowed
-    NaN of either sign or +inf (reported), a NaN at a forbidden token, the
-    threshold among the most negative finite values, no allowed finite value,
-    and exactly K allowed finite values."""
-    announce(f"two-pass selection on raw bf16 codes masked={masked}")
-    B, k, V = 8, 2, 40960
+def test_two_pass_selection_on_raw_codes(masked, V):
+    """bf16 rows, 16-byte aligned, of a call with top-k 50 and top-p.  At
+    V=40960 the single-pass selection takes both cuts from the line maxima
+    and the staged candidates; at V=270336 (more lines than it holds) the
+    two-pass selection counts the rows on raw 16-bit codes and takes element
+    by element the batches with an allowed NaN or +inf and the windows that
+    start at the bottom of the code range.  Rows with -inf among the values,
+    an allowed NaN of either sign or +inf (reported), a NaN at a forbidden
+    token, the threshold among the most negative finite values, no allowed
+    finite value, and exactly K allowed finite values."""
+    announce(f"top-k and top-p selection on bf16 rows masked={masked} V={V}")
+    B, k = 8, 2
     wl = _custom(B, k, V, dense=False, seed=131 + masked)
     g = torch.Generator(device=DEV)
     g.manual_seed(132 + masked)
