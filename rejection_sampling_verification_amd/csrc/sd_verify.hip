@@ -2088,7 +2088,7 @@ __device__ __forceinline__ uint3 pick_digit(LinesShared &sh, int hb, uint32_t K,
 // than K.  Wave 0 scans 16 bins per lane with a shuffle prefix over the
 // lanes; one barrier publishes the result, after which the bins are cleared
 // (the next use comes after another barrier).
-__device__ __forceinline__ uint2 window_pick(LinesShared &sh, uint32_t *hist, uint32_t K) {
+__device__ __forceinline__ uint2 window_pick(LinesShared &sh, uint32_t *hist, uint32_t K, bool clear = true) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     if (wave_id() == 0) {
         uint32_t c[16];
@@ -2128,7 +2128,7 @@ __device__ __forceinline__ uint2 window_pick(LinesShared &sh, uint32_t *hist, ui
     }
     __syncthreads();
     const uint2 r = make_uint2(sh.digit, sh.above);
-    reinterpret_cast<uint4 *>(hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    if (clear) reinterpret_cast<uint4 *>(hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
     return r;
 }
 
@@ -2508,6 +2508,100 @@ __device__ float topp_staged(const CT *tcodes, int ntok, uint32_t tcode, uint32_
     return value_of_code<ET>(prefix);
 }
 
+// Top-p over what top-k keeps, read off the staged tokens' window histogram
+// (bf16 rows whose K-th largest lies in the window): bin d counts the kept
+// tokens of code top - d, and a bf16 bin holds one value, so its mass is its
+// count times that value's mass 2^((l - M) log2(e) / T) (fp64, the selection
+// passes' arithmetic); top-k keeps bins 0..dk.  The cut is the first bin from
+// the top at which the mass reaches top_p of the kept total, the owning
+// thread's last kept bin on a rounding shortfall.  Returns the cut's code and
+// sets *flag as the passes do.  All threads call it; hist is only read.
+__device__ uint32_t topp_window_bf16(const uint32_t *hist, uint32_t dk, uint32_t top, float T, float top_p,
+                                     double *red, uint32_t *flag) {
+    constexpr int NW = kLinesThreads / kWave;
+    static_assert(kWin == 4 * kLinesThreads, "four bins per thread");
+    __shared__ uint32_t first[NW];
+    __shared__ uint32_t dsel;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+    const double cd = kLog2e / static_cast<double>(T);
+    const double mcd = static_cast<double>(bf16_value_of_digit(top)) * cd;
+    const uint4 q = reinterpret_cast<const uint4 *>(hist)[tid];
+    const uint32_t n[4] = {q.x, q.y, q.z, q.w};
+    double m[4], s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t d = 4u * uint32_t(tid) + uint32_t(j);
+        m[j] = (n[j] != 0u && d <= dk)
+                   ? static_cast<double>(n[j]) *
+                         exp2_precise_nonpos(fma(static_cast<double>(bf16_value_of_digit(top - d)), cd, -mcd))
+                   : 0.0;
+        s += m[j];
+    }
+    double pre = s;  // inclusive prefix over the threads (bins by descending value)
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(pre, o);
+        if (lane >= o) pre += t;
+    }
+    if (lane == kWave - 1) red[wave] = pre;
+    __syncthreads();
+    double before = 0.0, total = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const double t = red[w];
+        if (w < wave) before += t;
+        total += t;
+    }
+    pre += before;
+    const double target = static_cast<double>(top_p) * total;
+    const uint64_t hit = __ballot(pre >= target);
+    if (lane == 0) first[wave] = hit ? static_cast<uint32_t>(__builtin_ctzll(hit)) : uint32_t(kWave);
+    __syncthreads();
+    int owner = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        if (owner < 0 && first[w] < uint32_t(kWave)) owner = w * kWave + static_cast<int>(first[w]);
+    if (tid == (owner >= 0 ? owner : static_cast<int>(dk / 4u))) {
+        double acc = pre - s, at = 0.0;
+        int pick = -1;
+        if (owner >= 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (pick < 0 && m[j] > 0.0) {
+                    if (acc + m[j] >= target) {
+                        pick = j;
+                        at = m[j];
+                    } else {
+                        acc += m[j];
+                    }
+                }
+            }
+        }
+        if (pick < 0) {  // a rounding shortfall: this thread's last kept bin
+            acc = pre - s;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n[j] != 0u && 4u * uint32_t(tid) + uint32_t(j) <= dk) pick = j;
+            if (pick < 0) pick = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < pick) acc += m[j];
+                if (j == pick) at = m[j];
+            }
+        }
+        red[NW] = acc;
+        red[NW + 1] = at;
+        dsel = 4u * uint32_t(tid) + uint32_t(pick);
+    }
+    __syncthreads();
+    const double above = red[NW], at = red[NW + 1];
+    const uint32_t d = dsel;
+    const double eps = kTopPFlagEps * total;
+    *flag = (fabs(above + at - target) < eps || fabs(target - above) < eps) ? 1u : 0u;
+    __syncthreads();  // red, first and dsel are reused
+    return top - d;
+}
+
 // A bf16 or fp32 value's code as the line maxima hold it, and the 32-bit
 // order-preserving code of a line maximum.
 template <typename ET>
@@ -2775,7 +2869,8 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
         if (!cut) {
             tcode = 1u;
         } else {
-            const uint2 pk = window_pick(sh, hist, Ku);
+            // with top-p on bf16 rows the counts stay for its cut
+            const uint2 pk = window_pick(sh, hist, Ku, !(BF && use_p));
             if (pk.x < uint32_t(kWin)) {
                 if constexpr (BF) tcode = top - pk.x;
                 else tcode = refine_low16(sh, top - pk.x, Ku, pk.y, visit_tokens);
@@ -2784,12 +2879,17 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
             }
         }
         if (use_p) {
-            // ---- top-p over what top-k keeps, all of it staged (the window
-            // histogram is free again: its bins hold the masses)
+            // ---- top-p over what top-k keeps: from the window histogram's
+            // counts when the cut lies in it (bf16), else over the staged
+            // tokens (the histogram's bins then hold their masses)
             const float tauk = cut ? value_of_code<ET>(tcode) : -INFINITY;
             uint32_t flag = 0u;
-            const float tp = topp_staged<ET, CT>(tcodes, ntok, tcode, lmax, T, Pp,
-                                                 reinterpret_cast<double *>(hist), pred, &flag);
+            float tp;
+            if (BF && cut && top - tcode < uint32_t(kWin))
+                tp = value_of_code<ET>(topp_window_bf16(hist, top - tcode, top, T, Pp, pred, &flag));
+            else
+                tp = topp_staged<ET, CT>(tcodes, ntok, tcode, lmax, T, Pp, reinterpret_cast<double *>(hist),
+                                         pred, &flag);
             if (tid == 0) a.tau_flag[row] = flag;
             if (tp > tauk) {
                 tcode = line_code_of<ET>(tp);
