@@ -508,7 +508,7 @@ def main():
 
     import torch
     import rejection_sampling_verification_amd as sdv
-    from workloads import algorithmic_bytes, make_workload
+    from workloads import algorithmic_bytes, make_workload, residual_q_values
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -599,9 +599,7 @@ def main():
     vd = sdv.Verifier(B, k, V, lg.dtype, dev, debug=True, **vkw)
     r = vd(lg, *call_args, **kw)
     torch.cuda.synchronize()
-    kb = (wl["draft_offsets"][1:] - wl["draft_offsets"][:-1]) if ragged else k
-    n_res = int((r.out_num_accepted < kb).sum().item()) if wl["draft_probs"] is not None else 0
-    algo = algorithmic_bytes(wl, n_res)
+    algo = algorithmic_bytes(wl, residual_q_values(wl, r.out_num_accepted))
     flags = [int(f) for f in r.flags.cpu().tolist()]
 
     ceiling = copy_ceiling_gbps()

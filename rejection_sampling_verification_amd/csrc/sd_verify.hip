@@ -2024,6 +2024,8 @@ struct LinesArgs {
     DraftRec *drec;          // [rows]
     float *tau;              // [rows], written for every row
     uint32_t *tau_flag;      // [rows], written for every row (0: no top-p here)
+    uint16_t *klist;         // dense q: [rows, kCandLines] the lines holding a kept token, ascending
+    uint32_t *kcount;        // dense q: [rows] their number, kNoLineList when not listed; or nullptr
     const int32_t *off;      // ragged: draft offsets, or nullptr
     const int32_t *row_req;  // ragged: request of each row
     const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
@@ -2034,6 +2036,7 @@ struct LinesArgs {
 constexpr int kLinesThreads = 256;
 constexpr int kLinesMax = 4096;   // lines of a row, 16 per thread (bf16 V <= 262144, fp32 V <= 131072)
 constexpr int kCandLines = 128;   // candidate lines whose tokens are staged in LDS
+constexpr uint32_t kNoLineList = 0xffffffffu;  // a row whose kept tokens are not listed by line
 constexpr int kWin = 1024;        // keys in the window histogram
 
 struct LinesShared {
@@ -2675,10 +2678,12 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
     const int K = uniform_load(a.top_k + b);
     const float Pp = TOPP ? uniform_load(a.top_p + b) : 0.0f;
     const bool use_p = TOPP && Pp > 0.0f && Pp < 1.0f;
-    // the row is not cut unless a cut is found below
+    // the row is not cut unless a cut is found below, and its kept tokens are
+    // not listed unless the staged path lists them
     if (tid == 0) {
         a.tau[row] = -INFINITY;
         a.tau_flag[row] = 0u;
+        if (a.kcount) a.kcount[row] = kNoLineList;
     }
     if (!(T > 0.0f && T <= FLT_MAX) || (K <= 0 && !use_p)) return;
     const BlockStat *st = a.bstats + row * a.C;
@@ -2960,6 +2965,18 @@ __global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) 
             a.bstats[r.row * a.C + c] = out;
             if (has_x) a.drec[r.row].sx = sx;
         }
+        // ---- 6. the lines holding a kept token, ascending (dense q): a
+        // residual max(p - q, 0) drawn from this row is zero elsewhere
+        if (a.kcount != nullptr && wave < 2) {  // ncand <= 128: two waves cover the candidates
+            const auto kept = [&](int s) { return s < int(ncand) && cmax[s] >= tcode; };
+            const uint64_t b0 = __ballot(kept(lane)), b1 = __ballot(kept(kWave + lane));
+            const int s = wave * kWave + lane;
+            const uint64_t bw = wave == 0 ? b0 : b1;
+            const uint32_t pos = (wave == 0 ? 0u : uint32_t(__popcll(b0))) +
+                                 uint32_t(__popcll(bw & ((1ull << lane) - 1ull)));
+            if (kept(s)) a.klist[row * kCandLines + pos] = cand[s];
+            if (tid == 0) a.kcount[row] = uint32_t(__popcll(b0) + __popcll(b1));
+        }
     } else {
         tcode = tau_code_global<ET, MASKED>(a, sh, row, L, Ku);
         cut = tcode != 0u;
@@ -3027,6 +3044,8 @@ struct FinalArgs {
     DenseJob *jobs;    // [B] dense q only
     double *wmass;     // [B, C] dense q only: residual mass per block
     int split_dense;   // dense q: 1 = residual masses by the grid-wide kernels
+    const uint16_t *klist;   // dense q after the single-pass selection: [rows, kCandLines], or nullptr
+    const uint32_t *kcount;  // [rows]: listed lines, kNoLineList when a row's are not listed
     const int32_t *off;      // ragged: [B + 1] draft offsets, or nullptr
     const uint32_t *off_ok;  // ragged: 1 when the offsets are consistent
     uint32_t *sweep;         // the row-statistics sweep's claim counters, reset here
@@ -3146,6 +3165,95 @@ struct DenseSlab {  // one wave's share of a block: P logits and P q values per 
         return wave_sum_d(static_cast<double>(acc));
     }
 };
+
+// Residual masses W_c of a row whose kept tokens lie in nl listed lines (the
+// single-pass selection's list): max(p - q, 0) is zero wherever p is, so only
+// those lines can add to W_c and every other block's W_c is zero.  Eight
+// threads take a line, P tokens each (every listed line's loads in flight at
+// once: at most 128 lines, two per thread); each sums its tokens in fp32, the
+// line's eight sums meet in fp64, and each block adds its lines in list
+// order.  lsum: nl doubles, lline: nl ints of LDS.  All threads call it;
+// rows are 16-byte aligned (the single pass takes no others).
+template <typename ET>
+__device__ void sparse_block_masses(const FinalArgs &a, int64_t row, const float *qrow, uint32_t nl, float c,
+                                    float M, double S, float tau, double *Wout, double *lsum, int *lline) {
+    constexpr int P = Logit<ET>::kPer16;
+    static_assert(kCandLines * 8 <= 2 * kFinalThreads, "two line groups per thread");
+    const int tid = threadIdx.x, C = a.C, V = a.V;
+    const float invS = static_cast<float>(1.0 / S);
+    const ET *rowp = reinterpret_cast<const ET *>(a.logits) + row * V;
+    const uint8_t *mb = a.mask ? reinterpret_cast<const uint8_t *>(a.mask + row * a.W) : nullptr;
+    const uint16_t *list = a.klist + row * kCandLines;
+    for (int cb = tid; cb < C; cb += kFinalThreads) Wout[cb] = 0.0;
+    int line[2];
+    bool has[2];
+    uint4 lw[2];
+    float qv[2][P];
+    uint32_t bits[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = tid + u * kFinalThreads;
+        has[u] = t < int(nl) * 8;
+        line[u] = has[u] ? int(list[t >> 3]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t tok = line_token<ET>(line[u]) + ((tid + u * kFinalThreads) & 7) * P;
+        has[u] = has[u] && tok < V;
+        lw[u] = make_uint4(0u, 0u, 0u, 0u);
+        bits[u] = 0u;
+#pragma unroll
+        for (int e = 0; e < P; ++e) qv[u][e] = 0.0f;
+        if (has[u]) {
+            lw[u] = *reinterpret_cast<const uint4 *>(rowp + tok);
+#pragma unroll
+            for (int h = 0; h < P / 4; ++h) {
+                const float4 f = *reinterpret_cast<const float4 *>(qrow + tok + 4 * h);
+                qv[u][4 * h] = f.x;
+                qv[u][4 * h + 1] = f.y;
+                qv[u][4 * h + 2] = f.z;
+                qv[u][4 * h + 3] = f.w;
+            }
+            bits[u] = 0xffu;
+            if (mb != nullptr) {
+                const uint32_t byte = mb[tok >> 3];
+                bits[u] = (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float lv[P];
+        Logit<ET>::unpack(lw[u], lv);
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const bool live = ((bits[u] >> e) & 1u) && lv[e] > -INFINITY && !(lv[e] < tau);
+            const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[e], c, -M)) * invS : 0.0f;
+            acc += live ? fmaxf(p - qv[u][e], 0.0f) : 0.0f;
+        }
+        double d = static_cast<double>(acc);  // the line's eight sums, lanes 8j .. 8j + 7
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 4);
+        const int t = tid + u * kFinalThreads;
+        if ((t & 7) == 0 && t < int(nl) * 8) {
+            lsum[t >> 3] = d;
+            lline[t >> 3] = line[u];
+        }
+    }
+    lds_barrier();
+    constexpr int LPB = (kBlock / (kWave * P)) * 8;
+    // each block's run of lines, summed in list order by the thread at its start
+    for (int i = tid; i < int(nl); i += kFinalThreads) {
+        const int cb = lline[i] / LPB;
+        if (i == 0 || lline[i - 1] / LPB != cb) {
+            double w = 0.0;
+            for (int j = i; j < int(nl) && lline[j] / LPB == cb; ++j) w += lsum[j];
+            Wout[cb] = w;
+        }
+    }
+}
 
 template <typename ET, bool ALIGNED>
 __device__ void dense_block_masses(const ET *rowp, const uint32_t *mrow, const float *qrow, int V,
@@ -3775,7 +3883,9 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     __shared__ FinalShared sh;
-    extern __shared__ double sW[];  // dense q, short rows: per-block residual mass [C]
+    // dense q, short rows or listed lines: per-block residual mass [C]; with
+    // listed lines also their sums [kCandLines] and indices [kCandLines]
+    extern __shared__ double sW[];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const ReqGeom geo = req_geom(a.off, a.off_ok, b, a.k);
@@ -3936,7 +4046,19 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
             double wdense = 1.0;  // the winning block's residual mass
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
-            if (DENSE && SPLIT && mode == kModeDense) {
+            // a row whose kept tokens the single-pass selection listed by
+            // line: its residual masses come from those lines alone, here
+            uint32_t nl = kNoLineList;
+            if (DENSE && mode == kModeDense && a.kcount != nullptr) nl = uniform_load(a.kcount + geo.row0 + n);
+            const bool listed = DENSE && nl != kNoLineList;
+            if (listed) {
+                const int64_t row = geo.row0 + n;
+                sparse_block_masses<ET>(a, row, qrow, nl, c, sh.M[n], sh.S[n], a.tau ? a.tau[row] : -INFINITY, sW,
+                                        sW + C, reinterpret_cast<int *>(sW + C + kCandLines));
+                lds_barrier();
+                l1 = residual_level1([&](int, int cb) { return sW[cb]; }, C, key, b, n, &wdense);
+            }
+            if (DENSE && SPLIT && mode == kModeDense && !listed) {
                 // left to the residual kernels; -1 stands in until they write y
                 if (tid == 0) {
                     DenseJob j;
@@ -3953,7 +4075,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 }
                 deferred = true;
             }
-            if (DENSE && !SPLIT && mode == kModeDense) {
+            if (DENSE && !SPLIT && mode == kModeDense && !listed) {
                 const int64_t row = geo.row0 + n;
                 dense_block_masses<ET, ALIGNED>(
                     reinterpret_cast<const ET *>(a.logits) + row * V,
@@ -3973,7 +4095,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
                 const int2 r2 =
                     level2<ET, ALIGNED>(a, sh, b, n, geo.row0 + n, n < k ? sh.X[n] : -1, l1.c, mode, c,
                                         invT, qrow, sh.staged_c == l1.c, attempt,
-                                        (DENSE && !SPLIT && mode == kModeDense) ? wdense : 1.0);
+                                        (DENSE && (listed || !SPLIT) && mode == kModeDense) ? wdense : 1.0);
                 if (r2.x >= 0) {
                     y = r2.x;
                     fg = l1.flag + r2.y;
@@ -4295,7 +4417,7 @@ struct Layout {
     int64_t rows;
     int C, W, nchunk;
     size_t off_sweep, off_bstats, off_drec, off_tau, off_tauflag, off_jobs, off_wmass, off_rowreq, off_offok, off_tally,
-        off_linemax, total;
+        off_linemax, off_klist, off_kcount, total;
     int nslot;
 };
 
@@ -4340,7 +4462,11 @@ inline Layout layout_of(const sd_params *p) {
     const size_t line_bytes = lines_fit(p) ? size_t(L.rows) * L.C *
                                                  (p->logits_dtype == SD_DTYPE_BF16 ? kBlock / 64 * 2 : kBlock / 32 * 4)
                                            : 0;
-    L.total = L.off_linemax + align256(line_bytes);
+    L.off_klist = L.off_linemax + align256(line_bytes);
+    // with them, each row's list of the lines that hold a kept token
+    const size_t nlist = lines_fit(p) ? size_t(L.rows) : 0;
+    L.off_kcount = L.off_klist + align256(nlist * kCandLines * sizeof(uint16_t));
+    L.total = L.off_kcount + align256(nlist * sizeof(uint32_t));
     return L;
 }
 
@@ -4484,6 +4610,12 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     fa.off_ok = ra.off_ok;
     fa.jobs = reinterpret_cast<DenseJob *>(ws + L.off_jobs);
     fa.wmass = reinterpret_cast<double *>(ws + L.off_wmass);
+    // dense q after the single-pass selection: the rows' kept-line lists
+    const bool listed = draft_probs != nullptr && single_pass;
+    uint16_t *klist = listed ? reinterpret_cast<uint16_t *>(ws + L.off_klist) : nullptr;
+    uint32_t *kcount = listed ? reinterpret_cast<uint32_t *>(ws + L.off_kcount) : nullptr;
+    fa.klist = klist;
+    fa.kcount = kcount;
     // Long rows: the residual masses of the rejected rows are summed by a
     // grid over (request, block); short rows are summed inside the finalize
     // kernel, which saves two launches.
@@ -4572,6 +4704,8 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         la.drec = ra.drec;
         la.tau = tau_arr;
         la.tau_flag = tau_flag;
+        la.klist = klist;
+        la.kcount = kcount;
         la.off = ra.off;
         la.row_req = ra.row_req;
         la.off_ok = ra.off_ok;
@@ -4585,7 +4719,10 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
         hipLaunchKernelGGL(k5, dim3(static_cast<unsigned>(L.rows)), dim3(kLinesThreads), 0, stream, la);
         if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     }
-    const size_t dyn_lds = (draft_probs && !fa.split_dense) ? size_t(L.C) * sizeof(double) : 0;
+    const size_t dyn_lds =
+        (draft_probs && (!fa.split_dense || listed))
+            ? size_t(L.C) * sizeof(double) + (listed ? size_t(kCandLines) * (sizeof(double) + sizeof(int)) : 0)
+            : 0;
     hipLaunchKernelGGL(k2, dim3(B), dim3(kFinalThreads), dyn_lds, stream, fa);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
     if (fa.split_dense) {

@@ -233,13 +233,43 @@ def to_numpy(wl, requests=None):
             for key, v in wl.items()}
 
 
-def algorithmic_bytes(wl, n_residual_rows=None):
+def algorithmic_bytes(wl, residual_q=0):
+    """Bytes the method has to move for one call: every logit once, every mask
+    word once, the q values a residual draw depends on (residual_q of them in
+    all: the whole q row of a rejected position without a top-k cut, only the
+    kept tokens' values with one, since max(p - q, 0) is zero wherever the cut
+    sets p to zero), the q gathers at the drafts, the draft ids, temperatures
+    and outputs."""
     if "draft_offsets" in wl:
-        return _algorithmic_bytes_ragged(wl, n_residual_rows)
-    return _algorithmic_bytes_uniform(wl, n_residual_rows)
+        return _algorithmic_bytes_ragged(wl, residual_q)
+    return _algorithmic_bytes_uniform(wl, residual_q)
 
 
-def _algorithmic_bytes_ragged(wl, n_residual_rows=None):
+def residual_q_values(wl, num_accepted):
+    """The q values the residual draws of one call depend on: for each sampling
+    request (temperature > 0) that rejected a draft, V without a top-k cut,
+    else its top-k (the kept tokens).  Zero for one-hot drafts."""
+    if wl["draft_probs"] is None:
+        return 0
+    import numpy as np
+    T = wl["temperature"].cpu().numpy()
+    nacc = np.asarray(num_accepted.cpu().numpy() if hasattr(num_accepted, "cpu") else num_accepted)
+    if "draft_offsets" in wl:
+        off = wl["draft_offsets"].cpu().numpy()
+        kb = off[1:] - off[:-1]
+        V = wl["logits"].shape[1]
+    else:
+        kb = np.full(T.shape, wl["logits"].shape[1] - 1)
+        V = wl["logits"].shape[2]
+    rejected = (nacc >= 0) & (nacc < kb) & (T > 0)
+    per = np.full(T.shape, V, dtype=np.int64)
+    if wl.get("top_k") is not None:
+        K = wl["top_k"].cpu().numpy().astype(np.int64)
+        per = np.where(K > 0, np.minimum(K, V), V)
+    return int(per[rejected].sum())
+
+
+def _algorithmic_bytes_ragged(wl, residual_q=0):
     logits = wl["logits"]
     rows, V = logits.shape
     B = wl["draft_offsets"].shape[0] - 1
@@ -248,16 +278,12 @@ def _algorithmic_bytes_ragged(wl, n_residual_rows=None):
     if wl["bitmask"] is not None:
         total += wl["bitmask"].numel() * 4
     if wl["draft_probs"] is not None:
-        total += T * 4 + int(n_residual_rows or 0) * V * 4
+        total += T * 4 + int(residual_q) * 4
     total += T * 4 + B * 4 + rows * 4 + B * 4
     return total
 
 
-def _algorithmic_bytes_uniform(wl, n_residual_rows=None):
-    """Bytes the method has to move for one call: every logit once, every mask
-    word once, one draft-probability row per residual draw (dense q, no top-k;
-    n_residual_rows = requests that rejected a draft), the q gathers at the
-    drafts, the draft ids, temperatures and outputs."""
+def _algorithmic_bytes_uniform(wl, residual_q=0):
     logits = wl["logits"]
     B, kp1, V = logits.shape
     k = kp1 - 1
@@ -265,9 +291,7 @@ def _algorithmic_bytes_uniform(wl, n_residual_rows=None):
     if wl["bitmask"] is not None:
         total += wl["bitmask"].numel() * 4
     if wl["draft_probs"] is not None:
-        total += B * k * 4
-        if n_residual_rows:
-            total += int(n_residual_rows) * V * 4
+        total += B * k * 4 + int(residual_q) * 4
     total += B * k * 4 + B * 4 + B * kp1 * 4 + B * 4
     return total
 
