@@ -3166,92 +3166,103 @@ struct DenseSlab {  // one wave's share of a block: P logits and P q values per 
     }
 };
 
-// Residual masses W_c of a row whose kept tokens lie in nl listed lines (the
-// single-pass selection's list): max(p - q, 0) is zero wherever p is, so only
-// those lines can add to W_c and every other block's W_c is zero.  Eight
-// threads take a line, P tokens each (every listed line's loads in flight at
-// once: at most 128 lines, two per thread); each sums its tokens in fp32, the
-// line's eight sums meet in fp64, and each block adds its lines in list
-// order.  lsum: nl doubles, lline: nl ints of LDS.  All threads call it;
-// rows are 16-byte aligned (the single pass takes no others).
+// Residual masses W_c of a row from its lines (128-byte runs of the sweep's
+// lane order, 8 groups of P tokens): with a list (the single-pass
+// selection's lines holding a kept token, nl of them) only those lines, since
+// max(p - q, 0) is zero wherever p is and every other block's W_c is zero;
+// without one (nl = kNoLineList) every line of the row, kCandLines at a time
+// (a chunk covers whole blocks).  Eight threads take a line, P tokens each
+// (a chunk's loads all in flight at once, two groups per thread); each sums
+// its tokens in fp32, the line's eight sums meet in fp64, and each block adds
+// its lines in order.  lsum: kCandLines doubles, lline: kCandLines ints of
+// LDS.  All threads call it; rows are 16-byte aligned (the single pass takes
+// no others).
 template <typename ET>
-__device__ void sparse_block_masses(const FinalArgs &a, int64_t row, const float *qrow, uint32_t nl, float c,
-                                    float M, double S, float tau, double *Wout, double *lsum, int *lline) {
+__device__ void line_block_masses(const FinalArgs &a, int64_t row, const float *qrow, uint32_t nl, float c,
+                                  float M, double S, float tau, double *Wout, double *lsum, int *lline) {
     constexpr int P = Logit<ET>::kPer16;
+    constexpr int LPB = (kBlock / (kWave * P)) * 8;
     static_assert(kCandLines * 8 <= 2 * kFinalThreads, "two line groups per thread");
+    static_assert(kCandLines % LPB == 0, "a chunk of lines covers whole blocks");
     const int tid = threadIdx.x, C = a.C, V = a.V;
     const float invS = static_cast<float>(1.0 / S);
     const ET *rowp = reinterpret_cast<const ET *>(a.logits) + row * V;
     const uint8_t *mb = a.mask ? reinterpret_cast<const uint8_t *>(a.mask + row * a.W) : nullptr;
+    const bool listed = nl != kNoLineList;
     const uint16_t *list = a.klist + row * kCandLines;
+    const int total = listed ? int(nl) : C * LPB;
     for (int cb = tid; cb < C; cb += kFinalThreads) Wout[cb] = 0.0;
-    int line[2];
-    bool has[2];
-    uint4 lw[2];
-    float qv[2][P];
-    uint32_t bits[2];
+    if (total == 0) lds_barrier();  // (each chunk ends with one)
+    for (int base = 0; base < total; base += kCandLines) {
+        const int n = min(kCandLines, total - base);  // lines of this chunk
+        int line[2];
+        bool has[2];
+        uint4 lw[2];
+        float qv[2][P];
+        uint32_t bits[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int t = tid + u * kFinalThreads;
-        has[u] = t < int(nl) * 8;
-        line[u] = has[u] ? int(list[t >> 3]) : 0;
-    }
+        for (int u = 0; u < 2; ++u) {
+            const int t = tid + u * kFinalThreads;
+            has[u] = t < n * 8;
+            line[u] = !has[u] ? 0 : (listed ? int(list[t >> 3]) : base + (t >> 3));
+        }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int64_t tok = line_token<ET>(line[u]) + ((tid + u * kFinalThreads) & 7) * P;
-        has[u] = has[u] && tok < V;
-        lw[u] = make_uint4(0u, 0u, 0u, 0u);
-        bits[u] = 0u;
+        for (int u = 0; u < 2; ++u) {
+            const int64_t tok = line_token<ET>(line[u]) + ((tid + u * kFinalThreads) & 7) * P;
+            has[u] = has[u] && tok < V;
+            lw[u] = make_uint4(0u, 0u, 0u, 0u);
+            bits[u] = 0u;
 #pragma unroll
-        for (int e = 0; e < P; ++e) qv[u][e] = 0.0f;
-        if (has[u]) {
-            lw[u] = *reinterpret_cast<const uint4 *>(rowp + tok);
+            for (int e = 0; e < P; ++e) qv[u][e] = 0.0f;
+            if (has[u]) {
+                lw[u] = *reinterpret_cast<const uint4 *>(rowp + tok);
 #pragma unroll
-            for (int h = 0; h < P / 4; ++h) {
-                const float4 f = *reinterpret_cast<const float4 *>(qrow + tok + 4 * h);
-                qv[u][4 * h] = f.x;
-                qv[u][4 * h + 1] = f.y;
-                qv[u][4 * h + 2] = f.z;
-                qv[u][4 * h + 3] = f.w;
+                for (int h = 0; h < P / 4; ++h) {
+                    const float4 f = *reinterpret_cast<const float4 *>(qrow + tok + 4 * h);
+                    qv[u][4 * h] = f.x;
+                    qv[u][4 * h + 1] = f.y;
+                    qv[u][4 * h + 2] = f.z;
+                    qv[u][4 * h + 3] = f.w;
+                }
+                bits[u] = 0xffu;
+                if (mb != nullptr) {
+                    const uint32_t byte = mb[tok >> 3];
+                    bits[u] = (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
+                }
             }
-            bits[u] = 0xffu;
-            if (mb != nullptr) {
-                const uint32_t byte = mb[tok >> 3];
-                bits[u] = (P == 8) ? byte : (byte >> (uint32_t(tok) & 4u));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float lv[P];
+            Logit<ET>::unpack(lw[u], lv);
+            float acc = 0.0f;
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                const bool live = ((bits[u] >> e) & 1u) && lv[e] > -INFINITY && !(lv[e] < tau);
+                const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[e], c, -M)) * invS : 0.0f;
+                acc += live ? fmaxf(p - qv[u][e], 0.0f) : 0.0f;
+            }
+            double d = static_cast<double>(acc);  // the line's eight sums, lanes 8j .. 8j + 7
+            d += __shfl_xor(d, 1);
+            d += __shfl_xor(d, 2);
+            d += __shfl_xor(d, 4);
+            const int t = tid + u * kFinalThreads;
+            if ((t & 7) == 0 && t < n * 8) {
+                lsum[t >> 3] = d;
+                lline[t >> 3] = line[u];
             }
         }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        float lv[P];
-        Logit<ET>::unpack(lw[u], lv);
-        float acc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < P; ++e) {
-            const bool live = ((bits[u] >> e) & 1u) && lv[e] > -INFINITY && !(lv[e] < tau);
-            const float p = live ? __builtin_amdgcn_exp2f(fmaf(lv[e], c, -M)) * invS : 0.0f;
-            acc += live ? fmaxf(p - qv[u][e], 0.0f) : 0.0f;
+        lds_barrier();
+        // each block's run of lines, summed in order by the thread at its start
+        for (int i = tid; i < n; i += kFinalThreads) {
+            const int cb = lline[i] / LPB;
+            if (i == 0 || lline[i - 1] / LPB != cb) {
+                double w = 0.0;
+                for (int j = i; j < n && lline[j] / LPB == cb; ++j) w += lsum[j];
+                Wout[cb] = w;
+            }
         }
-        double d = static_cast<double>(acc);  // the line's eight sums, lanes 8j .. 8j + 7
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        d += __shfl_xor(d, 4);
-        const int t = tid + u * kFinalThreads;
-        if ((t & 7) == 0 && t < int(nl) * 8) {
-            lsum[t >> 3] = d;
-            lline[t >> 3] = line[u];
-        }
-    }
-    lds_barrier();
-    constexpr int LPB = (kBlock / (kWave * P)) * 8;
-    // each block's run of lines, summed in list order by the thread at its start
-    for (int i = tid; i < int(nl); i += kFinalThreads) {
-        const int cb = lline[i] / LPB;
-        if (i == 0 || lline[i - 1] / LPB != cb) {
-            double w = 0.0;
-            for (int j = i; j < int(nl) && lline[j] / LPB == cb; ++j) w += lsum[j];
-            Wout[cb] = w;
-        }
+        lds_barrier();  // lsum and lline are reused by the next chunk
     }
 }
 
@@ -4046,16 +4057,18 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             int mode = (n == k) ? kModeP : (DENSE ? kModeDense : kModeOneHot);
             double wdense = 1.0;  // the winning block's residual mass
             Level1 l1 = (mode == kModeOneHot) ? sh.l1x[n] : sh.l1p[n];
-            // a row whose kept tokens the single-pass selection listed by
-            // line: its residual masses come from those lines alone, here
+            // after the single-pass selection (kcount given) the residual
+            // masses come from the lines of the row, here: from the listed
+            // lines that hold a kept token alone, or from every line of a
+            // long row the selection did not list (no grid-wide residual
+            // pass runs then); short unlisted rows stream their blocks below
             uint32_t nl = kNoLineList;
             if (DENSE && mode == kModeDense && a.kcount != nullptr) nl = uniform_load(a.kcount + geo.row0 + n);
-            const bool listed = DENSE && nl != kNoLineList;
+            const bool listed = DENSE && mode == kModeDense && a.kcount != nullptr && (SPLIT || nl != kNoLineList);
             if (listed) {
                 const int64_t row = geo.row0 + n;
-                sparse_block_masses<ET>(a, row, qrow, nl, c, sh.M[n], sh.S[n], a.tau ? a.tau[row] : -INFINITY, sW,
-                                        sW + C, reinterpret_cast<int *>(sW + C + kCandLines));
-                lds_barrier();
+                line_block_masses<ET>(a, row, qrow, nl, c, sh.M[n], sh.S[n], a.tau ? a.tau[row] : -INFINITY, sW,
+                                      sW + C, reinterpret_cast<int *>(sW + C + kCandLines));
                 l1 = residual_level1([&](int, int cb) { return sW[cb]; }, C, key, b, n, &wdense);
             }
             if (DENSE && SPLIT && mode == kModeDense && !listed) {
@@ -4725,7 +4738,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
             : 0;
     hipLaunchKernelGGL(k2, dim3(B), dim3(kFinalThreads), dyn_lds, stream, fa);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;
-    if (fa.split_dense) {
+    if (fa.split_dense && !listed) {
         const DenseFn k3 = bf16 ? pick_dense_mass<uint16_t>(aligned) : pick_dense_mass<float>(aligned);
         const DenseFn k4 = bf16 ? pick_dense_draw<uint16_t>(aligned) : pick_dense_draw<float>(aligned);
         const unsigned gx = static_cast<unsigned>((L.C + kThreads / kWave - 1) / (kThreads / kWave));
