@@ -2037,6 +2037,7 @@ constexpr int kLinesThreads = 256;
 constexpr int kLinesMax = 4096;   // lines of a row, 16 per thread (bf16 V <= 262144, fp32 V <= 131072)
 constexpr int kCandLines = 128;   // candidate lines whose tokens are staged in LDS
 constexpr uint32_t kNoLineList = 0xffffffffu;  // a row whose kept tokens are not listed by line
+constexpr int kResLines = kFinalThreads / 2;   // lines per residual chunk: four groups per finalize thread
 constexpr int kWin = 1024;        // keys in the window histogram
 
 struct LinesShared {
@@ -3170,20 +3171,22 @@ struct DenseSlab {  // one wave's share of a block: P logits and P q values per 
 // lane order, 8 groups of P tokens): with a list (the single-pass
 // selection's lines holding a kept token, nl of them) only those lines, since
 // max(p - q, 0) is zero wherever p is and every other block's W_c is zero;
-// without one (nl = kNoLineList) every line of the row, kCandLines at a time
+// without one (nl = kNoLineList) every line of the row, kResLines at a time
 // (a chunk covers whole blocks).  Eight threads take a line, P tokens each
-// (a chunk's loads all in flight at once, two groups per thread); each sums
-// its tokens in fp32, the line's eight sums meet in fp64, and each block adds
-// its lines in order.  lsum: kCandLines doubles, lline: kCandLines ints of
-// LDS.  All threads call it; rows are 16-byte aligned (the single pass takes
-// no others).
+// (a chunk's loads all in flight at once, four groups per thread); each sums
+// its tokens in fp32 and the line's eight sums meet in fp64.  Each block adds
+// its lines in order: a listed block's run by one thread, a whole block by a
+// wave (its fixed reduction order).  lsum: kResLines doubles, lline:
+// kResLines ints of LDS.  All threads call it; rows are 16-byte aligned (the
+// single pass takes no others).
 template <typename ET>
 __device__ void line_block_masses(const FinalArgs &a, int64_t row, const float *qrow, uint32_t nl, float c,
                                   float M, double S, float tau, double *Wout, double *lsum, int *lline) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int LPB = (kBlock / (kWave * P)) * 8;
-    static_assert(kCandLines * 8 <= 2 * kFinalThreads, "two line groups per thread");
-    static_assert(kCandLines % LPB == 0, "a chunk of lines covers whole blocks");
+    constexpr int U = kResLines * 8 / kFinalThreads;  // line groups per thread
+    static_assert(kCandLines <= kResLines, "a list fits one chunk");
+    static_assert(kResLines % LPB == 0 && kResLines / LPB <= kFinalWaves, "a chunk is whole blocks, a wave each");
     const int tid = threadIdx.x, C = a.C, V = a.V;
     const float invS = static_cast<float>(1.0 / S);
     const ET *rowp = reinterpret_cast<const ET *>(a.logits) + row * V;
@@ -3193,21 +3196,21 @@ __device__ void line_block_masses(const FinalArgs &a, int64_t row, const float *
     const int total = listed ? int(nl) : C * LPB;
     for (int cb = tid; cb < C; cb += kFinalThreads) Wout[cb] = 0.0;
     if (total == 0) lds_barrier();  // (each chunk ends with one)
-    for (int base = 0; base < total; base += kCandLines) {
-        const int n = min(kCandLines, total - base);  // lines of this chunk
-        int line[2];
-        bool has[2];
-        uint4 lw[2];
-        float qv[2][P];
-        uint32_t bits[2];
+    for (int base = 0; base < total; base += kResLines) {
+        const int n = min(kResLines, total - base);  // lines of this chunk
+        int line[U];
+        bool has[U];
+        uint4 lw[U];
+        float qv[U][P];
+        uint32_t bits[U];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int t = tid + u * kFinalThreads;
             has[u] = t < n * 8;
             line[u] = !has[u] ? 0 : (listed ? int(list[t >> 3]) : base + (t >> 3));
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t tok = line_token<ET>(line[u]) + ((tid + u * kFinalThreads) & 7) * P;
             has[u] = has[u] && tok < V;
             lw[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -3232,7 +3235,7 @@ __device__ void line_block_masses(const FinalArgs &a, int64_t row, const float *
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
             float lv[P];
             Logit<ET>::unpack(lw[u], lv);
             float acc = 0.0f;
@@ -3253,13 +3256,22 @@ __device__ void line_block_masses(const FinalArgs &a, int64_t row, const float *
             }
         }
         lds_barrier();
-        // each block's run of lines, summed in order by the thread at its start
-        for (int i = tid; i < n; i += kFinalThreads) {
-            const int cb = lline[i] / LPB;
-            if (i == 0 || lline[i - 1] / LPB != cb) {
-                double w = 0.0;
-                for (int j = i; j < n && lline[j] / LPB == cb; ++j) w += lsum[j];
-                Wout[cb] = w;
+        if (listed) {
+            // each block's run of lines, summed in order by the thread at its start
+            for (int i = tid; i < n; i += kFinalThreads) {
+                const int cb = lline[i] / LPB;
+                if (i == 0 || lline[i - 1] / LPB != cb) {
+                    double w = 0.0;
+                    for (int j = i; j < n && lline[j] / LPB == cb; ++j) w += lsum[j];
+                    Wout[cb] = w;
+                }
+            }
+        } else {
+            // whole blocks (n is a multiple of LPB): block w of the chunk by wave w
+            const int wave = wave_id(), lane = tid & (kWave - 1);
+            if (wave * LPB < n) {
+                const double w = wave_sum_d(lane < LPB ? lsum[wave * LPB + lane] : 0.0);
+                if (lane == 0) Wout[(base + wave * LPB) / LPB] = w;
             }
         }
         lds_barrier();  // lsum and lline are reused by the next chunk
@@ -4068,7 +4080,7 @@ __global__ __launch_bounds__(kFinalThreads) void finalize_kernel(FinalArgs a) {
             if (listed) {
                 const int64_t row = geo.row0 + n;
                 line_block_masses<ET>(a, row, qrow, nl, c, sh.M[n], sh.S[n], a.tau ? a.tau[row] : -INFINITY, sW,
-                                      sW + C, reinterpret_cast<int *>(sW + C + kCandLines));
+                                      sW + C, reinterpret_cast<int *>(sW + C + kResLines));
                 l1 = residual_level1([&](int, int cb) { return sW[cb]; }, C, key, b, n, &wdense);
             }
             if (DENSE && SPLIT && mode == kModeDense && !listed) {
@@ -4734,7 +4746,7 @@ extern "C" int sd_verify(const void *target_logits, const int32_t *draft_token_i
     }
     const size_t dyn_lds =
         (draft_probs && (!fa.split_dense || listed))
-            ? size_t(L.C) * sizeof(double) + (listed ? size_t(kCandLines) * (sizeof(double) + sizeof(int)) : 0)
+            ? size_t(L.C) * sizeof(double) + (listed ? size_t(kResLines) * (sizeof(double) + sizeof(int)) : 0)
             : 0;
     hipLaunchKernelGGL(k2, dim3(B), dim3(kFinalThreads), dyn_lds, stream, fa);
     if (hipGetLastError() != hipSuccess) return SD_ERR_HIP;

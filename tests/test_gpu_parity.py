@@ -286,18 +286,20 @@ def test_dense_residual_from_listed_lines(V, dtype):
     lists by line draw the residual from those lines alone, beside rows it
     does not list (top-k 0, more candidate lines than it stages) in the same
     call; with and without top-p and a mask, rows of 20 blocks (residual
-    inside the finalize kernel) and 35 blocks (the grid-wide residual for
-    the rows not listed)."""
-    announce(f"dense residual from listed lines V={V} dtype={dtype}")
+    inside the finalize kernel) and 35 blocks (the grid-wide residual for the
+    rows not listed, on a grid of fewer request rows than requests, each
+    taking a stripe of them)."""
+    B = 48 if V < 65536 else 160
+    announce(f"dense residual from listed lines B={B} V={V} dtype={dtype}")
     for masked in (False, True):
-        wl = _custom(48, 4, V, dtype=dtype, dense=True, masked=masked, greedy_frac=0.1, density=0.5,
+        wl = _custom(B, 4, V, dtype=dtype, dense=True, masked=masked, greedy_frac=0.1, density=0.5,
                      seed=41 + masked, x_argmax_frac=0.2, top_k=(0, 1, 5, 50, 400))
         assert_parity(run_gpu(wl), run_oracle(wl))
         g = torch.Generator(device=DEV)
         g.manual_seed(43 + masked)
-        wl["top_p"] = torch.where(torch.rand(48, generator=g, device=DEV) < 0.5,
-                                  torch.rand(48, generator=g, device=DEV) * 0.9 + 0.05,
-                                  torch.zeros(48, device=DEV)).contiguous()
+        wl["top_p"] = torch.where(torch.rand(B, generator=g, device=DEV) < 0.5,
+                                  torch.rand(B, generator=g, device=DEV) * 0.9 + 0.05,
+                                  torch.zeros(B, device=DEV)).contiguous()
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
