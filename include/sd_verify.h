@@ -185,7 +185,7 @@ int sd_verify(const void *target_logits, const int32_t *draft_token_ids,
 
 /* Bytes of the static device scratch behind sd_verify_noalloc: every call
  * whose sd_verify_workspace_size is at most this fits (the B=512, k=12,
- * V=151936 long-draft shape with top-k needs about 41 MB). */
+ * V=151936 long-draft shape with top-k needs about 42 MB). */
 #define SD_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* sd_verify for callers that cannot allocate device memory: code under HIP

@@ -7,11 +7,11 @@
 //                  for its LDS: checks the draft offsets and maps every
 //                  packed row to its request (otherwise the sweep's
 //                  workgroups do both themselves).
-//   [topk]         calls with top-p, and top-k calls whose rows the
-//                  single-pass selection cannot take (unaligned rows, very
-//                  large V): each top-k / top-p row's threshold tau, from a
-//                  pass over the row before the sweep (bf16 rows counted on
-//                  their raw 16-bit codes).
+//   [topk]         calls with top-p and no top-k, and top-k calls whose rows
+//                  the single-pass selection cannot take (unaligned rows,
+//                  very large V): each top-k / top-p row's threshold tau,
+//                  from a pass over the row before the sweep (bf16 rows
+//                  counted on their raw 16-bit codes).
 //   row_stats      the sweep, the only full pass over the logits: waves claim
 //                  2048-token blocks of all rows, stream them from HBM in
 //                  16-byte loads, apply the grammar bitmask and temperature
@@ -22,13 +22,17 @@
 //                      Sc = sum_j 2^(l_j * c - Mc), c = log2(e) / T, and the
 //                      block's level-1 Gumbel key;
 //                    greedy rows:   (max_j l_j, lowest index of that max);
-//                    sampling rows of a single-pass top-k call: the code of
-//                      every 128-byte line's largest allowed logit instead;
+//                    sampling rows of a single-pass top-k / top-p call: the
+//                      code of every 128-byte line's largest allowed logit
+//                      instead;
 //                  plus each draft row's record: l(x), the mask bit, q(x) and
 //                  the draft block's mass without the draft.
-//   [topk_lines]   single-pass top-k: each row's tau from the line maxima and
-//                  the few lines that can hold kept tokens, then the row's
-//                  block statistics over the kept tokens.
+//   [topk_lines]   single-pass top-k (and top-p after it): each row's tau
+//                  from the line maxima and the few lines that can hold kept
+//                  tokens, then the row's block statistics over the kept
+//                  tokens and, with dense drafts, the list of the lines that
+//                  hold a kept token (the only lines a residual draw from the
+//                  row can weigh).
 //   finalize       one 512-thread workgroup per request: folds the block
 //                  statistics into each row's max and normaliser, forms p(x)
 //                  and q(x), draws the accept uniforms from Philox, finds the
@@ -37,12 +41,15 @@
 //                  residual max(p - q, 0), from p without the draft (one-hot
 //                  drafts, infra-guide 5.2 section 4.3) or from p at the bonus
 //                  position by two-level Gumbel-max: level 1 over block
-//                  masses, level 2 over the chosen block's 2048 tokens.  It
+//                  masses, level 2 over the chosen block's 2048 tokens.  A
+//                  dense residual sums the listed lines after the single-pass
+//                  selection, otherwise the rejected row (short rows).  It
 //                  writes the outputs and adds R, I, D, A (fanout, "Name the
 //                  three counters") through a slot tally.
-//   [dense_mass,   dense drafts over long rows: the residual's block masses
-//    dense_draw]   of every rejected row on a grid of (block, request)
-//                  workgroups, then its draw.
+//   [dense_mass,   dense drafts over long rows, without the single-pass
+//    dense_draw]   selection: the residual's block masses of every rejected
+//                  row on a grid of (block, request) workgroups, then its
+//                  draw.
 //   [histogram]    requests per accepted length, when asked for.
 #include <hip/hip_runtime.h>
 #include <float.h>
