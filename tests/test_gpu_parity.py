@@ -303,6 +303,51 @@ def test_dense_residual_from_listed_lines(V, dtype):
         assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+@pytest.mark.parametrize("cut", ["top_k", "top_k_top_p"])
+def test_chi_square_listed_residual(cut):
+    """Emitted tokens follow the cut target law when the residual comes from
+    the lines the single-pass selection lists: bf16 rows of two blocks
+    (V=4096), the kept tokens spread over several lines of both, dense q
+    spread over the whole row, so that most positions reject and resample."""
+    from scipy import stats
+    from oracle import verify as ov
+    announce(f"chi-square of the listed-line residual ({cut})")
+    B, k, V = 50000, 2, 4096
+    g = torch.Generator(device="cpu")
+    g.manual_seed(23)
+    l1 = torch.randn((k + 1, V), generator=g).to(torch.bfloat16)
+    allowed = torch.ones((k + 1, V), dtype=torch.bool)
+    T = 0.9
+    top_k = 20 if cut == "top_k" else 30
+    top_p = 0.8 if cut == "top_k_top_p" else 0.0
+    p = np.array([ov.target_distribution(l1[i].double().numpy(), allowed[i].numpy(), T, top_k, top_p)[0]
+                  for i in range(k + 1)])
+    q1 = torch.softmax(torch.randn((k, V), generator=g), -1)
+    x = torch.stack([torch.multinomial(q1[i], B, replacement=True, generator=g) for i in range(k)], 1)
+    wl = {"logits": l1.expand(B, k + 1, V).contiguous().to(DEV),
+          "draft_token_ids": x.to(torch.int32).to(DEV),
+          "draft_probs": q1.expand(B, k, V).contiguous().to(DEV),
+          "bitmask": None,
+          "temperature": torch.full((B,), T, device=DEV),
+          "top_k": torch.full((B,), top_k, dtype=torch.int32, device=DEV),
+          "top_p": torch.full((B,), top_p, device=DEV) if top_p else None,
+          "seed": 2025}
+    runs = [run_gpu(wl, seed=2025 + r) for r in range(4)]
+    tok = np.concatenate([g["out_tokens"] for g in runs])
+    na = np.concatenate([g["out_num_accepted"] for g in runs])
+    assert (na == 0).mean() > 0.5  # most draws are residual draws
+    for i in range(k + 1):
+        sel = na >= i
+        counts = np.bincount(tok[sel, i], minlength=V)
+        assert counts[p[i] == 0].sum() == 0
+        if sel.sum() < 2000:  # too few requests reach this position for the test
+            continue
+        live = p[i] > 0
+        assert live.sum() >= 10
+        pv = stats.chisquare(counts[live], p[i][live] * counts[live].sum()).pvalue
+        assert pv > 1e-3, (cut, i, pv)
+
+
 def test_top_p_extreme_temperatures_masks_and_errors():
     """Top-p at temperatures that push masses to underflow or make them all
     alike, on masked rows, beside greedy requests and requests in error."""
