@@ -448,6 +448,19 @@ def test_long_k_with_top_p_scaled():
     assert_parity(run_gpu(wl), run_oracle(wl))
 
 
+def test_long_k_top_p_full_every_request():
+    """The full long_k call with top-p 0.9 on every request (the cut read off
+    the single pass's token window, the residual from the listed lines),
+    every request against the oracle."""
+    announce("long_k full B=512 k=12 V=151936 top-k 50 top-p 0.9, every request against the oracle")
+    wl = make_workload("long_k", device=DEV)
+    wl["top_p"] = torch.full((512,), 0.9, device=DEV)
+    gpu = run_gpu(wl)
+    orc = run_oracle_parallel(wl)
+    assert_parity(gpu, orc)
+    assert int(gpu["counters"][3]) == int(orc["counters"][3]) and gpu["status"] == 0
+
+
 # ------------------------------------------------------- shapes and variants
 
 @pytest.mark.parametrize("V", [1, 7, 8, 1001, 2047, 2048, 2049, 6144, 6150])
