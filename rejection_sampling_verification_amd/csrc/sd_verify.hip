@@ -2631,7 +2631,7 @@ __device__ __forceinline__ uint32_t code32_of_line(uint32_t c) {
 // by passes over the row; rows of requests with top-p alone (top-k 0) take the
 // passes and their block statistics from global memory.
 template <typename ET, bool MASKED, bool TOPP>
-__global__ __launch_bounds__(kLinesThreads) void topk_lines_kernel(LinesArgs a) {
+__global__ __launch_bounds__(kLinesThreads) __attribute__((amdgpu_waves_per_eu(6))) void topk_lines_kernel(LinesArgs a) {
     constexpr int P = Logit<ET>::kPer16;
     constexpr int G = kBlock / (kWave * P);
     constexpr int LPB = G * 8;            // lines per block
