@@ -43,7 +43,8 @@
 //                  position by two-level Gumbel-max: level 1 over block
 //                  masses, level 2 over the chosen block's 2048 tokens.  A
 //                  dense residual sums the listed lines after the single-pass
-//                  selection, otherwise the rejected row (short rows).  It
+//                  selection (every line of a long row it did not list), and
+//                  otherwise the rejected row of a short row here.  It
 //                  writes the outputs and adds R, I, D, A (fanout, "Name the
 //                  three counters") through a slot tally.
 //   [dense_mass,   dense drafts over long rows, without the single-pass
