@@ -103,6 +103,19 @@ def test_workspace_size():
     assert ws >= rows * C * 8 + rows * 4 and ws % 256 == 0
 
 
+def test_workspace_size_with_top_k():
+    """A top-k array adds the line maxima (2 bytes per 64 bf16 tokens of every
+    row) and each row's list of kept lines (128 two-byte entries and a count);
+    the long-draft shape with top-k still fits the allocation-free scratch."""
+    import rejection_sampling_verification_amd as sdv
+    B, k, V = 512, 12, 151936
+    rows, C = B * (k + 1), -(-V // 2048)
+    plain = sdv.sd_verify_workspace_size(B, k, V)
+    with_k = sdv.sd_verify_workspace_size(B, k, V, top_k=True)
+    assert with_k - plain >= rows * C * 32 * 2 + rows * (128 * 2 + 4)
+    assert with_k % 256 == 0 and with_k <= 64 << 20
+
+
 def test_host_argument_checks_return_before_any_launch():
     import rejection_sampling_verification_amd as sdv
     lib = sdv.library()
