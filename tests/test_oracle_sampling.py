@@ -343,6 +343,28 @@ def test_two_level_gumbel_chi_square(block):
     assert _chi2_ok(counts, r / r.sum())
 
 
+@pytest.mark.parametrize("top_k,top_p", [(20, 0.0), (0, 0.7), (50, 0.9), (1, 0.0)])
+def test_dense_residual_lives_on_the_kept_set(top_k, top_p):
+    """With a top-k or top-p cut, p is zero outside the kept tokens, so the
+    dense residual max(p - q, 0) is too: the residual over the kept tokens
+    alone equals the residual over the whole row (what the kernels' listed
+    lines rely on), for q spread over every token."""
+    rng = np.random.default_rng(71 + top_k)
+    V = 5000
+    for _ in range(5):
+        l = rng.normal(0.0, 2.0, V)
+        allowed = rng.random(V) < 0.8
+        p, _ = ov.target_distribution(l, allowed, 0.8, top_k, top_p)
+        q = special.softmax(rng.normal(0.0, 1.0, V))
+        r = ov.residual_weights(p, q, -1, one_hot=False)
+        kept = p > 0
+        assert kept.sum() < allowed.sum()  # the cut removes tokens
+        assert np.all(r[~kept] == 0.0)
+        r_kept = np.zeros(V)
+        r_kept[kept] = np.maximum(p[kept] - q[kept], 0.0)
+        assert np.array_equal(r, r_kept)
+
+
 def test_one_hot_equals_explicit_one_hot_q():
     rng = np.random.default_rng(30)
     B, k, V = 120, 4, 300
